@@ -1,0 +1,330 @@
+#!/usr/bin/env python3
+"""Benchmark of the gradient all-reduce on one MI355X.
+
+One step = one all-reduce of the workload (default: 40 virtual ranks of 300M
+fp32 gradients each, 48 GB, 64 equal buckets issued last-first, each gated
+by its own ready event on the library's side stream), inputs resident in HBM.
+Prints one JSON line: achieved HBM GB/s (the algorithmic bytes of the fused
+pass, every rank's input read once and its result written once, over the
+step time), the roofline of the dominant kernel from HIP events around each
+of its launches, the CPU oracle timed on a bounded sample of the same
+workload, and side measurements (step-by-step mode, overlap with a streaming
+compute kernel).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s and % of peak per all-reduce (300M fp32, P=40 ring)"
+PEAK_HBM_GBPS = 8000.0
+FUSED_KERNEL = "fused_kernel"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    with open(os.path.join(ROOT, "sgd_gradient_all_amd", "csrc", "kernels.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload, mode):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{FUSED_KERNEL}_{workload}_traffic.json")
+    if mode != "fused" or not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="ring_p40_300m_64b")
+    ap.add_argument("--mode", default="fused", choices=["fused", "stepwise"])
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the step-by-step and overlap measurements")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-buckets", type=int, default=20,
+                    help="buckets of the workload the CPU oracle is timed on")
+    ap.add_argument("--calib-copy-gib", type=float, default=0.0,
+                    help="also run one plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: the all-reduce runs P virtual ranks on a single "
+              f"MI355X, so --gpus {args.gpus} (WORLD_SIZE={world}) is not supported; "
+              f"run with --gpus 1", flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sgd_gradient_all_amd as ddl
+    import synth
+    from synth.workloads import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    tdt = torch.float32 if w.dtype == "f32" else torch.float16
+    sdt = synth.F32 if w.dtype == "f32" else synth.F16
+    torch.cuda.set_device(0)
+    dev_name = torch.cuda.get_device_name(0)
+    log(f"bench: {w.name} ({w.description}) on {dev_name}, mode={args.mode}")
+
+    # inputs, generated in HBM
+    bufs = [torch.empty(w.n, dtype=tdt, device="cuda") for _ in range(w.P)]
+    for r, b in enumerate(bufs):
+        synth.fill_device(b.data_ptr(), w.n, sdt, w.dist, w.seed, r, sigma=w.sigma)
+    torch.cuda.synchronize()
+    log("bench: inputs ready")
+
+    topo = ddl.topo(w.topo, w.k, w.rows, w.cols)
+    buckets = w.bucket_list()
+    main_stream = torch.cuda.current_stream()
+
+    def make_events():
+        return [torch.cuda.Event() for _ in buckets] if w.side_stream else None
+
+    def record_all(evs):
+        if evs:
+            for e in evs:
+                e.record(main_stream)
+
+    def timed(plan, steps, warmup):
+        evs = make_events()
+        for _ in range(warmup):
+            record_all(evs)
+            plan.execute(bufs, events=evs, stream=main_stream)
+        torch.cuda.synchronize()
+        plan.profile_read()  # drop the warm-up launches
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(main_stream)
+        for _ in range(steps):
+            record_all(evs)
+            plan.execute(bufs, events=evs, stream=main_stream)
+        t1.record(main_stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        kms, launches, kmax = plan.profile_read()
+        return ms, kms, launches, kmax
+
+    plan = ddl.Plan(w.P, w.n, w.dtype, w.op, topo, buckets, args.mode)
+    plan.set_profiling(True)
+    _, hbm_bytes = plan.traffic()
+    ms, kms, launches, kmax = timed(plan, args.steps, args.warmup)
+    value = hbm_bytes / (ms * 1e-3) / 1e9
+    launches_per_step = launches / args.steps
+    avg_launch_ms = kms / launches
+    bytes_per_launch = hbm_bytes / launches_per_step
+    achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
+    log(f"bench: {ms:.3f} ms/step, {value:.1f} GB/s; {launches_per_step:.0f} launches/step, "
+        f"avg {avg_launch_ms * 1e3:.1f} us, kernel-side {achieved:.1f} GB/s")
+    esize = 4 if w.dtype == "f32" else 2
+    bus_bw = 2 * (w.P - 1) / w.P * w.n * esize / (ms * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded counter-based generator, generated in HBM)",
+        "config": {"workload": w.name, "P": w.P, "n": w.n, "topology": w.topo, "k": w.k,
+                   "rows": w.rows, "cols": w.cols, "op": w.op, "buckets": len(buckets),
+                   "side_stream": w.side_stream, "mode": args.mode,
+                   "bytes_per_step": hbm_bytes},
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
+        "bus_bw_GBps": round(bus_bw, 2),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": FUSED_KERNEL if args.mode == "fused" else "step_kernel",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": measured_traffic(w.name, args.mode),
+            "launches_per_step": launches_per_step,
+            "avg_launch_us": round(avg_launch_ms * 1e3, 2),
+            "max_launch_us": round(kmax * 1e3, 2),
+            "algorithmic_bytes_per_launch": int(bytes_per_launch),
+        },
+        "device": dev_name,
+    }
+    plan.destroy()
+
+    if args.calib_copy_gib > 0:
+        nel = int(args.calib_copy_gib * (1 << 30) / 4)
+        a = torch.empty(nel, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1.0)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        result["calib_copy_bytes"] = 2 * nel * 4
+        del a, b
+
+    if not args.no_extras:
+        result.update(extras(args, w, bufs, topo, buckets, main_stream, torch, ddl, synth,
+                             hbm_bytes, ms))
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, w, topo, torch, ddl, synth, np)
+
+    print(json.dumps(result), flush=True)
+
+
+def extras(args, w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_bytes, fused_ms):
+    out = {}
+    # the step-by-step schedule on the same buffers
+    plan = ddl.Plan(w.P, w.n, w.dtype, w.op, topo, buckets, "stepwise")
+    plan.set_profiling(True)
+    _, sbytes = plan.traffic()
+    evs = [torch.cuda.Event() for _ in buckets] if w.side_stream else None
+    for _ in range(1):
+        if evs:
+            for e in evs:
+                e.record(main_stream)
+        plan.execute(bufs, events=evs, stream=main_stream)
+    torch.cuda.synchronize()
+    plan.profile_read()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    steps = 3
+    t0.record(main_stream)
+    for _ in range(steps):
+        if evs:
+            for e in evs:
+                e.record(main_stream)
+        plan.execute(bufs, events=evs, stream=main_stream)
+    t1.record(main_stream)
+    torch.cuda.synchronize()
+    sms = t0.elapsed_time(t1) / steps
+    kms, launches, _ = plan.profile_read()
+    out["stepwise"] = {"ms_per_step": round(sms, 3),
+                       "hbm_GBps": round(sbytes / (sms * 1e-3) / 1e9, 1),
+                       "bytes_per_step": sbytes,
+                       "launches_per_step": launches // steps,
+                       "kernel_GBps": round(sbytes * steps / (kms * 1e-3) / 1e9, 1)}
+    plan.destroy()
+    log(f"bench: stepwise {sms:.3f} ms/step")
+
+    if w.side_stream:
+        # overlap with a streaming compute kernel standing in for the rest of
+        # back-propagation: 0.925 x the all-reduce's bytes (the Baidu
+        # article's ~370 ms compute vs ~400 ms communication), in one slice
+        # per bucket; bucket b waits for slice b
+        nb = len(buckets)
+        comp_elems = int(0.925 * fused_bytes / 8) // (4 * nb) * (4 * nb)
+        free = torch.cuda.mem_get_info()[0]
+        if comp_elems * 4 > free * 0.9:
+            comp_elems = int(free * 0.9 / 4) // (4 * nb) * (4 * nb)
+        scratch = torch.zeros(comp_elems, dtype=torch.float32, device="cuda")
+        per = comp_elems // nb
+        cs = main_stream.cuda_stream
+
+        def compute_slices(evs):
+            for i in range(nb):
+                synth.stream_compute(scratch.data_ptr() + 4 * i * per, per, 1.0, 0.0, cs)
+                if evs is not None:
+                    evs[i].record(main_stream)
+
+        plan = ddl.Plan(w.P, w.n, w.dtype, w.op, topo, buckets, "fused")
+        evs = [torch.cuda.Event() for _ in buckets]
+        compute_slices(None)
+        torch.cuda.synchronize()
+        reps = 3
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(main_stream)
+        for _ in range(reps):
+            compute_slices(None)
+        t1.record(main_stream)
+        torch.cuda.synchronize()
+        t_comp = t0.elapsed_time(t1) / reps
+        compute_slices(evs)
+        plan.execute(bufs, events=evs, stream=main_stream)
+        torch.cuda.synchronize()
+        t0.record(main_stream)
+        for _ in range(reps):
+            compute_slices(evs)
+            plan.execute(bufs, events=evs, stream=main_stream)
+        t1.record(main_stream)
+        torch.cuda.synchronize()
+        t_both = t0.elapsed_time(t1) / reps
+        comp_bytes = 2 * 4 * comp_elems
+        out["overlap"] = {
+            "t_allreduce_ms": round(fused_ms, 3), "t_compute_ms": round(t_comp, 3),
+            "t_both_ms": round(t_both, 3),
+            "overlap_efficiency": round((fused_ms + t_comp - t_both) / min(fused_ms, t_comp), 3),
+            "combined_hbm_GBps": round((fused_bytes + comp_bytes) / (t_both * 1e-3) / 1e9, 1),
+            "compute_bytes": comp_bytes,
+        }
+        plan.destroy()
+        del scratch
+        torch.cuda.empty_cache()
+        log(f"bench: overlap {out['overlap']}")
+    return out
+
+
+def cpu_baseline(args, w, topo, torch, ddl, synth, np):
+    """The CPU oracle as it stands, single-threaded, on the first buckets (in
+    issue order) of the same workload; inputs generated on the GPU by the
+    same seeded generator and copied to the host.  The GPU result of a fresh
+    all-reduce of each sampled bucket is compared with the oracle's."""
+    import oracle as orc
+    kinds = {"ring": orc.RING, "multiring": orc.MULTIRING, "torus2d": orc.TORUS2D}
+    sdt = synth.F32 if w.dtype == "f32" else synth.F16
+    tdt = torch.float32 if w.dtype == "f32" else torch.float16
+    sample = w.bucket_list()[:max(1, args.cpu_buckets)]
+    secs, nbytes, mismatched = 0.0, 0, 0
+    for off, cnt in sample:
+        dev = [torch.empty(cnt, dtype=tdt, device="cuda") for _ in range(w.P)]
+        for r, t in enumerate(dev):
+            synth.fill_device(t.data_ptr(), cnt, sdt, w.dist, w.seed, r, first=off,
+                              sigma=w.sigma)
+        torch.cuda.synchronize()
+        host = [t.cpu().numpy() for t in dev]
+        plan = ddl.Plan(w.P, cnt, w.dtype, w.op, topo, None, "fused")
+        plan.execute(dev)
+        torch.cuda.synchronize()
+        plan.destroy()
+        t0 = time.perf_counter()
+        orc.allreduce(host, op=orc.MEAN if w.op == "mean" else orc.SUM, kind=kinds[w.topo],
+                      k=w.k, rows=w.rows, cols=w.cols)
+        secs += time.perf_counter() - t0
+        nbytes += 2 * w.P * cnt * (4 if w.dtype == "f32" else 2)
+        got = dev[0].cpu().numpy()
+        mismatched += int(np.count_nonzero(got.view(np.uint8) != host[0].view(np.uint8)))
+        del dev, host
+    log(f"bench: cpu oracle {nbytes / secs / 1e9:.2f} GB/s over {len(sample)} buckets, "
+        f"{secs:.1f} s")
+    return {"value": round(nbytes / secs / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{len(sample)} of {len(w.bucket_list())} buckets in issue order "
+                      f"({w.P} ranks x {sample[0][1]} elements each), single-threaded C, "
+                      f"same algorithmic bytes as the GPU figure",
+            "seconds": round(secs, 2),
+            "host_cpus": os.cpu_count(),
+            "bytes_differing_from_gpu": mismatched}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,204 @@
+/*
+ * ddl.h -- C ABI of libddl.so, the MI355X (gfx950) gradient all-reduce.
+ *
+ * The operation (Baidu Ring-Allreduce article, part 4, section "总结";
+ * Sony "224秒训练ResNet-50" article, the paragraph on synchronising and
+ * averaging gradients): P equal-length gradient buffers are summed -- or
+ * averaged -- so that every rank ends with the same values.  The all-reduce
+ * runs on subsets of the parameters, and the subsets of the output layer go
+ * first so that communication overlaps the rest of back-propagation (same
+ * Baidu article, its opening paragraphs).  The pages ship the algorithm as a
+ * C library that any framework or MPI program can embed (Baidu article,
+ * "总结"; IBM DDL blog, last paragraph; "[论文解读] PowerAI DDL", ABSTRACT);
+ * this is that library for one GPU that holds the buffers of P virtual ranks.
+ *
+ * Schedules:
+ *  - DDL_RING: ring reduce-scatter then ring all-gather (Baidu article,
+ *    "总结" and its reference 4, Patarasuk & Yuan).  Chunk c of a segment
+ *    of L elements is piece c of split(L, P, q) (below); in reduce-scatter
+ *    step t = 0..P-2 ring position x sends chunk (x-t) mod P to position x+1,
+ *    which adds it to its own; in all-gather step t position x sends chunk
+ *    (x+1-t) mod P to x+1, which keeps it.
+ *  - DDL_MULTIRING: k rings ("[论文解读] PowerAI DDL", ABSTRACT and
+ *    "提出的方法"); every bucket is split into k parts by split(L, k, q) and
+ *    part j goes round ring j.
+ *  - DDL_TORUS2D: rows x cols grid, rank (i, j) = i*cols + j (Sony article,
+ *    "2D-Torus All-reduce", Fig. 1 and Fig. 2): ring reduce-scatter along
+ *    each row over split(L, cols, q); ring all-reduce down column j over
+ *    row-chunk (j+1) mod cols, split into rows sub-chunks; ring all-gather
+ *    along each row.
+ * split(L, m, q): piece c is [b_c, b_{c+1}), b_c = min(L, q*floor(c*ceil(L/q)/m)),
+ * b_m = L, with q = 16 bytes / element size, so every piece of an aligned
+ * segment starts on a 16-byte boundary.
+ *
+ * Arithmetic: DDL_F32 adds in binary32, round to nearest even, subnormals
+ * kept.  DDL_F16 stores and exchanges binary16 (Sony article, "训练设置":
+ * FP16 gradient exchange): every step computes in binary32 and rounds the
+ * result to binary16 (nearest even).  DDL_MEAN divides once by P, correctly
+ * rounded, at the add that completes each chunk's sum, before any copy.
+ * Results are bit-identical between DDL_STEPWISE and DDL_FUSED, independent
+ * of bucket issue order, and identical on every rank.
+ *
+ * Ownership: the caller owns the buffers (device memory, in place), streams
+ * and events.  A plan owns its host and device tables and one side stream;
+ * it allocates device memory once, on its first execution, never per call.
+ *
+ * Errors: every entry point returns DDL_OK (0) or a negative DDL_E_* code;
+ * arguments are validated before anything is enqueued, so a failed call
+ * enqueues no work.  No C++ exception crosses this interface.
+ */
+#ifndef DDL_H
+#define DDL_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Largest P a plan accepts (the rank pointers travel as kernel arguments). */
+#define DDL_MAX_RANKS 128
+
+typedef enum { DDL_F32 = 0, DDL_F16 = 1 } ddl_dtype;
+typedef enum { DDL_SUM = 0, DDL_MEAN = 1 } ddl_op;
+typedef enum { DDL_RING = 0, DDL_MULTIRING = 1, DDL_TORUS2D = 2 } ddl_topo_kind;
+
+/* DDL_STEPWISE launches one kernel per schedule step (every pair of every
+ * ring, and every bucket of a group, in that one launch).  DDL_FUSED makes
+ * one pass per bucket group: each element is read once from every rank,
+ * summed in the order the schedule would sum it, and written to every rank. */
+typedef enum { DDL_STEPWISE = 0, DDL_FUSED = 1 } ddl_mode;
+
+typedef struct {
+    int kind;              /* ddl_topo_kind */
+    int k;                 /* DDL_MULTIRING: number of rings (>= 1) */
+    int rows, cols;        /* DDL_TORUS2D: rows * cols == P */
+    const int *ring_order; /* NULL = identity; else P ints (DDL_RING) or k*P
+                              (DDL_MULTIRING): ring j puts rank
+                              ring_order[j*P + x] at position x.  Each ring must
+                              be a permutation of 0..P-1.  Must be NULL for
+                              DDL_TORUS2D.  Copied at plan creation. */
+} ddl_topo;
+
+typedef struct {
+    size_t offset;         /* first element of the bucket */
+    size_t count;          /* elements (0 allowed: nothing to do) */
+    void *ready_event;     /* hipEvent_t the bucket waits for, or NULL: ready
+                              when the call is made on the caller's stream */
+} ddl_bucket;
+
+typedef struct ddl_plan_s *ddl_plan;
+
+enum {
+    DDL_OK = 0,
+    DDL_E_NULL = -1,     /* a required pointer is NULL */
+    DDL_E_ARG = -2,      /* P, n, dtype, op, mode or topology out of range */
+    DDL_E_BUCKETS = -3,  /* buckets do not tile [0, n) exactly */
+    DDL_E_ALIGN = -4,    /* a rank buffer is not 16-byte aligned */
+    DDL_E_HIP = -5,      /* a HIP runtime call failed */
+    DDL_E_NOMEM = -6,    /* host or device allocation failed */
+    DDL_E_BUSY = -7,     /* the plan still has work in flight */
+    DDL_E_DEVICE = -8    /* executed on a device other than the plan's */
+};
+
+/* Build the schedule for P ranks of n elements each.  buckets[0..nbuckets)
+ * is the issue order (output layer first for back-propagation overlap) and
+ * must tile [0, n) without gap or overlap; their ready_event fields are not
+ * used here.  Bucket offsets that are not a multiple of q = 16 B / element
+ * size are accepted but run on a slower element-wise path.  Host-only: no
+ * HIP call is made, so a plan can be built and inspected without a GPU. */
+int ddl_plan_create(ddl_plan *out, int P, size_t n, ddl_dtype dtype, ddl_op op,
+                    const ddl_topo *topo, const ddl_bucket *buckets, int nbuckets,
+                    ddl_mode mode);
+
+/* Enqueue the all-reduce of bufs[0..P) (device pointers, each 16-byte
+ * aligned, n elements) on the current HIP device.
+ *  ready_events  NULL, or nbuckets hipEvent_t (entries may be NULL) in bucket
+ *                list order: bucket b's work waits for ready_events[b].
+ *  stream        the caller's hipStream_t (NULL = default stream).  Buckets
+ *                without an event wait for the work already enqueued on it.
+ *  done_event    NULL or a hipEvent_t recorded when every bucket is done.
+ * Buckets with events run on the plan's side stream, in list order; the
+ * caller's stream is made to wait for the whole all-reduce before its next
+ * work.  Asynchronous: returns after enqueueing; do not touch bufs until
+ * done_event completes or the stream is synchronised.  The first call on a
+ * plan uploads its tables (a synchronous copy, once).  Concurrent calls on
+ * one plan are serialised by a mutex; calls on different plans that share
+ * buffers race. */
+int ddl_plan_execute(ddl_plan plan, void *const *bufs, void *const *ready_events,
+                     void *stream, void *done_event);
+
+/* One-shot form: looks up (or builds and caches) the plan for these
+ * arguments -- the cache key is everything except the buffers and events --
+ * and executes it with the buckets' ready_event fields.  Thread-safe. */
+int ddl_allreduce(void *const *bufs, int P, size_t n, ddl_dtype dtype, ddl_op op,
+                  const ddl_topo *topo, const ddl_bucket *buckets, int nbuckets,
+                  ddl_mode mode, void *stream, void *done_event);
+
+/* Traffic of the schedule.  sent_elems_per_rank (NULL or P entries): the
+ * elements each rank sends over the whole schedule, 2 (P-1)/P * n for a ring
+ * when P*q divides every bucket (Patarasuk & Yuan's bandwidth-optimal
+ * count; the Baidu article's "1.2 GB gradient -> about 2.4 GB sent and
+ * received").  hbm_bytes (NULL allowed): the HBM bytes the plan's kernels
+ * read plus write per execution -- 2 P n s for DDL_FUSED, 5 (P-1) n s for
+ * DDL_STEPWISE (3 L s per reduce-scatter step, 2 L s per all-gather step). */
+int ddl_plan_traffic(ddl_plan plan, size_t *sent_elems_per_rank, size_t *hbm_bytes);
+
+/* Free the plan.  Returns DDL_E_BUSY, and frees nothing, while work the plan
+ * enqueued has not completed. */
+int ddl_plan_destroy(ddl_plan plan);
+
+/* Drop every plan ddl_allreduce cached (DDL_E_BUSY if one is in flight). */
+int ddl_cache_clear(void);
+
+/* Static text for a DDL_* code. */
+const char *ddl_strerror(int code);
+
+/* ---- merging of ready buckets ------------------------------------------ *
+ * IBM's multi-ring trades latency against bandwidth ("[论文解读] PowerAI
+ * DDL", ABSTRACT).  At execution consecutive buckets (in list order) whose
+ * ready events are equal -- NULL included -- always share one group of
+ * launches.  With a threshold > 0, a group also absorbs following buckets
+ * with other events until it holds that many bytes per rank; it then waits
+ * for all their events before it starts.  Default 0. */
+int ddl_plan_set_coalesce_bytes(ddl_plan plan, size_t bytes);
+
+/* ---- measurement -------------------------------------------------------- *
+ * With profiling on, every kernel launch is bracketed by a pair of HIP events
+ * on the stream it is launched on.  ddl_plan_profile_read waits for the last
+ * of them and reports, for all launches since the previous read, the sum of
+ * their durations (ms), their number and the longest one; then it starts a
+ * new count.  Costs a few microseconds per launch. */
+int ddl_plan_set_profiling(ddl_plan plan, int enable);
+int ddl_plan_profile_read(ddl_plan plan, double *total_ms, int *launches, double *max_ms);
+
+/* ---- schedule introspection (host-only; used by the tests) ------------- */
+typedef enum { DDL_K_REDUCE = 0, DDL_K_GATHER = 1, DDL_K_FUSED = 2 } ddl_launch_kind;
+
+/* One pair transfer of one step: rank dst combines elements
+ * [offset, offset+count) of rank src into its own (DDL_K_REDUCE, dividing
+ * by P afterwards when divide is set) or copies them (DDL_K_GATHER). */
+typedef struct {
+    int src, dst, divide, step;
+    size_t offset, count;
+} ddl_step_item;
+
+/* Number of schedule steps of one bucket (2(P-1) ring and multi-ring,
+ * 2(rows-1) + 2(cols-1) torus) and the kind of step s. */
+int ddl_plan_num_steps(ddl_plan plan, int *steps);
+int ddl_plan_step_kind(ddl_plan plan, int step, int *kind);
+/* The items of step `step` for bucket `bucket` (list index).  *count gets the
+ * number of items; up to cap of them are written to out (out may be NULL). */
+int ddl_plan_step_items(ddl_plan plan, int step, int bucket, ddl_step_item *out,
+                        int cap, int *count);
+/* The fused spans of bucket `bucket`: span i covers [offset[i], offset[i]+
+ * count[i]) and sums ranks chain[i*P .. i*P+P-1] in that order, in groups
+ * of `group` consecutive entries (group = P for rings, cols for the torus):
+ * each group left to right, then the group sums left to right. */
+int ddl_plan_fused_spans(ddl_plan plan, int bucket, size_t *offset, size_t *count,
+                         int *chain, int cap, int *nspans, int *group);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

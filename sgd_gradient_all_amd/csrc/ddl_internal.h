@@ -1,0 +1,86 @@
+// ddl_internal.h -- layouts shared by the schedule generator (host C++) and
+// the gfx950 kernels.  Not part of the public interface.
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/ddl.h"
+
+namespace ddl {
+
+// One workgroup = 256 lanes = 4 wave64.
+constexpr int kBlock = 256;
+// Every lane moves 16 bytes per vector access (one dwordx4).
+constexpr int kVecBytes = 16;
+// Vectors per lane per tile: step kernels (one source, one destination)
+// and the fused kernel (P sources, P destinations).
+constexpr int kStepVecsPerLane = 4;
+constexpr int kFusedVecsPerLane = 1;
+
+// Elements of one tile, by element size.
+constexpr uint64_t step_tile_elems(int esz) {
+    return (uint64_t)kBlock * kStepVecsPerLane * (kVecBytes / esz);
+}
+constexpr uint64_t fused_tile_elems(int esz) {
+    return (uint64_t)kBlock * kFusedVecsPerLane * (kVecBytes / esz);
+}
+
+enum : uint32_t {
+    kItemDivide = 1u,   // divide by P after the add (mean epilogue)
+    kItemAligned = 2u,  // offset is a multiple of 16 B / element size
+};
+
+// One pair transfer of one step (device layout, 32 bytes).
+struct DevItem {
+    uint64_t off;    // first element
+    uint64_t len;    // elements
+    int32_t src;     // sending rank
+    int32_t dst;     // receiving rank
+    uint32_t flags;  // kItem*
+    uint32_t pad;
+};
+
+// One span of the fused pass (device layout, 24 bytes): elements
+// [off, off+len) are summed over chain[chain_off .. chain_off+P).
+struct DevSpan {
+    uint64_t off;
+    uint64_t len;
+    uint32_t chain_off;
+    uint32_t flags;  // kItemAligned
+};
+
+// Rank base pointers, passed by value as a kernel argument.
+struct RankPtrs {
+    void *p[DDL_MAX_RANKS];
+};
+
+// Arguments of one step launch: the tiles of items [item_lo, item_hi) of a
+// step; tile t of the launch is global tile prefix[item_lo] + t.
+struct StepArgs {
+    const DevItem *items;
+    const uint32_t *prefix;
+    uint32_t item_lo, item_hi;
+    uint32_t tile_base;
+    float divisor;   // P, for the mean
+};
+
+// Arguments of one fused launch over spans [span_lo, span_hi).
+struct FusedArgs {
+    const DevSpan *spans;
+    const uint32_t *prefix;
+    const uint8_t *chains;
+    uint32_t span_lo, span_hi;
+    uint32_t tile_base;
+    int P;
+    int group;       // chain entries per group (P for rings, cols for the torus)
+    int mean;        // divide by P at the end
+    float divisor;
+};
+
+// Kernel launchers (kernels.hip).  Return hipError_t as int.
+int launch_step(int dtype, int kind, const RankPtrs &bufs, const StepArgs &a,
+                uint32_t tiles, void *stream);
+int launch_fused(int dtype, const RankPtrs &bufs, const FusedArgs &a, uint32_t tiles,
+                 void *stream);
+
+}  // namespace ddl

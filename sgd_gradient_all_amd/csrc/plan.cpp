@@ -1,0 +1,582 @@
+// plan.cpp -- the C ABI: plans, the plan cache, and the bucket dispatcher.
+//
+// The dispatcher issues buckets in list order -- output layer first, so the
+// all-reduce of the gradients back-propagation finishes first can overlap the
+// rest of it (Baidu Ring-Allreduce article, part 4, opening paragraphs).  A
+// bucket with a ready event waits for it on the plan's side stream; buckets
+// whose events are equal (NULL included) share one group of launches, so a
+// step of all of them is one kernel.  With no event at all the work goes on
+// the caller's stream directly.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "ddl_internal.h"
+#include "schedule.h"
+
+using namespace ddl;
+
+struct ddl_plan_s {
+    Schedule s;
+    int mode = DDL_FUSED;
+    size_t coalesce_bytes = 0;
+
+    std::mutex mu;
+    int device = -1;        // bound at first execution
+    hipStream_t side = nullptr;
+    hipEvent_t call_ev = nullptr, done_ev = nullptr, last_ev = nullptr;
+    bool in_flight = false;
+
+    // device copies of the tables of the plan's mode
+    DevItem *d_items = nullptr;
+    uint32_t *d_prefix = nullptr;
+    std::vector<size_t> item_base, prefix_base;  // per step, into the above
+    DevSpan *d_spans = nullptr;
+    uint32_t *d_span_prefix = nullptr;
+    uint8_t *d_chains = nullptr;
+
+    // profiling
+    bool profiling = false;
+    std::vector<hipEvent_t> prof;   // pairs (start, end)
+    int prof_used = 0;
+};
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// device state
+// ---------------------------------------------------------------------------
+template <class T>
+int upload(T **dst, const T *src, size_t count) {
+    if (count == 0) {
+        *dst = nullptr;
+        return DDL_OK;
+    }
+    if (hipMalloc((void **)dst, count * sizeof(T)) != hipSuccess)
+        return DDL_E_NOMEM;
+    if (hipMemcpy(*dst, src, count * sizeof(T), hipMemcpyHostToDevice) != hipSuccess)
+        return DDL_E_HIP;
+    return DDL_OK;
+}
+
+void release_device(ddl_plan p) {
+    if (p->device < 0)
+        return;
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    (void)hipSetDevice(p->device);
+    (void)hipFree(p->d_items);
+    (void)hipFree(p->d_prefix);
+    (void)hipFree(p->d_spans);
+    (void)hipFree(p->d_span_prefix);
+    (void)hipFree(p->d_chains);
+    for (hipEvent_t e : p->prof)
+        (void)hipEventDestroy(e);
+    if (p->call_ev)
+        (void)hipEventDestroy(p->call_ev);
+    if (p->done_ev)
+        (void)hipEventDestroy(p->done_ev);
+    if (p->last_ev)
+        (void)hipEventDestroy(p->last_ev);
+    if (p->side)
+        (void)hipStreamDestroy(p->side);
+    (void)hipSetDevice(cur);
+    p->device = -1;
+}
+
+int bind_device(ddl_plan p, int dev) {
+    p->device = dev;
+    if (hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking) != hipSuccess)
+        return DDL_E_HIP;
+    if (hipEventCreateWithFlags(&p->call_ev, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&p->done_ev, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&p->last_ev, hipEventDisableTiming) != hipSuccess)
+        return DDL_E_HIP;
+    const Schedule &s = p->s;
+    int rc = DDL_OK;
+    if (p->mode == DDL_STEPWISE) {
+        std::vector<DevItem> items;
+        std::vector<uint32_t> prefix;
+        for (int st = 0; st < s.nsteps; ++st) {
+            p->item_base.push_back(items.size());
+            p->prefix_base.push_back(prefix.size());
+            items.insert(items.end(), s.items[st].begin(), s.items[st].end());
+            prefix.insert(prefix.end(), s.prefix[st].begin(), s.prefix[st].end());
+        }
+        if ((rc = upload(&p->d_items, items.data(), items.size())) ||
+            (rc = upload(&p->d_prefix, prefix.data(), prefix.size())))
+            return rc;
+    } else {
+        if ((rc = upload(&p->d_spans, s.spans.data(), s.spans.size())) ||
+            (rc = upload(&p->d_span_prefix, s.span_prefix.data(), s.span_prefix.size())) ||
+            (rc = upload(&p->d_chains, s.chains.data(), s.chains.size())))
+            return rc;
+    }
+    return DDL_OK;
+}
+
+// ---------------------------------------------------------------------------
+// launches
+// ---------------------------------------------------------------------------
+// A grid holds at most 2^32 - 1 work-items in x: cut bigger launches.
+constexpr uint32_t kMaxTilesPerLaunch = 1u << 23;
+
+struct Launcher {
+    ddl_plan p;
+    const RankPtrs &bufs;
+    hipStream_t stream;
+
+    int bracket_begin() {
+        if (!p->profiling)
+            return DDL_OK;
+        if ((size_t)(2 * p->prof_used + 2) > p->prof.size()) {
+            hipEvent_t a, b;
+            if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess)
+                return DDL_E_HIP;
+            p->prof.push_back(a);
+            p->prof.push_back(b);
+        }
+        return hipEventRecord(p->prof[2 * p->prof_used], stream) == hipSuccess ? DDL_OK
+                                                                               : DDL_E_HIP;
+    }
+    int bracket_end() {
+        if (!p->profiling)
+            return DDL_OK;
+        if (hipEventRecord(p->prof[2 * p->prof_used + 1], stream) != hipSuccess)
+            return DDL_E_HIP;
+        ++p->prof_used;
+        return DDL_OK;
+    }
+
+    int step(int st, uint32_t lo, uint32_t hi) {
+        const Schedule &s = p->s;
+        if (lo == hi)
+            return DDL_OK;
+        const uint32_t *pre = s.prefix[st].data();
+        StepArgs a;
+        a.items = p->d_items + p->item_base[st];
+        a.prefix = p->d_prefix + p->prefix_base[st];
+        a.item_lo = lo;
+        a.item_hi = hi;
+        a.divisor = (float)s.P;
+        for (uint32_t t = pre[lo]; t < pre[hi]; t += kMaxTilesPerLaunch) {
+            const uint32_t tiles = std::min(kMaxTilesPerLaunch, pre[hi] - t);
+            a.tile_base = t;
+            int rc = bracket_begin();
+            if (rc)
+                return rc;
+            if (launch_step(s.dtype, s.step_kind[st], bufs, a, tiles, stream) != hipSuccess)
+                return DDL_E_HIP;
+            if ((rc = bracket_end()))
+                return rc;
+        }
+        return DDL_OK;
+    }
+
+    int fused(uint32_t lo, uint32_t hi) {
+        const Schedule &s = p->s;
+        if (lo == hi)
+            return DDL_OK;
+        const uint32_t *pre = s.span_prefix.data();
+        FusedArgs a;
+        a.spans = p->d_spans;
+        a.prefix = p->d_span_prefix;
+        a.chains = p->d_chains;
+        a.span_lo = lo;
+        a.span_hi = hi;
+        a.P = s.P;
+        a.group = s.group;
+        a.mean = s.op == DDL_MEAN;
+        a.divisor = (float)s.P;
+        for (uint32_t t = pre[lo]; t < pre[hi]; t += kMaxTilesPerLaunch) {
+            const uint32_t tiles = std::min(kMaxTilesPerLaunch, pre[hi] - t);
+            a.tile_base = t;
+            int rc = bracket_begin();
+            if (rc)
+                return rc;
+            if (launch_fused(s.dtype, bufs, a, tiles, stream) != hipSuccess)
+                return DDL_E_HIP;
+            if ((rc = bracket_end()))
+                return rc;
+        }
+        return DDL_OK;
+    }
+
+    // every launch of buckets [b0, b1)
+    int group(int b0, int b1) {
+        const Schedule &s = p->s;
+        if (p->mode == DDL_FUSED)
+            return fused(s.span_at[b0], s.span_at[b1]);
+        for (int st = 0; st < s.nsteps; ++st) {
+            int rc = step(st, s.item_at[st][b0], s.item_at[st][b1]);
+            if (rc)
+                return rc;
+        }
+        return DDL_OK;
+    }
+};
+
+int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stream_,
+                   void *done_event) {
+    const Schedule &s = p->s;
+    for (int r = 0; r < s.P; ++r) {
+        if (!bufs[r] && s.n)
+            return DDL_E_NULL;
+        if ((uintptr_t)bufs[r] % kVecBytes)
+            return DDL_E_ALIGN;
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return DDL_E_HIP;
+    if (p->device < 0) {
+        int rc = bind_device(p, dev);
+        if (rc) {
+            release_device(p);
+            return rc;
+        }
+    } else if (p->device != dev) {
+        return DDL_E_DEVICE;
+    }
+    RankPtrs rp;
+    std::memset(&rp, 0, sizeof(rp));
+    for (int r = 0; r < s.P; ++r)
+        rp.p[r] = bufs[r];
+
+    hipStream_t cs = static_cast<hipStream_t>(stream_);
+    const int nb = (int)s.buckets.size();
+    bool any_event = false;
+    for (int b = 0; ready && b < nb; ++b)
+        any_event = any_event || ready[b] != nullptr;
+    hipStream_t ls = any_event ? p->side : cs;
+    if (any_event && hipEventRecord(p->call_ev, cs) != hipSuccess)
+        return DDL_E_HIP;
+
+    Launcher L{p, rp, ls};
+    const size_t esz = (size_t)s.esz;
+    int b0 = 0;
+    while (b0 < nb) {
+        // the group: equal events, then (with a threshold) more buckets
+        // until it holds coalesce_bytes per rank
+        void *ev0 = ready ? ready[b0] : nullptr;
+        int b1 = b0 + 1;
+        size_t bytes = s.buckets[b0].len * esz;
+        while (b1 < nb) {
+            void *ev = ready ? ready[b1] : nullptr;
+            if (ev == ev0 || (p->coalesce_bytes && bytes < p->coalesce_bytes)) {
+                bytes += s.buckets[b1].len * esz;
+                ++b1;
+            } else {
+                break;
+            }
+        }
+        if (any_event) {
+            void *last = reinterpret_cast<void *>(1);
+            for (int b = b0; b < b1; ++b) {
+                void *ev = ready[b] ? ready[b] : static_cast<void *>(p->call_ev);
+                if (ev == last)
+                    continue;
+                if (hipStreamWaitEvent(p->side, static_cast<hipEvent_t>(ev), 0) != hipSuccess)
+                    return DDL_E_HIP;
+                last = ev;
+            }
+        }
+        int rc = L.group(b0, b1);
+        if (rc)
+            return rc;
+        b0 = b1;
+    }
+    if (any_event) {
+        if (hipEventRecord(p->done_ev, p->side) != hipSuccess ||
+            hipStreamWaitEvent(cs, p->done_ev, 0) != hipSuccess)
+            return DDL_E_HIP;
+    }
+    if (done_event && hipEventRecord(static_cast<hipEvent_t>(done_event), ls) != hipSuccess)
+        return DDL_E_HIP;
+    if (hipEventRecord(p->last_ev, ls) != hipSuccess)
+        return DDL_E_HIP;
+    p->in_flight = true;
+    return DDL_OK;
+}
+
+bool busy(ddl_plan p) {
+    if (!p->in_flight || p->device < 0)
+        return false;
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    (void)hipSetDevice(p->device);
+    const hipError_t q = hipEventQuery(p->last_ev);
+    (void)hipSetDevice(cur);
+    if (q == hipErrorNotReady)
+        return true;
+    p->in_flight = false;
+    return false;
+}
+
+// ---------------------------------------------------------------------------
+// plan cache of ddl_allreduce
+// ---------------------------------------------------------------------------
+std::mutex g_cache_mu;
+std::map<std::string, ddl_plan> g_cache;
+
+void put(std::string &k, const void *p, size_t n) { k.append((const char *)p, n); }
+
+std::string cache_key(int dev, int P, size_t n, int dtype, int op, const ddl_topo &t,
+                      const ddl_bucket *buckets, int nb, int mode) {
+    std::string k;
+    const int hdr[] = {dev, P, dtype, op, t.kind, t.k, t.rows, t.cols, nb, mode,
+                       t.ring_order ? 1 : 0};
+    put(k, hdr, sizeof(hdr));
+    put(k, &n, sizeof(n));
+    if (t.ring_order) {
+        const size_t cnt = (size_t)(t.kind == DDL_MULTIRING ? std::max(t.k, 0) : 1) * P;
+        put(k, t.ring_order, cnt * sizeof(int));
+    }
+    for (int b = 0; b < nb; ++b) {
+        put(k, &buckets[b].offset, sizeof(size_t));
+        put(k, &buckets[b].count, sizeof(size_t));
+    }
+    return k;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" {
+
+const char *ddl_strerror(int code) {
+    switch (code) {
+    case DDL_OK: return "ok";
+    case DDL_E_NULL: return "a required pointer is NULL";
+    case DDL_E_ARG: return "argument out of range (P, n, dtype, op, mode or topology)";
+    case DDL_E_BUCKETS: return "buckets do not tile [0, n) exactly";
+    case DDL_E_ALIGN: return "a rank buffer is not 16-byte aligned";
+    case DDL_E_HIP: return "a HIP runtime call failed";
+    case DDL_E_NOMEM: return "allocation failed";
+    case DDL_E_BUSY: return "the plan still has work in flight";
+    case DDL_E_DEVICE: return "executed on a device other than the plan's";
+    default: return "unknown error";
+    }
+}
+
+int ddl_plan_create(ddl_plan *out, int P, size_t n, ddl_dtype dtype, ddl_op op,
+                    const ddl_topo *topo, const ddl_bucket *buckets, int nbuckets,
+                    ddl_mode mode) {
+    if (!out || !topo)
+        return DDL_E_NULL;
+    *out = nullptr;
+    if (mode != DDL_STEPWISE && mode != DDL_FUSED)
+        return DDL_E_ARG;
+    ddl_plan p = new (std::nothrow) ddl_plan_s;
+    if (!p)
+        return DDL_E_NOMEM;
+    int rc;
+    try {
+        rc = build_schedule(p->s, P, n, dtype, op, *topo, buckets, nbuckets);
+    } catch (const std::bad_alloc &) {
+        rc = DDL_E_NOMEM;
+    } catch (...) {
+        rc = DDL_E_ARG;
+    }
+    if (rc) {
+        delete p;
+        return rc;
+    }
+    p->mode = mode;
+    *out = p;
+    return DDL_OK;
+}
+
+int ddl_plan_execute(ddl_plan plan, void *const *bufs, void *const *ready_events,
+                     void *stream, void *done_event) {
+    if (!plan || !bufs)
+        return DDL_E_NULL;
+    std::lock_guard<std::mutex> lk(plan->mu);
+    try {
+        return execute_locked(plan, bufs, ready_events, stream, done_event);
+    } catch (...) {
+        return DDL_E_NOMEM;
+    }
+}
+
+int ddl_allreduce(void *const *bufs, int P, size_t n, ddl_dtype dtype, ddl_op op,
+                  const ddl_topo *topo, const ddl_bucket *buckets, int nbuckets,
+                  ddl_mode mode, void *stream, void *done_event) {
+    if (!bufs || !topo || (nbuckets > 0 && !buckets))
+        return DDL_E_NULL;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return DDL_E_HIP;
+    ddl_plan p = nullptr;
+    try {
+        std::lock_guard<std::mutex> lk(g_cache_mu);
+        const std::string key =
+            cache_key(dev, P, n, dtype, op, *topo, buckets, std::max(nbuckets, 0), mode);
+        auto it = g_cache.find(key);
+        if (it != g_cache.end()) {
+            p = it->second;
+        } else {
+            int rc = ddl_plan_create(&p, P, n, dtype, op, topo, buckets, nbuckets, mode);
+            if (rc)
+                return rc;
+            g_cache[key] = p;
+        }
+        std::vector<void *> ev(std::max(nbuckets, 0), nullptr);
+        for (int b = 0; b < nbuckets; ++b)
+            ev[b] = buckets[b].ready_event;
+        return ddl_plan_execute(p, bufs, nbuckets ? ev.data() : nullptr, stream, done_event);
+    } catch (...) {
+        return DDL_E_NOMEM;
+    }
+}
+
+int ddl_plan_traffic(ddl_plan plan, size_t *sent, size_t *hbm_bytes) {
+    if (!plan)
+        return DDL_E_NULL;
+    const Schedule &s = plan->s;
+    if (sent)
+        for (int r = 0; r < s.P; ++r)
+            sent[r] = (size_t)s.sent[r];
+    if (hbm_bytes)
+        *hbm_bytes = (size_t)(plan->mode == DDL_FUSED ? s.fused_bytes : s.step_bytes);
+    return DDL_OK;
+}
+
+int ddl_plan_destroy(ddl_plan plan) {
+    if (!plan)
+        return DDL_E_NULL;
+    {
+        std::lock_guard<std::mutex> lk(plan->mu);
+        if (busy(plan))
+            return DDL_E_BUSY;
+        release_device(plan);
+    }
+    delete plan;
+    return DDL_OK;
+}
+
+int ddl_cache_clear(void) {
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    for (auto &kv : g_cache) {
+        std::lock_guard<std::mutex> pl(kv.second->mu);
+        if (busy(kv.second))
+            return DDL_E_BUSY;
+    }
+    for (auto &kv : g_cache) {
+        release_device(kv.second);
+        delete kv.second;
+    }
+    g_cache.clear();
+    return DDL_OK;
+}
+
+int ddl_plan_set_coalesce_bytes(ddl_plan plan, size_t bytes) {
+    if (!plan)
+        return DDL_E_NULL;
+    std::lock_guard<std::mutex> lk(plan->mu);
+    plan->coalesce_bytes = bytes;
+    return DDL_OK;
+}
+
+int ddl_plan_set_profiling(ddl_plan plan, int enable) {
+    if (!plan)
+        return DDL_E_NULL;
+    std::lock_guard<std::mutex> lk(plan->mu);
+    plan->profiling = enable != 0;
+    return DDL_OK;
+}
+
+int ddl_plan_profile_read(ddl_plan plan, double *total_ms, int *launches, double *max_ms) {
+    if (!plan)
+        return DDL_E_NULL;
+    std::lock_guard<std::mutex> lk(plan->mu);
+    double tot = 0, mx = 0;
+    for (int i = 0; i < plan->prof_used; ++i) {
+        float ms = 0;
+        if (hipEventSynchronize(plan->prof[2 * i + 1]) != hipSuccess ||
+            hipEventElapsedTime(&ms, plan->prof[2 * i], plan->prof[2 * i + 1]) != hipSuccess)
+            return DDL_E_HIP;
+        tot += ms;
+        mx = std::max(mx, (double)ms);
+    }
+    if (total_ms)
+        *total_ms = tot;
+    if (launches)
+        *launches = plan->prof_used;
+    if (max_ms)
+        *max_ms = mx;
+    plan->prof_used = 0;
+    return DDL_OK;
+}
+
+int ddl_plan_num_steps(ddl_plan plan, int *steps) {
+    if (!plan || !steps)
+        return DDL_E_NULL;
+    *steps = plan->s.nsteps;
+    return DDL_OK;
+}
+
+int ddl_plan_step_kind(ddl_plan plan, int step, int *kind) {
+    if (!plan || !kind)
+        return DDL_E_NULL;
+    if (step < 0 || step >= plan->s.nsteps)
+        return DDL_E_ARG;
+    *kind = plan->s.step_kind[step];
+    return DDL_OK;
+}
+
+int ddl_plan_step_items(ddl_plan plan, int step, int bucket, ddl_step_item *out, int cap,
+                        int *count) {
+    if (!plan || !count)
+        return DDL_E_NULL;
+    const Schedule &s = plan->s;
+    if (step < 0 || step >= s.nsteps || bucket < 0 || bucket >= (int)s.buckets.size())
+        return DDL_E_ARG;
+    const uint32_t lo = s.item_at[step][bucket], hi = s.item_at[step][bucket + 1];
+    *count = (int)(hi - lo);
+    for (uint32_t i = lo; out && i < hi && (int)(i - lo) < cap; ++i) {
+        const DevItem &it = s.items[step][i];
+        ddl_step_item &o = out[i - lo];
+        o.src = it.src;
+        o.dst = it.dst;
+        o.divide = (it.flags & kItemDivide) ? 1 : 0;
+        o.step = step;
+        o.offset = (size_t)it.off;
+        o.count = (size_t)it.len;
+    }
+    return DDL_OK;
+}
+
+int ddl_plan_fused_spans(ddl_plan plan, int bucket, size_t *offset, size_t *count, int *chain,
+                         int cap, int *nspans, int *group) {
+    if (!plan || !nspans)
+        return DDL_E_NULL;
+    const Schedule &s = plan->s;
+    if (bucket < 0 || bucket >= (int)s.buckets.size())
+        return DDL_E_ARG;
+    const uint32_t lo = s.span_at[bucket], hi = s.span_at[bucket + 1];
+    *nspans = (int)(hi - lo);
+    if (group)
+        *group = s.group;
+    for (uint32_t i = lo; i < hi && (int)(i - lo) < cap; ++i) {
+        const DevSpan &sp = s.spans[i];
+        if (offset)
+            offset[i - lo] = (size_t)sp.off;
+        if (count)
+            count[i - lo] = (size_t)sp.len;
+        if (chain)
+            for (int r = 0; r < s.P; ++r)
+                chain[(size_t)(i - lo) * s.P + r] = s.chains[sp.chain_off + r];
+    }
+    return DDL_OK;
+}
+
+}  // extern "C"

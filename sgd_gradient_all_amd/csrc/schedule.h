@@ -1,0 +1,64 @@
+// schedule.h -- host schedule generator: turns (P, n, topology, buckets)
+// into the step tables and fused-span tables the kernels walk.
+#pragma once
+
+#include <stdint.h>
+
+#include <vector>
+
+#include "ddl_internal.h"
+
+namespace ddl {
+
+struct Bucket {
+    uint64_t off, len;
+};
+
+struct Schedule {
+    // arguments
+    int P = 0;
+    uint64_t n = 0;
+    int dtype = DDL_F32;
+    int esz = 4;
+    uint64_t q = 4;          // split quantum: 16 bytes / element size
+    int op = DDL_SUM;
+    int kind = DDL_RING;
+    int k = 1;               // rings (multi-ring), 1 otherwise
+    int rows = 1, cols = 1;  // torus grid
+    std::vector<int> order;  // k*P: ring j puts rank order[j*P + x] at position x
+    std::vector<Bucket> buckets;  // issue order
+
+    // step tables.  Step s of every bucket forms one list, bucket-major, so
+    // any run of consecutive buckets is a contiguous item range of a step.
+    int nsteps = 0;
+    std::vector<int> step_kind;                  // [s] DDL_K_REDUCE | DDL_K_GATHER
+    std::vector<std::vector<DevItem>> items;     // [s] items
+    std::vector<std::vector<uint32_t>> item_at;  // [s] first item of bucket b, nb+1
+    std::vector<std::vector<uint32_t>> prefix;   // [s] tile prefix, nitems+1
+
+    // fused tables: spans bucket-major, P chain entries each
+    int group = 1;                       // chain entries per group
+    std::vector<DevSpan> spans;
+    std::vector<uint32_t> span_at;       // first span of bucket b, nb+1
+    std::vector<uint32_t> span_prefix;   // tile prefix, nspans+1
+    std::vector<uint8_t> chains;
+
+    // accounting
+    std::vector<uint64_t> sent;          // [P] elements sent per rank
+    uint64_t step_bytes = 0;             // HBM bytes of the stepwise path
+    uint64_t fused_bytes = 0;            // HBM bytes of the fused path
+};
+
+// Split of a length-L segment into m pieces with quantum q: piece c is
+// [b[c], b[c+1]), b[c] = min(L, q*floor(c*ceil(L/q)/m)).
+void split_segment(uint64_t L, int m, uint64_t q, std::vector<uint64_t> &b);
+
+// Validates the arguments and builds every table.  Returns a DDL_* code.
+int build_schedule(Schedule &s, int P, uint64_t n, int dtype, int op,
+                   const ddl_topo &topo, const ddl_bucket *buckets, int nbuckets);
+
+// Proves the tables race-free: within one step no element of any rank that
+// one item writes is read or written by another item.  Returns true if so.
+bool check_schedule(const Schedule &s);
+
+}  // namespace ddl

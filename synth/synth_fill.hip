@@ -1,0 +1,112 @@
+// synth_fill.hip -- device side of the seeded synthetic gradients (the
+// definitions are in synth.h; synth.c is the host side and must produce the
+// same bits), and the streaming compute kernel the overlap measurement runs
+// beside the all-reduce.  None of the all-reduce's arithmetic is here.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr uint64_t kG = 0x9E3779B97F4A7C15ull;
+
+__host__ __device__ __forceinline__ uint64_t mix64(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+// One IEEE operation per step, in the order synth.c takes them.
+__device__ __forceinline__ float value_f32(int dist, uint64_t key, int rank, uint64_t e,
+                                           double scale) {
+    switch (dist) {
+    case 0: {  // uniform [-1, 1)
+        int32_t u = (int32_t)(mix64(key + (e + 1) * kG) >> 40);
+        return (float)(u - (1 << 23)) * 0x1p-23f;
+    }
+    case 1: {  // Irwin-Hall approximation of N(0, sigma^2)
+        int64_t s = 0;
+        for (int j = 0; j < 6; ++j) {
+            uint64_t w = mix64(key + (6 * e + (uint64_t)j + 1) * kG);
+            s += (int64_t)(w & 0xffffffffull) + (int64_t)(w >> 32);
+        }
+        int64_t T = 2 * s - 12 * (int64_t)0xffffffffll;
+        return __double2float_rn(__dmul_rn((double)T, scale));
+    }
+    case 2:
+        return (float)(rank + 1);
+    default:
+        return (float)((int)(mix64(key + (e + 1) * kG) >> 57) - 64);
+    }
+}
+
+__global__ void fill_f32(float *dst, int dist, uint64_t key, int rank, uint64_t first,
+                         uint64_t count, double scale) {
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride)
+        dst[i] = value_f32(dist, key, rank, first + i, scale);
+}
+
+__global__ void fill_f16(_Float16 *dst, int dist, uint64_t key, int rank, uint64_t first,
+                         uint64_t count, double scale) {
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride)
+        dst[i] = (_Float16)value_f32(dist, key, rank, first + i, scale);
+}
+
+// a = alpha * a + beta over n floats, 16 bytes per lane access: stands in for
+// the backward-pass compute the all-reduce overlaps with.
+__global__ void stream_compute(float *a, uint64_t n, float alpha, float beta) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const uint64_t nv = n / 4;
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    f32x4 *v = reinterpret_cast<f32x4 *>(a);
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nv; i += stride) {
+        f32x4 x = v[i];
+        v[i] = x * alpha + beta;
+    }
+    for (uint64_t i = nv * 4 + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += stride)
+        a[i] = a[i] * alpha + beta;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Elements [first, first+count) of rank `rank` into device memory dst
+// (dtype 0 = binary32, 1 = binary16).  Returns a hipError_t.
+int synth_fill_device(void *dst, int dtype, int dist, uint64_t seed, int rank, uint64_t first,
+                      uint64_t count, double sigma, void *stream) {
+    if (count == 0)
+        return 0;
+    if (!dst)
+        return (int)hipErrorInvalidValue;
+    const uint64_t key = mix64(seed + (uint64_t)(rank + 1) * kG);
+    const double scale = sigma * 0x1p-33;
+    const uint64_t blocks64 = (count + 255) / 256;
+    const unsigned blocks = (unsigned)(blocks64 < 65536 ? blocks64 : 65536);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dtype == 0)
+        hipLaunchKernelGGL(fill_f32, dim3(blocks), dim3(256), 0, s, static_cast<float *>(dst),
+                           dist, key, rank, first, count, scale);
+    else
+        hipLaunchKernelGGL(fill_f16, dim3(blocks), dim3(256), 0, s,
+                           static_cast<_Float16 *>(dst), dist, key, rank, first, count, scale);
+    return (int)hipGetLastError();
+}
+
+// In-place a = alpha * a + beta over n floats (a 16-byte aligned).
+int synth_stream_compute(void *a, uint64_t n, float alpha, float beta, void *stream) {
+    if (n == 0)
+        return 0;
+    if (!a || ((uintptr_t)a & 15))
+        return (int)hipErrorInvalidValue;
+    const uint64_t blocks64 = (n / 4 + 255) / 256;
+    const unsigned blocks = (unsigned)(blocks64 < 8192 ? (blocks64 ? blocks64 : 1) : 8192);
+    hipLaunchKernelGGL(stream_compute, dim3(blocks), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<float *>(a), n, alpha,
+                       beta);
+    return (int)hipGetLastError();
+}
+
+}  // extern "C"

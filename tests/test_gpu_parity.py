@@ -1,0 +1,315 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bit-exact comparison of every element at sizes the oracle walks in seconds
+(several tiles and ragged tails), and of sampled elements plus whole-buffer
+properties at the full workload sizes, in the launch configuration the
+benchmark times.  Every test names its case on stdout before touching the GPU.
+"""
+import numpy as np
+import pytest
+
+import oracle as orc
+import sgd_gradient_all_amd as ddl
+import synth
+from synth.workloads import WORKLOADS, Workload
+
+from _helpers import (KINDS, OPS, bucket_of, ddl_topo, host_inputs, np_dtype, oracle_at,
+                      oracle_full, say, synth_dtype, sample_indices)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+TORCH_DT = {"f32": torch.float32, "f16": torch.float16}
+
+
+def to_device(arrs):
+    return [torch.from_numpy(a).cuda() for a in arrs]
+
+
+def to_host(ts):
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in ts]
+
+
+def bitwise_equal(a, b):
+    a = np.ascontiguousarray(a)
+    b = np.ascontiguousarray(b)
+    if a.tobytes() == b.tobytes():
+        return True
+    fa, fb = a.astype(np.float64), b.astype(np.float64)
+    same = (a.view(np.uint16 if a.dtype == np.float16 else np.uint32)
+            == b.view(np.uint16 if b.dtype == np.float16 else np.uint32))
+    return bool(np.all(same | (np.isnan(fa) & np.isnan(fb))))
+
+
+def run_ddl(bufs, w, mode, op=None, plan_api=True, events=None, stream=None):
+    t = ddl_topo(w)
+    if plan_api:
+        plan = ddl.Plan(w.P, w.n, w.dtype, op or w.op, t, w.bucket_list(), mode)
+        plan.execute(bufs, events=events, stream=stream)
+        torch.cuda.synchronize()
+        plan.destroy()
+    else:
+        ddl.ddl_allreduce(bufs, w.n, w.dtype, op or w.op, t, w.bucket_list(), mode,
+                          stream=stream, events=events)
+        torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# small cases: every element, every rank, bit for bit
+# ---------------------------------------------------------------------------
+def small_cases():
+    cases = []
+    for dtype in ("f32", "f16"):
+        for P, n in ((1, 1000), (2, 1), (3, 2), (4, 4099), (5, 12347), (8, 100_003),
+                     (16, 70_001)):
+            cases.append(Workload(f"ring-P{P}-n{n}-{dtype}", P, n, dtype, "sum", "ring",
+                                  dist="uniform", seed=P + n))
+        for P, k, n in ((4, 2, 9_999), (16, 4, 250_007), (6, 3, 17)):
+            cases.append(Workload(f"mring-P{P}-k{k}-n{n}-{dtype}", P, n, dtype, "mean",
+                                  "multiring", k=k, dist="normal", sigma=1e-2, seed=n))
+        for R, C, n in ((2, 2, 5_003), (4, 4, 200_009), (2, 3, 77_777), (3, 1, 1_001),
+                        (1, 5, 1_234)):
+            cases.append(Workload(f"torus-{R}x{C}-n{n}-{dtype}", R * C, n, dtype, "mean",
+                                  "torus2d", rows=R, cols=C, dist="normal", sigma=1e-2,
+                                  seed=n + R))
+    # bucket lists, reverse order, with offsets that are not multiples of 16 B
+    sizes = [37, 4096, 5, 0, 100_000, 1, 2048, 777]
+    offs = np.concatenate([[0], np.cumsum(sizes)[:-1]]).tolist()
+    bl = list(zip(offs, sizes))[::-1]
+    for dtype in ("f32", "f16"):
+        cases.append(Workload(f"buckets-ring-P6-{dtype}", 6, sum(sizes), dtype, "mean", "ring",
+                              dist="normal", sigma=1e-2, seed=99, buckets=bl))
+        cases.append(Workload(f"buckets-torus-2x4-{dtype}", 8, sum(sizes), dtype, "sum",
+                              "torus2d", rows=2, cols=4, dist="uniform", seed=98, buckets=bl))
+    return cases
+
+
+@pytest.mark.parametrize("w", small_cases(), ids=lambda w: w.name)
+@pytest.mark.parametrize("mode", ["fused", "stepwise"])
+@pytest.mark.parametrize("op", ["sum", "mean"])
+def test_small_bitwise(w, mode, op):
+    say(f"case {w.name} mode={mode} op={op}")
+    g = host_inputs(w)
+    ref = [x.copy() for x in g]
+    oracle_full(w, ref, op=op)
+    bufs = to_device(g)
+    run_ddl(bufs, w, mode, op=op, plan_api=(mode == "fused"))
+    out = to_host(bufs)
+    for r in range(w.P):
+        assert bitwise_equal(out[r], ref[r]), (w.name, mode, op, r)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_subnormals_and_specials(dtype):
+    say(f"case subnormals/specials {dtype}")
+    dt = np_dtype(dtype)
+    P, n = 4, 4096
+    rng = np.random.default_rng(3)
+    tiny = np.float32(2.0 ** -130) if dtype == "f32" else np.float32(2.0 ** -20)
+    g = [(rng.integers(-50, 50, n).astype(np.float32) * tiny).astype(dt) for _ in range(P)]
+    g[1][7] = np.inf
+    g[2][9] = np.nan
+    g[0][11], g[3][11] = np.inf, -np.inf
+    w = Workload("sub", P, n, dtype, "mean", "ring")
+    for mode in ("fused", "stepwise"):
+        for op in ("sum", "mean"):
+            ref = [x.copy() for x in g]
+            oracle_full(w, ref, op=op)
+            assert np.any(ref[0][:] != 0)
+            bufs = to_device(g)
+            run_ddl(bufs, w, mode, op=op)
+            out = to_host(bufs)
+            for r in range(P):
+                assert bitwise_equal(out[r], ref[r]), (mode, op, r)
+
+
+def test_closed_form_rank_plus_one():
+    for name in ("ring_p4_1m_sum", "multiring_k4_p16_resnet50", "torus_4x4_resnet50_f16"):
+        w = WORKLOADS[name]
+        say(f"case closed form {name}")
+        bufs = [torch.full((w.n,), r + 1, dtype=TORCH_DT[w.dtype], device="cuda")
+                for r in range(w.P)]
+        for mode in ("fused", "stepwise"):
+            for op, want in (("sum", w.P * (w.P + 1) / 2), ("mean", (w.P + 1) / 2)):
+                for r, b in enumerate(bufs):
+                    b.fill_(r + 1)
+                run_ddl(bufs, w, mode, op=op)
+                for b in bufs:
+                    assert bool((b == want).all()), (name, mode, op)
+
+
+# ---------------------------------------------------------------------------
+# the measured workloads at full size
+# ---------------------------------------------------------------------------
+def device_inputs(w):
+    bufs = [torch.empty(w.n, dtype=TORCH_DT[w.dtype], device="cuda") for _ in range(w.P)]
+    for r, b in enumerate(bufs):
+        synth.fill_device(b.data_ptr(), w.n, synth_dtype(w.dtype), w.dist, w.seed, r,
+                          sigma=w.sigma)
+    torch.cuda.synchronize()
+    return bufs
+
+
+def ranks_identical(bufs):
+    iv = torch.int16 if bufs[0].dtype == torch.float16 else torch.int32
+    return all(torch.equal(bufs[0].view(iv), b.view(iv)) for b in bufs[1:])
+
+
+def test_synth_device_matches_host():
+    for dtype in ("f32", "f16"):
+        for dist, sigma in (("uniform", 1.0), ("normal", 1e-3), ("normal", 1e-2),
+                            ("smallint", 1.0), ("rankconst", 1.0)):
+            say(f"case synth {dtype} {dist}")
+            n, first = 300_001, 123_456_789
+            t = torch.empty(n, dtype=TORCH_DT[dtype], device="cuda")
+            synth.fill_device(t.data_ptr(), n, synth_dtype(dtype), dist, 7, 3, first=first,
+                              sigma=sigma)
+            got = to_host([t])[0]
+            want = synth.fill_host(n, synth_dtype(dtype), dist, 7, 3, first=first, sigma=sigma)
+            assert got.tobytes() == want.tobytes(), (dtype, dist)
+
+
+@pytest.mark.parametrize("name", ["ring_p4_1m_sum", "multiring_k4_p16_resnet50",
+                                  "torus_4x4_resnet50_f16"])
+def test_workload_full_bitwise(name):
+    """Every element of every rank against the oracle's full walk, both
+    modes, buckets as the workload issues them."""
+    w = WORKLOADS[name]
+    say(f"case workload {name}: host inputs")
+    g = host_inputs(w)
+    ref = [x.copy() for x in g]
+    oracle_full(w, ref)
+    for mode in ("fused", "stepwise"):
+        say(f"case workload {name} mode={mode}")
+        bufs = to_device(g)
+        run_ddl(bufs, w, mode, plan_api=False)
+        out = to_host(bufs)
+        for r in range(w.P):
+            assert bitwise_equal(out[r], ref[r]), (name, mode, r)
+        del bufs
+    ddl.ddl_cache_clear()
+    y64 = orc.sum_f64(g, op=OPS[w.op])
+    err = np.linalg.norm(ref[0].astype(np.float64) - y64) / np.linalg.norm(y64)
+    assert err <= (1e-6 if w.dtype == "f32" else 2e-3), err
+
+
+@pytest.mark.parametrize("name", ["ring_p8_300m_mean", "ring_p40_300m_64b"])
+def test_workload_full_size_sampled(name):
+    """Full size, generated on the GPU: sampled elements against the oracle,
+    every rank bit-identical, fused and stepwise bit-identical everywhere."""
+    w = WORKLOADS[name]
+    say(f"case workload {name}: device inputs ({w.P} x {w.n})")
+    bufs = device_inputs(w)
+    copy = [b.clone() for b in bufs]
+    stream = torch.cuda.current_stream()
+    events = None
+    if w.side_stream:
+        events = [torch.cuda.Event() for _ in w.bucket_list()]
+        for e in events:
+            e.record(stream)
+    say(f"case workload {name}: fused")
+    plan = ddl.Plan(w.P, w.n, w.dtype, w.op, ddl_topo(w), w.bucket_list(), "fused")
+    plan.execute(bufs, events=events, stream=stream)
+    torch.cuda.synchronize()
+    assert ranks_identical(bufs)
+    idx = sample_indices(w, 3000, seed=1)
+    want, inputs = oracle_at(w, idx)
+    it = torch.from_numpy(idx.astype(np.int64)).cuda()
+    for r in (0, w.P // 2, w.P - 1):
+        got = bufs[r][it].cpu().numpy()
+        assert bitwise_equal(got, want), (name, r)
+    # accuracy against binary64 on the sample
+    y64 = np.sum(np.stack(inputs).astype(np.float64), axis=0) / (w.P if w.op == "mean" else 1)
+    err = np.linalg.norm(want.astype(np.float64) - y64) / np.linalg.norm(y64)
+    assert err <= 1e-6, err
+    plan.destroy()
+    say(f"case workload {name}: stepwise")
+    plan = ddl.Plan(w.P, w.n, w.dtype, w.op, ddl_topo(w), w.bucket_list(), "stepwise")
+    plan.execute(copy, events=events, stream=stream)
+    torch.cuda.synchronize()
+    iv = torch.int32
+    assert all(torch.equal(a.view(iv), b.view(iv)) for a, b in zip(bufs, copy))
+    plan.destroy()
+    del bufs, copy
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# dispatcher: ready events gate buckets
+# ---------------------------------------------------------------------------
+def test_ready_events_gate_buckets():
+    """Inputs are written by kernels queued behind a long kernel on the main
+    stream, bucket by bucket, each followed by its event.  The all-reduce is
+    enqueued right after: correct results need every bucket to have waited
+    for its own event."""
+    say("case ready events")
+    w = Workload("events", 8, 64 * 65_536, "f32", "mean", "ring", dist="normal", sigma=1e-3,
+                 seed=11, buckets=[(i * 65_536, 65_536) for i in reversed(range(64))])
+    bufs = [torch.full((w.n,), float("nan"), device="cuda") for _ in range(w.P)]
+    scratch = torch.zeros(1 << 27, device="cuda")
+    main = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    synth.stream_compute(scratch.data_ptr(), scratch.numel(), 1.0001, 0.5, main.cuda_stream)
+    events = []
+    for off, cnt in w.bucket_list():
+        for r, b in enumerate(bufs):
+            synth.fill_device(b.data_ptr() + 4 * off, cnt, synth.F32, w.dist, w.seed, r,
+                              first=off, sigma=w.sigma, stream=main.cuda_stream)
+        e = torch.cuda.Event()
+        e.record(main)
+        events.append(e)
+    plan = ddl.Plan(w.P, w.n, w.dtype, w.op, ddl_topo(w), w.bucket_list(), "fused")
+    plan.execute(bufs, events=events, stream=main)
+    torch.cuda.synchronize()
+    g = host_inputs(w)
+    oracle_full(w, g)
+    out = to_host(bufs)
+    for r in range(w.P):
+        assert bitwise_equal(out[r], g[r]), r
+    plan.destroy()
+
+
+def test_misaligned_buffer_is_rejected_and_nothing_runs():
+    say("case misaligned")
+    P, n = 4, 1000
+    base = [torch.arange(n + 8, dtype=torch.float32, device="cuda") for _ in range(P)]
+    before = [b.clone() for b in base]
+    ptrs = [b.data_ptr() + 4 for b in base]  # 4-byte offset: not 16-byte aligned
+    plan = ddl.Plan(P, n, "f32", "sum", ddl.topo("ring"))
+    with pytest.raises(ddl.DDLError) as ei:
+        plan.execute(ptrs)
+    assert ei.value.code == -4
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(base, before))
+    plan.destroy()
+
+
+def test_profiling_counts_launches():
+    say("case profiling")
+    w = WORKLOADS["multiring_k4_p16_resnet50"]
+    bufs = [torch.ones(w.n, device="cuda") for _ in range(w.P)]
+    for mode, launches in (("fused", 1), ("stepwise", 30)):
+        plan = ddl.Plan(w.P, w.n, w.dtype, "sum", ddl_topo(w), w.bucket_list(), mode)
+        plan.set_profiling(True)
+        plan.execute(bufs)
+        plan.execute(bufs)
+        total, cnt, mx = plan.profile_read()
+        assert cnt == 2 * launches, (mode, cnt)
+        assert total > 0 and mx <= total
+        plan.destroy()
+
+
+def test_plan_reuse_and_cache():
+    say("case reuse")
+    w = Workload("reuse", 5, 10_000, "f32", "sum", "ring", dist="smallint", seed=4)
+    g = host_inputs(w)
+    want = np.sum(np.stack(g).astype(np.int64), axis=0)
+    for _ in range(3):
+        bufs = to_device(g)
+        ddl.ddl_allreduce(bufs, w.n, "f32", "sum", ddl.topo("ring"))
+        out = to_host(bufs)
+        for r in range(w.P):
+            assert np.array_equal(out[r].astype(np.int64), want)
+    ddl.ddl_cache_clear()

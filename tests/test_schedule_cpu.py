@@ -1,0 +1,225 @@
+"""Host-side checks of libddl.so (no GPU calls).
+
+- the library loads and exports every function include/ddl.h declares;
+- argument validation returns the documented codes;
+- the schedule generator's tables, replayed on the host by a small table
+  interpreter written here, reproduce the oracle bit for bit (step tables and
+  fused chains), and move the traffic the oracle counts.
+"""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle as orc
+import sgd_gradient_all_amd as ddl
+from sgd_gradient_all_amd import _ddl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    with open(os.path.join(ROOT, "include", "ddl.h")) as f:
+        text = f.read()
+    declared = set(re.findall(r"^\s*(?:int|const char \*)\s*(ddl_\w+)\s*\(", text, re.M))
+    assert {"ddl_plan_create", "ddl_plan_execute", "ddl_allreduce", "ddl_plan_traffic",
+            "ddl_plan_destroy", "ddl_strerror"} <= declared
+    out = subprocess.run(["nm", "-D", "--defined-only", _ddl._LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (ddl_\w+)", out))
+    assert declared <= exported, declared - exported
+    lib = ddl.lib()
+    for name in declared:
+        assert hasattr(lib, name)
+
+
+def test_strerror_covers_every_code():
+    for code in range(0, -9, -1):
+        assert ddl.ddl_strerror(code) != "unknown error"
+    assert ddl.ddl_strerror(-99) == "unknown error"
+
+
+def _create_rc(P, n, dtype=0, op=0, kind=0, k=1, rows=0, cols=0, order=None, buckets=None,
+               mode=1):
+    import ctypes
+    t = _ddl.topo(kind, k, rows, cols, order)
+    barr, nb = _ddl._buckets(buckets)
+    h = ctypes.c_void_p()
+    rc = ddl.lib().ddl_plan_create(ctypes.byref(h), P, n, dtype, op, ctypes.byref(t), barr, nb,
+                                   mode)
+    if rc == 0:
+        ddl.lib().ddl_plan_destroy(h)
+    return rc
+
+
+def test_argument_validation():
+    assert _create_rc(4, 100) == 0
+    assert _create_rc(0, 100) == -2
+    assert _create_rc(129, 100) == -2
+    assert _create_rc(4, 100, dtype=7) == -2
+    assert _create_rc(4, 100, op=3) == -2
+    assert _create_rc(4, 100, mode=5) == -2
+    assert _create_rc(4, 100, kind=2, rows=3, cols=2) == -2
+    assert _create_rc(4, 100, kind=2, rows=2, cols=2, order=[0, 1, 2, 3]) == -2
+    assert _create_rc(4, 100, kind=1, k=0) == -2
+    assert _create_rc(4, 100, order=[0, 1, 1, 3]) == -2
+    assert _create_rc(4, 100, order=[0, 1, 2, 4]) == -2
+    assert _create_rc(4, 100, buckets=[(0, 50), (40, 60)]) == -3
+    assert _create_rc(4, 100, buckets=[(0, 50), (60, 40)]) == -3
+    assert _create_rc(4, 100, buckets=[(0, 50), (50, 60)]) == -3
+    assert _create_rc(4, 100, buckets=[(50, 50), (0, 50), (10, 0)]) == 0
+    assert _create_rc(4, 0) == 0
+    assert _create_rc(128, 10) == 0
+
+
+# ---------------------------------------------------------------------------
+# a table interpreter: replays the plan's tables on host arrays with numpy
+# arithmetic (binary32 add / divide; binary16 through binary32, rounded)
+# ---------------------------------------------------------------------------
+def _add(a, b, dtype):
+    if dtype == np.float32:
+        return a + b
+    return (a.astype(np.float32) + b.astype(np.float32)).astype(np.float16)
+
+
+def _div(a, P, dtype):
+    if dtype == np.float32:
+        return a / np.float32(P)
+    return (a.astype(np.float32) / np.float32(P)).astype(np.float16)
+
+
+def interpret_steps(plan, bufs, nbuckets, dtype):
+    steps = plan.num_steps()
+    for b in range(nbuckets):
+        for s in range(steps):
+            kind = plan.step_kind(s)
+            items = plan.step_items(s, b)
+            # all items of a step read before any writes land (they are
+            # race-free, this keeps the replay honest either way)
+            staged = [(src, dst, div, off, cnt, bufs[src][off:off + cnt].copy())
+                      for src, dst, div, off, cnt in items]
+            for src, dst, div, off, cnt, data in staged:
+                if kind == ddl.DDL_K_REDUCE:
+                    r = _add(bufs[dst][off:off + cnt], data, dtype)
+                    if div:
+                        r = _div(r, len(bufs), dtype)
+                    bufs[dst][off:off + cnt] = r
+                else:
+                    bufs[dst][off:off + cnt] = data
+
+
+def interpret_fused(plan, bufs, nbuckets, dtype, mean):
+    P = len(bufs)
+    for b in range(nbuckets):
+        spans, group = plan.fused_spans(b)
+        for off, cnt, chain in spans:
+            acc = None
+            for g in range(0, P, group):
+                gacc = bufs[chain[g]][off:off + cnt].copy()
+                for r in chain[g + 1:g + group]:
+                    gacc = _add(gacc, bufs[r][off:off + cnt], dtype)
+                acc = gacc if acc is None else _add(acc, gacc, dtype)
+            if mean:
+                acc = _div(acc, P, dtype)
+            for r in range(P):
+                bufs[r][off:off + cnt] = acc
+
+
+def _cases():
+    rng = np.random.default_rng(21)
+    cases = []
+    for P in (1, 2, 3, 4, 5, 8, 12, 16):
+        for kind in ("ring", "multiring", "torus2d"):
+            for dtype in (np.float32, np.float16):
+                n = int(rng.integers(1, 400))
+                k, rows, cols, order = 1, 0, 0, None
+                if kind == "multiring":
+                    k = int(rng.integers(1, 5))
+                    order = np.concatenate([rng.permutation(P) for _ in range(k)]).tolist()
+                elif kind == "torus2d":
+                    divs = [d for d in range(1, P + 1) if P % d == 0]
+                    rows = int(rng.choice(divs))
+                    cols = P // rows
+                elif rng.random() < 0.5:
+                    order = rng.permutation(P).tolist()
+                nb = int(rng.integers(1, 4))
+                cuts = sorted(set(int(c) for c in rng.integers(0, n, nb - 1))) if nb > 1 else []
+                edges = [0] + cuts + [n]
+                buckets = [(edges[i], edges[i + 1] - edges[i]) for i in range(len(edges) - 1)]
+                buckets = buckets[::-1]
+                cases.append((P, n, kind, k, rows, cols, order, dtype, buckets))
+    return cases
+
+
+@pytest.mark.parametrize("case", _cases(), ids=lambda c: f"P{c[0]}-n{c[1]}-{c[2]}-{c[7].__name__}")
+@pytest.mark.parametrize("op", ["sum", "mean"])
+def test_tables_replay_to_the_oracle(case, op):
+    P, n, kind, k, rows, cols, order, dtype, buckets = case
+    rng = np.random.default_rng(P * 1000 + n)
+    g = [rng.standard_normal(n).astype(dtype) for _ in range(P)]
+    kinds = {"ring": orc.RING, "multiring": orc.MULTIRING, "torus2d": orc.TORUS2D}
+    ref = [x.copy() for x in g]
+    sent_ref = orc.allreduce(ref, op=orc.MEAN if op == "mean" else orc.SUM, kind=kinds[kind],
+                             k=k, rows=rows, cols=cols, ring_order=order, buckets=buckets)
+    t = ddl.topo(kind, k, rows, cols, order)
+    dt = "f32" if dtype == np.float32 else "f16"
+    for mode in ("stepwise", "fused"):
+        plan = ddl.Plan(P, n, dt, op, t, buckets, mode)
+        bufs = [x.copy() for x in g]
+        if mode == "stepwise":
+            interpret_steps(plan, bufs, len(buckets), dtype)
+        else:
+            interpret_fused(plan, bufs, len(buckets), dtype, op == "mean")
+        for r in range(P):
+            assert bufs[r].tobytes() == ref[r].tobytes(), (mode, r)
+        sent, hbm = plan.traffic()
+        assert sent == [int(v) for v in sent_ref]
+        esz = np.dtype(dtype).itemsize
+        if mode == "fused":
+            assert hbm == 2 * P * n * esz
+        else:
+            assert hbm == 5 * (P - 1) * n * esz
+        plan.destroy()
+
+
+def test_step_counts_and_kinds():
+    for P, kind, rows, cols, want in ((8, "ring", 0, 0, 14), (16, "multiring", 0, 0, 30),
+                                      (16, "torus2d", 4, 4, 12), (6, "torus2d", 2, 3, 6),
+                                      (1, "ring", 0, 0, 0)):
+        plan = ddl.Plan(P, 1000, "f32", "mean", ddl.topo(kind, 4, rows, cols))
+        assert plan.num_steps() == want
+        kinds = [plan.step_kind(s) for s in range(want)]
+        assert kinds == [ddl.DDL_K_REDUCE] * (want // 2) + [ddl.DDL_K_GATHER] * (want // 2)
+        plan.destroy()
+
+
+def test_headline_table_sizes():
+    # 40 ranks, 64 buckets of 4,687,500 fp32: 78 steps of 40 pairs each per
+    # bucket, 40 fused spans per bucket with chunks of 117,184 or 117,188
+    n = 300_000_000
+    buckets = [(i * 4_687_500, 4_687_500) for i in reversed(range(64))]
+    plan = ddl.Plan(40, n, "f32", "mean", ddl.topo("ring"), buckets, "fused")
+    assert plan.num_steps() == 78
+    assert len(plan.step_items(0, 0)) == 40
+    spans, group = plan.fused_spans(0)
+    assert len(spans) == 40 and group == 40
+    assert {c for _, c, _ in spans} == {117_184, 117_188}
+    assert spans[0][0] == 63 * 4_687_500
+    sent, hbm = plan.traffic()
+    # 40 * 4 does not divide 4,687,500, so chunks differ by 4 elements: the
+    # total is exact, each rank is within 2 chunk-size steps per bucket of
+    # the even share 2 (P-1)/P n
+    assert sum(sent) == 2 * 39 * n
+    assert all(abs(s - 2 * 39 * n // 40) <= 64 * 2 * 4 for s in sent)
+    assert hbm == 2 * 40 * n * 4
+    plan.destroy()
+
+
+def test_plan_create_needs_no_gpu():
+    # plan creation and inspection are host-only; no HIP call is made
+    plan = ddl.Plan(16, 25_557_032, "f16", "mean", ddl.topo("torus2d", rows=4, cols=4))
+    spans, group = plan.fused_spans(0)
+    assert group == 4 and len(spans) == 16
+    plan.destroy()
