@@ -31,8 +31,13 @@ def log(*a):
 
 
 def kernel_source_hash():
-    with open(os.path.join(ROOT, "sgd_gradient_all_amd", "csrc", "kernels.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the fused kernel's sources: counter figures taken on another
+    version of the kernel are not reported."""
+    h = hashlib.sha256()
+    for name in ("fused_kernel.hip", "device_common.h", "ddl_internal.h"):
+        with open(os.path.join(ROOT, "sgd_gradient_all_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload, mode):
@@ -58,7 +63,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the step-by-step and overlap measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-buckets", type=int, default=20,
+    ap.add_argument("--cpu-buckets", type=int, default=64,
                     help="buckets of the workload the CPU oracle is timed on")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run one plain device copy of this size (counter calibration)")

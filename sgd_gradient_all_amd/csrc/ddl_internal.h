@@ -8,14 +8,29 @@
 
 namespace ddl {
 
-// One workgroup = 256 lanes = 4 wave64.
-constexpr int kBlock = 256;
+// One workgroup = 256 lanes = 4 wave64 (tuning knob).
+#ifndef DDL_BLOCK
+#define DDL_BLOCK 256
+#endif
+constexpr int kBlock = DDL_BLOCK;
 // Every lane moves 16 bytes per vector access (one dwordx4).
 constexpr int kVecBytes = 16;
 // Vectors per lane per tile: step kernels (one source, one destination)
-// and the fused kernel (P sources, P destinations).
-constexpr int kStepVecsPerLane = 4;
-constexpr int kFusedVecsPerLane = 1;
+// and the fused kernel (P sources, P destinations).  Tuning knobs.
+#ifndef DDL_STEP_VPL
+#define DDL_STEP_VPL 4
+#endif
+#ifndef DDL_FUSED_VPL
+#define DDL_FUSED_VPL 1
+#endif
+#ifndef DDL_FUSED_TPW
+#define DDL_FUSED_TPW 1
+#endif
+constexpr int kStepVecsPerLane = DDL_STEP_VPL;
+constexpr int kFusedVecsPerLane = DDL_FUSED_VPL;
+// Consecutive tiles one fused workgroup walks (address translations of the
+// P rank streams are reused from tile to tile).
+constexpr int kFusedTilesPerGroup = DDL_FUSED_TPW;
 
 // Elements of one tile, by element size.
 constexpr uint64_t step_tile_elems(int esz) {
@@ -70,7 +85,8 @@ struct FusedArgs {
     const uint32_t *prefix;
     const uint8_t *chains;
     uint32_t span_lo, span_hi;
-    uint32_t tile_base;
+    uint32_t tile_base;  // first tile of this launch
+    uint32_t tile_end;   // one past the last tile of this launch
     int P;
     int group;       // chain entries per group (P for rings, cols for the torus)
     int mean;        // divide by P at the end

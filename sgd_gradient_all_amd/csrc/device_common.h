@@ -1,0 +1,89 @@
+// device_common.h -- element types, vector accesses and the tile lookup
+// shared by the step kernels and the fused kernel (gfx950).
+//
+// Arithmetic follows the schedule exactly:
+//  - binary32: a + b in round-to-nearest-even with subnormals kept (the
+//    library is built without fast-math or denormal flushing, and with
+//    packed fp32 math disabled);
+//  - binary16 (Sony "224秒训练ResNet-50" article, "训练设置": FP16 gradient
+//    exchange): every add is done in binary32 and rounded to binary16, the
+//    type the partial sums travel in between steps;
+//  - mean: one correctly rounded binary32 division by P (binary16: of the
+//    value widened to binary32, then rounded to binary16), fused into the
+//    store of the add that completes the sum (Baidu Ring-Allreduce article,
+//    "总结": gradients are averaged).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "ddl_internal.h"
+
+namespace ddl {
+namespace dev {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// Keeps the compiler from narrowing "binary32 divide, then round to
+// binary16" into a binary16 divide, whose lowering is not the correctly
+// rounded binary32 quotient this library promises.
+__device__ __forceinline__ f32x8 opaque(f32x8 v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+__device__ __forceinline__ float opaque1(float v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+struct F32 {
+    using T = float;
+    using V = f32x4;
+    static constexpr int N = 4;
+    __device__ static V add(V a, V b) { return a + b; }
+    __device__ static V div(V a, float d) { return a / d; }
+    __device__ static T add1(T a, T b) { return a + b; }
+    __device__ static T div1(T a, float d) { return a / d; }
+};
+
+struct F16 {
+    using T = _Float16;
+    using V = f16x8;
+    static constexpr int N = 8;
+    __device__ static V add(V a, V b) {
+        f32x8 s = __builtin_convertvector(a, f32x8) + __builtin_convertvector(b, f32x8);
+        return __builtin_convertvector(s, f16x8);
+    }
+    __device__ static V div(V a, float d) {
+        f32x8 q = opaque(__builtin_convertvector(a, f32x8) / d);
+        return __builtin_convertvector(q, f16x8);
+    }
+    __device__ static T add1(T a, T b) { return (T)((float)a + (float)b); }
+    __device__ static T div1(T a, float d) { return (T)opaque1((float)a / d); }
+};
+
+template <class V>
+__device__ __forceinline__ V ldv(const void *p) {
+    return *reinterpret_cast<const V *>(p);
+}
+template <class V>
+__device__ __forceinline__ void stv(void *p, V v) {
+    *reinterpret_cast<V *>(p) = v;
+}
+// Largest i in [lo, hi) with prefix[i] <= tile (prefix is non-decreasing,
+// prefix[lo] <= tile < prefix[hi]).  Uniform across the workgroup.
+__device__ __forceinline__ uint32_t find_item(const uint32_t *__restrict__ prefix,
+                                              uint32_t lo, uint32_t hi, uint32_t tile) {
+    while (hi - lo > 1) {
+        uint32_t mid = lo + ((hi - lo) >> 1);
+        if (prefix[mid] <= tile)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    return lo;
+}
+
+}  // namespace dev
+}  // namespace ddl

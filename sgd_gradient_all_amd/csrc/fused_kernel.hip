@@ -1,0 +1,239 @@
+// fused_kernel.hip -- the single-pass all-reduce (gfx950).
+//
+// Every element is read once from each of the P ranks, summed in the order
+// the schedule sums it, divided by P for the mean, and written once to each
+// rank: 2 P s bytes per element, the floor for this operation.  It is
+// bit-identical to the step-by-step walk because every dependency of the
+// schedule is per element.
+#include "device_common.h"
+
+namespace ddl {
+namespace {
+
+using namespace dev;
+
+// Streaming accesses.  Tuning knobs: non-temporal loads / stores (every
+// element is touched once per pass, so there is nothing to keep in cache),
+// and the number of loads issued ahead of the add chain.
+#ifndef DDL_NT_LOAD
+#define DDL_NT_LOAD 0
+#endif
+#ifndef DDL_NT_STORE
+#define DDL_NT_STORE 1
+#endif
+#ifndef DDL_LOAD_BATCH
+#define DDL_LOAD_BATCH 8
+#endif
+constexpr int kBatch = DDL_LOAD_BATCH;
+
+template <class V>
+__device__ __forceinline__ V ld_stream(const void *p) {
+#if DDL_NT_LOAD
+    return __builtin_nontemporal_load(reinterpret_cast<const V *>(p));
+#else
+    return *reinterpret_cast<const V *>(p);
+#endif
+}
+template <class V>
+__device__ __forceinline__ void st_stream(void *p, V v) {
+#if DDL_NT_STORE
+    __builtin_nontemporal_store(v, reinterpret_cast<V *>(p));
+#else
+    *reinterpret_cast<V *>(p) = v;
+#endif
+}
+
+// ---------------------------------------------------------------------------
+// fused pass: every element is read once from each of the P ranks, summed in
+// the order the schedule sums it -- chain[0..P) in groups of `group`
+// entries, each group left to right, then the group sums left to right --
+// divided by P for the mean, and written once to each rank.
+//
+// The rank pointers, in chain order, are staged in LDS before the first
+// store, so the data loads never wait behind a table load; they are issued
+// eight at a time ahead of the serial add chain.
+// ---------------------------------------------------------------------------
+template <class E>
+struct Chain {
+    using V = typename E::V;
+    V acc = {}, gacc = {};
+    int pos = 0;
+    bool first_group = true;
+    __device__ __forceinline__ void push(V x, int group) {
+        gacc = pos == 0 ? x : E::add(gacc, x);
+        if (++pos == group) {
+            acc = first_group ? gacc : E::add(acc, gacc);
+            first_group = false;
+            pos = 0;
+        }
+    }
+};
+
+// Sums of U element vectors -- e + u * kBlock * N, u < U -- over the chain,
+// the loads of kBatch ranks issued ahead of their adds.  Ungrouped (rings):
+// one chain of P entries.  Grouped (torus): chains of `group` entries, then
+// their sums.
+template <class E, bool kGrouped, int U>
+__device__ __forceinline__ void fused_vecs(const typename E::T *const *sp, int P, int group,
+                                           uint64_t e, typename E::V (&out)[U]) {
+    using V = typename E::V;
+    constexpr uint64_t kStride = (uint64_t)kBlock * E::N;
+    if (!kGrouped) {
+        V acc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            acc[u] = ld_stream<V>(sp[0] + e + u * kStride);
+        int b = 1;
+        for (; b + kBatch <= P; b += kBatch) {
+            V x[kBatch][U];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j)
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    x[j][u] = ld_stream<V>(sp[b + j] + e + u * kStride);
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j)
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    acc[u] = E::add(acc[u], x[j][u]);
+        }
+        for (; b < P; ++b)
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                acc[u] = E::add(acc[u], ld_stream<V>(sp[b] + e + u * kStride));
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            out[u] = acc[u];
+        return;
+    }
+    Chain<E> c[U];
+    int b = 0;
+    for (; b + kBatch <= P; b += kBatch) {
+        V x[kBatch][U];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                x[j][u] = ld_stream<V>(sp[b + j] + e + u * kStride);
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                c[u].push(x[j][u], group);
+    }
+    for (; b < P; ++b)
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            c[u].push(ld_stream<V>(sp[b] + e + u * kStride), group);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        out[u] = c[u].acc;
+}
+
+template <class E, int U>
+__device__ __forceinline__ void store_all(const RankPtrs &bufs, int P, uint64_t e,
+                                          const typename E::V (&v)[U]) {
+    using T = typename E::T;
+    constexpr uint64_t kStride = (uint64_t)kBlock * E::N;
+    for (int r = 0; r < P; ++r)
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            st_stream<typename E::V>(static_cast<T *>(bufs.p[r]) + e + u * kStride, v[u]);
+}
+
+template <class E, bool kGrouped>
+__global__ __launch_bounds__(kBlock) void fused_kernel(RankPtrs bufs, FusedArgs a) {
+    using T = typename E::T;
+    using V = typename E::V;
+    constexpr int U = kFusedVecsPerLane;
+    constexpr uint64_t kTile = fused_tile_elems(sizeof(T));
+    __shared__ const T *src[DDL_MAX_RANKS];
+    const int P = a.P;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t first = a.tile_base + blockIdx.x * (uint32_t)kFusedTilesPerGroup;
+    const uint32_t last = min(first + (uint32_t)kFusedTilesPerGroup, a.tile_end);
+    uint32_t i = a.span_lo, have = UINT32_MAX;
+    for (uint32_t tile = first; tile < last; ++tile) {
+        i = find_item(a.prefix, i, a.span_hi, tile);
+        const DevSpan sp = a.spans[i];
+        if (i != have) {
+            // a new span: its chain decides which rank is read first
+            if (have != UINT32_MAX)
+                __syncthreads();
+            for (int j = (int)tid; j < P; j += kBlock)
+                src[j] = static_cast<const T *>(bufs.p[a.chains[sp.chain_off + j]]);
+            __syncthreads();
+            have = i;
+        }
+        const uint64_t t0 = (uint64_t)(tile - a.prefix[i]) * kTile;
+        const uint64_t rem = sp.len - t0;
+        const uint32_t cnt = (uint32_t)(rem < kTile ? rem : kTile);
+        const uint64_t base = sp.off + t0;
+        uint32_t done = 0;
+        if (sp.flags & kItemAligned) {
+            const uint32_t nvec = cnt / E::N;
+            if (nvec == (uint32_t)(U * kBlock)) {
+                const uint64_t e = base + (uint64_t)tid * E::N;
+                V acc[U];
+                fused_vecs<E, kGrouped, U>(src, P, a.group, e, acc);
+                if (a.mean)
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        acc[u] = E::div(acc[u], a.divisor);
+                store_all<E, U>(bufs, P, e, acc);
+            } else {
+                for (uint32_t v = tid; v < nvec; v += kBlock) {
+                    const uint64_t e = base + (uint64_t)v * E::N;
+                    V acc[1];
+                    fused_vecs<E, kGrouped, 1>(src, P, a.group, e, acc);
+                    if (a.mean)
+                        acc[0] = E::div(acc[0], a.divisor);
+                    store_all<E, 1>(bufs, P, e, acc);
+                }
+            }
+            done = nvec * E::N;
+        }
+        for (uint32_t k = done + tid; k < cnt; k += kBlock) {
+            const uint64_t e = base + k;
+            T acc = 0, gacc = 0;
+            int pos = 0;
+            bool first_group = true;
+            for (int j = 0; j < P; ++j) {
+                T x = src[j][e];
+                gacc = pos == 0 ? x : E::add1(gacc, x);
+                if (++pos == a.group) {
+                    acc = first_group ? gacc : E::add1(acc, gacc);
+                    first_group = false;
+                    pos = 0;
+                }
+            }
+            if (a.mean)
+                acc = E::div1(acc, a.divisor);
+            for (int r = 0; r < P; ++r)
+                static_cast<T *>(bufs.p[r])[e] = acc;
+        }
+    }
+}
+
+}  // namespace
+
+int launch_fused(int dtype, const RankPtrs &bufs, const FusedArgs &a, uint32_t tiles,
+                 void *stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    dim3 grid((tiles + kFusedTilesPerGroup - 1) / kFusedTilesPerGroup), block(kBlock);
+    const bool grouped = a.group != a.P;
+    if (dtype == DDL_F32) {
+        if (grouped)
+            hipLaunchKernelGGL((fused_kernel<F32, true>), grid, block, 0, s, bufs, a);
+        else
+            hipLaunchKernelGGL((fused_kernel<F32, false>), grid, block, 0, s, bufs, a);
+    } else {
+        if (grouped)
+            hipLaunchKernelGGL((fused_kernel<F16, true>), grid, block, 0, s, bufs, a);
+        else
+            hipLaunchKernelGGL((fused_kernel<F16, false>), grid, block, 0, s, bufs, a);
+    }
+    return (int)hipGetLastError();
+}
+
+}  // namespace ddl

@@ -198,6 +198,7 @@ struct Launcher {
         for (uint32_t t = pre[lo]; t < pre[hi]; t += kMaxTilesPerLaunch) {
             const uint32_t tiles = std::min(kMaxTilesPerLaunch, pre[hi] - t);
             a.tile_base = t;
+            a.tile_end = t + tiles;
             int rc = bracket_begin();
             if (rc)
                 return rc;

@@ -1,0 +1,101 @@
+// step_kernels.hip -- one launch per schedule step (gfx950).
+//
+// A launch covers every pair of every ring of every bucket in the group: the
+// schedule is race-free within a step, so all pairs run at once.  Each lane
+// moves dwordx4 vectors of one source and one destination chunk.  The
+// stores stay cached: the next step reads what this one wrote.
+#include "device_common.h"
+
+namespace ddl {
+namespace {
+
+using namespace dev;
+
+// ---------------------------------------------------------------------------
+// step kernels: one launch = one schedule step over every pair of every ring
+// of every bucket in the group.  Reduce: dst = dst (+) src (then / P when the
+// item completes its chunk's sum).  Gather: dst = src.
+// ---------------------------------------------------------------------------
+template <class E, bool kReduce>
+__global__ __launch_bounds__(kBlock) void step_kernel(RankPtrs bufs, StepArgs a) {
+    using T = typename E::T;
+    using V = typename E::V;
+    constexpr uint64_t kTile = step_tile_elems(sizeof(T));
+    const uint32_t tile = a.tile_base + blockIdx.x;
+    const uint32_t i = find_item(a.prefix, a.item_lo, a.item_hi, tile);
+    const DevItem it = a.items[i];
+    const uint64_t t0 = (uint64_t)(tile - a.prefix[i]) * kTile;
+    const uint64_t rem = it.len - t0;
+    const uint32_t cnt = (uint32_t)(rem < kTile ? rem : kTile);
+    T *dst = static_cast<T *>(bufs.p[it.dst]) + it.off + t0;
+    const T *src = static_cast<const T *>(bufs.p[it.src]) + it.off + t0;
+    const bool divide = kReduce && (it.flags & kItemDivide);
+    const uint32_t tid = threadIdx.x;
+    uint32_t done = 0;
+    if (it.flags & kItemAligned) {
+        const uint32_t nvec = cnt / E::N;
+        if (nvec == (uint32_t)(kStepVecsPerLane * kBlock)) {
+            V s[kStepVecsPerLane], d[kStepVecsPerLane];
+#pragma unroll
+            for (int j = 0; j < kStepVecsPerLane; ++j) {
+                s[j] = ldv<V>(src + (size_t)(j * kBlock + tid) * E::N);
+                if (kReduce)
+                    d[j] = ldv<V>(dst + (size_t)(j * kBlock + tid) * E::N);
+            }
+#pragma unroll
+            for (int j = 0; j < kStepVecsPerLane; ++j) {
+                V r = s[j];
+                if (kReduce) {
+                    r = E::add(d[j], s[j]);
+                    if (divide)
+                        r = E::div(r, a.divisor);
+                }
+                stv<V>(dst + (size_t)(j * kBlock + tid) * E::N, r);
+            }
+        } else {
+            for (uint32_t v = tid; v < nvec; v += kBlock) {
+                V r = ldv<V>(src + (size_t)v * E::N);
+                if (kReduce) {
+                    r = E::add(ldv<V>(dst + (size_t)v * E::N), r);
+                    if (divide)
+                        r = E::div(r, a.divisor);
+                }
+                stv<V>(dst + (size_t)v * E::N, r);
+            }
+        }
+        done = nvec * E::N;
+    }
+    // element-wise: the ragged end of a segment, or a whole item whose
+    // offset is not vector aligned
+    for (uint32_t e = done + tid; e < cnt; e += kBlock) {
+        T r = src[e];
+        if (kReduce) {
+            r = E::add1(dst[e], r);
+            if (divide)
+                r = E::div1(r, a.divisor);
+        }
+        dst[e] = r;
+    }
+}
+
+}  // namespace
+
+int launch_step(int dtype, int kind, const RankPtrs &bufs, const StepArgs &a,
+                uint32_t tiles, void *stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    dim3 grid(tiles), block(kBlock);
+    if (dtype == DDL_F32) {
+        if (kind == DDL_K_REDUCE)
+            hipLaunchKernelGGL((step_kernel<F32, true>), grid, block, 0, s, bufs, a);
+        else
+            hipLaunchKernelGGL((step_kernel<F32, false>), grid, block, 0, s, bufs, a);
+    } else {
+        if (kind == DDL_K_REDUCE)
+            hipLaunchKernelGGL((step_kernel<F16, true>), grid, block, 0, s, bufs, a);
+        else
+            hipLaunchKernelGGL((step_kernel<F16, false>), grid, block, 0, s, bufs, a);
+    }
+    return (int)hipGetLastError();
+}
+
+}  // namespace ddl
