@@ -20,14 +20,21 @@ constexpr int kVecBytes = 16;
 #ifndef DDL_STEP_VPL
 #define DDL_STEP_VPL 4
 #endif
-#ifndef DDL_FUSED_VPL
-#define DDL_FUSED_VPL 1
+#ifndef DDL_FUSED_VPL_F32
+#define DDL_FUSED_VPL_F32 1
+#endif
+#ifndef DDL_FUSED_VPL_F16
+#define DDL_FUSED_VPL_F16 2
 #endif
 #ifndef DDL_FUSED_TPW
 #define DDL_FUSED_TPW 1
 #endif
 constexpr int kStepVecsPerLane = DDL_STEP_VPL;
-constexpr int kFusedVecsPerLane = DDL_FUSED_VPL;
+// Fused pass, vectors per lane per tile: one dwordx4 of binary32, two of
+// binary16 (measured best for the 40-rank fp32 and 16-rank fp16 passes).
+constexpr int fused_vecs_per_lane(int esz) {
+    return esz == 4 ? DDL_FUSED_VPL_F32 : DDL_FUSED_VPL_F16;
+}
 // Consecutive tiles one fused workgroup walks (address translations of the
 // P rank streams are reused from tile to tile).
 constexpr int kFusedTilesPerGroup = DDL_FUSED_TPW;
@@ -37,7 +44,7 @@ constexpr uint64_t step_tile_elems(int esz) {
     return (uint64_t)kBlock * kStepVecsPerLane * (kVecBytes / esz);
 }
 constexpr uint64_t fused_tile_elems(int esz) {
-    return (uint64_t)kBlock * kFusedVecsPerLane * (kVecBytes / esz);
+    return (uint64_t)kBlock * fused_vecs_per_lane(esz) * (kVecBytes / esz);
 }
 
 enum : uint32_t {

@@ -5,6 +5,8 @@
 // rank: 2 P s bytes per element, the floor for this operation.  It is
 // bit-identical to the step-by-step walk because every dependency of the
 // schedule is per element.
+#include <stdlib.h>
+
 #include "device_common.h"
 
 namespace ddl {
@@ -12,27 +14,35 @@ namespace {
 
 using namespace dev;
 
-// Streaming accesses.  Tuning knobs: non-temporal loads / stores (every
-// element is touched once per pass, so there is nothing to keep in cache),
-// and the number of loads issued ahead of the add chain.
-#ifndef DDL_NT_LOAD
-#define DDL_NT_LOAD 0
-#endif
+// Streaming accesses.  Every element is touched once per pass, so the
+// results are written with non-temporal stores.  Loads are non-temporal for
+// passes over at most kNtLoadMaxRanks ranks: measured on MI355X, that wins
+// 5-8% at 8 and 16 ranks and loses 4% at 40 (tuning knobs below, and the
+// environment variable DDL_FUSED_NT_LOAD_MAX_P at run time).
 #ifndef DDL_NT_STORE
 #define DDL_NT_STORE 1
+#endif
+#ifndef DDL_NT_LOAD_MAX_P
+#define DDL_NT_LOAD_MAX_P 24
 #endif
 #ifndef DDL_LOAD_BATCH
 #define DDL_LOAD_BATCH 8
 #endif
 constexpr int kBatch = DDL_LOAD_BATCH;
-
-template <class V>
-__device__ __forceinline__ V ld_stream(const void *p) {
-#if DDL_NT_LOAD
-    return __builtin_nontemporal_load(reinterpret_cast<const V *>(p));
-#else
-    return *reinterpret_cast<const V *>(p);
+// Waves per SIMD the register allocation must allow: 8 for one vector per
+// lane (no spills at 56 VGPRs), 4 for two.
+#ifndef DDL_FUSED_WAVES_1
+#define DDL_FUSED_WAVES_1 8
 #endif
+#ifndef DDL_FUSED_WAVES_2
+#define DDL_FUSED_WAVES_2 4
+#endif
+
+template <class V, bool kNt>
+__device__ __forceinline__ V ld_stream(const void *p) {
+    if (kNt)
+        return __builtin_nontemporal_load(reinterpret_cast<const V *>(p));
+    return *reinterpret_cast<const V *>(p);
 }
 template <class V>
 __device__ __forceinline__ void st_stream(void *p, V v) {
@@ -73,7 +83,7 @@ struct Chain {
 // the loads of kBatch ranks issued ahead of their adds.  Ungrouped (rings):
 // one chain of P entries.  Grouped (torus): chains of `group` entries, then
 // their sums.
-template <class E, bool kGrouped, int U>
+template <class E, bool kGrouped, bool kNt, int U>
 __device__ __forceinline__ void fused_vecs(const typename E::T *const *sp, int P, int group,
                                            uint64_t e, typename E::V (&out)[U]) {
     using V = typename E::V;
@@ -82,7 +92,7 @@ __device__ __forceinline__ void fused_vecs(const typename E::T *const *sp, int P
         V acc[U];
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            acc[u] = ld_stream<V>(sp[0] + e + u * kStride);
+            acc[u] = ld_stream<V, kNt>(sp[0] + e + u * kStride);
         int b = 1;
         for (; b + kBatch <= P; b += kBatch) {
             V x[kBatch][U];
@@ -90,7 +100,7 @@ __device__ __forceinline__ void fused_vecs(const typename E::T *const *sp, int P
             for (int j = 0; j < kBatch; ++j)
 #pragma unroll
                 for (int u = 0; u < U; ++u)
-                    x[j][u] = ld_stream<V>(sp[b + j] + e + u * kStride);
+                    x[j][u] = ld_stream<V, kNt>(sp[b + j] + e + u * kStride);
 #pragma unroll
             for (int j = 0; j < kBatch; ++j)
 #pragma unroll
@@ -100,7 +110,7 @@ __device__ __forceinline__ void fused_vecs(const typename E::T *const *sp, int P
         for (; b < P; ++b)
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                acc[u] = E::add(acc[u], ld_stream<V>(sp[b] + e + u * kStride));
+                acc[u] = E::add(acc[u], ld_stream<V, kNt>(sp[b] + e + u * kStride));
 #pragma unroll
         for (int u = 0; u < U; ++u)
             out[u] = acc[u];
@@ -114,7 +124,7 @@ __device__ __forceinline__ void fused_vecs(const typename E::T *const *sp, int P
         for (int j = 0; j < kBatch; ++j)
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                x[j][u] = ld_stream<V>(sp[b + j] + e + u * kStride);
+                x[j][u] = ld_stream<V, kNt>(sp[b + j] + e + u * kStride);
 #pragma unroll
         for (int j = 0; j < kBatch; ++j)
 #pragma unroll
@@ -124,7 +134,7 @@ __device__ __forceinline__ void fused_vecs(const typename E::T *const *sp, int P
     for (; b < P; ++b)
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            c[u].push(ld_stream<V>(sp[b] + e + u * kStride), group);
+            c[u].push(ld_stream<V, kNt>(sp[b] + e + u * kStride), group);
 #pragma unroll
     for (int u = 0; u < U; ++u)
         out[u] = c[u].acc;
@@ -141,11 +151,14 @@ __device__ __forceinline__ void store_all(const RankPtrs &bufs, int P, uint64_t 
             st_stream<typename E::V>(static_cast<T *>(bufs.p[r]) + e + u * kStride, v[u]);
 }
 
-template <class E, bool kGrouped>
-__global__ __launch_bounds__(kBlock) void fused_kernel(RankPtrs bufs, FusedArgs a) {
+template <class E, bool kGrouped, bool kNt>
+__global__ __launch_bounds__(kBlock)
+__attribute__((amdgpu_waves_per_eu(fused_vecs_per_lane(sizeof(typename E::T)) == 1
+                                       ? DDL_FUSED_WAVES_1 : DDL_FUSED_WAVES_2)))
+void fused_kernel(RankPtrs bufs, FusedArgs a) {
     using T = typename E::T;
     using V = typename E::V;
-    constexpr int U = kFusedVecsPerLane;
+    constexpr int U = fused_vecs_per_lane(sizeof(T));
     constexpr uint64_t kTile = fused_tile_elems(sizeof(T));
     __shared__ const T *src[DDL_MAX_RANKS];
     const int P = a.P;
@@ -175,7 +188,7 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(RankPtrs bufs, FusedArgs 
             if (nvec == (uint32_t)(U * kBlock)) {
                 const uint64_t e = base + (uint64_t)tid * E::N;
                 V acc[U];
-                fused_vecs<E, kGrouped, U>(src, P, a.group, e, acc);
+                fused_vecs<E, kGrouped, kNt, U>(src, P, a.group, e, acc);
                 if (a.mean)
 #pragma unroll
                     for (int u = 0; u < U; ++u)
@@ -185,7 +198,7 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(RankPtrs bufs, FusedArgs 
                 for (uint32_t v = tid; v < nvec; v += kBlock) {
                     const uint64_t e = base + (uint64_t)v * E::N;
                     V acc[1];
-                    fused_vecs<E, kGrouped, 1>(src, P, a.group, e, acc);
+                    fused_vecs<E, kGrouped, kNt, 1>(src, P, a.group, e, acc);
                     if (a.mean)
                         acc[0] = E::div(acc[0], a.divisor);
                     store_all<E, 1>(bufs, P, e, acc);
@@ -217,21 +230,41 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(RankPtrs bufs, FusedArgs 
 
 }  // namespace
 
+namespace {
+
+int nt_load_max_ranks() {
+    static const int v = [] {
+        const char *e = getenv("DDL_FUSED_NT_LOAD_MAX_P");
+        return e ? atoi(e) : DDL_NT_LOAD_MAX_P;
+    }();
+    return v;
+}
+
+template <class E, bool kGrouped>
+void launch_e(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a) {
+    if (a.P <= nt_load_max_ranks())
+        hipLaunchKernelGGL((fused_kernel<E, kGrouped, true>), grid, dim3(kBlock), 0, s, bufs, a);
+    else
+        hipLaunchKernelGGL((fused_kernel<E, kGrouped, false>), grid, dim3(kBlock), 0, s, bufs, a);
+}
+
+}  // namespace
+
 int launch_fused(int dtype, const RankPtrs &bufs, const FusedArgs &a, uint32_t tiles,
                  void *stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    dim3 grid((tiles + kFusedTilesPerGroup - 1) / kFusedTilesPerGroup), block(kBlock);
+    dim3 grid((tiles + kFusedTilesPerGroup - 1) / kFusedTilesPerGroup);
     const bool grouped = a.group != a.P;
     if (dtype == DDL_F32) {
         if (grouped)
-            hipLaunchKernelGGL((fused_kernel<F32, true>), grid, block, 0, s, bufs, a);
+            launch_e<F32, true>(grid, s, bufs, a);
         else
-            hipLaunchKernelGGL((fused_kernel<F32, false>), grid, block, 0, s, bufs, a);
+            launch_e<F32, false>(grid, s, bufs, a);
     } else {
         if (grouped)
-            hipLaunchKernelGGL((fused_kernel<F16, true>), grid, block, 0, s, bufs, a);
+            launch_e<F16, true>(grid, s, bufs, a);
         else
-            hipLaunchKernelGGL((fused_kernel<F16, false>), grid, block, 0, s, bufs, a);
+            launch_e<F16, false>(grid, s, bufs, a);
     }
     return (int)hipGetLastError();
 }
