@@ -127,7 +127,9 @@ def main():
         kms, launches, kmax = plan.profile_read()
         return ms, kms, launches, kmax
 
+    t_plan = time.perf_counter()
     plan = ddl.Plan(w.P, w.n, w.dtype, w.op, topo, buckets, args.mode)
+    plan_build_ms = (time.perf_counter() - t_plan) * 1e3
     plan.set_profiling(True)
     _, hbm_bytes = plan.traffic()
     ms, kms, launches, kmax = timed(plan, args.steps, args.warmup)
@@ -173,6 +175,7 @@ def main():
             "max_launch_us": round(kmax * 1e3, 2),
             "algorithmic_bytes_per_launch": int(bytes_per_launch),
         },
+        "plan_build_ms": round(plan_build_ms, 2),
         "device": dev_name,
     }
     plan.destroy()

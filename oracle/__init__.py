@@ -44,6 +44,8 @@ def lib():
         L.ddl_oracle_allreduce.restype = i32
         L.ddl_oracle_sum_f64.argtypes = [ctypes.POINTER(vp), i32, u64, i32, i32, vp]
         L.ddl_oracle_sum_f64.restype = i32
+        L.ddl_oracle_sgd.argtypes = [ctypes.POINTER(vp), i32, vp, u64, i32, ctypes.c_float]
+        L.ddl_oracle_sgd.restype = i32
         L.ddl_oracle_split.argtypes = [u64, i32, u64, ctypes.POINTER(u64)]
         L.ddl_oracle_split.restype = None
         for name in ("ddl_oracle_f16_to_f32", "ddl_oracle_f32_to_f16"):
@@ -145,6 +147,19 @@ def sum_f64(bufs, op=SUM):
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return out
+
+
+def sgd(weights, y, lr):
+    """In place: every float32 array in weights takes w - lr * y (binary32,
+    product then difference), y the all-reduced gradient."""
+    L = lib()
+    for w in weights:
+        assert w.dtype == np.float32 and w.flags.c_contiguous and w.shape == y.shape
+    ptrs = (ctypes.c_void_p * len(weights))(*[w.ctypes.data for w in weights])
+    rc = L.ddl_oracle_sgd(ptrs, len(weights), y.ctypes.data, y.size, _dtype_code(y.dtype),
+                          float(lr))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
 
 
 def split(L_, m, q):

@@ -37,6 +37,9 @@
  * chunk's sum (the last reduce-scatter step that covers all P ranks), before
  * any copy, so every rank receives the same bits.
  *
+ * After the all-reduce, ddl_oracle_sgd is the plain SGD step w = w - lr*y
+ * that synchronous SGD takes with the averaged gradient.
+ *
  * Parity pins (tests/test_oracle_*.py): closed forms, exact small-integer
  * sums, hand-worked adversarial examples of the chain order, rank identity,
  * the traffic identity and the pages' "about 2.4 GB", reductions between the
@@ -430,6 +433,23 @@ int ddl_oracle_allreduce(void *const *bufs, int P, uint64_t n, int dtype, int op
                              bucket_off[b], bucket_len[b], mean);
     }
     free(w.msg);
+    fpenv_leave(env);
+    return 0;
+}
+
+int ddl_oracle_sgd(float *const *weights, int nweights, const void *y, uint64_t count,
+                   int dtype, float lr)
+{
+    if (nweights < 1 || !weights || (!y && count))
+        return -1;
+    unsigned int env = fpenv_enter();
+    for (int r = 0; r < nweights; ++r) {
+        for (uint64_t e = 0; e < count; ++e) {
+            float g = dtype == ORC_F32 ? ((const float *)y)[e] : h2f(((const uint16_t *)y)[e]);
+            float step = lr * g;
+            weights[r][e] = weights[r][e] - step;
+        }
+    }
     fpenv_leave(env);
     return 0;
 }

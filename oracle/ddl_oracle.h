@@ -62,6 +62,16 @@ int ddl_oracle_allreduce(void *const *bufs, int P, uint64_t n, int dtype, int op
                          int nbuckets, uint64_t q, uint64_t win_lo, uint64_t win_hi,
                          uint64_t *sent);
 
+/* Plain SGD step after the all-reduce (the Baidu article, "总结": the
+ * all-reduce serves synchronous stochastic gradient descent):
+ * for every replica r < nweights and element e < count
+ *     w_r[e] = w_r[e] - lr * y[e]
+ * in binary32, two roundings (the product, then the difference), where y is
+ * the all-reduced gradient (identical on every rank) widened to binary32.
+ * weights: nweights binary32 host arrays; y: count elements of dtype. */
+int ddl_oracle_sgd(float *const *weights, int nweights, const void *y, uint64_t count,
+                   int dtype, float lr);
+
 /* The plain definition: out[e] = sum over ranks of g_r[e] in binary64,
  * divided by P for ORC_MEAN.  Reference for tolerance checks. */
 int ddl_oracle_sum_f64(const void *const *bufs, int P, uint64_t count, int dtype,

@@ -12,11 +12,6 @@ import pytest
 
 import oracle as orc
 
-TOPOS = [
-    # (kind, k, rows, cols) for a given P, generated below
-]
-
-
 def topologies(P):
     """Every schedule the oracle knows, at P ranks."""
     out = [("ring", dict(kind=orc.RING))]
@@ -455,3 +450,44 @@ def test_oracle_rejects_bad_arguments():
         orc.allreduce(g, buckets=[(0, 4), (2, 4)])
     with pytest.raises(ValueError):
         orc.allreduce(g, buckets=[(0, 4)])
+
+
+# ---------------------------------------------------------------------------
+# the SGD step after the all-reduce: w - lr * y, binary32, two roundings
+# ---------------------------------------------------------------------------
+def test_sgd_closed_forms():
+    w = np.array([1.0, 0.5, -3.0, 0.0], np.float32)
+    y = np.array([2.0, 1.0, -4.0, 0.0], np.float32)
+    orc.sgd([w], y, 0.5)
+    assert w.tolist() == [0.0, 0.0, -1.0, 0.0]
+    # binary16 gradients are widened exactly
+    w16 = np.array([1.0, 1.0], np.float32)
+    orc.sgd([w16], np.array([2.0, -0.25], np.float16), 0.25)
+    assert w16.tolist() == [0.5, 1.0625]
+
+
+def test_sgd_two_roundings_not_fused():
+    # lr * y rounds before the subtraction: pick values where a fused
+    # multiply-add would round differently
+    rng = np.random.default_rng(31)
+    w = rng.standard_normal(100000).astype(np.float32)
+    y = rng.standard_normal(100000).astype(np.float32)
+    lr = np.float32(0.1)
+    got = w.copy()
+    orc.sgd([got], y, float(lr))
+    want = w - (lr * y)                       # numpy float32: two roundings
+    assert np.array_equal(got, want)
+    fused = (w.astype(np.float64) - np.float64(lr) * y.astype(np.float64)).astype(np.float32)
+    assert np.count_nonzero(fused != got) > 0
+
+
+def test_sgd_every_replica_and_allreduce_then_update():
+    # after a mean all-reduce every replica moves by the same step
+    rng = np.random.default_rng(32)
+    P, L = 5, 203
+    g = [rng.standard_normal(L).astype(np.float32) for _ in range(P)]
+    out, _ = run(g, op=orc.MEAN)
+    ws = [np.full(L, 3.0, np.float32) for _ in range(P)]
+    orc.sgd(ws, out[0], 0.01)
+    for w in ws:
+        assert np.array_equal(w, np.float32(3.0) - np.float32(0.01) * out[0])
