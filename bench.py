@@ -293,7 +293,65 @@ def extras(args, w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_b
         del scratch
         torch.cuda.empty_cache()
         log(f"bench: overlap {out['overlap']}")
+
+    out["sgd"] = sgd_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_ms)
     return out
+
+
+def sgd_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_ms):
+    """The SGD step fused into the all-reduce's epilogue, against the
+    all-reduce followed by a separate update of every replica."""
+    lr = 0.01
+    esz = 4 if w.dtype == "f32" else 2
+    free = torch.cuda.mem_get_info()[0]
+    nrep = w.P if w.P * w.n * 4 < 0.8 * free else 1
+    weights = [torch.empty(w.n, dtype=torch.float32, device="cuda") for _ in range(nrep)]
+    for t in weights:
+        synth.fill_device(t.data_ptr(), w.n, synth.F32, "uniform", 77, 0)
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event() for _ in buckets] if w.side_stream else None
+    plan = ddl.Plan(w.P, w.n, w.dtype, w.op, topo, buckets, "fused")
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {"replicas": nrep, "lr": lr}
+    for keep in (True, False):
+        def one():
+            if evs:
+                for e in evs:
+                    e.record(main_stream)
+            plan.execute_sgd(bufs, weights, lr, keep_grads=keep, events=evs, stream=main_stream)
+        one()
+        torch.cuda.synchronize()
+        reps = 3
+        t0.record(main_stream)
+        for _ in range(reps):
+            one()
+        t1.record(main_stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / reps
+        nbytes = (2 if keep else 1) * w.P * w.n * esz + 2 * 4 * nrep * w.n
+        res["keep_grads" if keep else "drop_grads"] = {
+            "ms": round(ms, 3), "hbm_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "bytes": nbytes}
+    plan.destroy()
+    # the unfused baseline: the all-reduce, then w -= lr * y on every replica
+    gview = [b if b.dtype == torch.float32 else b.float() for b in bufs[:1]]
+    def separate():
+        torch._foreach_add_(weights, [gview[0]] * nrep, alpha=-lr)
+    separate()
+    torch.cuda.synchronize()
+    reps = 3
+    t0.record(main_stream)
+    for _ in range(reps):
+        separate()
+    t1.record(main_stream)
+    torch.cuda.synchronize()
+    upd_ms = t0.elapsed_time(t1) / reps
+    res["separate_update_ms"] = round(upd_ms, 3)
+    res["allreduce_plus_separate_ms"] = round(fused_ms + upd_ms, 3)
+    del weights
+    torch.cuda.empty_cache()
+    log(f"bench: sgd {res}")
+    return res
 
 
 def cpu_baseline(args, w, topo, torch, ddl, synth, np):

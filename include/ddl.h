@@ -128,6 +128,28 @@ int ddl_plan_create(ddl_plan *out, int P, size_t n, ddl_dtype dtype, ddl_op op,
 int ddl_plan_execute(ddl_plan plan, void *const *bufs, void *const *ready_events,
                      void *stream, void *done_event);
 
+/* The all-reduce followed by the SGD step it serves, fused into the
+ * reduction's epilogue (the Baidu article, "总结": the all-reduce averages
+ * gradients for synchronous stochastic gradient descent).  Once the reduced
+ * gradient y reaches a rank, that rank's binary32 weights take
+ *     w[e] = w[e] - lr * y[e]
+ * (binary16 y widened exactly; the product rounded before the difference).
+ *  weights     nweights device pointers to n binary32 elements, 16-byte
+ *              aligned: nweights == P gives one replica per rank (each
+ *              updated once), nweights == 1 one replica shared by all ranks
+ *              (updated once).  Replicas must not overlap each other or bufs.
+ *  keep_grads  1: bufs end with the all-reduce result as ddl_plan_execute
+ *              leaves them.  0 (DDL_FUSED plans only): bufs are left as they
+ *              were -- the reduced gradient is consumed by the update and
+ *              never written, saving P writes per element.
+ * In DDL_STEPWISE plans the owner of each chunk updates at the add that
+ * completes the sum and every other rank when the all-gather delivers it.
+ * Other arguments and the asynchrony are those of ddl_plan_execute.
+ * DDL_E_ARG for any other nweights, or keep_grads == 0 on a stepwise plan. */
+int ddl_plan_execute_sgd(ddl_plan plan, void *const *bufs, void *const *weights, int nweights,
+                         float lr, int keep_grads, void *const *ready_events, void *stream,
+                         void *done_event);
+
 /* One-shot form: looks up (or builds and caches) the plan for these
  * arguments -- the cache key is everything except the buffers and events --
  * and executes it with the buckets' ready_event fields.  Thread-safe. */

@@ -61,6 +61,8 @@ def lib():
             "ddl_plan_execute": ([vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp], i32),
             "ddl_allreduce": ([ctypes.POINTER(vp), i32, sz, i32, i32, P_topo, P_bucket, i32,
                                i32, vp, vp], i32),
+            "ddl_plan_execute_sgd": ([vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32,
+                                      ctypes.c_float, i32, ctypes.POINTER(vp), vp, vp], i32),
             "ddl_plan_traffic": ([vp, ctypes.POINTER(sz), ctypes.POINTER(sz)], i32),
             "ddl_plan_destroy": ([vp], i32),
             "ddl_cache_clear": ([], i32),
@@ -174,6 +176,19 @@ class Plan:
             ev = (ctypes.c_void_p * max(1, len(events)))(*[_ptr(e) for e in events])
         _check(lib().ddl_plan_execute(self.handle, _bufs(bufs), ev, _ptr(stream),
                                       _ptr(done_event)), "ddl_plan_execute")
+
+    def execute_sgd(self, bufs, weights, lr, keep_grads=True, events=None, stream=None,
+                    done_event=None):
+        """All-reduce, then w = w - lr * y on every weight replica (one per rank,
+        or a single shared one), fused into the reduction's epilogue."""
+        if len(bufs) != self.P:
+            raise ValueError(f"expected {self.P} buffers, got {len(bufs)}")
+        ev = None
+        if events is not None:
+            ev = (ctypes.c_void_p * max(1, len(events)))(*[_ptr(e) for e in events])
+        _check(lib().ddl_plan_execute_sgd(self.handle, _bufs(bufs), _bufs(weights), len(weights),
+                                          float(lr), 1 if keep_grads else 0, ev, _ptr(stream),
+                                          _ptr(done_event)), "ddl_plan_execute_sgd")
 
     def traffic(self):
         sent = (ctypes.c_size_t * self.P)()

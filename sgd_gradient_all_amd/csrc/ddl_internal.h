@@ -50,6 +50,7 @@ constexpr uint64_t fused_tile_elems(int esz) {
 enum : uint32_t {
     kItemDivide = 1u,   // divide by P after the add (mean epilogue)
     kItemAligned = 2u,  // offset is a multiple of 16 B / element size
+    kItemFinal = 4u,    // this add completes the chunk's sum (its owner)
 };
 
 // One pair transfer of one step (device layout, 32 bytes).
@@ -100,10 +101,22 @@ struct FusedArgs {
     float divisor;
 };
 
-// Kernel launchers (kernels.hip).  Return hipError_t as int.
+// The SGD step fused into the all-reduce's epilogue: binary32 weight
+// replicas w[0..nweights) (nweights 1 = one replica shared by all ranks,
+// or P = one per rank) take w - lr * y once the reduced value y reaches
+// them.  keep_grads = 0 (fused pass only) leaves the gradient buffers as
+// they were instead of writing y back.
+struct SgdArgs {
+    RankPtrs w;
+    float lr;
+    int nweights;
+    int keep_grads;
+};
+
+// Kernel launchers.  sgd may be null (plain all-reduce).  Return hipError_t.
 int launch_step(int dtype, int kind, const RankPtrs &bufs, const StepArgs &a,
-                uint32_t tiles, void *stream);
-int launch_fused(int dtype, const RankPtrs &bufs, const FusedArgs &a, uint32_t tiles,
-                 void *stream);
+                const SgdArgs *sgd, uint32_t tiles, void *stream);
+int launch_fused(int dtype, const RankPtrs &bufs, const FusedArgs &a, const SgdArgs *sgd,
+                 uint32_t tiles, void *stream);
 
 }  // namespace ddl

@@ -37,10 +37,14 @@ __device__ __forceinline__ float opaque1(float v) {
     return v;
 }
 
+// E::W is the binary32 vector of the N elements of one E::V (the weights
+// of the SGD step are binary32 whatever the gradient type).
 struct F32 {
     using T = float;
     using V = f32x4;
+    using W = f32x4;
     static constexpr int N = 4;
+    __device__ static W widen(V a) { return a; }
     __device__ static V add(V a, V b) { return a + b; }
     __device__ static V div(V a, float d) { return a / d; }
     __device__ static T add1(T a, T b) { return a + b; }
@@ -50,7 +54,9 @@ struct F32 {
 struct F16 {
     using T = _Float16;
     using V = f16x8;
+    using W = f32x8;
     static constexpr int N = 8;
+    __device__ static W widen(V a) { return __builtin_convertvector(a, f32x8); }
     __device__ static V add(V a, V b) {
         f32x8 s = __builtin_convertvector(a, f32x8) + __builtin_convertvector(b, f32x8);
         return __builtin_convertvector(s, f16x8);
@@ -62,6 +68,15 @@ struct F16 {
     __device__ static T add1(T a, T b) { return (T)((float)a + (float)b); }
     __device__ static T div1(T a, float d) { return (T)opaque1((float)a / d); }
 };
+
+// The SGD step w - lr * y in binary32: the product is rounded before the
+// difference (the library is built with -ffp-contract=off, so no fused
+// multiply-add is formed).
+template <class W>
+__device__ __forceinline__ W sgd_step(W w, W y, float lr) {
+    const W step = y * lr;
+    return w - step;
+}
 
 template <class V>
 __device__ __forceinline__ V ldv(const void *p) {

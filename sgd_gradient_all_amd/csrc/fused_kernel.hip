@@ -151,11 +151,24 @@ __device__ __forceinline__ void store_all(const RankPtrs &bufs, int P, uint64_t 
             st_stream<typename E::V>(static_cast<T *>(bufs.p[r]) + e + u * kStride, v[u]);
 }
 
-template <class E, bool kGrouped, bool kNt>
-__global__ __launch_bounds__(kBlock)
-__attribute__((amdgpu_waves_per_eu(fused_vecs_per_lane(sizeof(typename E::T)) == 1
-                                       ? DDL_FUSED_WAVES_1 : DDL_FUSED_WAVES_2)))
-void fused_kernel(RankPtrs bufs, FusedArgs a) {
+// The SGD step of every weight replica on the reduced vectors v[0..U) of
+// element e (binary32 weights; non-temporal like the rest of the pass).
+template <class E, bool kNt, int U>
+__device__ __forceinline__ void sgd_all(const SgdArgs *g, uint64_t e,
+                                        const typename E::V (&v)[U]) {
+    using W = typename E::W;
+    constexpr uint64_t kStride = (uint64_t)kBlock * E::N;
+    for (int r = 0; r < g->nweights; ++r)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float *wp = static_cast<float *>(g->w.p[r]) + e + u * kStride;
+            st_stream<W>(wp, sgd_step<W>(ld_stream<W, kNt>(wp), E::widen(v[u]), g->lr));
+        }
+}
+
+template <class E, bool kGrouped, bool kNt, bool kSgd>
+__device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs &a,
+                                           const SgdArgs *g) {
     using T = typename E::T;
     using V = typename E::V;
     constexpr int U = fused_vecs_per_lane(sizeof(T));
@@ -193,7 +206,10 @@ void fused_kernel(RankPtrs bufs, FusedArgs a) {
 #pragma unroll
                     for (int u = 0; u < U; ++u)
                         acc[u] = E::div(acc[u], a.divisor);
-                store_all<E, U>(bufs, P, e, acc);
+                if (!kSgd || g->keep_grads)
+                    store_all<E, U>(bufs, P, e, acc);
+                if (kSgd)
+                    sgd_all<E, kNt, U>(g, e, acc);
             } else {
                 for (uint32_t v = tid; v < nvec; v += kBlock) {
                     const uint64_t e = base + (uint64_t)v * E::N;
@@ -201,7 +217,10 @@ void fused_kernel(RankPtrs bufs, FusedArgs a) {
                     fused_vecs<E, kGrouped, kNt, 1>(src, P, a.group, e, acc);
                     if (a.mean)
                         acc[0] = E::div(acc[0], a.divisor);
-                    store_all<E, 1>(bufs, P, e, acc);
+                    if (!kSgd || g->keep_grads)
+                        store_all<E, 1>(bufs, P, e, acc);
+                    if (kSgd)
+                        sgd_all<E, kNt, 1>(g, e, acc);
                 }
             }
             done = nvec * E::N;
@@ -222,10 +241,33 @@ void fused_kernel(RankPtrs bufs, FusedArgs a) {
             }
             if (a.mean)
                 acc = E::div1(acc, a.divisor);
-            for (int r = 0; r < P; ++r)
-                static_cast<T *>(bufs.p[r])[e] = acc;
+            if (!kSgd || g->keep_grads)
+                for (int r = 0; r < P; ++r)
+                    static_cast<T *>(bufs.p[r])[e] = acc;
+            if (kSgd)
+                for (int r = 0; r < g->nweights; ++r) {
+                    float *wp = static_cast<float *>(g->w.p[r]) + e;
+                    *wp = sgd_step<float>(*wp, (float)acc, g->lr);
+                }
         }
     }
+}
+
+#define DDL_FUSED_OCCUPANCY                                                      \
+    __attribute__((amdgpu_waves_per_eu(fused_vecs_per_lane(sizeof(typename E::T)) == 1 \
+                                           ? DDL_FUSED_WAVES_1                        \
+                                           : DDL_FUSED_WAVES_2)))
+
+template <class E, bool kGrouped, bool kNt>
+__global__ __launch_bounds__(kBlock) DDL_FUSED_OCCUPANCY
+void fused_kernel(RankPtrs bufs, FusedArgs a) {
+    fused_body<E, kGrouped, kNt, false>(bufs, a, nullptr);
+}
+
+template <class E, bool kGrouped, bool kNt>
+__global__ __launch_bounds__(kBlock) DDL_FUSED_OCCUPANCY
+void fused_sgd_kernel(RankPtrs bufs, FusedArgs a, SgdArgs g) {
+    fused_body<E, kGrouped, kNt, true>(bufs, a, &g);
 }
 
 }  // namespace
@@ -241,30 +283,41 @@ int nt_load_max_ranks() {
 }
 
 template <class E, bool kGrouped>
-void launch_e(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a) {
-    if (a.P <= nt_load_max_ranks())
-        hipLaunchKernelGGL((fused_kernel<E, kGrouped, true>), grid, dim3(kBlock), 0, s, bufs, a);
-    else
-        hipLaunchKernelGGL((fused_kernel<E, kGrouped, false>), grid, dim3(kBlock), 0, s, bufs, a);
+void launch_e(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a,
+              const SgdArgs *sgd) {
+    const dim3 block(kBlock);
+    const bool nt = a.P <= nt_load_max_ranks();
+    if (sgd) {
+        if (nt)
+            hipLaunchKernelGGL((fused_sgd_kernel<E, kGrouped, true>), grid, block, 0, s, bufs, a,
+                               *sgd);
+        else
+            hipLaunchKernelGGL((fused_sgd_kernel<E, kGrouped, false>), grid, block, 0, s, bufs,
+                               a, *sgd);
+    } else if (nt) {
+        hipLaunchKernelGGL((fused_kernel<E, kGrouped, true>), grid, block, 0, s, bufs, a);
+    } else {
+        hipLaunchKernelGGL((fused_kernel<E, kGrouped, false>), grid, block, 0, s, bufs, a);
+    }
 }
 
 }  // namespace
 
-int launch_fused(int dtype, const RankPtrs &bufs, const FusedArgs &a, uint32_t tiles,
-                 void *stream) {
+int launch_fused(int dtype, const RankPtrs &bufs, const FusedArgs &a, const SgdArgs *sgd,
+                 uint32_t tiles, void *stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     dim3 grid((tiles + kFusedTilesPerGroup - 1) / kFusedTilesPerGroup);
     const bool grouped = a.group != a.P;
     if (dtype == DDL_F32) {
         if (grouped)
-            launch_e<F32, true>(grid, s, bufs, a);
+            launch_e<F32, true>(grid, s, bufs, a, sgd);
         else
-            launch_e<F32, false>(grid, s, bufs, a);
+            launch_e<F32, false>(grid, s, bufs, a, sgd);
     } else {
         if (grouped)
-            launch_e<F16, true>(grid, s, bufs, a);
+            launch_e<F16, true>(grid, s, bufs, a, sgd);
         else
-            launch_e<F16, false>(grid, s, bufs, a);
+            launch_e<F16, false>(grid, s, bufs, a, sgd);
     }
     return (int)hipGetLastError();
 }

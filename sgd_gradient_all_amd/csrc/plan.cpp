@@ -113,12 +113,13 @@ int bind_device(ddl_plan p, int dev) {
         if ((rc = upload(&p->d_items, items.data(), items.size())) ||
             (rc = upload(&p->d_prefix, prefix.data(), prefix.size())))
             return rc;
-    } else {
-        if ((rc = upload(&p->d_spans, s.spans.data(), s.spans.size())) ||
-            (rc = upload(&p->d_span_prefix, s.span_prefix.data(), s.span_prefix.size())) ||
-            (rc = upload(&p->d_chains, s.chains.data(), s.chains.size())))
-            return rc;
     }
+    // the fused tables are small; stepwise plans keep them for the one-rank
+    // SGD step, which has no schedule step to ride on
+    if ((rc = upload(&p->d_spans, s.spans.data(), s.spans.size())) ||
+        (rc = upload(&p->d_span_prefix, s.span_prefix.data(), s.span_prefix.size())) ||
+        (rc = upload(&p->d_chains, s.chains.data(), s.chains.size())))
+        return rc;
     return DDL_OK;
 }
 
@@ -132,6 +133,7 @@ struct Launcher {
     ddl_plan p;
     const RankPtrs &bufs;
     hipStream_t stream;
+    const SgdArgs *sgd;  // null for the plain all-reduce
 
     int bracket_begin() {
         if (!p->profiling)
@@ -172,7 +174,7 @@ struct Launcher {
             int rc = bracket_begin();
             if (rc)
                 return rc;
-            if (launch_step(s.dtype, s.step_kind[st], bufs, a, tiles, stream) != hipSuccess)
+            if (launch_step(s.dtype, s.step_kind[st], bufs, a, sgd, tiles, stream) != hipSuccess)
                 return DDL_E_HIP;
             if ((rc = bracket_end()))
                 return rc;
@@ -202,7 +204,7 @@ struct Launcher {
             int rc = bracket_begin();
             if (rc)
                 return rc;
-            if (launch_fused(s.dtype, bufs, a, tiles, stream) != hipSuccess)
+            if (launch_fused(s.dtype, bufs, a, sgd, tiles, stream) != hipSuccess)
                 return DDL_E_HIP;
             if ((rc = bracket_end()))
                 return rc;
@@ -213,7 +215,7 @@ struct Launcher {
     // every launch of buckets [b0, b1)
     int group(int b0, int b1) {
         const Schedule &s = p->s;
-        if (p->mode == DDL_FUSED)
+        if (p->mode == DDL_FUSED || (sgd && s.P == 1))
             return fused(s.span_at[b0], s.span_at[b1]);
         for (int st = 0; st < s.nsteps; ++st) {
             int rc = step(st, s.item_at[st][b0], s.item_at[st][b1]);
@@ -225,13 +227,21 @@ struct Launcher {
 };
 
 int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stream_,
-                   void *done_event) {
+                   void *done_event, const SgdArgs *sgd) {
     const Schedule &s = p->s;
     for (int r = 0; r < s.P; ++r) {
         if (!bufs[r] && s.n)
             return DDL_E_NULL;
         if ((uintptr_t)bufs[r] % kVecBytes)
             return DDL_E_ALIGN;
+    }
+    if (sgd) {
+        for (int r = 0; r < sgd->nweights; ++r) {
+            if (!sgd->w.p[r] && s.n)
+                return DDL_E_NULL;
+            if ((uintptr_t)sgd->w.p[r] % kVecBytes)
+                return DDL_E_ALIGN;
+        }
     }
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
@@ -259,7 +269,7 @@ int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stre
     if (any_event && hipEventRecord(p->call_ev, cs) != hipSuccess)
         return DDL_E_HIP;
 
-    Launcher L{p, rp, ls};
+    Launcher L{p, rp, ls, sgd};
     const size_t esz = (size_t)s.esz;
     int b0 = 0;
     while (b0 < nb) {
@@ -402,7 +412,31 @@ int ddl_plan_execute(ddl_plan plan, void *const *bufs, void *const *ready_events
         return DDL_E_NULL;
     std::lock_guard<std::mutex> lk(plan->mu);
     try {
-        return execute_locked(plan, bufs, ready_events, stream, done_event);
+        return execute_locked(plan, bufs, ready_events, stream, done_event, nullptr);
+    } catch (...) {
+        return DDL_E_NOMEM;
+    }
+}
+
+int ddl_plan_execute_sgd(ddl_plan plan, void *const *bufs, void *const *weights, int nweights,
+                         float lr, int keep_grads, void *const *ready_events, void *stream,
+                         void *done_event) {
+    if (!plan || !bufs || !weights)
+        return DDL_E_NULL;
+    if (nweights != 1 && nweights != plan->s.P)
+        return DDL_E_ARG;
+    if (!keep_grads && plan->mode != DDL_FUSED)
+        return DDL_E_ARG;
+    SgdArgs g;
+    std::memset(&g, 0, sizeof(g));
+    for (int r = 0; r < nweights; ++r)
+        g.w.p[r] = weights[r];
+    g.lr = lr;
+    g.nweights = nweights;
+    g.keep_grads = keep_grads ? 1 : 0;
+    std::lock_guard<std::mutex> lk(plan->mu);
+    try {
+        return execute_locked(plan, bufs, ready_events, stream, done_event, &g);
     } catch (...) {
         return DDL_E_NOMEM;
     }

@@ -41,7 +41,7 @@ class Builder {
   public:
     explicit Builder(Schedule &s) : s_(s) {}
 
-    void emit(int step, int src, int dst, uint64_t off, uint64_t len, bool divide) {
+    void emit(int step, int src, int dst, uint64_t off, uint64_t len, uint32_t flags) {
         if (len == 0)
             return;
         DevItem it;
@@ -49,7 +49,7 @@ class Builder {
         it.len = len;
         it.src = src;
         it.dst = dst;
-        it.flags = (divide ? kItemDivide : 0u) | (off % s_.q == 0 ? kItemAligned : 0u);
+        it.flags = flags | (off % s_.q == 0 ? kItemAligned : 0u);
         it.pad = 0;
         s_.items[step].push_back(it);
         s_.sent[src] += len;
@@ -57,16 +57,19 @@ class Builder {
     }
 
     // ring reduce-scatter of [off, off+L) over positions ring[0..m), steps
-    // step0 .. step0+m-2
+    // step0 .. step0+m-2.  In the last reducing phase (final) the last step
+    // completes every chunk's sum: those items carry kItemFinal, and
+    // kItemDivide for the mean.
     void reduce_scatter(const int *ring, int m, uint64_t off, uint64_t L, int step0,
-                        bool divide_last) {
+                        bool final) {
         std::vector<uint64_t> b;
         split_segment(L, m, s_.q, b);
+        const uint32_t last = final ? (kItemFinal | (s_.op == DDL_MEAN ? kItemDivide : 0u)) : 0u;
         for (int t = 0; t + 1 < m; ++t)
             for (int x = 0; x < m; ++x) {
                 const int c = wrap(x - t, m);
                 emit(step0 + t, ring[x], ring[(x + 1) % m], off + b[c], b[c + 1] - b[c],
-                     divide_last && t == m - 2);
+                     t == m - 2 ? last : 0u);
             }
     }
 
@@ -77,7 +80,7 @@ class Builder {
         for (int t = 0; t + 1 < m; ++t)
             for (int x = 0; x < m; ++x) {
                 const int c = wrap(x + 1 - t, m);
-                emit(step0 + t, ring[x], ring[(x + 1) % m], off + b[c], b[c + 1] - b[c], false);
+                emit(step0 + t, ring[x], ring[(x + 1) % m], off + b[c], b[c + 1] - b[c], 0u);
             }
     }
 
@@ -97,14 +100,13 @@ class Builder {
 
     void ring_bucket(const Bucket &bk) {
         const int P = s_.P;
-        const bool mean = s_.op == DDL_MEAN;
         std::vector<uint64_t> parts, b;
         split_segment(bk.len, s_.k, s_.q, parts);
         std::vector<int> chain(P);
         for (int j = 0; j < s_.k; ++j) {
             const int *ring = &s_.order[(size_t)j * P];
             const uint64_t off = bk.off + parts[j], len = parts[j + 1] - parts[j];
-            reduce_scatter(ring, P, off, len, 0, mean);
+            reduce_scatter(ring, P, off, len, 0, true);
             all_gather(ring, P, off, len, P - 1);
             // piece c is summed starting at position c, round the ring
             split_segment(len, P, s_.q, b);
@@ -118,7 +120,6 @@ class Builder {
 
     void torus_bucket(const Bucket &bk) {
         const int R = s_.rows, C = s_.cols, P = s_.P;
-        const bool mean = s_.op == DDL_MEAN;
         std::vector<int> ring(std::max(R, C));
         std::vector<uint64_t> cb, sub;
         split_segment(bk.len, C, s_.q, cb);
@@ -126,14 +127,13 @@ class Builder {
         for (int i = 0; i < R; ++i) {
             for (int j = 0; j < C; ++j)
                 ring[j] = i * C + j;
-            reduce_scatter(ring.data(), C, bk.off, bk.len, 0, mean && R == 1);
+            reduce_scatter(ring.data(), C, bk.off, bk.len, 0, R == 1);
         }
         for (int j = 0; j < C; ++j) {
             const int c = (j + 1) % C;
             for (int i = 0; i < R; ++i)
                 ring[i] = i * C + j;
-            reduce_scatter(ring.data(), R, bk.off + cb[c], cb[c + 1] - cb[c], col_rs,
-                           mean && R > 1);
+            reduce_scatter(ring.data(), R, bk.off + cb[c], cb[c + 1] - cb[c], col_rs, R > 1);
             all_gather(ring.data(), R, bk.off + cb[c], cb[c + 1] - cb[c], col_ag);
         }
         for (int i = 0; i < R; ++i) {

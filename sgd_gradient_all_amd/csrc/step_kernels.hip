@@ -15,11 +15,18 @@ using namespace dev;
 // step kernels: one launch = one schedule step over every pair of every ring
 // of every bucket in the group.  Reduce: dst = dst (+) src (then / P when the
 // item completes its chunk's sum).  Gather: dst = src.
+//
+// With kSgd the weights take their SGD step where the reduced value reaches
+// a rank: the owner at the add that completes the sum (kItemFinal), every
+// other rank when the all-gather delivers it (one replica per rank), or the
+// owner alone (one shared replica).
 // ---------------------------------------------------------------------------
-template <class E, bool kReduce>
-__global__ __launch_bounds__(kBlock) void step_kernel(RankPtrs bufs, StepArgs a) {
+template <class E, bool kReduce, bool kSgd>
+__device__ __forceinline__ void step_body(const RankPtrs &bufs, const StepArgs &a,
+                                          const SgdArgs *g) {
     using T = typename E::T;
     using V = typename E::V;
+    using W = typename E::W;
     constexpr uint64_t kTile = step_tile_elems(sizeof(T));
     const uint32_t tile = a.tile_base + blockIdx.x;
     const uint32_t i = find_item(a.prefix, a.item_lo, a.item_hi, tile);
@@ -30,6 +37,12 @@ __global__ __launch_bounds__(kBlock) void step_kernel(RankPtrs bufs, StepArgs a)
     T *dst = static_cast<T *>(bufs.p[it.dst]) + it.off + t0;
     const T *src = static_cast<const T *>(bufs.p[it.src]) + it.off + t0;
     const bool divide = kReduce && (it.flags & kItemDivide);
+    float *w = nullptr;
+    float lr = 0.0f;
+    if (kSgd && (kReduce ? (it.flags & kItemFinal) != 0 : g->nweights > 1)) {
+        w = static_cast<float *>(g->w.p[g->nweights == 1 ? 0 : it.dst]) + it.off + t0;
+        lr = g->lr;
+    }
     const uint32_t tid = threadIdx.x;
     uint32_t done = 0;
     if (it.flags & kItemAligned) {
@@ -51,6 +64,10 @@ __global__ __launch_bounds__(kBlock) void step_kernel(RankPtrs bufs, StepArgs a)
                         r = E::div(r, a.divisor);
                 }
                 stv<V>(dst + (size_t)(j * kBlock + tid) * E::N, r);
+                if (kSgd && w) {
+                    float *wp = w + (size_t)(j * kBlock + tid) * E::N;
+                    stv<W>(wp, sgd_step<W>(ldv<W>(wp), E::widen(r), lr));
+                }
             }
         } else {
             for (uint32_t v = tid; v < nvec; v += kBlock) {
@@ -61,6 +78,10 @@ __global__ __launch_bounds__(kBlock) void step_kernel(RankPtrs bufs, StepArgs a)
                         r = E::div(r, a.divisor);
                 }
                 stv<V>(dst + (size_t)v * E::N, r);
+                if (kSgd && w) {
+                    float *wp = w + (size_t)v * E::N;
+                    stv<W>(wp, sgd_step<W>(ldv<W>(wp), E::widen(r), lr));
+                }
             }
         }
         done = nvec * E::N;
@@ -75,26 +96,52 @@ __global__ __launch_bounds__(kBlock) void step_kernel(RankPtrs bufs, StepArgs a)
                 r = E::div1(r, a.divisor);
         }
         dst[e] = r;
+        if (kSgd && w)
+            w[e] = sgd_step<float>(w[e], (float)r, lr);
     }
+}
+
+template <class E, bool kReduce>
+__global__ __launch_bounds__(kBlock) void step_kernel(RankPtrs bufs, StepArgs a) {
+    step_body<E, kReduce, false>(bufs, a, nullptr);
+}
+
+template <class E, bool kReduce>
+__global__ __launch_bounds__(kBlock) void step_sgd_kernel(RankPtrs bufs, StepArgs a,
+                                                          SgdArgs g) {
+    step_body<E, kReduce, true>(bufs, a, &g);
+}
+
+}  // namespace
+
+namespace {
+
+template <class E>
+void launch_e(int kind, dim3 grid, hipStream_t s, const RankPtrs &bufs, const StepArgs &a,
+              const SgdArgs *sgd) {
+    const dim3 block(kBlock);
+    if (sgd) {
+        if (kind == DDL_K_REDUCE)
+            hipLaunchKernelGGL((step_sgd_kernel<E, true>), grid, block, 0, s, bufs, a, *sgd);
+        else
+            hipLaunchKernelGGL((step_sgd_kernel<E, false>), grid, block, 0, s, bufs, a, *sgd);
+        return;
+    }
+    if (kind == DDL_K_REDUCE)
+        hipLaunchKernelGGL((step_kernel<E, true>), grid, block, 0, s, bufs, a);
+    else
+        hipLaunchKernelGGL((step_kernel<E, false>), grid, block, 0, s, bufs, a);
 }
 
 }  // namespace
 
 int launch_step(int dtype, int kind, const RankPtrs &bufs, const StepArgs &a,
-                uint32_t tiles, void *stream) {
+                const SgdArgs *sgd, uint32_t tiles, void *stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    dim3 grid(tiles), block(kBlock);
-    if (dtype == DDL_F32) {
-        if (kind == DDL_K_REDUCE)
-            hipLaunchKernelGGL((step_kernel<F32, true>), grid, block, 0, s, bufs, a);
-        else
-            hipLaunchKernelGGL((step_kernel<F32, false>), grid, block, 0, s, bufs, a);
-    } else {
-        if (kind == DDL_K_REDUCE)
-            hipLaunchKernelGGL((step_kernel<F16, true>), grid, block, 0, s, bufs, a);
-        else
-            hipLaunchKernelGGL((step_kernel<F16, false>), grid, block, 0, s, bufs, a);
-    }
+    if (dtype == DDL_F32)
+        launch_e<F32>(kind, dim3(tiles), s, bufs, a, sgd);
+    else
+        launch_e<F16>(kind, dim3(tiles), s, bufs, a, sgd);
     return (int)hipGetLastError();
 }
 

@@ -223,3 +223,17 @@ def test_plan_create_needs_no_gpu():
     spans, group = plan.fused_spans(0)
     assert group == 4 and len(spans) == 16
     plan.destroy()
+
+
+def test_sgd_argument_validation_before_any_gpu_call():
+    import ctypes
+    P = 4
+    for mode, nweights, keep, want in (("fused", 2, 1, -2), ("fused", 0, 1, -2),
+                                       ("stepwise", 4, 0, -2), ("stepwise", 1, 0, -2)):
+        plan = ddl.Plan(P, 1000, "f32", "mean", ddl.topo("ring"), None, mode)
+        bufs = (ctypes.c_void_p * P)(*[16 * (r + 1) for r in range(P)])
+        w = (ctypes.c_void_p * max(1, nweights))(*[4096 * (r + 1) for r in range(max(1, nweights))])
+        rc = ddl.lib().ddl_plan_execute_sgd(plan.handle, bufs, w, nweights, 0.1, keep, None, None,
+                                            None)
+        assert rc == want, (mode, nweights, keep, rc)
+        plan.destroy()
