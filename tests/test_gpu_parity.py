@@ -313,3 +313,118 @@ def test_plan_reuse_and_cache():
         for r in range(w.P):
             assert np.array_equal(out[r].astype(np.int64), want)
     ddl.ddl_cache_clear()
+
+
+# ---------------------------------------------------------------------------
+# dispatcher: grouping threshold, stream semantics, busy plans; edge shapes
+# ---------------------------------------------------------------------------
+def test_coalesce_threshold_merges_event_gated_buckets():
+    """161 ResNet-50 buckets, each with its own ready event: with a 16 MB
+    threshold consecutive buckets share launches (fewer launches), results
+    bit-identical to one group per bucket and to the oracle."""
+    w = WORKLOADS["multiring_k4_p16_resnet50"]
+    say("case coalesce threshold")
+    g = host_inputs(w)
+    ref = [x.copy() for x in g]
+    oracle_full(w, ref)
+    stream = torch.cuda.current_stream()
+    counts = {}
+    for mode in ("fused", "stepwise"):
+        for thr in (0, 16 << 20):
+            bufs = to_device(g)
+            events = [torch.cuda.Event() for _ in w.bucket_list()]
+            for e in events:
+                e.record(stream)
+            plan = ddl.Plan(w.P, w.n, w.dtype, w.op, ddl_topo(w), w.bucket_list(), mode)
+            plan.set_coalesce_bytes(thr)
+            plan.set_profiling(True)
+            plan.execute(bufs, events=events, stream=stream)
+            _, launches, _ = plan.profile_read()
+            counts[(mode, thr)] = launches
+            out = to_host(bufs)
+            plan.destroy()
+            for r in (0, 7, 15):
+                assert bitwise_equal(out[r], ref[r]), (mode, thr, r)
+    assert counts[("fused", 0)] == 161 and counts[("stepwise", 0)] == 161 * 30
+    assert counts[("fused", 16 << 20)] < 20
+    assert counts[("stepwise", 16 << 20)] == 30 * counts[("fused", 16 << 20)]
+
+
+def test_caller_stream_waits_for_side_stream_work():
+    """Work enqueued on the caller's stream right after an event-gated
+    all-reduce sees its result without any host synchronisation."""
+    say("case caller stream ordering")
+    w = Workload("order", 8, 1 << 22, "f32", "mean", "ring", dist="normal", sigma=1e-2,
+                 seed=12, buckets=[(i << 18, 1 << 18) for i in reversed(range(16))])
+    g = host_inputs(w)
+    ref = [x.copy() for x in g]
+    oracle_full(w, ref)
+    bufs = to_device(g)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    events = [torch.cuda.Event() for _ in w.bucket_list()]
+    for e in events:
+        e.record(stream)
+    plan = ddl.Plan(w.P, w.n, w.dtype, w.op, ddl_topo(w), w.bucket_list(), "stepwise")
+    plan.execute(bufs, events=events, stream=stream)
+    snap = bufs[3].clone()          # enqueued on the caller stream, no host sync
+    torch.cuda.synchronize()
+    assert bitwise_equal(snap.cpu().numpy(), ref[3])
+    plan.destroy()
+
+
+def test_destroy_with_work_in_flight_is_busy():
+    say("case busy destroy")
+    P, n = 8, 1 << 20
+    bufs = [torch.ones(n, device="cuda") for _ in range(P)]
+    scratch = torch.zeros(1 << 28, device="cuda")
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    for _ in range(8):   # keep the stream busy for several milliseconds
+        synth.stream_compute(scratch.data_ptr(), scratch.numel(), 1.0, 0.0, stream.cuda_stream)
+    plan = ddl.Plan(P, n, "f32", "sum", ddl.topo("ring"))
+    plan.execute(bufs, stream=stream)
+    rc = ddl.lib().ddl_plan_destroy(plan.handle)
+    assert rc == -7
+    torch.cuda.synchronize()
+    plan.destroy()
+    assert bool((bufs[5] == P).all())
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_max_ranks(dtype):
+    say(f"case 128 ranks {dtype}")
+    for w in (Workload("ring128", 128, 40_003, dtype, "mean", "ring", dist="normal",
+                       sigma=1e-2, seed=128),
+              Workload("torus8x16", 128, 40_003, dtype, "mean", "torus2d", rows=8, cols=16,
+                       dist="normal", sigma=1e-2, seed=129)):
+        g = host_inputs(w)
+        ref = [x.copy() for x in g]
+        oracle_full(w, ref)
+        for mode in ("fused", "stepwise"):
+            bufs = to_device(g)
+            run_ddl(bufs, w, mode)
+            out = to_host(bufs)
+            for r in (0, 63, 127):
+                assert bitwise_equal(out[r], ref[r]), (w.name, mode, r)
+
+
+def test_custom_ring_orders():
+    say("case custom ring orders")
+    rng = np.random.default_rng(17)
+    for P, k, dtype in ((6, 1, "f32"), (16, 4, "f16"), (40, 3, "f32")):
+        n = 50_021
+        order = np.concatenate([rng.permutation(P) for _ in range(k)]).tolist()
+        g = [rng.standard_normal(n).astype(np_dtype(dtype)) for _ in range(P)]
+        ref = [x.copy() for x in g]
+        kind = "ring" if k == 1 else "multiring"
+        orc.allreduce(ref, op=orc.MEAN, kind=KINDS[kind], k=k, ring_order=order)
+        for mode in ("fused", "stepwise"):
+            bufs = to_device(g)
+            plan = ddl.Plan(P, n, dtype, "mean", ddl.topo(kind, k, ring_order=order), None,
+                            mode)
+            plan.execute(bufs)
+            out = to_host(bufs)
+            plan.destroy()
+            for r in (0, P - 1):
+                assert bitwise_equal(out[r], ref[r]), (P, k, mode, r)
