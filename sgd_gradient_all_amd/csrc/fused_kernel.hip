@@ -25,8 +25,11 @@ using namespace dev;
 #ifndef DDL_NT_LOAD_MAX_P
 #define DDL_NT_LOAD_MAX_P 24
 #endif
+// Loads a lane issues ahead of their adds.  Measured on MI355X, one is best
+// or within 1% of best: the many-stream pass saturates HBM, and more
+// requests in flight per wave only lengthen the queues (8 costs up to 5%).
 #ifndef DDL_LOAD_BATCH
-#define DDL_LOAD_BATCH 8
+#define DDL_LOAD_BATCH 1
 #endif
 constexpr int kBatch = DDL_LOAD_BATCH;
 // Waves per SIMD the register allocation must allow: 8 for one vector per
@@ -44,6 +47,19 @@ __device__ __forceinline__ V ld_stream(const void *p) {
         return __builtin_nontemporal_load(reinterpret_cast<const V *>(p));
     return *reinterpret_cast<const V *>(p);
 }
+
+// The rank streams are read through global (address space 1) pointers built
+// from addresses kept in LDS.  A generic pointer would compile to FLAT
+// loads, which also count against the LDS wait counter: every wait for the
+// next address would then wait for all data loads in flight.
+#define DDL_GLOBAL __attribute__((address_space(1)))
+template <class V, bool kNt>
+__device__ __forceinline__ V ld_global(uint64_t addr) {
+    const V DDL_GLOBAL *p = reinterpret_cast<const V DDL_GLOBAL *>(addr);
+    if (kNt)
+        return __builtin_nontemporal_load(p);
+    return *p;
+}
 template <class V>
 __device__ __forceinline__ void st_stream(void *p, V v) {
 #if DDL_NT_STORE
@@ -59,9 +75,8 @@ __device__ __forceinline__ void st_stream(void *p, V v) {
 // entries, each group left to right, then the group sums left to right --
 // divided by P for the mean, and written once to each rank.
 //
-// The rank pointers, in chain order, are staged in LDS before the first
-// store, so the data loads never wait behind a table load; they are issued
-// eight at a time ahead of the serial add chain.
+// The rank addresses, in chain order, are staged in LDS before the first
+// store, so the data loads never wait behind a table load.
 // ---------------------------------------------------------------------------
 template <class E>
 struct Chain {
@@ -79,65 +94,45 @@ struct Chain {
     }
 };
 
-// Sums of U element vectors -- e + u * kBlock * N, u < U -- over the chain,
-// the loads of kBatch ranks issued ahead of their adds.  Ungrouped (rings):
-// one chain of P entries.  Grouped (torus): chains of `group` entries, then
+// Sums of U element vectors -- e + u * kBlock * N, u < U -- over the chain.
+// The ranks go in batches of kBatch from the first one; every load of a
+// batch is issued before the batch's adds.  In a partial last batch the
+// missing slots
+// re-load the batch's last rank (a line already in flight) and their adds
+// are skipped, which keeps every load unconditional.  Ungrouped (rings): one
+// chain of P entries.  Grouped (torus): chains of `group` entries, then
 // their sums.
 template <class E, bool kGrouped, bool kNt, int U>
-__device__ __forceinline__ void fused_vecs(const typename E::T *const *sp, int P, int group,
+__device__ __forceinline__ void fused_vecs(const uint64_t *sp, int P, int group,
                                            uint64_t e, typename E::V (&out)[U]) {
     using V = typename E::V;
     constexpr uint64_t kStride = (uint64_t)kBlock * E::N;
-    if (!kGrouped) {
-        V acc[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            acc[u] = ld_stream<V, kNt>(sp[0] + e + u * kStride);
-        int b = 1;
-        for (; b + kBatch <= P; b += kBatch) {
-            V x[kBatch][U];
-#pragma unroll
-            for (int j = 0; j < kBatch; ++j)
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-                    x[j][u] = ld_stream<V, kNt>(sp[b + j] + e + u * kStride);
-#pragma unroll
-            for (int j = 0; j < kBatch; ++j)
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-                    acc[u] = E::add(acc[u], x[j][u]);
-        }
-        for (; b < P; ++b)
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                acc[u] = E::add(acc[u], ld_stream<V, kNt>(sp[b] + e + u * kStride));
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            out[u] = acc[u];
-        return;
-    }
     Chain<E> c[U];
-    int b = 0;
-    for (; b + kBatch <= P; b += kBatch) {
+    V acc[U];
+    for (int b = 0; b < P; b += kBatch) {
+        const int nb = min(kBatch, P - b);
         V x[kBatch][U];
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j)
+        for (int j = 0; j < kBatch; ++j) {
+            const uint64_t p = sp[b + (j < nb ? j : nb - 1)] + e * sizeof(typename E::T);
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                x[j][u] = ld_stream<V, kNt>(sp[b + j] + e + u * kStride);
+                x[j][u] = ld_global<V, kNt>(p + u * kStride * sizeof(typename E::T));
+        }
 #pragma unroll
         for (int j = 0; j < kBatch; ++j)
+            if (j < nb)
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                c[u].push(x[j][u], group);
+                for (int u = 0; u < U; ++u) {
+                    if (kGrouped)
+                        c[u].push(x[j][u], group);
+                    else
+                        acc[u] = b + j == 0 ? x[j][u] : E::add(acc[u], x[j][u]);
+                }
     }
-    for (; b < P; ++b)
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            c[u].push(ld_stream<V, kNt>(sp[b] + e + u * kStride), group);
 #pragma unroll
     for (int u = 0; u < U; ++u)
-        out[u] = c[u].acc;
+        out[u] = kGrouped ? c[u].acc : acc[u];
 }
 
 template <class E, int U>
@@ -173,7 +168,7 @@ __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs
     using V = typename E::V;
     constexpr int U = fused_vecs_per_lane(sizeof(T));
     constexpr uint64_t kTile = fused_tile_elems(sizeof(T));
-    __shared__ const T *src[DDL_MAX_RANKS];
+    __shared__ uint64_t src[DDL_MAX_RANKS];  // rank stream addresses, chain order
     const int P = a.P;
     const uint32_t tid = threadIdx.x;
     const uint32_t first = a.tile_base + blockIdx.x * (uint32_t)kFusedTilesPerGroup;
@@ -187,7 +182,7 @@ __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs
             if (have != UINT32_MAX)
                 __syncthreads();
             for (int j = (int)tid; j < P; j += kBlock)
-                src[j] = static_cast<const T *>(bufs.p[a.chains[sp.chain_off + j]]);
+                src[j] = reinterpret_cast<uint64_t>(bufs.p[a.chains[sp.chain_off + j]]);
             __syncthreads();
             have = i;
         }
@@ -231,7 +226,7 @@ __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs
             int pos = 0;
             bool first_group = true;
             for (int j = 0; j < P; ++j) {
-                T x = src[j][e];
+                T x = *reinterpret_cast<const T DDL_GLOBAL *>(src[j] + e * sizeof(T));
                 gacc = pos == 0 ? x : E::add1(gacc, x);
                 if (++pos == a.group) {
                     acc = first_group ? gacc : E::add1(acc, gacc);
