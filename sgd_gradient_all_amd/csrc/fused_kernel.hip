@@ -15,10 +15,11 @@ namespace {
 using namespace dev;
 
 // Streaming accesses.  Every element is touched once per pass, so the
-// results are written with non-temporal stores.  Loads are non-temporal for
-// passes over at most kNtLoadMaxRanks ranks: measured on MI355X, that wins
-// 5-8% at 8 and 16 ranks and loses 4% at 40 (tuning knobs below, and the
-// environment variable DDL_FUSED_NT_LOAD_MAX_P at run time).
+// results are written with non-temporal stores.  Loads are non-temporal when
+// P times the vectors per lane is at most DDL_NT_LOAD_MAX_P (24; the
+// environment variable DDL_FUSED_NT_LOAD_MAX_P overrides it at run time).
+// Measured on MI355X: +7..+15% for binary32 at 8 and 16 ranks and binary16
+// at 8, -4% for binary32 at 40 ranks, -9..-14% for binary16 at 16.
 #ifndef DDL_NT_STORE
 #define DDL_NT_STORE 1
 #endif
@@ -281,7 +282,7 @@ template <class E, bool kGrouped>
 void launch_e(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a,
               const SgdArgs *sgd) {
     const dim3 block(kBlock);
-    const bool nt = a.P <= nt_load_max_ranks();
+    const bool nt = a.P * fused_vecs_per_lane(sizeof(typename E::T)) <= nt_load_max_ranks();
     if (sgd) {
         if (nt)
             hipLaunchKernelGGL((fused_sgd_kernel<E, kGrouped, true>), grid, block, 0, s, bufs, a,
