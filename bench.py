@@ -225,11 +225,33 @@ def extras(args, w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_b
     t1.record(main_stream)
     torch.cuda.synchronize()
     sms = t0.elapsed_time(t1) / steps
+    # the same execution captured once into a HIP graph and replayed: the
+    # thousands of step launches are then issued by one graph launch
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(main_stream)
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            if evs:
+                for e in evs:
+                    e.record(cap)
+            plan.execute(bufs, events=evs, stream=cap)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    t0.record(main_stream)
+    for _ in range(steps):
+        graph.replay()
+    t1.record(main_stream)
+    torch.cuda.synchronize()
+    gms = t0.elapsed_time(t1) / steps
+    del graph
     plan.set_profiling(True)
     step_once()
     torch.cuda.synchronize()
     kms, launches, _ = plan.profile_read()
     out["stepwise"] = {"ms_per_step": round(sms, 3),
+                       "graph_ms_per_step": round(gms, 3),
                        "hbm_GBps": round(sbytes / (sms * 1e-3) / 1e9, 1),
                        "fused_floor_equiv_GBps": round(fused_bytes / (sms * 1e-3) / 1e9, 1),
                        "bytes_per_step": sbytes,

@@ -428,3 +428,60 @@ def test_custom_ring_orders():
             plan.destroy()
             for r in (0, P - 1):
                 assert bitwise_equal(out[r], ref[r]), (P, k, mode, r)
+
+
+@pytest.mark.parametrize("mode", ["fused", "stepwise"])
+def test_hip_graph_capture_and_replay(mode):
+    """An execution captured into a HIP graph (after one eager call has bound
+    the plan) replays to the oracle's result, replay after replay, with the
+    inputs restored eagerly in between."""
+    say(f"case graph capture {mode}")
+    w = Workload("graph", 16, 1 << 20, "f32", "mean", "multiring", k=4, dist="normal",
+                 sigma=1e-2, seed=21, buckets=[(i << 16, 1 << 16) for i in reversed(range(16))])
+    g = host_inputs(w)
+    ref = [x.copy() for x in g]
+    oracle_full(w, ref)
+    src = to_device(g)
+    bufs = [t.clone() for t in src]
+    plan = ddl.Plan(w.P, w.n, w.dtype, w.op, ddl_topo(w), w.bucket_list(), mode)
+    plan.execute(bufs, stream=torch.cuda.current_stream())   # binds the plan
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            plan.execute(bufs, stream=s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for b, x in zip(bufs, src):
+            b.copy_(x)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        out = [b.cpu().numpy() for b in bufs]
+        for r in (0, 9, 15):
+            assert bitwise_equal(out[r], ref[r]), (mode, rep, r)
+    del graph
+    torch.cuda.synchronize()
+    plan.destroy()
+
+
+def test_ddl_allreduce_with_bucket_events():
+    say("case ddl_allreduce events")
+    w = Workload("oneshot-ev", 6, 6 * 40_000, "f32", "mean", "ring", dist="normal", sigma=1e-2,
+                 seed=22, buckets=[(i * 40_000, 40_000) for i in reversed(range(6))])
+    g = host_inputs(w)
+    ref = [x.copy() for x in g]
+    oracle_full(w, ref)
+    bufs = to_device(g)
+    stream = torch.cuda.current_stream()
+    events = [torch.cuda.Event() for _ in w.bucket_list()]
+    for e in events:
+        e.record(stream)
+    ddl.ddl_allreduce(bufs, w.n, "f32", "mean", ddl.topo("ring"), w.bucket_list(), "stepwise",
+                      stream=stream, events=events)
+    out = to_host(bufs)
+    for r in range(w.P):
+        assert bitwise_equal(out[r], ref[r]), r
+    ddl.ddl_cache_clear()

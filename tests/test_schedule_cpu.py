@@ -237,3 +237,18 @@ def test_sgd_argument_validation_before_any_gpu_call():
                                             None)
         assert rc == want, (mode, nweights, keep, rc)
         plan.destroy()
+
+
+def test_schedule_generator_under_sanitizers(tmp_path):
+    """The host schedule generator, built with AddressSanitizer and
+    UndefinedBehaviorSanitizer (g++, host code only), through random
+    configurations with an independent coverage/race/traffic check."""
+    exe = tmp_path / "schedule_asan"
+    src = os.path.join(ROOT, "tests", "schedule_asan_driver.cpp")
+    lib_src = os.path.join(ROOT, "sgd_gradient_all_amd", "csrc", "schedule.cpp")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=undefined", "-I", os.path.join(ROOT, "include"),
+                    src, lib_src, "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe), "400"], capture_output=True, text=True, timeout=600)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert "ok 400 cases" in out.stdout
