@@ -185,6 +185,11 @@ const char *ddl_strerror(int code);
  * for all their events before it starts.  Default 0. */
 int ddl_plan_set_coalesce_bytes(ddl_plan plan, size_t bytes);
 
+/* Event-gated groups alternate over n side streams (1..4, default 1) in
+ * list order.  Buckets are independent all-reduces, so a group's kernel may
+ * start while the previous one drains; the results do not change. */
+int ddl_plan_set_side_streams(ddl_plan plan, int n);
+
 /* ---- measurement -------------------------------------------------------- *
  * With profiling on, every kernel launch is bracketed by a pair of HIP events
  * on the stream it is launched on.  ddl_plan_profile_read waits for the last

@@ -68,6 +68,7 @@ def lib():
             "ddl_cache_clear": ([], i32),
             "ddl_strerror": ([i32], ctypes.c_char_p),
             "ddl_plan_set_coalesce_bytes": ([vp, sz], i32),
+            "ddl_plan_set_side_streams": ([vp, i32], i32),
             "ddl_plan_set_profiling": ([vp, i32], i32),
             "ddl_plan_profile_read": ([vp, ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double)],
@@ -198,6 +199,9 @@ class Plan:
 
     def set_coalesce_bytes(self, nbytes):
         _check(lib().ddl_plan_set_coalesce_bytes(self.handle, nbytes), "set_coalesce_bytes")
+
+    def set_side_streams(self, n):
+        _check(lib().ddl_plan_set_side_streams(self.handle, n), "set_side_streams")
 
     def set_profiling(self, on=True):
         _check(lib().ddl_plan_set_profiling(self.handle, 1 if on else 0), "set_profiling")

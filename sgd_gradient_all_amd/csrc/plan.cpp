@@ -23,15 +23,19 @@
 
 using namespace ddl;
 
+constexpr int kMaxSideStreams = 4;
+
 struct ddl_plan_s {
     Schedule s;
     int mode = DDL_FUSED;
     size_t coalesce_bytes = 0;
+    int nside = 1;          // side streams event-gated groups alternate over
 
     std::mutex mu;
     int device = -1;        // bound at first execution
-    hipStream_t side = nullptr;
-    hipEvent_t call_ev = nullptr, done_ev = nullptr, last_ev = nullptr;
+    hipStream_t side[kMaxSideStreams] = {};
+    hipEvent_t side_done[kMaxSideStreams] = {};
+    hipEvent_t call_ev = nullptr, last_ev = nullptr;
     bool in_flight = false;
 
     // device copies of the tables of the plan's mode
@@ -81,22 +85,28 @@ void release_device(ddl_plan p) {
         (void)hipEventDestroy(e);
     if (p->call_ev)
         (void)hipEventDestroy(p->call_ev);
-    if (p->done_ev)
-        (void)hipEventDestroy(p->done_ev);
     if (p->last_ev)
         (void)hipEventDestroy(p->last_ev);
-    if (p->side)
-        (void)hipStreamDestroy(p->side);
+    for (int i = 0; i < kMaxSideStreams; ++i) {
+        if (p->side_done[i])
+            (void)hipEventDestroy(p->side_done[i]);
+        if (p->side[i])
+            (void)hipStreamDestroy(p->side[i]);
+        p->side[i] = nullptr;
+        p->side_done[i] = nullptr;
+    }
     (void)hipSetDevice(cur);
     p->device = -1;
 }
 
 int bind_device(ddl_plan p, int dev) {
     p->device = dev;
-    if (hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking) != hipSuccess)
-        return DDL_E_HIP;
+    // default-priority streams only
+    for (int i = 0; i < kMaxSideStreams; ++i)
+        if (hipStreamCreateWithFlags(&p->side[i], hipStreamNonBlocking) != hipSuccess ||
+            hipEventCreateWithFlags(&p->side_done[i], hipEventDisableTiming) != hipSuccess)
+            return DDL_E_HIP;
     if (hipEventCreateWithFlags(&p->call_ev, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&p->done_ev, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&p->last_ev, hipEventDisableTiming) != hipSuccess)
         return DDL_E_HIP;
     const Schedule &s = p->s;
@@ -265,13 +275,13 @@ int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stre
     bool any_event = false;
     for (int b = 0; ready && b < nb; ++b)
         any_event = any_event || ready[b] != nullptr;
-    hipStream_t ls = any_event ? p->side : cs;
+    hipStream_t ls = any_event ? p->side[0] : cs;
     if (any_event && hipEventRecord(p->call_ev, cs) != hipSuccess)
         return DDL_E_HIP;
 
     Launcher L{p, rp, ls, sgd};
     const size_t esz = (size_t)s.esz;
-    int b0 = 0;
+    int b0 = 0, g = 0, used = 0;
     while (b0 < nb) {
         // the group: equal events, then (with a threshold) more buckets
         // until it holds coalesce_bytes per rank
@@ -288,12 +298,17 @@ int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stre
             }
         }
         if (any_event) {
+            // groups alternate over the side streams: independent buckets,
+            // so one group's tail overlaps the next one's start
+            const int si = g % p->nside;
+            L.stream = p->side[si];
+            used = std::max(used, si + 1);
             void *last = reinterpret_cast<void *>(1);
             for (int b = b0; b < b1; ++b) {
                 void *ev = ready[b] ? ready[b] : static_cast<void *>(p->call_ev);
                 if (ev == last)
                     continue;
-                if (hipStreamWaitEvent(p->side, static_cast<hipEvent_t>(ev), 0) != hipSuccess)
+                if (hipStreamWaitEvent(L.stream, static_cast<hipEvent_t>(ev), 0) != hipSuccess)
                     return DDL_E_HIP;
                 last = ev;
             }
@@ -302,10 +317,16 @@ int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stre
         if (rc)
             return rc;
         b0 = b1;
+        ++g;
     }
     if (any_event) {
-        if (hipEventRecord(p->done_ev, p->side) != hipSuccess ||
-            hipStreamWaitEvent(cs, p->done_ev, 0) != hipSuccess)
+        // side stream 0 joins the others, then the caller's stream joins it
+        for (int i = 1; i < used; ++i)
+            if (hipEventRecord(p->side_done[i], p->side[i]) != hipSuccess ||
+                hipStreamWaitEvent(p->side[0], p->side_done[i], 0) != hipSuccess)
+                return DDL_E_HIP;
+        if (hipEventRecord(p->side_done[0], p->side[0]) != hipSuccess ||
+            hipStreamWaitEvent(cs, p->side_done[0], 0) != hipSuccess)
             return DDL_E_HIP;
     }
     if (done_event && hipEventRecord(static_cast<hipEvent_t>(done_event), ls) != hipSuccess)
@@ -518,6 +539,16 @@ int ddl_plan_set_coalesce_bytes(ddl_plan plan, size_t bytes) {
         return DDL_E_NULL;
     std::lock_guard<std::mutex> lk(plan->mu);
     plan->coalesce_bytes = bytes;
+    return DDL_OK;
+}
+
+int ddl_plan_set_side_streams(ddl_plan plan, int n) {
+    if (!plan)
+        return DDL_E_NULL;
+    if (n < 1 || n > kMaxSideStreams)
+        return DDL_E_ARG;
+    std::lock_guard<std::mutex> lk(plan->mu);
+    plan->nside = n;
     return DDL_OK;
 }
 

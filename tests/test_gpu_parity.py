@@ -485,3 +485,28 @@ def test_ddl_allreduce_with_bucket_events():
     for r in range(w.P):
         assert bitwise_equal(out[r], ref[r]), r
     ddl.ddl_cache_clear()
+
+
+@pytest.mark.parametrize("nside", [2, 4])
+def test_several_side_streams(nside):
+    say(f"case side streams {nside}")
+    w = Workload("sides", 8, 24 * 50_000, "f32", "mean", "ring", dist="normal", sigma=1e-2,
+                 seed=23, buckets=[(i * 50_000, 50_000) for i in reversed(range(24))])
+    g = host_inputs(w)
+    ref = [x.copy() for x in g]
+    oracle_full(w, ref)
+    stream = torch.cuda.current_stream()
+    for mode in ("fused", "stepwise"):
+        bufs = to_device(g)
+        events = [torch.cuda.Event() for _ in w.bucket_list()]
+        for e in events:
+            e.record(stream)
+        plan = ddl.Plan(w.P, w.n, w.dtype, w.op, ddl_topo(w), w.bucket_list(), mode)
+        plan.set_side_streams(nside)
+        plan.execute(bufs, events=events, stream=stream)
+        snap = bufs[2].clone()       # on the caller stream, no host sync
+        out = to_host(bufs)
+        plan.destroy()
+        for r in range(w.P):
+            assert bitwise_equal(out[r], ref[r]), (mode, r)
+        assert bitwise_equal(snap.cpu().numpy(), ref[2])
