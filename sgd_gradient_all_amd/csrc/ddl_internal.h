@@ -17,9 +17,6 @@ constexpr int kBlock = DDL_BLOCK;
 constexpr int kVecBytes = 16;
 // Vectors per lane per tile: step kernels (one source, one destination)
 // and the fused kernel (P sources, P destinations).  Tuning knobs.
-#ifndef DDL_STEP_VPL
-#define DDL_STEP_VPL 4
-#endif
 #ifndef DDL_FUSED_VPL_F32
 #define DDL_FUSED_VPL_F32 1
 #endif
@@ -29,7 +26,6 @@ constexpr int kVecBytes = 16;
 #ifndef DDL_FUSED_TPW
 #define DDL_FUSED_TPW 1
 #endif
-constexpr int kStepVecsPerLane = DDL_STEP_VPL;
 // Fused pass, vectors per lane per tile: one dwordx4 of binary32, two of
 // binary16 (measured best for the 40-rank fp32 and 16-rank fp16 passes).
 constexpr int fused_vecs_per_lane(int esz) {
@@ -40,8 +36,10 @@ constexpr int fused_vecs_per_lane(int esz) {
 constexpr int kFusedTilesPerGroup = DDL_FUSED_TPW;
 
 // Elements of one tile, by element size.
-constexpr uint64_t step_tile_elems(int esz) {
-    return (uint64_t)kBlock * kStepVecsPerLane * (kVecBytes / esz);
+// Step kernels take 1, 2 or 4 vectors per lane per tile; each plan picks
+// one from the length of its items (schedule.cpp, pick_step_vpl).
+constexpr uint64_t step_tile_elems(int esz, int vpl) {
+    return (uint64_t)kBlock * vpl * (kVecBytes / esz);
 }
 constexpr uint64_t fused_tile_elems(int esz) {
     return (uint64_t)kBlock * fused_vecs_per_lane(esz) * (kVecBytes / esz);
@@ -114,7 +112,7 @@ struct SgdArgs {
 };
 
 // Kernel launchers.  sgd may be null (plain all-reduce).  Return hipError_t.
-int launch_step(int dtype, int kind, const RankPtrs &bufs, const StepArgs &a,
+int launch_step(int dtype, int kind, int vpl, const RankPtrs &bufs, const StepArgs &a,
                 const SgdArgs *sgd, uint32_t tiles, void *stream);
 int launch_fused(int dtype, const RankPtrs &bufs, const FusedArgs &a, const SgdArgs *sgd,
                  uint32_t tiles, void *stream);

@@ -184,7 +184,8 @@ struct Launcher {
             int rc = bracket_begin();
             if (rc)
                 return rc;
-            if (launch_step(s.dtype, s.step_kind[st], bufs, a, sgd, tiles, stream) != hipSuccess)
+            if (launch_step(s.dtype, s.step_kind[st], s.step_vpl, bufs, a, sgd, tiles, stream) !=
+                hipSuccess)
                 return DDL_E_HIP;
             if ((rc = bracket_end()))
                 return rc;

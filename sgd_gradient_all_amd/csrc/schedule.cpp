@@ -159,6 +159,27 @@ class Builder {
     Schedule &s_;
 };
 
+// Vectors per lane of the step kernels, from the mean item length.  Measured
+// on MI355X: long items (a 300M-element bucket over 8 ranks, 37.5M-element
+// chunks) run best with one vector per lane -- fewer requests in flight per
+// wave; chunks of ~10^5 elements with two; short items (the ResNet-50
+// tensors, ~2.5K-element chunks) with four, which keeps the number of
+// workgroups -- each of which looks its item up -- low.
+int pick_step_vpl(const Schedule &s) {
+    uint64_t total = 0, count = 0;
+    for (const auto &step : s.items)
+        for (const DevItem &it : step) {
+            total += it.len;
+            ++count;
+        }
+    const uint64_t mean = count ? total / count : 0;
+    if (mean >= (4ull << 20))
+        return 1;
+    if (mean >= (64ull << 10))
+        return 2;
+    return 4;
+}
+
 bool tiles_prefix(const std::vector<uint64_t> &lens, uint64_t tile, std::vector<uint32_t> &pre) {
     pre.assign(lens.size() + 1, 0);
     uint64_t acc = 0;
@@ -283,12 +304,13 @@ int build_schedule(Schedule &s, int P, uint64_t n, int dtype, int op, const ddl_
     s.span_at[nb] = (uint32_t)s.spans.size();
 
     s.prefix.assign(s.nsteps, {});
+    s.step_vpl = pick_step_vpl(s);
     std::vector<uint64_t> lens;
     for (int st = 0; st < s.nsteps; ++st) {
         lens.clear();
         for (const DevItem &it : s.items[st])
             lens.push_back(it.len);
-        if (!tiles_prefix(lens, step_tile_elems(s.esz), s.prefix[st]))
+        if (!tiles_prefix(lens, step_tile_elems(s.esz, s.step_vpl), s.prefix[st]))
             return DDL_E_ARG;
     }
     lens.clear();

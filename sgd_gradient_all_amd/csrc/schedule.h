@@ -35,6 +35,7 @@ struct Schedule {
     std::vector<std::vector<DevItem>> items;     // [s] items
     std::vector<std::vector<uint32_t>> item_at;  // [s] first item of bucket b, nb+1
     std::vector<std::vector<uint32_t>> prefix;   // [s] tile prefix, nitems+1
+    int step_vpl = 4;                            // step kernels' vectors per lane
 
     // fused tables: spans bucket-major, P chain entries each
     int group = 1;                       // chain entries per group

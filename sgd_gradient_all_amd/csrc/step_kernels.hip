@@ -21,13 +21,13 @@ using namespace dev;
 // other rank when the all-gather delivers it (one replica per rank), or the
 // owner alone (one shared replica).
 // ---------------------------------------------------------------------------
-template <class E, bool kReduce, bool kSgd>
+template <class E, bool kReduce, bool kSgd, int VPL>
 __device__ __forceinline__ void step_body(const RankPtrs &bufs, const StepArgs &a,
                                           const SgdArgs *g) {
     using T = typename E::T;
     using V = typename E::V;
     using W = typename E::W;
-    constexpr uint64_t kTile = step_tile_elems(sizeof(T));
+    constexpr uint64_t kTile = step_tile_elems(sizeof(T), VPL);
     const uint32_t tile = a.tile_base + blockIdx.x;
     const uint32_t i = find_item(a.prefix, a.item_lo, a.item_hi, tile);
     const DevItem it = a.items[i];
@@ -47,16 +47,16 @@ __device__ __forceinline__ void step_body(const RankPtrs &bufs, const StepArgs &
     uint32_t done = 0;
     if (it.flags & kItemAligned) {
         const uint32_t nvec = cnt / E::N;
-        if (nvec == (uint32_t)(kStepVecsPerLane * kBlock)) {
-            V s[kStepVecsPerLane], d[kStepVecsPerLane];
+        if (nvec == (uint32_t)(VPL * kBlock)) {
+            V s[VPL], d[VPL];
 #pragma unroll
-            for (int j = 0; j < kStepVecsPerLane; ++j) {
+            for (int j = 0; j < VPL; ++j) {
                 s[j] = ldv<V>(src + (size_t)(j * kBlock + tid) * E::N);
                 if (kReduce)
                     d[j] = ldv<V>(dst + (size_t)(j * kBlock + tid) * E::N);
             }
 #pragma unroll
-            for (int j = 0; j < kStepVecsPerLane; ++j) {
+            for (int j = 0; j < VPL; ++j) {
                 V r = s[j];
                 if (kReduce) {
                     r = E::add(d[j], s[j]);
@@ -101,47 +101,60 @@ __device__ __forceinline__ void step_body(const RankPtrs &bufs, const StepArgs &
     }
 }
 
-template <class E, bool kReduce>
+template <class E, bool kReduce, int VPL>
 __global__ __launch_bounds__(kBlock) void step_kernel(RankPtrs bufs, StepArgs a) {
-    step_body<E, kReduce, false>(bufs, a, nullptr);
+    step_body<E, kReduce, false, VPL>(bufs, a, nullptr);
 }
 
-template <class E, bool kReduce>
+template <class E, bool kReduce, int VPL>
 __global__ __launch_bounds__(kBlock) void step_sgd_kernel(RankPtrs bufs, StepArgs a,
                                                           SgdArgs g) {
-    step_body<E, kReduce, true>(bufs, a, &g);
+    step_body<E, kReduce, true, VPL>(bufs, a, &g);
 }
 
 }  // namespace
 
 namespace {
 
-template <class E>
-void launch_e(int kind, dim3 grid, hipStream_t s, const RankPtrs &bufs, const StepArgs &a,
+template <class E, int VPL>
+void launch_v(int kind, dim3 grid, hipStream_t s, const RankPtrs &bufs, const StepArgs &a,
               const SgdArgs *sgd) {
     const dim3 block(kBlock);
     if (sgd) {
         if (kind == DDL_K_REDUCE)
-            hipLaunchKernelGGL((step_sgd_kernel<E, true>), grid, block, 0, s, bufs, a, *sgd);
+            hipLaunchKernelGGL((step_sgd_kernel<E, true, VPL>), grid, block, 0, s, bufs, a,
+                               *sgd);
         else
-            hipLaunchKernelGGL((step_sgd_kernel<E, false>), grid, block, 0, s, bufs, a, *sgd);
+            hipLaunchKernelGGL((step_sgd_kernel<E, false, VPL>), grid, block, 0, s, bufs, a,
+                               *sgd);
         return;
     }
     if (kind == DDL_K_REDUCE)
-        hipLaunchKernelGGL((step_kernel<E, true>), grid, block, 0, s, bufs, a);
+        hipLaunchKernelGGL((step_kernel<E, true, VPL>), grid, block, 0, s, bufs, a);
     else
-        hipLaunchKernelGGL((step_kernel<E, false>), grid, block, 0, s, bufs, a);
+        hipLaunchKernelGGL((step_kernel<E, false, VPL>), grid, block, 0, s, bufs, a);
+}
+
+template <class E>
+void launch_e(int kind, int vpl, dim3 grid, hipStream_t s, const RankPtrs &bufs,
+              const StepArgs &a, const SgdArgs *sgd) {
+    if (vpl == 1)
+        launch_v<E, 1>(kind, grid, s, bufs, a, sgd);
+    else if (vpl == 2)
+        launch_v<E, 2>(kind, grid, s, bufs, a, sgd);
+    else
+        launch_v<E, 4>(kind, grid, s, bufs, a, sgd);
 }
 
 }  // namespace
 
-int launch_step(int dtype, int kind, const RankPtrs &bufs, const StepArgs &a,
+int launch_step(int dtype, int kind, int vpl, const RankPtrs &bufs, const StepArgs &a,
                 const SgdArgs *sgd, uint32_t tiles, void *stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == DDL_F32)
-        launch_e<F32>(kind, dim3(tiles), s, bufs, a, sgd);
+        launch_e<F32>(kind, vpl, dim3(tiles), s, bufs, a, sgd);
     else
-        launch_e<F16>(kind, dim3(tiles), s, bufs, a, sgd);
+        launch_e<F16>(kind, vpl, dim3(tiles), s, bufs, a, sgd);
     return (int)hipGetLastError();
 }
 

@@ -62,8 +62,10 @@ def run_ddl(bufs, w, mode, op=None, plan_api=True, events=None, stream=None):
 def small_cases():
     cases = []
     for dtype in ("f32", "f16"):
+        # (3, 400_003) and (2, 8_400_011) give step items long enough for the
+        # step kernels' two- and one-vector-per-lane tiles
         for P, n in ((1, 1000), (2, 1), (3, 2), (4, 4099), (5, 12347), (8, 100_003),
-                     (16, 70_001)):
+                     (16, 70_001), (3, 400_003), (2, 8_400_011)):
             cases.append(Workload(f"ring-P{P}-n{n}-{dtype}", P, n, dtype, "sum", "ring",
                                   dist="uniform", seed=P + n))
         for P, k, n in ((4, 2, 9_999), (16, 4, 250_007), (6, 3, 17)):
