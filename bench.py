@@ -23,7 +23,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "achieved HBM GB/s and % of peak per all-reduce (300M fp32, P=40 ring)"
 PEAK_HBM_GBPS = 8000.0
-FUSED_KERNEL = "fused_kernel"
+# committed counter summaries: one file per form of the fused pass
+TRAFFIC_FILES = {1: ("fused_kernel", "hbm_bytes_per_launch"),
+                 2: ("fused_pass", "hbm_bytes_per_pass")}
 
 
 def log(*a):
@@ -40,17 +42,21 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, mode):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"{FUSED_KERNEL}_{workload}_traffic.json")
-    if mode != "fused" or not os.path.exists(path):
+def measured_traffic(workload, mode, passes):
+    """HBM bytes per launch (one-kernel form) or per reduce + broadcast pair
+    (two-kernel form) from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source."""
+    if mode != "fused" or passes not in TRAFFIC_FILES:
+        return None
+    stem, key = TRAFFIC_FILES[passes]
+    path = os.path.join(ROOT, "profiles", f"{stem}_{workload}_traffic.json")
+    if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get(key)
 
 
 def main():
@@ -60,6 +66,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ring_p40_300m_64b")
     ap.add_argument("--mode", default="fused", choices=["fused", "stepwise"])
+    ap.add_argument("--passes", type=int, default=0, choices=[0, 1, 2],
+                    help="fused pass form: 0 the plan's choice, 1 one kernel, "
+                         "2 reduce + broadcast kernels")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the step-by-step and overlap measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -122,6 +131,9 @@ def main():
     t_plan = time.perf_counter()
     plan = ddl.Plan(w.P, w.n, w.dtype, w.op, topo, buckets, args.mode)
     plan_build_ms = (time.perf_counter() - t_plan) * 1e3
+    if args.mode == "fused":
+        plan.set_fused_passes(args.passes)
+    passes = plan.fused_passes()
     _, hbm_bytes = plan.traffic()
     evs = make_events()
     for _ in range(args.warmup):
@@ -135,15 +147,41 @@ def main():
     plan.set_profiling(True)
     plan.profile_read()
     ms_prof = run_steps(plan, evs, args.steps)
-    kms, launches, kmax = plan.profile_read()
+    kinds = plan.profile_read_kinds()
     value = hbm_bytes / (ms * 1e-3) / 1e9
+    kernels = {}
+    if passes == 2:
+        # the unit is one reduce + broadcast pair: the fused pass of a group,
+        # credited with the pass's algorithmic bytes (every rank's input read
+        # once, every rank's result written once); the reduced values the
+        # broadcast re-reads are counted in the per-kernel figures
+        red, bc = kinds["fused_reduce"], kinds["broadcast"]
+        launches = red[1]
+        avg_launch_ms = red[0] / red[1] + bc[0] / bc[1]
+        kmax = red[2] + bc[2]
+        bytes_per_launch = hbm_bytes / (launches / args.steps)
+        rk = bytes_per_launch * (w.P + 1) / (2 * w.P)   # P reads + 1 write
+        bk = bytes_per_launch / 2                        # 1 read + P-1 writes
+        for name, (tot, cnt, mx), nb in (("fused_reduce_kernel", red, rk),
+                                          ("bcast_kernel", bc, bk)):
+            kernels[name] = {"launches_per_step": cnt / args.steps,
+                             "avg_launch_us": round(tot / cnt * 1e3, 2),
+                             "max_launch_us": round(mx * 1e3, 2),
+                             "algorithmic_bytes_per_launch": int(nb),
+                             "GBps": round(nb / (tot / cnt * 1e-3) / 1e9, 1)}
+        kernel_name = "fused pass: fused_reduce_kernel + bcast_kernel"
+    else:
+        kms = sum(v[0] for v in kinds.values())
+        launches = sum(v[1] for v in kinds.values())
+        kmax = max(v[2] for v in kinds.values())
+        avg_launch_ms = kms / launches
+        bytes_per_launch = hbm_bytes / (launches / args.steps)
+        kernel_name = "fused_kernel" if args.mode == "fused" else "step_kernel"
     launches_per_step = launches / args.steps
-    avg_launch_ms = kms / launches
-    bytes_per_launch = hbm_bytes / launches_per_step
     achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
-    log(f"bench: {ms:.3f} ms/step, {value:.1f} GB/s; {launches_per_step:.0f} launches/step, "
-        f"avg {avg_launch_ms * 1e3:.1f} us, kernel-side {achieved:.1f} GB/s "
-        f"(profiled steps {ms_prof:.3f} ms)")
+    log(f"bench: {ms:.3f} ms/step, {value:.1f} GB/s; {launches_per_step:.0f} "
+        f"{'passes' if passes == 2 else 'launches'}/step, avg {avg_launch_ms * 1e3:.1f} us, "
+        f"kernel-side {achieved:.1f} GB/s (profiled steps {ms_prof:.3f} ms) {kernels or ''}")
     esize = 4 if w.dtype == "f32" else 2
     bus_bw = 2 * (w.P - 1) / w.P * w.n * esize / (ms * 1e-3) / 1e9
 
@@ -163,23 +201,24 @@ def main():
         "config": {"workload": w.name, "P": w.P, "n": w.n, "topology": w.topo, "k": w.k,
                    "rows": w.rows, "cols": w.cols, "op": w.op, "buckets": len(buckets),
                    "side_stream": w.side_stream, "mode": args.mode,
-                   "bytes_per_step": hbm_bytes},
+                   "fused_passes": passes, "bytes_per_step": hbm_bytes},
         "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "bus_bw_GBps": round(bus_bw, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": FUSED_KERNEL if args.mode == "fused" else "step_kernel",
+            "kernel": kernel_name,
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
-            "traffic": measured_traffic(w.name, args.mode),
+            "traffic": measured_traffic(w.name, args.mode, passes),
             "launches_per_step": launches_per_step,
             "avg_launch_us": round(avg_launch_ms * 1e3, 2),
             "max_launch_us": round(kmax * 1e3, 2),
             "algorithmic_bytes_per_launch": int(bytes_per_launch),
             "profiled_ms_per_step": round(ms_prof, 4),
         },
+        **({"pass_kernels": kernels} if kernels else {}),
         "plan_build_ms": round(plan_build_ms, 2),
         "device": dev_name,
     }

@@ -190,6 +190,43 @@ int ddl_plan_set_coalesce_bytes(ddl_plan plan, size_t bytes);
  * start while the previous one drains; the results do not change. */
 int ddl_plan_set_side_streams(ddl_plan plan, int n);
 
+/* Form of a fused plan's pass (fused mode only; the SGD variant always uses
+ * the first).  passes = 1: one kernel reads every rank and writes every rank.
+ * passes = 2: a reduce kernel reads every rank and writes the result to rank
+ * 0, then a broadcast kernel copies it from rank 0 to ranks 1..P-1 while it
+ * is still in the device caches, so HBM serves a read phase and then a write
+ * phase.  passes = 0 (default): automatic, two kernels when P times the
+ * vectors each lane streams (1 for binary32, 2 for binary16) is at least 32.
+ * The results are bit-identical either way; only the speed differs.
+ * Returns DDL_E_ARG for other values.  Takes effect at the next execute.
+ * ddl_plan_get_fused_passes reports the form the next plain execute uses
+ * (0 for a stepwise plan). */
+int ddl_plan_set_fused_passes(ddl_plan plan, int passes);
+int ddl_plan_get_fused_passes(ddl_plan plan, int *passes);
+
+/* ---- tuning ------------------------------------------------------------ *
+ * Process-wide knobs of the fused pass's kernels, for benchmarks.  They
+ * change speed only, never results, and take effect at the next launch.
+ * ddl_set_tuning with a negative value restores the default; both return
+ * DDL_E_ARG for an unknown knob. */
+typedef enum {
+    /* two-kernel form: ranks each broadcast workgroup writes; 0 = automatic
+     * (2 from 32 ranks on; below, 3 for binary16 and 7 for binary32) */
+    DDL_TUNE_BCAST_RANKS = 0,
+    /* two-kernel form: 1 = the reduce kernel's loads are non-temporal
+     * (default), 0 = cached */
+    DDL_TUNE_REDUCE_NT_LOAD = 1,
+    /* one-kernel form: loads are non-temporal while P x vectors per lane is
+     * at most this (default 24) */
+    DDL_TUNE_FUSED_NT_LOAD_MAX_P = 2,
+    /* tile anchoring of the plans created afterwards: 0 = automatic (tables
+     * whose ranges average at least 2 tiles), 1 = never, 2 = always */
+    DDL_TUNE_ANCHOR = 3,
+    DDL_TUNE_COUNT = 4
+} ddl_tune_knob;
+int ddl_set_tuning(int knob, int value);
+int ddl_get_tuning(int knob, int *value);
+
 /* ---- measurement -------------------------------------------------------- *
  * With profiling on, every kernel launch is bracketed by a pair of HIP events
  * on the stream it is launched on.  ddl_plan_profile_read waits for the last
@@ -198,9 +235,22 @@ int ddl_plan_set_side_streams(ddl_plan plan, int n);
  * new count.  Costs a few microseconds per launch. */
 int ddl_plan_set_profiling(ddl_plan plan, int enable);
 int ddl_plan_profile_read(ddl_plan plan, double *total_ms, int *launches, double *max_ms);
+/* The same, per launch kind: each argument (or NULL) is an array of
+ * DDL_K_COUNT entries indexed by ddl_launch_kind. */
+int ddl_plan_profile_read_kinds(ddl_plan plan, double *total_ms, int *launches,
+                                double *max_ms);
 
 /* ---- schedule introspection (host-only; used by the tests) ------------- */
-typedef enum { DDL_K_REDUCE = 0, DDL_K_GATHER = 1, DDL_K_FUSED = 2 } ddl_launch_kind;
+/* Kernel launches: a reduce-scatter step, an all-gather step, the one-kernel
+ * fused pass, and the two kernels of the two-kernel fused pass. */
+typedef enum {
+    DDL_K_REDUCE = 0,
+    DDL_K_GATHER = 1,
+    DDL_K_FUSED = 2,
+    DDL_K_FUSED_REDUCE = 3,
+    DDL_K_BROADCAST = 4,
+    DDL_K_COUNT = 5
+} ddl_launch_kind;
 
 /* One pair transfer of one step: rank dst combines elements
  * [offset, offset+count) of rank src into its own (DDL_K_REDUCE, dividing

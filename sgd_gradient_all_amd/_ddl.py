@@ -10,7 +10,9 @@ DDL_F32, DDL_F16 = 0, 1
 DDL_SUM, DDL_MEAN = 0, 1
 DDL_RING, DDL_MULTIRING, DDL_TORUS2D = 0, 1, 2
 DDL_STEPWISE, DDL_FUSED = 0, 1
-DDL_K_REDUCE, DDL_K_GATHER, DDL_K_FUSED = 0, 1, 2
+DDL_K_REDUCE, DDL_K_GATHER, DDL_K_FUSED, DDL_K_FUSED_REDUCE, DDL_K_BROADCAST = 0, 1, 2, 3, 4
+DDL_K_COUNT = 5
+LAUNCH_KINDS = ("reduce", "gather", "fused", "fused_reduce", "broadcast")
 
 _DTYPES = {"f32": DDL_F32, "f16": DDL_F16, "float32": DDL_F32, "float16": DDL_F16}
 _OPS = {"sum": DDL_SUM, "mean": DDL_MEAN}
@@ -69,6 +71,13 @@ def lib():
             "ddl_strerror": ([i32], ctypes.c_char_p),
             "ddl_plan_set_coalesce_bytes": ([vp, sz], i32),
             "ddl_plan_set_side_streams": ([vp, i32], i32),
+            "ddl_plan_set_fused_passes": ([vp, i32], i32),
+            "ddl_set_tuning": ([i32, i32], i32),
+            "ddl_get_tuning": ([i32, ctypes.POINTER(i32)], i32),
+            "ddl_plan_get_fused_passes": ([vp, ctypes.POINTER(i32)], i32),
+            "ddl_plan_profile_read_kinds": ([vp, ctypes.POINTER(ctypes.c_double),
+                                             ctypes.POINTER(i32),
+                                             ctypes.POINTER(ctypes.c_double)], i32),
             "ddl_plan_set_profiling": ([vp, i32], i32),
             "ddl_plan_profile_read": ([vp, ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double)],
@@ -154,6 +163,20 @@ def ddl_cache_clear():
     _check(lib().ddl_cache_clear(), "ddl_cache_clear")
 
 
+TUNE = {"bcast_ranks": 0, "reduce_nt_load": 1, "fused_nt_load_max_p": 2, "anchor": 3}
+
+
+def set_tuning(knob, value):
+    """Process-wide kernel knob (ddl_set_tuning); value < 0 restores the default."""
+    _check(lib().ddl_set_tuning(_code(TUNE, knob), int(value)), "ddl_set_tuning")
+
+
+def get_tuning(knob):
+    v = ctypes.c_int()
+    _check(lib().ddl_get_tuning(_code(TUNE, knob), ctypes.byref(v)), "ddl_get_tuning")
+    return v.value
+
+
 class Plan:
     """Owner of a ddl_plan (ddl_plan_create / execute / traffic / destroy)."""
 
@@ -203,6 +226,15 @@ class Plan:
     def set_side_streams(self, n):
         _check(lib().ddl_plan_set_side_streams(self.handle, n), "set_side_streams")
 
+    def set_fused_passes(self, passes):
+        """0 automatic, 1 one kernel, 2 reduce kernel + broadcast kernel."""
+        _check(lib().ddl_plan_set_fused_passes(self.handle, int(passes)), "set_fused_passes")
+
+    def fused_passes(self):
+        v = ctypes.c_int()
+        _check(lib().ddl_plan_get_fused_passes(self.handle, ctypes.byref(v)), "fused_passes")
+        return v.value
+
     def set_profiling(self, on=True):
         _check(lib().ddl_plan_set_profiling(self.handle, 1 if on else 0), "set_profiling")
 
@@ -212,6 +244,15 @@ class Plan:
         _check(lib().ddl_plan_profile_read(self.handle, ctypes.byref(tot), ctypes.byref(cnt),
                                            ctypes.byref(mx)), "profile_read")
         return tot.value, cnt.value, mx.value
+
+    def profile_read_kinds(self):
+        """{kind name: (total ms, launches, longest ms)} since the last read."""
+        tot = (ctypes.c_double * DDL_K_COUNT)()
+        mx = (ctypes.c_double * DDL_K_COUNT)()
+        cnt = (ctypes.c_int * DDL_K_COUNT)()
+        _check(lib().ddl_plan_profile_read_kinds(self.handle, tot, cnt, mx),
+               "profile_read_kinds")
+        return {LAUNCH_KINDS[k]: (tot[k], cnt[k], mx[k]) for k in range(DDL_K_COUNT)}
 
     def num_steps(self):
         s = ctypes.c_int()

@@ -45,6 +45,28 @@ constexpr uint64_t fused_tile_elems(int esz) {
     return (uint64_t)kBlock * fused_vecs_per_lane(esz) * (kVecBytes / esz);
 }
 
+// Tiling of a range [off, off + len): tile j covers
+// [max(off, off - s + j * tile), min(off + len, off - s + (j + 1) * tile)).
+// With s = off % tile ("anchored") every tile but the range's first and
+// last starts at a multiple of the tile size (4 KB for the fused pass), so a
+// wave's 1 KB access covers whole 128-byte cache lines; with s = 0 the tiles
+// start at off.  Measured on MI355X, tiles starting 16-48 bytes into a line
+// cost 9% (one-kernel pass) to 15% (two-kernel pass) at 40 ranks, and the
+// schedule's chunk boundaries fall on 16-byte multiples only.  Anchoring
+// costs a tile per range, so tables of short ranges keep s = 0.
+constexpr uint64_t tile_shift(uint64_t off, uint64_t tile, bool anchor) {
+    return anchor ? off % tile : 0;
+}
+constexpr uint64_t tile_count(uint64_t len, uint64_t s, uint64_t tile) {
+    return len ? (s + len + tile - 1) / tile : 0;
+}
+constexpr uint64_t tile_lo(uint64_t off, uint64_t s, uint64_t tile, uint64_t j) {
+    return j == 0 ? off : off - s + j * tile;
+}
+constexpr uint64_t tile_hi(uint64_t off, uint64_t len, uint64_t s, uint64_t tile, uint64_t j) {
+    return off - s + (j + 1) * tile < off + len ? off - s + (j + 1) * tile : off + len;
+}
+
 enum : uint32_t {
     kItemDivide = 1u,   // divide by P after the add (mean epilogue)
     kItemAligned = 2u,  // offset is a multiple of 16 B / element size
@@ -83,12 +105,14 @@ struct StepArgs {
     uint32_t item_lo, item_hi;
     uint32_t tile_base;
     float divisor;   // P, for the mean
+    int anchor;      // tiles anchored at multiples of the tile size
 };
 
 // Arguments of one fused launch over spans [span_lo, span_hi).
 struct FusedArgs {
     const DevSpan *spans;
     const uint32_t *prefix;
+    const uint32_t *tile_span;  // [t] span of tile t
     const uint8_t *chains;
     uint32_t span_lo, span_hi;
     uint32_t tile_base;  // first tile of this launch
@@ -97,6 +121,21 @@ struct FusedArgs {
     int group;       // chain entries per group (P for rings, cols for the torus)
     int mean;        // divide by P at the end
     float divisor;
+    int anchor;      // tiles anchored at multiples of the tile size
+};
+
+// Arguments of one broadcast launch (second kernel of the two-kernel fused
+// form): elements [off, off + len) of rank 0 are copied to ranks 1..P-1,
+// ranks_per_group of them per workgroup, so each tile of fused_tile_elems
+// elements takes ngroups = ceil((P-1) / ranks_per_group) workgroups.  A
+// group's buckets are copied as the contiguous runs of memory they form, so
+// the kernel needs no tables.  aligned: off is a multiple of 16 bytes.
+struct BcastArgs {
+    uint64_t off, len;
+    int P;
+    int ranks_per_group;
+    int ngroups;
+    int aligned;
 };
 
 // The SGD step fused into the all-reduce's epilogue: binary32 weight
@@ -111,10 +150,15 @@ struct SgdArgs {
     int keep_grads;
 };
 
+// Current value of a ddl_tune_knob (its default unless ddl_set_tuning set it).
+int tuning(int knob);
+
 // Kernel launchers.  sgd may be null (plain all-reduce).  Return hipError_t.
 int launch_step(int dtype, int kind, int vpl, const RankPtrs &bufs, const StepArgs &a,
                 const SgdArgs *sgd, uint32_t tiles, void *stream);
+// home: the reduce kernel of the two-kernel form (result to rank 0 only).
 int launch_fused(int dtype, const RankPtrs &bufs, const FusedArgs &a, const SgdArgs *sgd,
-                 uint32_t tiles, void *stream);
+                 bool home, uint32_t tiles, void *stream);
+int launch_bcast(int dtype, const RankPtrs &bufs, const BcastArgs &a, void *stream);
 
 }  // namespace ddl

@@ -1,12 +1,20 @@
-// fused_kernel.hip -- the single-pass all-reduce (gfx950).
+// fused_kernel.hip -- the fused all-reduce pass (gfx950).
 //
 // Every element is read once from each of the P ranks, summed in the order
 // the schedule sums it, divided by P for the mean, and written once to each
 // rank: 2 P s bytes per element, the floor for this operation.  It is
 // bit-identical to the step-by-step walk because every dependency of the
 // schedule is per element.
-#include <stdlib.h>
-
+//
+// The pass runs in one of two forms:
+//  - one kernel (fused_kernel): each workgroup reads its tile from all P
+//    ranks and writes the result to all P ranks;
+//  - two kernels over the same tiles: fused_reduce_kernel reads all P ranks
+//    and writes the result to rank 0 only, through the cache; then
+//    bcast_kernel copies rank 0's result, still cache-resident, to ranks
+//    1..P-1.  HBM then sees a read phase and a write phase instead of reads
+//    and writes interleaved, which is faster from 16 ranks on (measured on
+//    MI355X: 40 ranks +13..+32%, 16 ranks +7..+20%, 8 ranks -4..-7%).
 #include "device_common.h"
 
 namespace ddl {
@@ -15,16 +23,13 @@ namespace {
 using namespace dev;
 
 // Streaming accesses.  Every element is touched once per pass, so the
-// results are written with non-temporal stores.  Loads are non-temporal when
-// P times the vectors per lane is at most DDL_NT_LOAD_MAX_P (24; the
-// environment variable DDL_FUSED_NT_LOAD_MAX_P overrides it at run time).
-// Measured on MI355X: +7..+15% for binary32 at 8 and 16 ranks and binary16
-// at 8, -4% for binary32 at 40 ranks, -9..-14% for binary16 at 16.
+// results are written with non-temporal stores.  In the one-kernel form,
+// loads are non-temporal when P times the vectors per lane is at most 24
+// (knob DDL_TUNE_FUSED_NT_LOAD_MAX_P).  Measured on MI355X: +7..+15% for
+// binary32 at 8 and 16 ranks and binary16 at 8, -4% for binary32 at 40
+// ranks, -9..-14% for binary16 at 16.
 #ifndef DDL_NT_STORE
 #define DDL_NT_STORE 1
-#endif
-#ifndef DDL_NT_LOAD_MAX_P
-#define DDL_NT_LOAD_MAX_P 24
 #endif
 // Loads a lane issues ahead of their adds.  Measured on MI355X, one is best
 // or within 1% of best: the many-stream pass saturates HBM, and more
@@ -162,7 +167,24 @@ __device__ __forceinline__ void sgd_all(const SgdArgs *g, uint64_t e,
         }
 }
 
-template <class E, bool kGrouped, bool kNt, bool kSgd>
+// Stores of the reduced vectors v[0..U) of element e to rank 0 only, with
+// ordinary (cached) stores: the broadcast kernel that follows re-reads them.
+template <class E, int U>
+__device__ __forceinline__ void store_home(const RankPtrs &bufs, uint64_t e,
+                                           const typename E::V (&v)[U]) {
+    using T = typename E::T;
+    using V = typename E::V;
+    constexpr uint64_t kStride = (uint64_t)kBlock * E::N;
+    V DDL_GLOBAL *h = reinterpret_cast<V DDL_GLOBAL *>(
+        reinterpret_cast<uint64_t>(bufs.p[0]) + e * sizeof(T));
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        h[u * (kStride / E::N)] = v[u];
+}
+
+// kHome: write the result to rank 0 only (the first kernel of the two-kernel
+// form); otherwise to every rank.
+template <class E, bool kGrouped, bool kNt, bool kSgd, bool kHome>
 __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs &a,
                                            const SgdArgs *g) {
     using T = typename E::T;
@@ -176,7 +198,7 @@ __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs
     const uint32_t last = min(first + (uint32_t)kFusedTilesPerGroup, a.tile_end);
     uint32_t i = a.span_lo, have = UINT32_MAX;
     for (uint32_t tile = first; tile < last; ++tile) {
-        i = find_item(a.prefix, i, a.span_hi, tile);
+        i = a.tile_span[tile];
         const DevSpan sp = a.spans[i];
         if (i != have) {
             // a new span: its chain decides which rank is read first
@@ -187,10 +209,10 @@ __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs
             __syncthreads();
             have = i;
         }
-        const uint64_t t0 = (uint64_t)(tile - a.prefix[i]) * kTile;
-        const uint64_t rem = sp.len - t0;
-        const uint32_t cnt = (uint32_t)(rem < kTile ? rem : kTile);
-        const uint64_t base = sp.off + t0;
+        const uint64_t j = tile - a.prefix[i];
+        const uint64_t sh = tile_shift(sp.off, kTile, a.anchor);
+        const uint64_t base = tile_lo(sp.off, sh, kTile, j);
+        const uint32_t cnt = (uint32_t)(tile_hi(sp.off, sp.len, sh, kTile, j) - base);
         uint32_t done = 0;
         if (sp.flags & kItemAligned) {
             const uint32_t nvec = cnt / E::N;
@@ -202,7 +224,9 @@ __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs
 #pragma unroll
                     for (int u = 0; u < U; ++u)
                         acc[u] = E::div(acc[u], a.divisor);
-                if (!kSgd || g->keep_grads)
+                if (kHome)
+                    store_home<E, U>(bufs, e, acc);
+                else if (!kSgd || g->keep_grads)
                     store_all<E, U>(bufs, P, e, acc);
                 if (kSgd)
                     sgd_all<E, kNt, U>(g, e, acc);
@@ -213,7 +237,9 @@ __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs
                     fused_vecs<E, kGrouped, kNt, 1>(src, P, a.group, e, acc);
                     if (a.mean)
                         acc[0] = E::div(acc[0], a.divisor);
-                    if (!kSgd || g->keep_grads)
+                    if (kHome)
+                        store_home<E, 1>(bufs, e, acc);
+                    else if (!kSgd || g->keep_grads)
                         store_all<E, 1>(bufs, P, e, acc);
                     if (kSgd)
                         sgd_all<E, kNt, 1>(g, e, acc);
@@ -237,7 +263,9 @@ __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs
             }
             if (a.mean)
                 acc = E::div1(acc, a.divisor);
-            if (!kSgd || g->keep_grads)
+            if (kHome)
+                static_cast<T *>(bufs.p[0])[e] = acc;
+            else if (!kSgd || g->keep_grads)
                 for (int r = 0; r < P; ++r)
                     static_cast<T *>(bufs.p[r])[e] = acc;
             if (kSgd)
@@ -257,32 +285,102 @@ __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs
 template <class E, bool kGrouped, bool kNt>
 __global__ __launch_bounds__(kBlock) DDL_FUSED_OCCUPANCY
 void fused_kernel(RankPtrs bufs, FusedArgs a) {
-    fused_body<E, kGrouped, kNt, false>(bufs, a, nullptr);
+    fused_body<E, kGrouped, kNt, false, false>(bufs, a, nullptr);
 }
 
 template <class E, bool kGrouped, bool kNt>
 __global__ __launch_bounds__(kBlock) DDL_FUSED_OCCUPANCY
 void fused_sgd_kernel(RankPtrs bufs, FusedArgs a, SgdArgs g) {
-    fused_body<E, kGrouped, kNt, true>(bufs, a, &g);
+    fused_body<E, kGrouped, kNt, true, false>(bufs, a, &g);
+}
+
+template <class E, bool kGrouped, bool kNt>
+__global__ __launch_bounds__(kBlock) DDL_FUSED_OCCUPANCY
+void fused_reduce_kernel(RankPtrs bufs, FusedArgs a) {
+    fused_body<E, kGrouped, kNt, false, true>(bufs, a, nullptr);
+}
+
+// ---------------------------------------------------------------------------
+// broadcast: the second kernel of the two-kernel form.  Workgroup b copies
+// anchored tile b / ngroups of the run [off, off + len) from rank 0 to ranks
+// 1 + g * ranks_per_group ... (at most P - 1), g = b % ngroups.  The copy is
+// of the bits: no arithmetic.  No table is read, so a workgroup's first
+// access is the load of the values it copies.
+// ---------------------------------------------------------------------------
+template <class E>
+__global__ __launch_bounds__(kBlock) void bcast_kernel(RankPtrs bufs, BcastArgs a) {
+    using T = typename E::T;
+    using V = typename E::V;
+    constexpr int U = fused_vecs_per_lane(sizeof(T));
+    constexpr uint64_t kTile = fused_tile_elems(sizeof(T));
+    constexpr uint64_t kStride = (uint64_t)kBlock * E::N;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t ng = (uint32_t)a.ngroups;
+    const uint64_t j = blockIdx.x / ng;
+    const int grp = (int)(blockIdx.x % ng);
+    const uint64_t sh = tile_shift(a.off, kTile, true);
+    if (j >= tile_count(a.len, sh, kTile))
+        return;
+    const uint64_t base = tile_lo(a.off, sh, kTile, j);
+    const uint32_t cnt = (uint32_t)(tile_hi(a.off, a.len, sh, kTile, j) - base);
+    const int r0 = 1 + grp * a.ranks_per_group;
+    const int r1 = min(a.P, r0 + a.ranks_per_group);
+    const T DDL_GLOBAL *home =
+        reinterpret_cast<const T DDL_GLOBAL *>(reinterpret_cast<uint64_t>(bufs.p[0]));
+    uint32_t done = 0;
+    if (a.aligned) {
+        const uint32_t nvec = cnt / E::N;
+        if (nvec == (uint32_t)(U * kBlock)) {
+            const uint64_t e = base + (uint64_t)tid * E::N;
+            V v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                v[u] = *reinterpret_cast<const V DDL_GLOBAL *>(home + e + u * kStride);
+            for (int r = r0; r < r1; ++r)
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    st_stream<V>(static_cast<T *>(bufs.p[r]) + e + u * kStride, v[u]);
+        } else {
+            for (uint32_t k = tid; k < nvec; k += kBlock) {
+                const uint64_t e = base + (uint64_t)k * E::N;
+                const V v = *reinterpret_cast<const V DDL_GLOBAL *>(home + e);
+                for (int r = r0; r < r1; ++r)
+                    st_stream<V>(static_cast<T *>(bufs.p[r]) + e, v);
+            }
+        }
+        done = nvec * E::N;
+    }
+    for (uint32_t k = done + tid; k < cnt; k += kBlock) {
+        const uint64_t e = base + k;
+        const T x = home[e];
+        for (int r = r0; r < r1; ++r)
+            static_cast<T *>(bufs.p[r])[e] = x;
+    }
 }
 
 }  // namespace
 
 namespace {
 
-int nt_load_max_ranks() {
-    static const int v = [] {
-        const char *e = getenv("DDL_FUSED_NT_LOAD_MAX_P");
-        return e ? atoi(e) : DDL_NT_LOAD_MAX_P;
-    }();
-    return v;
-}
-
 template <class E, bool kGrouped>
 void launch_e(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a,
-              const SgdArgs *sgd) {
+              const SgdArgs *sgd, bool home) {
     const dim3 block(kBlock);
-    const bool nt = a.P * fused_vecs_per_lane(sizeof(typename E::T)) <= nt_load_max_ranks();
+    if (home) {
+        // the reduce kernel reads the ranks with non-temporal loads whatever
+        // P: the P input streams must not evict the results the broadcast
+        // kernel re-reads (measured on MI355X, 40 ranks: 6031 GB/s against
+        // 5242 with cached loads)
+        if (tuning(DDL_TUNE_REDUCE_NT_LOAD) != 0)
+            hipLaunchKernelGGL((fused_reduce_kernel<E, kGrouped, true>), grid, block, 0, s, bufs,
+                               a);
+        else
+            hipLaunchKernelGGL((fused_reduce_kernel<E, kGrouped, false>), grid, block, 0, s,
+                               bufs, a);
+        return;
+    }
+    const bool nt = a.P * fused_vecs_per_lane(sizeof(typename E::T)) <=
+                    tuning(DDL_TUNE_FUSED_NT_LOAD_MAX_P);
     if (sgd) {
         if (nt)
             hipLaunchKernelGGL((fused_sgd_kernel<E, kGrouped, true>), grid, block, 0, s, bufs, a,
@@ -300,21 +398,38 @@ void launch_e(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a
 }  // namespace
 
 int launch_fused(int dtype, const RankPtrs &bufs, const FusedArgs &a, const SgdArgs *sgd,
-                 uint32_t tiles, void *stream) {
+                 bool home, uint32_t tiles, void *stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     dim3 grid((tiles + kFusedTilesPerGroup - 1) / kFusedTilesPerGroup);
     const bool grouped = a.group != a.P;
     if (dtype == DDL_F32) {
         if (grouped)
-            launch_e<F32, true>(grid, s, bufs, a, sgd);
+            launch_e<F32, true>(grid, s, bufs, a, sgd, home);
         else
-            launch_e<F32, false>(grid, s, bufs, a, sgd);
+            launch_e<F32, false>(grid, s, bufs, a, sgd, home);
     } else {
         if (grouped)
-            launch_e<F16, true>(grid, s, bufs, a, sgd);
+            launch_e<F16, true>(grid, s, bufs, a, sgd, home);
         else
-            launch_e<F16, false>(grid, s, bufs, a, sgd);
+            launch_e<F16, false>(grid, s, bufs, a, sgd, home);
     }
+    return (int)hipGetLastError();
+}
+
+int launch_bcast(int dtype, const RankPtrs &bufs, const BcastArgs &a, void *stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint64_t tile = fused_tile_elems(dtype == DDL_F32 ? 4 : 2);
+    const uint64_t blocks =
+        tile_count(a.len, tile_shift(a.off, tile, true), tile) * (uint64_t)a.ngroups;
+    if (a.ngroups < 1 || a.ranks_per_group < 1 || blocks * kBlock > 0xffffffffull)
+        return (int)hipErrorInvalidValue;
+    if (blocks == 0)
+        return (int)hipSuccess;
+    const dim3 grid((uint32_t)blocks), block(kBlock);
+    if (dtype == DDL_F32)
+        hipLaunchKernelGGL((bcast_kernel<F32>), grid, block, 0, s, bufs, a);
+    else
+        hipLaunchKernelGGL((bcast_kernel<F16>), grid, block, 0, s, bufs, a);
     return (int)hipGetLastError();
 }
 

@@ -10,6 +10,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstring>
 #include <map>
 #include <memory>
@@ -25,11 +26,31 @@ using namespace ddl;
 
 constexpr int kMaxSideStreams = 4;
 
+// process-wide tuning knobs (ddl_set_tuning); -1 = default
+std::atomic<int> g_tune[DDL_TUNE_COUNT] = {-1, -1, -1, -1};
+constexpr int kTuneDefault[DDL_TUNE_COUNT] = {
+    0,   // DDL_TUNE_BCAST_RANKS: automatic
+    1,   // DDL_TUNE_REDUCE_NT_LOAD: on
+    24,  // DDL_TUNE_FUSED_NT_LOAD_MAX_P
+    0,   // DDL_TUNE_ANCHOR: automatic
+};
+
+namespace ddl {
+int tuning(int knob) {
+    if (knob < 0 || knob >= DDL_TUNE_COUNT)
+        return 0;
+    const int v = g_tune[knob].load(std::memory_order_relaxed);
+    return v < 0 ? kTuneDefault[knob] : v;
+}
+}  // namespace ddl
+constexpr int kLaunchKinds = DDL_K_COUNT;
+
 struct ddl_plan_s {
     Schedule s;
     int mode = DDL_FUSED;
     size_t coalesce_bytes = 0;
     int nside = 1;          // side streams event-gated groups alternate over
+    int fused_passes = 0;   // 0 automatic, 1 one kernel, 2 reduce + broadcast
 
     std::mutex mu;
     int device = -1;        // bound at first execution
@@ -44,11 +65,13 @@ struct ddl_plan_s {
     std::vector<size_t> item_base, prefix_base;  // per step, into the above
     DevSpan *d_spans = nullptr;
     uint32_t *d_span_prefix = nullptr;
+    uint32_t *d_span_of_tile = nullptr;
     uint8_t *d_chains = nullptr;
 
     // profiling
     bool profiling = false;
     std::vector<hipEvent_t> prof;   // pairs (start, end)
+    std::vector<int> prof_kind;     // ddl_launch_kind of each pair
     int prof_used = 0;
 };
 
@@ -80,6 +103,7 @@ void release_device(ddl_plan p) {
     (void)hipFree(p->d_prefix);
     (void)hipFree(p->d_spans);
     (void)hipFree(p->d_span_prefix);
+    (void)hipFree(p->d_span_of_tile);
     (void)hipFree(p->d_chains);
     for (hipEvent_t e : p->prof)
         (void)hipEventDestroy(e);
@@ -128,6 +152,7 @@ int bind_device(ddl_plan p, int dev) {
     // SGD step, which has no schedule step to ride on
     if ((rc = upload(&p->d_spans, s.spans.data(), s.spans.size())) ||
         (rc = upload(&p->d_span_prefix, s.span_prefix.data(), s.span_prefix.size())) ||
+        (rc = upload(&p->d_span_of_tile, s.span_of_tile.data(), s.span_of_tile.size())) ||
         (rc = upload(&p->d_chains, s.chains.data(), s.chains.size())))
         return rc;
     return DDL_OK;
@@ -139,13 +164,42 @@ int bind_device(ddl_plan p, int dev) {
 // A grid holds at most 2^32 - 1 work-items in x: cut bigger launches.
 constexpr uint32_t kMaxTilesPerLaunch = 1u << 23;
 
+// Form of the fused pass: one kernel, or a reduce kernel that writes rank 0
+// and a broadcast kernel (see fused_kernel.hip).  Automatic: two kernels
+// when each lane streams at least 32 vectors (P times the vectors per lane),
+// where they measured faster on MI355X: 40 ranks fp32 +5%, 16 ranks fp16
+// +5%; 16 ranks fp32 -3%, 8 ranks -3%.  The SGD variant always takes one
+// kernel.
+int fused_passes(ddl_plan p, bool sgd) {
+    if (sgd || p->s.P < 2)
+        return 1;
+    if (p->fused_passes)
+        return p->fused_passes;
+    return p->s.P * fused_vecs_per_lane(p->s.esz) >= 32 ? 2 : 1;
+}
+
+// Ranks one broadcast workgroup writes (knob DDL_TUNE_BCAST_RANKS, 0 =
+// automatic).  Measured on MI355X (paired runs): 40 ranks fp32, two (5.45
+// TB/s; 4 within 1%, all 39 -4%, one -7%); 16 ranks fp16, three (5.47
+// against 5.35 with all 15); 16 ranks fp32, seven (5.51 against 5.26 with
+// all 15; the order of 7 and 15 changed between boxes).
+int bcast_ranks_per_group(int P, int esz) {
+    const int v = tuning(DDL_TUNE_BCAST_RANKS);
+    if (v > 0)
+        return std::min(v, std::max(P - 1, 1));
+    if (P >= 32)
+        return 2;
+    return std::min(esz == 2 ? 3 : 7, std::max(P - 1, 1));
+}
+
 struct Launcher {
     ddl_plan p;
     const RankPtrs &bufs;
     hipStream_t stream;
     const SgdArgs *sgd;  // null for the plain all-reduce
+    std::vector<Bucket> runs;
 
-    int bracket_begin() {
+    int bracket_begin(int kind) {
         if (!p->profiling)
             return DDL_OK;
         if ((size_t)(2 * p->prof_used + 2) > p->prof.size()) {
@@ -154,7 +208,9 @@ struct Launcher {
                 return DDL_E_HIP;
             p->prof.push_back(a);
             p->prof.push_back(b);
+            p->prof_kind.push_back(0);
         }
+        p->prof_kind[p->prof_used] = kind;
         return hipEventRecord(p->prof[2 * p->prof_used], stream) == hipSuccess ? DDL_OK
                                                                                : DDL_E_HIP;
     }
@@ -178,10 +234,11 @@ struct Launcher {
         a.item_lo = lo;
         a.item_hi = hi;
         a.divisor = (float)s.P;
+        a.anchor = s.step_anchor;
         for (uint32_t t = pre[lo]; t < pre[hi]; t += kMaxTilesPerLaunch) {
             const uint32_t tiles = std::min(kMaxTilesPerLaunch, pre[hi] - t);
             a.tile_base = t;
-            int rc = bracket_begin();
+            int rc = bracket_begin(s.step_kind[st]);
             if (rc)
                 return rc;
             if (launch_step(s.dtype, s.step_kind[st], s.step_vpl, bufs, a, sgd, tiles, stream) !=
@@ -193,14 +250,19 @@ struct Launcher {
         return DDL_OK;
     }
 
-    int fused(uint32_t lo, uint32_t hi) {
+    // the fused pass of buckets [b0, b1): one kernel, or the reduce kernel
+    // over their spans and then the broadcast over the runs of memory they
+    // cover
+    int fused(int b0, int b1) {
         const Schedule &s = p->s;
+        const uint32_t lo = s.span_at[b0], hi = s.span_at[b1];
         if (lo == hi)
             return DDL_OK;
         const uint32_t *pre = s.span_prefix.data();
         FusedArgs a;
         a.spans = p->d_spans;
         a.prefix = p->d_span_prefix;
+        a.tile_span = p->d_span_of_tile;
         a.chains = p->d_chains;
         a.span_lo = lo;
         a.span_hi = hi;
@@ -208,17 +270,58 @@ struct Launcher {
         a.group = s.group;
         a.mean = s.op == DDL_MEAN;
         a.divisor = (float)s.P;
+        a.anchor = s.fused_anchor;
+        const bool two = fused_passes(p, sgd != nullptr) == 2;
         for (uint32_t t = pre[lo]; t < pre[hi]; t += kMaxTilesPerLaunch) {
             const uint32_t tiles = std::min(kMaxTilesPerLaunch, pre[hi] - t);
             a.tile_base = t;
             a.tile_end = t + tiles;
-            int rc = bracket_begin();
+            int rc = bracket_begin(two ? DDL_K_FUSED_REDUCE : DDL_K_FUSED);
             if (rc)
                 return rc;
-            if (launch_fused(s.dtype, bufs, a, sgd, tiles, stream) != hipSuccess)
+            if (launch_fused(s.dtype, bufs, a, sgd, two, tiles, stream) != hipSuccess)
                 return DDL_E_HIP;
             if ((rc = bracket_end()))
                 return rc;
+        }
+        if (!two)
+            return DDL_OK;
+        runs.clear();
+        for (int b = b0; b < b1; ++b)
+            if (s.buckets[b].len)
+                runs.push_back(s.buckets[b]);
+        std::sort(runs.begin(), runs.end(),
+                  [](const Bucket &x, const Bucket &y) { return x.off < y.off; });
+        size_t m = 0;
+        for (size_t i = 1; i < runs.size(); ++i) {
+            if (runs[m].off + runs[m].len == runs[i].off)
+                runs[m].len += runs[i].len;
+            else
+                runs[++m] = runs[i];
+        }
+        runs.resize(runs.empty() ? 0 : m + 1);
+        BcastArgs bc;
+        bc.P = s.P;
+        bc.ranks_per_group = bcast_ranks_per_group(s.P, s.esz);
+        bc.ngroups = (s.P - 1 + bc.ranks_per_group - 1) / bc.ranks_per_group;
+        // a grid holds at most 2^32 - 1 work-items: runs are cut at
+        // multiples of max_elems, which keeps the tiles' anchoring (the
+        // broadcast always anchors: its runs are whole buckets)
+        const uint64_t tile = fused_tile_elems(s.esz);
+        const uint64_t max_elems = (uint64_t)(0xffffffu / (uint32_t)bc.ngroups) * tile;
+        for (const Bucket &r : runs) {
+            for (uint64_t o = r.off; o < r.off + r.len; o = (o / max_elems + 1) * max_elems) {
+                bc.off = o;
+                bc.len = std::min((o / max_elems + 1) * max_elems, r.off + r.len) - o;
+                bc.aligned = bc.off % s.q == 0;
+                int rc = bracket_begin(DDL_K_BROADCAST);
+                if (rc)
+                    return rc;
+                if (launch_bcast(s.dtype, bufs, bc, stream) != hipSuccess)
+                    return DDL_E_HIP;
+                if ((rc = bracket_end()))
+                    return rc;
+            }
         }
         return DDL_OK;
     }
@@ -227,7 +330,7 @@ struct Launcher {
     int group(int b0, int b1) {
         const Schedule &s = p->s;
         if (p->mode == DDL_FUSED || (sgd && s.P == 1))
-            return fused(s.span_at[b0], s.span_at[b1]);
+            return fused(b0, b1);
         for (int st = 0; st < s.nsteps; ++st) {
             int rc = step(st, s.item_at[st][b0], s.item_at[st][b1]);
             if (rc)
@@ -561,26 +664,88 @@ int ddl_plan_set_profiling(ddl_plan plan, int enable) {
     return DDL_OK;
 }
 
-int ddl_plan_profile_read(ddl_plan plan, double *total_ms, int *launches, double *max_ms) {
+int ddl_plan_profile_read_kinds(ddl_plan plan, double *total_ms, int *launches,
+                                double *max_ms) {
     if (!plan)
         return DDL_E_NULL;
     std::lock_guard<std::mutex> lk(plan->mu);
-    double tot = 0, mx = 0;
+    double tot[kLaunchKinds] = {}, mx[kLaunchKinds] = {};
+    int cnt[kLaunchKinds] = {};
     for (int i = 0; i < plan->prof_used; ++i) {
         float ms = 0;
         if (hipEventSynchronize(plan->prof[2 * i + 1]) != hipSuccess ||
             hipEventElapsedTime(&ms, plan->prof[2 * i], plan->prof[2 * i + 1]) != hipSuccess)
             return DDL_E_HIP;
-        tot += ms;
-        mx = std::max(mx, (double)ms);
+        const int k = plan->prof_kind[i];
+        tot[k] += ms;
+        mx[k] = std::max(mx[k], (double)ms);
+        ++cnt[k];
+    }
+    for (int k = 0; k < kLaunchKinds; ++k) {
+        if (total_ms)
+            total_ms[k] = tot[k];
+        if (launches)
+            launches[k] = cnt[k];
+        if (max_ms)
+            max_ms[k] = mx[k];
+    }
+    plan->prof_used = 0;
+    return DDL_OK;
+}
+
+int ddl_plan_profile_read(ddl_plan plan, double *total_ms, int *launches, double *max_ms) {
+    double tot[kLaunchKinds], mx[kLaunchKinds];
+    int cnt[kLaunchKinds];
+    const int rc = ddl_plan_profile_read_kinds(plan, tot, cnt, mx);
+    if (rc)
+        return rc;
+    double t = 0, m = 0;
+    int c = 0;
+    for (int k = 0; k < kLaunchKinds; ++k) {
+        t += tot[k];
+        c += cnt[k];
+        m = std::max(m, mx[k]);
     }
     if (total_ms)
-        *total_ms = tot;
+        *total_ms = t;
     if (launches)
-        *launches = plan->prof_used;
+        *launches = c;
     if (max_ms)
-        *max_ms = mx;
-    plan->prof_used = 0;
+        *max_ms = m;
+    return DDL_OK;
+}
+
+int ddl_set_tuning(int knob, int value) {
+    if (knob < 0 || knob >= DDL_TUNE_COUNT)
+        return DDL_E_ARG;
+    g_tune[knob].store(value < 0 ? -1 : value);
+    return DDL_OK;
+}
+
+int ddl_get_tuning(int knob, int *value) {
+    if (!value)
+        return DDL_E_NULL;
+    if (knob < 0 || knob >= DDL_TUNE_COUNT)
+        return DDL_E_ARG;
+    *value = tuning(knob);
+    return DDL_OK;
+}
+
+int ddl_plan_set_fused_passes(ddl_plan plan, int passes) {
+    if (!plan)
+        return DDL_E_NULL;
+    if (passes < 0 || passes > 2)
+        return DDL_E_ARG;
+    std::lock_guard<std::mutex> lk(plan->mu);
+    plan->fused_passes = passes;
+    return DDL_OK;
+}
+
+int ddl_plan_get_fused_passes(ddl_plan plan, int *passes) {
+    if (!plan || !passes)
+        return DDL_E_NULL;
+    std::lock_guard<std::mutex> lk(plan->mu);
+    *passes = plan->mode == DDL_FUSED ? fused_passes(plan, false) : 0;
     return DDL_OK;
 }
 

@@ -36,12 +36,15 @@ struct Schedule {
     std::vector<std::vector<uint32_t>> item_at;  // [s] first item of bucket b, nb+1
     std::vector<std::vector<uint32_t>> prefix;   // [s] tile prefix, nitems+1
     int step_vpl = 4;                            // step kernels' vectors per lane
+    bool step_anchor = false;                    // step tiles anchored (ddl_internal.h)
 
     // fused tables: spans bucket-major, P chain entries each
     int group = 1;                       // chain entries per group
     std::vector<DevSpan> spans;
     std::vector<uint32_t> span_at;       // first span of bucket b, nb+1
     std::vector<uint32_t> span_prefix;   // tile prefix, nspans+1
+    std::vector<uint32_t> span_of_tile;  // [t] the span fused tile t belongs to
+    bool fused_anchor = false;           // fused tiles anchored (ddl_internal.h)
     std::vector<uint8_t> chains;
 
     // accounting

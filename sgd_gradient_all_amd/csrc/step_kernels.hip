@@ -31,16 +31,17 @@ __device__ __forceinline__ void step_body(const RankPtrs &bufs, const StepArgs &
     const uint32_t tile = a.tile_base + blockIdx.x;
     const uint32_t i = find_item(a.prefix, a.item_lo, a.item_hi, tile);
     const DevItem it = a.items[i];
-    const uint64_t t0 = (uint64_t)(tile - a.prefix[i]) * kTile;
-    const uint64_t rem = it.len - t0;
-    const uint32_t cnt = (uint32_t)(rem < kTile ? rem : kTile);
-    T *dst = static_cast<T *>(bufs.p[it.dst]) + it.off + t0;
-    const T *src = static_cast<const T *>(bufs.p[it.src]) + it.off + t0;
+    const uint64_t j = tile - a.prefix[i];
+    const uint64_t sh = tile_shift(it.off, kTile, a.anchor);
+    const uint64_t lo = tile_lo(it.off, sh, kTile, j);
+    const uint32_t cnt = (uint32_t)(tile_hi(it.off, it.len, sh, kTile, j) - lo);
+    T *dst = static_cast<T *>(bufs.p[it.dst]) + lo;
+    const T *src = static_cast<const T *>(bufs.p[it.src]) + lo;
     const bool divide = kReduce && (it.flags & kItemDivide);
     float *w = nullptr;
     float lr = 0.0f;
     if (kSgd && (kReduce ? (it.flags & kItemFinal) != 0 : g->nweights > 1)) {
-        w = static_cast<float *>(g->w.p[g->nweights == 1 ? 0 : it.dst]) + it.off + t0;
+        w = static_cast<float *>(g->w.p[g->nweights == 1 ? 0 : it.dst]) + lo;
         lr = g->lr;
     }
     const uint32_t tid = threadIdx.x;

@@ -9,7 +9,8 @@
 //    (the generator's own race check must agree);
 //  - the traffic identity: the ranks send 2 (P-1) L elements per ring segment;
 //  - every fused span's chain is a permutation of the ranks, and the spans of
-//    a bucket tile it exactly.
+//    a bucket tile it exactly;
+//  - the fused tile -> span table agrees with the spans' tile prefix.
 // Exit status 0 when all checks pass; prints the failing case otherwise.
 #include <algorithm>
 #include <cstdio>
@@ -21,6 +22,14 @@
 
 using namespace ddl;
 
+// The library's tuning knobs live with the plans (plan.cpp, not linked
+// here).  The generator reads one, tile anchoring, which this driver cycles
+// through automatic / never / always.
+static int g_anchor = 0;
+namespace ddl {
+int tuning(int knob) { return knob == DDL_TUNE_ANCHOR ? g_anchor : 0; }
+}  // namespace ddl
+
 static int fail(const char *what, int P, uint64_t n, int kind) {
     std::printf("FAIL %s: P=%d n=%llu kind=%d\n", what, P, (unsigned long long)n, kind);
     return 1;
@@ -30,6 +39,7 @@ int main(int argc, char **argv) {
     const int cases = argc > 1 ? std::atoi(argv[1]) : 400;
     std::mt19937_64 rng(12345);
     for (int cs = 0; cs < cases; ++cs) {
+        g_anchor = cs % 3;
         const int P = 1 + (int)(rng() % 24);
         const uint64_t n = rng() % 3000;
         const int dtype = (int)(rng() % 2);
@@ -119,6 +129,13 @@ int main(int argc, char **argv) {
             }
             if (covered != s.buckets[b].len)
                 return fail("spans tile the bucket", P, n, topo.kind);
+        }
+        if (s.span_of_tile.size() != s.span_prefix.back())
+            return fail("one table entry per fused tile", P, n, topo.kind);
+        for (size_t t = 0; t < s.span_of_tile.size(); ++t) {
+            const uint32_t i = s.span_of_tile[t];
+            if (i >= s.spans.size() || s.span_prefix[i] > t || t >= s.span_prefix[i + 1])
+                return fail("tile -> span table", P, n, topo.kind);
         }
     }
     std::printf("ok %d cases\n", cases);

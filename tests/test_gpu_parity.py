@@ -43,10 +43,23 @@ def bitwise_equal(a, b):
     return bool(np.all(same | (np.isnan(fa) & np.isnan(fb))))
 
 
+# "fused1" / "fused2": a fused plan forced to its one-kernel / two-kernel
+# form; "fused" leaves the form to the plan.
+PASSES = {"fused1": 1, "fused2": 2}
+
+
+def make_plan(w, mode, op=None):
+    plan = ddl.Plan(w.P, w.n, w.dtype, op or w.op, ddl_topo(w), w.bucket_list(),
+                    "fused" if mode in PASSES else mode)
+    if mode in PASSES:
+        plan.set_fused_passes(PASSES[mode])
+    return plan
+
+
 def run_ddl(bufs, w, mode, op=None, plan_api=True, events=None, stream=None):
     t = ddl_topo(w)
-    if plan_api:
-        plan = ddl.Plan(w.P, w.n, w.dtype, op or w.op, t, w.bucket_list(), mode)
+    if plan_api or mode in PASSES:
+        plan = make_plan(w, mode, op)
         plan.execute(bufs, events=events, stream=stream)
         torch.cuda.synchronize()
         plan.destroy()
@@ -89,7 +102,7 @@ def small_cases():
 
 
 @pytest.mark.parametrize("w", small_cases(), ids=lambda w: w.name)
-@pytest.mark.parametrize("mode", ["fused", "stepwise"])
+@pytest.mark.parametrize("mode", ["fused1", "fused2", "stepwise"])
 @pytest.mark.parametrize("op", ["sum", "mean"])
 def test_small_bitwise(w, mode, op):
     say(f"case {w.name} mode={mode} op={op}")
@@ -115,7 +128,7 @@ def test_subnormals_and_specials(dtype):
     g[2][9] = np.nan
     g[0][11], g[3][11] = np.inf, -np.inf
     w = Workload("sub", P, n, dtype, "mean", "ring")
-    for mode in ("fused", "stepwise"):
+    for mode in ("fused1", "fused2", "stepwise"):
         for op in ("sum", "mean"):
             ref = [x.copy() for x in g]
             oracle_full(w, ref, op=op)
@@ -183,7 +196,7 @@ def test_workload_full_bitwise(name):
     g = host_inputs(w)
     ref = [x.copy() for x in g]
     oracle_full(w, ref)
-    for mode in ("fused", "stepwise"):
+    for mode in ("fused", "fused1", "fused2", "stepwise"):
         say(f"case workload {name} mode={mode}")
         bufs = to_device(g)
         run_ddl(bufs, w, mode, plan_api=False)
@@ -232,6 +245,19 @@ def test_workload_full_size_sampled(name):
     plan.execute(copy, events=events, stream=stream)
     torch.cuda.synchronize()
     iv = torch.int32
+    assert all(torch.equal(a.view(iv), b.view(iv)) for a, b in zip(bufs, copy))
+    plan.destroy()
+    # the fused pass's other form, on fresh inputs: bit-identical as well
+    plan = ddl.Plan(w.P, w.n, w.dtype, w.op, ddl_topo(w), w.bucket_list(), "fused")
+    other = 3 - plan.fused_passes()
+    say(f"case workload {name}: fused, {other} kernel(s)")
+    plan.set_fused_passes(other)
+    for r, b in enumerate(copy):
+        synth.fill_device(b.data_ptr(), w.n, synth_dtype(w.dtype), w.dist, w.seed, r,
+                          sigma=w.sigma)
+    torch.cuda.synchronize()
+    plan.execute(copy, events=events, stream=stream)
+    torch.cuda.synchronize()
     assert all(torch.equal(a.view(iv), b.view(iv)) for a, b in zip(bufs, copy))
     plan.destroy()
     del bufs, copy
@@ -292,14 +318,21 @@ def test_profiling_counts_launches():
     say("case profiling")
     w = WORKLOADS["multiring_k4_p16_resnet50"]
     bufs = [torch.ones(w.n, device="cuda") for _ in range(w.P)]
-    for mode, launches in (("fused", 1), ("stepwise", 30)):
-        plan = ddl.Plan(w.P, w.n, w.dtype, "sum", ddl_topo(w), w.bucket_list(), mode)
+    for mode, launches in (("fused1", {"fused": 1}),
+                           ("fused2", {"fused_reduce": 1, "broadcast": 1}),
+                           ("stepwise", {"reduce": 15, "gather": 15})):
+        plan = make_plan(w, mode, "sum")
         plan.set_profiling(True)
         plan.execute(bufs)
         plan.execute(bufs)
         total, cnt, mx = plan.profile_read()
-        assert cnt == 2 * launches, (mode, cnt)
+        assert cnt == 2 * sum(launches.values()), (mode, cnt)
         assert total > 0 and mx <= total
+        plan.execute(bufs)
+        kinds = plan.profile_read_kinds()
+        for k, (tot, c, m) in kinds.items():
+            assert c == launches.get(k, 0), (mode, k, c)
+            assert (tot > 0) == (c > 0) and m <= tot + 1e-12
         plan.destroy()
 
 
@@ -341,8 +374,13 @@ def test_coalesce_threshold_merges_event_gated_buckets():
             plan.set_coalesce_bytes(thr)
             plan.set_profiling(True)
             plan.execute(bufs, events=events, stream=stream)
-            _, launches, _ = plan.profile_read()
-            counts[(mode, thr)] = launches
+            kinds = plan.profile_read_kinds()
+            # launches that start a group's work: the fused pass's first
+            # kernel, or every step
+            counts[(mode, thr)] = sum(kinds[k][1] for k in ("fused", "fused_reduce", "reduce",
+                                                              "gather"))
+            if mode == "fused":
+                assert kinds["broadcast"][1] in (0, counts[(mode, thr)])
             out = to_host(bufs)
             plan.destroy()
             for r in (0, 7, 15):
@@ -352,10 +390,11 @@ def test_coalesce_threshold_merges_event_gated_buckets():
     assert counts[("stepwise", 16 << 20)] == 30 * counts[("fused", 16 << 20)]
 
 
-def test_caller_stream_waits_for_side_stream_work():
+@pytest.mark.parametrize("mode", ["stepwise", "fused2"])
+def test_caller_stream_waits_for_side_stream_work(mode):
     """Work enqueued on the caller's stream right after an event-gated
     all-reduce sees its result without any host synchronisation."""
-    say("case caller stream ordering")
+    say(f"case caller stream ordering {mode}")
     w = Workload("order", 8, 1 << 22, "f32", "mean", "ring", dist="normal", sigma=1e-2,
                  seed=12, buckets=[(i << 18, 1 << 18) for i in reversed(range(16))])
     g = host_inputs(w)
@@ -367,7 +406,7 @@ def test_caller_stream_waits_for_side_stream_work():
     events = [torch.cuda.Event() for _ in w.bucket_list()]
     for e in events:
         e.record(stream)
-    plan = ddl.Plan(w.P, w.n, w.dtype, w.op, ddl_topo(w), w.bucket_list(), "stepwise")
+    plan = make_plan(w, mode)
     plan.execute(bufs, events=events, stream=stream)
     snap = bufs[3].clone()          # enqueued on the caller stream, no host sync
     torch.cuda.synchronize()
@@ -403,7 +442,7 @@ def test_max_ranks(dtype):
         g = host_inputs(w)
         ref = [x.copy() for x in g]
         oracle_full(w, ref)
-        for mode in ("fused", "stepwise"):
+        for mode in ("fused1", "fused2", "stepwise"):
             bufs = to_device(g)
             run_ddl(bufs, w, mode)
             out = to_host(bufs)
@@ -421,10 +460,12 @@ def test_custom_ring_orders():
         ref = [x.copy() for x in g]
         kind = "ring" if k == 1 else "multiring"
         orc.allreduce(ref, op=orc.MEAN, kind=KINDS[kind], k=k, ring_order=order)
-        for mode in ("fused", "stepwise"):
+        for mode in ("fused1", "fused2", "stepwise"):
             bufs = to_device(g)
             plan = ddl.Plan(P, n, dtype, "mean", ddl.topo(kind, k, ring_order=order), None,
-                            mode)
+                            "fused" if mode in PASSES else mode)
+            if mode in PASSES:
+                plan.set_fused_passes(PASSES[mode])
             plan.execute(bufs)
             out = to_host(bufs)
             plan.destroy()
@@ -432,7 +473,7 @@ def test_custom_ring_orders():
                 assert bitwise_equal(out[r], ref[r]), (P, k, mode, r)
 
 
-@pytest.mark.parametrize("mode", ["fused", "stepwise"])
+@pytest.mark.parametrize("mode", ["fused1", "fused2", "stepwise"])
 def test_hip_graph_capture_and_replay(mode):
     """An execution captured into a HIP graph (after one eager call has bound
     the plan) replays to the oracle's result, replay after replay, with the
@@ -445,7 +486,7 @@ def test_hip_graph_capture_and_replay(mode):
     oracle_full(w, ref)
     src = to_device(g)
     bufs = [t.clone() for t in src]
-    plan = ddl.Plan(w.P, w.n, w.dtype, w.op, ddl_topo(w), w.bucket_list(), mode)
+    plan = make_plan(w, mode)
     plan.execute(bufs, stream=torch.cuda.current_stream())   # binds the plan
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
@@ -498,12 +539,12 @@ def test_several_side_streams(nside):
     ref = [x.copy() for x in g]
     oracle_full(w, ref)
     stream = torch.cuda.current_stream()
-    for mode in ("fused", "stepwise"):
+    for mode in ("fused1", "fused2", "stepwise"):
         bufs = to_device(g)
         events = [torch.cuda.Event() for _ in w.bucket_list()]
         for e in events:
             e.record(stream)
-        plan = ddl.Plan(w.P, w.n, w.dtype, w.op, ddl_topo(w), w.bucket_list(), mode)
+        plan = make_plan(w, mode)
         plan.set_side_streams(nside)
         plan.execute(bufs, events=events, stream=stream)
         snap = bufs[2].clone()       # on the caller stream, no host sync

@@ -56,6 +56,8 @@ def test_sgd_bitwise(w, mode, keep, shared):
     bufs = [torch.from_numpy(x).cuda() for x in g]
     weights = [torch.from_numpy(x).cuda() for x in w0]
     plan = ddl.Plan(w.P, w.n, w.dtype, w.op, ddl_topo(w), w.bucket_list(), mode)
+    if mode == "fused":
+        plan.set_fused_passes(2)   # ignored by the SGD variant (one kernel)
     plan.execute_sgd(bufs, weights, lr, keep_grads=keep)
     torch.cuda.synchronize()
     plan.destroy()

@@ -225,6 +225,45 @@ def test_plan_create_needs_no_gpu():
     plan.destroy()
 
 
+def test_fused_pass_form_setting():
+    # host-only: the automatic form is two kernels when P x vectors per lane
+    # (1 for f32, 2 for f16) reaches 32 (fused plans only); explicit 1 and 2
+    # stick; anything else is rejected
+    for P, dt, mode, want in ((8, "f32", "fused", 1), (16, "f32", "fused", 1),
+                              (31, "f32", "fused", 1), (32, "f32", "fused", 2),
+                              (40, "f32", "fused", 2), (15, "f16", "fused", 1),
+                              (16, "f16", "fused", 2), (1, "f32", "fused", 1),
+                              (40, "f32", "stepwise", 0)):
+        plan = ddl.Plan(P, 4096, dt, "mean", ddl.topo("ring"), None, mode)
+        assert plan.fused_passes() == want, (P, dt, mode)
+        if mode == "fused" and P > 1:
+            for v in (1, 2):
+                plan.set_fused_passes(v)
+                assert plan.fused_passes() == v
+            plan.set_fused_passes(0)
+            assert plan.fused_passes() == want
+        for bad in (-1, 3):
+            with pytest.raises(ddl.DDLError):
+                plan.set_fused_passes(bad)
+        plan.destroy()
+
+
+def test_tuning_knobs():
+    defaults = {"bcast_ranks": 0, "reduce_nt_load": 1, "fused_nt_load_max_p": 24, "anchor": 0}
+    for k, v in defaults.items():
+        assert ddl.get_tuning(k) == v, k
+    for k in defaults:
+        ddl.set_tuning(k, 5)
+        assert ddl.get_tuning(k) == 5
+        ddl.set_tuning(k, -1)
+        assert ddl.get_tuning(k) == defaults[k]
+    for bad in (-1, 4):
+        with pytest.raises(ddl.DDLError):
+            ddl.set_tuning(bad, 1)
+        with pytest.raises(ddl.DDLError):
+            ddl.get_tuning(bad)
+
+
 def test_sgd_argument_validation_before_any_gpu_call():
     import ctypes
     P = 4
