@@ -33,10 +33,11 @@ def log(*a):
 
 
 def kernel_source_hash():
-    """Hash of the fused kernel's sources: counter figures taken on another
-    version of the kernel are not reported."""
+    """Hash of the fused pass's sources (kernels, launch configuration, tile
+    tables): counter figures taken on another version are not reported."""
     h = hashlib.sha256()
-    for name in ("fused_kernel.hip", "device_common.h", "ddl_internal.h"):
+    for name in ("fused_kernel.hip", "device_common.h", "ddl_internal.h", "plan.cpp",
+                 "schedule.cpp"):
         with open(os.path.join(ROOT, "sgd_gradient_all_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -222,7 +222,12 @@ typedef enum {
     /* tile anchoring of the plans created afterwards: 0 = automatic (tables
      * whose ranges average at least 2 tiles), 1 = never, 2 = always */
     DDL_TUNE_ANCHOR = 3,
-    DDL_TUNE_COUNT = 4
+    /* loads each lane issues ahead of their adds (1, 2, 4 or 8; other values
+     * act as 1) in the one-kernel pass (default 1) and in the reduce kernel
+     * (default 4); the adds keep the schedule's order */
+    DDL_TUNE_FUSED_BATCH = 4,
+    DDL_TUNE_REDUCE_BATCH = 5,
+    DDL_TUNE_COUNT = 6
 } ddl_tune_knob;
 int ddl_set_tuning(int knob, int value);
 int ddl_get_tuning(int knob, int *value);

@@ -163,7 +163,8 @@ def ddl_cache_clear():
     _check(lib().ddl_cache_clear(), "ddl_cache_clear")
 
 
-TUNE = {"bcast_ranks": 0, "reduce_nt_load": 1, "fused_nt_load_max_p": 2, "anchor": 3}
+TUNE = {"bcast_ranks": 0, "reduce_nt_load": 1, "fused_nt_load_max_p": 2, "anchor": 3,
+        "fused_batch": 4, "reduce_batch": 5}
 
 
 def set_tuning(knob, value):

@@ -31,13 +31,13 @@ using namespace dev;
 #ifndef DDL_NT_STORE
 #define DDL_NT_STORE 1
 #endif
-// Loads a lane issues ahead of their adds.  Measured on MI355X, one is best
-// or within 1% of best: the many-stream pass saturates HBM, and more
-// requests in flight per wave only lengthen the queues (8 costs up to 5%).
-#ifndef DDL_LOAD_BATCH
-#define DDL_LOAD_BATCH 1
-#endif
-constexpr int kBatch = DDL_LOAD_BATCH;
+// Loads a lane issues ahead of their adds (kB, 1, 2, 4 or 8; knobs
+// DDL_TUNE_FUSED_BATCH and DDL_TUNE_REDUCE_BATCH).  The adds stay in chain
+// order; a batch only lets a wave keep kB requests in flight instead of
+// waiting for each load before issuing the next.  Measured on MI355X: the
+// read-only reduce kernel gains from 4 (+4.6% at 40 ranks, +2% at 16); the
+// one-kernel pass, whose writes share HBM with the reads, is best with 1
+// at 8 ranks (2: -1%, 4: -3.5%).
 // Waves per SIMD the register allocation must allow: 8 for one vector per
 // lane (no spills at 56 VGPRs), 4 for two.
 #ifndef DDL_FUSED_WAVES_1
@@ -101,32 +101,32 @@ struct Chain {
 };
 
 // Sums of U element vectors -- e + u * kBlock * N, u < U -- over the chain.
-// The ranks go in batches of kBatch from the first one; every load of a
+// The ranks go in batches of kB from the first one; every load of a
 // batch is issued before the batch's adds.  In a partial last batch the
 // missing slots
 // re-load the batch's last rank (a line already in flight) and their adds
 // are skipped, which keeps every load unconditional.  Ungrouped (rings): one
 // chain of P entries.  Grouped (torus): chains of `group` entries, then
 // their sums.
-template <class E, bool kGrouped, bool kNt, int U>
+template <class E, bool kGrouped, bool kNt, int U, int kB>
 __device__ __forceinline__ void fused_vecs(const uint64_t *sp, int P, int group,
                                            uint64_t e, typename E::V (&out)[U]) {
     using V = typename E::V;
     constexpr uint64_t kStride = (uint64_t)kBlock * E::N;
     Chain<E> c[U];
     V acc[U];
-    for (int b = 0; b < P; b += kBatch) {
-        const int nb = min(kBatch, P - b);
-        V x[kBatch][U];
+    for (int b = 0; b < P; b += kB) {
+        const int nb = min(kB, P - b);
+        V x[kB][U];
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
+        for (int j = 0; j < kB; ++j) {
             const uint64_t p = sp[b + (j < nb ? j : nb - 1)] + e * sizeof(typename E::T);
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 x[j][u] = ld_global<V, kNt>(p + u * kStride * sizeof(typename E::T));
         }
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j)
+        for (int j = 0; j < kB; ++j)
             if (j < nb)
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
@@ -184,7 +184,7 @@ __device__ __forceinline__ void store_home(const RankPtrs &bufs, uint64_t e,
 
 // kHome: write the result to rank 0 only (the first kernel of the two-kernel
 // form); otherwise to every rank.
-template <class E, bool kGrouped, bool kNt, bool kSgd, bool kHome>
+template <class E, bool kGrouped, bool kNt, bool kSgd, bool kHome, int kB>
 __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs &a,
                                            const SgdArgs *g) {
     using T = typename E::T;
@@ -219,7 +219,7 @@ __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs
             if (nvec == (uint32_t)(U * kBlock)) {
                 const uint64_t e = base + (uint64_t)tid * E::N;
                 V acc[U];
-                fused_vecs<E, kGrouped, kNt, U>(src, P, a.group, e, acc);
+                fused_vecs<E, kGrouped, kNt, U, kB>(src, P, a.group, e, acc);
                 if (a.mean)
 #pragma unroll
                     for (int u = 0; u < U; ++u)
@@ -234,7 +234,7 @@ __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs
                 for (uint32_t v = tid; v < nvec; v += kBlock) {
                     const uint64_t e = base + (uint64_t)v * E::N;
                     V acc[1];
-                    fused_vecs<E, kGrouped, kNt, 1>(src, P, a.group, e, acc);
+                    fused_vecs<E, kGrouped, kNt, 1, kB>(src, P, a.group, e, acc);
                     if (a.mean)
                         acc[0] = E::div(acc[0], a.divisor);
                     if (kHome)
@@ -282,22 +282,22 @@ __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs
                                            ? DDL_FUSED_WAVES_1                        \
                                            : DDL_FUSED_WAVES_2)))
 
-template <class E, bool kGrouped, bool kNt>
+template <class E, bool kGrouped, bool kNt, int kB>
 __global__ __launch_bounds__(kBlock) DDL_FUSED_OCCUPANCY
 void fused_kernel(RankPtrs bufs, FusedArgs a) {
-    fused_body<E, kGrouped, kNt, false, false>(bufs, a, nullptr);
+    fused_body<E, kGrouped, kNt, false, false, kB>(bufs, a, nullptr);
 }
 
 template <class E, bool kGrouped, bool kNt>
 __global__ __launch_bounds__(kBlock) DDL_FUSED_OCCUPANCY
 void fused_sgd_kernel(RankPtrs bufs, FusedArgs a, SgdArgs g) {
-    fused_body<E, kGrouped, kNt, true, false>(bufs, a, &g);
+    fused_body<E, kGrouped, kNt, true, false, 1>(bufs, a, &g);
 }
 
-template <class E, bool kGrouped, bool kNt>
+template <class E, bool kGrouped, bool kNt, int kB>
 __global__ __launch_bounds__(kBlock) DDL_FUSED_OCCUPANCY
 void fused_reduce_kernel(RankPtrs bufs, FusedArgs a) {
-    fused_body<E, kGrouped, kNt, false, true>(bufs, a, nullptr);
+    fused_body<E, kGrouped, kNt, false, true, kB>(bufs, a, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -362,6 +362,29 @@ __global__ __launch_bounds__(kBlock) void bcast_kernel(RankPtrs bufs, BcastArgs 
 
 namespace {
 
+// One-kernel pass (home false) or reduce kernel (home true) with kB loads
+// per batch.
+template <class E, bool kGrouped, bool kNt, int kB>
+void launch_b(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a, bool home) {
+    const dim3 block(kBlock);
+    if (home)
+        hipLaunchKernelGGL((fused_reduce_kernel<E, kGrouped, kNt, kB>), grid, block, 0, s, bufs,
+                           a);
+    else
+        hipLaunchKernelGGL((fused_kernel<E, kGrouped, kNt, kB>), grid, block, 0, s, bufs, a);
+}
+
+template <class E, bool kGrouped, bool kNt>
+void launch_nt(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a, bool home,
+               int batch) {
+    switch (batch) {
+    case 2: launch_b<E, kGrouped, kNt, 2>(grid, s, bufs, a, home); break;
+    case 4: launch_b<E, kGrouped, kNt, 4>(grid, s, bufs, a, home); break;
+    case 8: launch_b<E, kGrouped, kNt, 8>(grid, s, bufs, a, home); break;
+    default: launch_b<E, kGrouped, kNt, 1>(grid, s, bufs, a, home); break;
+    }
+}
+
 template <class E, bool kGrouped>
 void launch_e(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a,
               const SgdArgs *sgd, bool home) {
@@ -371,12 +394,11 @@ void launch_e(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a
         // P: the P input streams must not evict the results the broadcast
         // kernel re-reads (measured on MI355X, 40 ranks: 6031 GB/s against
         // 5242 with cached loads)
+        const int batch = tuning(DDL_TUNE_REDUCE_BATCH);
         if (tuning(DDL_TUNE_REDUCE_NT_LOAD) != 0)
-            hipLaunchKernelGGL((fused_reduce_kernel<E, kGrouped, true>), grid, block, 0, s, bufs,
-                               a);
+            launch_nt<E, kGrouped, true>(grid, s, bufs, a, true, batch);
         else
-            hipLaunchKernelGGL((fused_reduce_kernel<E, kGrouped, false>), grid, block, 0, s,
-                               bufs, a);
+            launch_nt<E, kGrouped, false>(grid, s, bufs, a, true, batch);
         return;
     }
     const bool nt = a.P * fused_vecs_per_lane(sizeof(typename E::T)) <=
@@ -388,11 +410,13 @@ void launch_e(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a
         else
             hipLaunchKernelGGL((fused_sgd_kernel<E, kGrouped, false>), grid, block, 0, s, bufs,
                                a, *sgd);
-    } else if (nt) {
-        hipLaunchKernelGGL((fused_kernel<E, kGrouped, true>), grid, block, 0, s, bufs, a);
-    } else {
-        hipLaunchKernelGGL((fused_kernel<E, kGrouped, false>), grid, block, 0, s, bufs, a);
+        return;
     }
+    const int batch = tuning(DDL_TUNE_FUSED_BATCH);
+    if (nt)
+        launch_nt<E, kGrouped, true>(grid, s, bufs, a, false, batch);
+    else
+        launch_nt<E, kGrouped, false>(grid, s, bufs, a, false, batch);
 }
 
 }  // namespace

@@ -27,12 +27,14 @@ using namespace ddl;
 constexpr int kMaxSideStreams = 4;
 
 // process-wide tuning knobs (ddl_set_tuning); -1 = default
-std::atomic<int> g_tune[DDL_TUNE_COUNT] = {-1, -1, -1, -1};
+std::atomic<int> g_tune[DDL_TUNE_COUNT] = {-1, -1, -1, -1, -1, -1};
 constexpr int kTuneDefault[DDL_TUNE_COUNT] = {
     0,   // DDL_TUNE_BCAST_RANKS: automatic
     1,   // DDL_TUNE_REDUCE_NT_LOAD: on
     24,  // DDL_TUNE_FUSED_NT_LOAD_MAX_P
     0,   // DDL_TUNE_ANCHOR: automatic
+    1,   // DDL_TUNE_FUSED_BATCH
+    4,   // DDL_TUNE_REDUCE_BATCH
 };
 
 namespace ddl {
