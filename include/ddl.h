@@ -185,9 +185,11 @@ const char *ddl_strerror(int code);
  * for all their events before it starts.  Default 0. */
 int ddl_plan_set_coalesce_bytes(ddl_plan plan, size_t bytes);
 
-/* Event-gated groups alternate over n side streams (1..4, default 1) in
- * list order.  Buckets are independent all-reduces, so a group's kernel may
- * start while the previous one drains; the results do not change. */
+/* Event-gated groups alternate over n side streams (1..4) in list order.
+ * Buckets are independent all-reduces, so a group's kernels may run while
+ * the previous group's drain; the results do not change.  n = 0 (default):
+ * automatic, 2 for stepwise plans and for fused plans whose buckets average
+ * under 4 MB per rank (short launches whose ramps overlap), else 1. */
 int ddl_plan_set_side_streams(ddl_plan plan, int n);
 
 /* Form of a fused plan's pass (fused mode only; the SGD variant always uses
