@@ -288,10 +288,10 @@ void fused_kernel(RankPtrs bufs, FusedArgs a) {
     fused_body<E, kGrouped, kNt, false, false, kB>(bufs, a, nullptr);
 }
 
-template <class E, bool kGrouped, bool kNt>
+template <class E, bool kGrouped, bool kNt, int kB>
 __global__ __launch_bounds__(kBlock) DDL_FUSED_OCCUPANCY
 void fused_sgd_kernel(RankPtrs bufs, FusedArgs a, SgdArgs g) {
-    fused_body<E, kGrouped, kNt, true, false, 1>(bufs, a, &g);
+    fused_body<E, kGrouped, kNt, true, false, kB>(bufs, a, &g);
 }
 
 template <class E, bool kGrouped, bool kNt, int kB>
@@ -362,33 +362,36 @@ __global__ __launch_bounds__(kBlock) void bcast_kernel(RankPtrs bufs, BcastArgs 
 
 namespace {
 
-// One-kernel pass (home false) or reduce kernel (home true) with kB loads
-// per batch.
+// One-kernel pass (home false; with the SGD step when sgd is set) or reduce
+// kernel (home true) with kB loads per batch.
 template <class E, bool kGrouped, bool kNt, int kB>
-void launch_b(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a, bool home) {
+void launch_b(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a,
+              const SgdArgs *sgd, bool home) {
     const dim3 block(kBlock);
     if (home)
         hipLaunchKernelGGL((fused_reduce_kernel<E, kGrouped, kNt, kB>), grid, block, 0, s, bufs,
                            a);
+    else if (sgd)
+        hipLaunchKernelGGL((fused_sgd_kernel<E, kGrouped, kNt, kB>), grid, block, 0, s, bufs, a,
+                           *sgd);
     else
         hipLaunchKernelGGL((fused_kernel<E, kGrouped, kNt, kB>), grid, block, 0, s, bufs, a);
 }
 
 template <class E, bool kGrouped, bool kNt>
-void launch_nt(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a, bool home,
-               int batch) {
+void launch_nt(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a,
+               const SgdArgs *sgd, bool home, int batch) {
     switch (batch) {
-    case 2: launch_b<E, kGrouped, kNt, 2>(grid, s, bufs, a, home); break;
-    case 4: launch_b<E, kGrouped, kNt, 4>(grid, s, bufs, a, home); break;
-    case 8: launch_b<E, kGrouped, kNt, 8>(grid, s, bufs, a, home); break;
-    default: launch_b<E, kGrouped, kNt, 1>(grid, s, bufs, a, home); break;
+    case 2: launch_b<E, kGrouped, kNt, 2>(grid, s, bufs, a, sgd, home); break;
+    case 4: launch_b<E, kGrouped, kNt, 4>(grid, s, bufs, a, sgd, home); break;
+    case 8: launch_b<E, kGrouped, kNt, 8>(grid, s, bufs, a, sgd, home); break;
+    default: launch_b<E, kGrouped, kNt, 1>(grid, s, bufs, a, sgd, home); break;
     }
 }
 
 template <class E, bool kGrouped>
 void launch_e(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a,
               const SgdArgs *sgd, bool home) {
-    const dim3 block(kBlock);
     if (home) {
         // the reduce kernel reads the ranks with non-temporal loads whatever
         // P: the P input streams must not evict the results the broadcast
@@ -396,27 +399,18 @@ void launch_e(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a
         // 5242 with cached loads)
         const int batch = tuning(DDL_TUNE_REDUCE_BATCH);
         if (tuning(DDL_TUNE_REDUCE_NT_LOAD) != 0)
-            launch_nt<E, kGrouped, true>(grid, s, bufs, a, true, batch);
+            launch_nt<E, kGrouped, true>(grid, s, bufs, a, nullptr, true, batch);
         else
-            launch_nt<E, kGrouped, false>(grid, s, bufs, a, true, batch);
+            launch_nt<E, kGrouped, false>(grid, s, bufs, a, nullptr, true, batch);
         return;
     }
     const bool nt = a.P * fused_vecs_per_lane(sizeof(typename E::T)) <=
                     tuning(DDL_TUNE_FUSED_NT_LOAD_MAX_P);
-    if (sgd) {
-        if (nt)
-            hipLaunchKernelGGL((fused_sgd_kernel<E, kGrouped, true>), grid, block, 0, s, bufs, a,
-                               *sgd);
-        else
-            hipLaunchKernelGGL((fused_sgd_kernel<E, kGrouped, false>), grid, block, 0, s, bufs,
-                               a, *sgd);
-        return;
-    }
     const int batch = tuning(DDL_TUNE_FUSED_BATCH);
     if (nt)
-        launch_nt<E, kGrouped, true>(grid, s, bufs, a, false, batch);
+        launch_nt<E, kGrouped, true>(grid, s, bufs, a, sgd, false, batch);
     else
-        launch_nt<E, kGrouped, false>(grid, s, bufs, a, false, batch);
+        launch_nt<E, kGrouped, false>(grid, s, bufs, a, sgd, false, batch);
 }
 
 }  // namespace

@@ -78,3 +78,29 @@ def test_knob_setting_is_bitwise(knob, value, expected):
         torch.cuda.synchronize()
         plan.destroy()
         assert all(bufs[r].cpu().numpy().tobytes() == ref[r].tobytes() for r in (0, w.P - 1))
+
+
+@pytest.mark.parametrize("batch", [2, 4, 8])
+def test_sgd_load_batch_is_bitwise(batch):
+    """The SGD variant of the one-kernel pass under every load batch."""
+    import oracle as orc
+    from _helpers import oracle_full
+    ddl.set_tuning("fused_batch", batch)
+    for w in CASES:
+        say(f"case tuning sgd fused_batch={batch} {w.name}")
+        g = host_inputs(w)
+        y = [x.copy() for x in g]
+        oracle_full(w, y)
+        rng = np.random.default_rng(w.seed)
+        w0 = [rng.standard_normal(w.n).astype(np.float32) for _ in range(w.P)]
+        want = [x.copy() for x in w0]
+        orc.sgd(want, y[0], 0.03)
+        bufs = [torch.from_numpy(x).cuda() for x in g]
+        weights = [torch.from_numpy(x).cuda() for x in w0]
+        plan = ddl.Plan(w.P, w.n, w.dtype, w.op, ddl_topo(w), w.bucket_list(), "fused")
+        plan.execute_sgd(bufs, weights, 0.03, keep_grads=True)
+        torch.cuda.synchronize()
+        plan.destroy()
+        for r in (0, w.P - 1):
+            assert weights[r].cpu().numpy().tobytes() == want[r].tobytes(), (batch, w.name, r)
+            assert bufs[r].cpu().numpy().tobytes() == y[r].tobytes(), (batch, w.name, r)
