@@ -88,8 +88,27 @@ __device__ __forceinline__ void stv(void *p, V v) {
 }
 // Largest i in [lo, hi) with prefix[i] <= tile (prefix is non-decreasing,
 // prefix[lo] <= tile < prefix[hi]).  Uniform across the workgroup.
+//
+// The items of a step are near-equal chunks, so the first probe is the
+// item a uniform spread of the tiles would give; it is checked with two
+// independent loads and, when it misses (skewed tables: buckets of very
+// different sizes in one group), bounds a binary search.  Two rounds of
+// loads instead of log2(items) dependent ones: a step's workgroups are
+// short-lived, and the search is on their critical path.
 __device__ __forceinline__ uint32_t find_item(const uint32_t *__restrict__ prefix,
                                               uint32_t lo, uint32_t hi, uint32_t tile) {
+    if (hi - lo > 1) {
+        const uint32_t t0 = prefix[lo], t1 = prefix[hi];
+        const uint32_t g =
+            lo + (uint32_t)((uint64_t)(tile - t0) * (uint64_t)(hi - lo) / (uint64_t)(t1 - t0));
+        const uint32_t a = prefix[g], b = prefix[g + 1];
+        if (a <= tile && tile < b)
+            return g;
+        if (a > tile)
+            hi = g;
+        else
+            lo = g + 1;
+    }
     while (hi - lo > 1) {
         uint32_t mid = lo + ((hi - lo) >> 1);
         if (prefix[mid] <= tile)
