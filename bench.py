@@ -363,7 +363,44 @@ def extras(args, w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_b
         log(f"bench: overlap {out['overlap']}")
 
     out["sgd"] = sgd_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_ms)
+    out["typed"] = typed_leg(main_stream, torch, ddl, synth)
     return out
+
+
+def typed_leg(main_stream, torch, ddl, synth):
+    """Buckets of their own element type: the mixed-precision ResNet-50
+    gradient (binary16 weights, binary32 BatchNorm and bias tensors) over 16
+    ranks and 4 rings, fused and stepwise."""
+    from synth.workloads import resnet50_mixed_typed_buckets
+    segs, nbytes = resnet50_mixed_typed_buckets()
+    P = 16
+    tb = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(P)]
+    for r, t in enumerate(tb):
+        for b, (off, cnt, dt) in enumerate(segs):
+            synth.fill_device(t.data_ptr() + off, cnt, synth.F32 if dt == "f32" else synth.F16,
+                              "normal", 40 + b, r, sigma=1e-2)
+    torch.cuda.synchronize()
+    res = {"ranks": P, "topology": "4 rings", "buckets": len(segs), "bytes_per_rank": nbytes}
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for mode in ("fused", "stepwise"):
+        plan = ddl.Plan.typed(P, nbytes, "mean", ddl.topo("multiring", 4), segs, mode)
+        _, hbm = plan.traffic()
+        plan.execute(tb, stream=main_stream)
+        torch.cuda.synchronize()
+        reps = 20
+        t0.record(main_stream)
+        for _ in range(reps):
+            plan.execute(tb, stream=main_stream)
+        t1.record(main_stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / reps
+        res[mode] = {"ms": round(ms, 4), "hbm_GBps": round(hbm / (ms * 1e-3) / 1e9, 1),
+                     "bytes": hbm}
+        plan.destroy()
+    del tb
+    torch.cuda.empty_cache()
+    log(f"bench: typed {res}")
+    return res
 
 
 def sgd_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_ms):

@@ -111,6 +111,35 @@ int ddl_plan_create(ddl_plan *out, int P, size_t n, ddl_dtype dtype, ddl_op op,
                     const ddl_topo *topo, const ddl_bucket *buckets, int nbuckets,
                     ddl_mode mode);
 
+/* A bucket with its own element type, for plans whose buckets do not all
+ * share one (some gradients exchanged in binary16, as the Sony ResNet-50
+ * article does, others in binary32).  Bucket b covers bytes
+ * [byte_offset, byte_offset + count * size(dtype)) of every rank's buffer. */
+typedef struct {
+    size_t byte_offset;    /* a multiple of the element size */
+    size_t count;          /* elements of dtype (0 allowed) */
+    ddl_dtype dtype;
+} ddl_typed_bucket;
+
+/* Build a plan over P ranks of nbytes bytes each whose buckets carry their
+ * own element type.  Each bucket is all-reduced exactly as a plain plan of
+ * its dtype would all-reduce it (same chains, same rounding), so the result
+ * is bit-identical to one plain plan per dtype.  The buckets must tile
+ * [0, nbytes) in bytes without gap or overlap (DDL_E_BUCKETS), and each
+ * byte_offset must be a multiple of its element size (DDL_E_BUCKETS); list
+ * order is issue order.  Run it with ddl_plan_execute (ready_events, if
+ * given, one per typed bucket in list order); consecutive buckets with equal
+ * events form a group, as in plain plans, and a group runs one pass (or one
+ * step sequence) per dtype it holds.
+ * ddl_plan_execute_sgd returns DDL_E_ARG for such a plan (its weights are
+ * indexed by element, which typed buckets do not define), and
+ * ddl_plan_traffic's per-rank counts add up elements of both types.
+ * Introspection calls take typed bucket indices.  Host-only, like
+ * ddl_plan_create. */
+int ddl_plan_create_typed(ddl_plan *out, int P, size_t nbytes, ddl_op op,
+                          const ddl_topo *topo, const ddl_typed_bucket *buckets, int nbuckets,
+                          ddl_mode mode);
+
 /* Enqueue the all-reduce of bufs[0..P) (device pointers, each 16-byte
  * aligned, n elements) on the current HIP device.
  *  ready_events  NULL, or nbuckets hipEvent_t (entries may be NULL) in bucket

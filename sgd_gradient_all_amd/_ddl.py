@@ -30,6 +30,11 @@ class ddl_bucket(ctypes.Structure):
                 ("ready_event", ctypes.c_void_p)]
 
 
+class ddl_typed_bucket(ctypes.Structure):
+    _fields_ = [("byte_offset", ctypes.c_size_t), ("count", ctypes.c_size_t),
+                ("dtype", ctypes.c_int)]
+
+
 class ddl_step_item(ctypes.Structure):
     _fields_ = [("src", ctypes.c_int), ("dst", ctypes.c_int), ("divide", ctypes.c_int),
                 ("step", ctypes.c_int), ("offset", ctypes.c_size_t),
@@ -60,6 +65,8 @@ def lib():
         sig = {
             "ddl_plan_create": ([ctypes.POINTER(vp), i32, sz, i32, i32, P_topo, P_bucket,
                                  i32, i32], i32),
+            "ddl_plan_create_typed": ([ctypes.POINTER(vp), i32, sz, i32, P_topo,
+                                       ctypes.POINTER(ddl_typed_bucket), i32, i32], i32),
             "ddl_plan_execute": ([vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp], i32),
             "ddl_allreduce": ([ctypes.POINTER(vp), i32, sz, i32, i32, P_topo, P_bucket, i32,
                                i32, vp, vp], i32),
@@ -192,6 +199,24 @@ class Plan:
                                      _code(_OPS, op), ctypes.byref(t), barr, nb,
                                      _code(_MODES, mode)), "ddl_plan_create")
         self.handle = h
+
+    @classmethod
+    def typed(cls, P, nbytes, op="sum", topology=None, buckets=(), mode="fused"):
+        """A plan whose buckets carry their own dtype: buckets is a list of
+        (byte_offset, count, dtype) in issue order (ddl_plan_create_typed)."""
+        self = cls.__new__(cls)
+        self.P, self.n, self.nbuckets = P, nbytes, len(buckets)
+        self.handle = None
+        t = topology if topology is not None else topo()
+        arr = (ddl_typed_bucket * max(1, len(buckets)))()
+        for i, (off, cnt, dt) in enumerate(buckets):
+            arr[i].byte_offset, arr[i].count, arr[i].dtype = off, cnt, _code(_DTYPES, dt)
+        h = ctypes.c_void_p()
+        _check(lib().ddl_plan_create_typed(ctypes.byref(h), P, nbytes, _code(_OPS, op),
+                                           ctypes.byref(t), arr, len(buckets),
+                                           _code(_MODES, mode)), "ddl_plan_create_typed")
+        self.handle = h
+        return self
 
     def execute(self, bufs, events=None, stream=None, done_event=None):
         if len(bufs) != self.P:

@@ -125,13 +125,19 @@ struct FusedArgs {
 };
 
 // Arguments of one broadcast launch (second kernel of the two-kernel fused
-// form): elements [off, off + len) of rank 0 are copied to ranks 1..P-1,
-// ranks_per_group of them per workgroup, so each tile of fused_tile_elems
-// elements takes ngroups = ceil((P-1) / ranks_per_group) workgroups.  A
-// group's buckets are copied as the contiguous runs of memory they form, so
-// the kernel needs no tables.  aligned: off is a multiple of 16 bytes.
+// form): rank 0's values are copied to ranks 1..P-1, ranks_per_group of
+// them per workgroup, so each tile of fused_tile_elems elements takes
+// ngroups = ceil((P-1) / ranks_per_group) workgroups.  Two modes:
+//  - run (spans == nullptr): the elements [off, off + len), one contiguous
+//    run of memory; no table is read.  aligned: off is a multiple of 16 B.
+//  - table: the anchored tiles [tile_base, tile_end) of the bucket table
+//    spans / prefix / tile_span, for groups whose buckets are not one run.
 struct BcastArgs {
     uint64_t off, len;
+    const DevSpan *spans;
+    const uint32_t *prefix;
+    const uint32_t *tile_span;
+    uint32_t tile_base, tile_end;
     int P;
     int ranks_per_group;
     int ngroups;

@@ -302,10 +302,11 @@ void fused_reduce_kernel(RankPtrs bufs, FusedArgs a) {
 
 // ---------------------------------------------------------------------------
 // broadcast: the second kernel of the two-kernel form.  Workgroup b copies
-// anchored tile b / ngroups of the run [off, off + len) from rank 0 to ranks
-// 1 + g * ranks_per_group ... (at most P - 1), g = b % ngroups.  The copy is
-// of the bits: no arithmetic.  No table is read, so a workgroup's first
-// access is the load of the values it copies.
+// anchored tile b / ngroups -- of the run [off, off + len), or of the bucket
+// table -- from rank 0 to ranks 1 + g * ranks_per_group ... (at most P - 1),
+// g = b % ngroups.  The copy is of the bits: no arithmetic.  In run mode no
+// table is read, so a workgroup's first access is the load of the values
+// it copies.
 // ---------------------------------------------------------------------------
 template <class E>
 __global__ __launch_bounds__(kBlock) void bcast_kernel(RankPtrs bufs, BcastArgs a) {
@@ -316,19 +317,31 @@ __global__ __launch_bounds__(kBlock) void bcast_kernel(RankPtrs bufs, BcastArgs 
     constexpr uint64_t kStride = (uint64_t)kBlock * E::N;
     const uint32_t tid = threadIdx.x;
     const uint32_t ng = (uint32_t)a.ngroups;
-    const uint64_t j = blockIdx.x / ng;
     const int grp = (int)(blockIdx.x % ng);
-    const uint64_t sh = tile_shift(a.off, kTile, true);
-    if (j >= tile_count(a.len, sh, kTile))
+    uint64_t off = a.off, len = a.len, j = blockIdx.x / ng;
+    bool aligned = a.aligned != 0;
+    if (a.spans) {
+        const uint32_t tile = a.tile_base + (uint32_t)j;
+        if (tile >= a.tile_end)
+            return;
+        const uint32_t i = a.tile_span[tile];
+        const DevSpan sp = a.spans[i];
+        off = sp.off;
+        len = sp.len;
+        aligned = (sp.flags & kItemAligned) != 0;
+        j = tile - a.prefix[i];
+    }
+    const uint64_t sh = tile_shift(off, kTile, true);
+    if (j >= tile_count(len, sh, kTile))
         return;
-    const uint64_t base = tile_lo(a.off, sh, kTile, j);
-    const uint32_t cnt = (uint32_t)(tile_hi(a.off, a.len, sh, kTile, j) - base);
+    const uint64_t base = tile_lo(off, sh, kTile, j);
+    const uint32_t cnt = (uint32_t)(tile_hi(off, len, sh, kTile, j) - base);
     const int r0 = 1 + grp * a.ranks_per_group;
     const int r1 = min(a.P, r0 + a.ranks_per_group);
     const T DDL_GLOBAL *home =
         reinterpret_cast<const T DDL_GLOBAL *>(reinterpret_cast<uint64_t>(bufs.p[0]));
     uint32_t done = 0;
-    if (a.aligned) {
+    if (aligned) {
         const uint32_t nvec = cnt / E::N;
         if (nvec == (uint32_t)(U * kBlock)) {
             const uint64_t e = base + (uint64_t)tid * E::N;
@@ -437,8 +450,9 @@ int launch_fused(int dtype, const RankPtrs &bufs, const FusedArgs &a, const SgdA
 int launch_bcast(int dtype, const RankPtrs &bufs, const BcastArgs &a, void *stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     const uint64_t tile = fused_tile_elems(dtype == DDL_F32 ? 4 : 2);
-    const uint64_t blocks =
-        tile_count(a.len, tile_shift(a.off, tile, true), tile) * (uint64_t)a.ngroups;
+    const uint64_t tiles = a.spans ? (uint64_t)(a.tile_end - a.tile_base)
+                                   : tile_count(a.len, tile_shift(a.off, tile, true), tile);
+    const uint64_t blocks = tiles * (uint64_t)a.ngroups;
     if (a.ngroups < 1 || a.ranks_per_group < 1 || blocks * kBlock > 0xffffffffull)
         return (int)hipErrorInvalidValue;
     if (blocks == 0)

@@ -47,8 +47,28 @@ int tuning(int knob) {
 }  // namespace ddl
 constexpr int kLaunchKinds = DDL_K_COUNT;
 
-struct ddl_plan_s {
+// One element type's share of a plan: its schedule and the device copies of
+// the tables of the plan's mode.
+struct Part {
     Schedule s;
+    DevItem *d_items = nullptr;
+    uint32_t *d_prefix = nullptr;
+    std::vector<size_t> item_base, prefix_base;  // per step, into the above
+    DevSpan *d_spans = nullptr;
+    uint32_t *d_span_prefix = nullptr;
+    uint32_t *d_span_of_tile = nullptr;
+    uint8_t *d_chains = nullptr;
+    DevSpan *d_bk_spans = nullptr;
+    uint32_t *d_bk_prefix = nullptr;
+    uint32_t *d_bk_of_tile = nullptr;
+};
+
+struct ddl_plan_s {
+    // one part per element type (a plain plan has one); buckets are issued
+    // in list order, entry i naming (part, bucket within that part)
+    std::vector<Part> parts;
+    std::vector<std::pair<int, int>> order;
+    bool typed = false;     // created with typed buckets (byte offsets)
     int mode = DDL_FUSED;
     size_t coalesce_bytes = 0;
     int nside = 0;          // side streams event-gated groups alternate over (0 auto)
@@ -60,15 +80,6 @@ struct ddl_plan_s {
     hipEvent_t side_done[kMaxSideStreams] = {};
     hipEvent_t call_ev = nullptr, last_ev = nullptr;
     bool in_flight = false;
-
-    // device copies of the tables of the plan's mode
-    DevItem *d_items = nullptr;
-    uint32_t *d_prefix = nullptr;
-    std::vector<size_t> item_base, prefix_base;  // per step, into the above
-    DevSpan *d_spans = nullptr;
-    uint32_t *d_span_prefix = nullptr;
-    uint32_t *d_span_of_tile = nullptr;
-    uint8_t *d_chains = nullptr;
 
     // profiling
     bool profiling = false;
@@ -101,12 +112,18 @@ void release_device(ddl_plan p) {
     int cur = 0;
     (void)hipGetDevice(&cur);
     (void)hipSetDevice(p->device);
-    (void)hipFree(p->d_items);
-    (void)hipFree(p->d_prefix);
-    (void)hipFree(p->d_spans);
-    (void)hipFree(p->d_span_prefix);
-    (void)hipFree(p->d_span_of_tile);
-    (void)hipFree(p->d_chains);
+    for (Part &pt : p->parts) {
+        (void)hipFree(pt.d_items);
+        (void)hipFree(pt.d_prefix);
+        (void)hipFree(pt.d_spans);
+        (void)hipFree(pt.d_span_prefix);
+        (void)hipFree(pt.d_span_of_tile);
+        (void)hipFree(pt.d_chains);
+        (void)hipFree(pt.d_bk_spans);
+        (void)hipFree(pt.d_bk_prefix);
+        (void)hipFree(pt.d_bk_of_tile);
+        pt = Part{std::move(pt.s)};
+    }
     for (hipEvent_t e : p->prof)
         (void)hipEventDestroy(e);
     if (p->call_ev)
@@ -135,28 +152,35 @@ int bind_device(ddl_plan p, int dev) {
     if (hipEventCreateWithFlags(&p->call_ev, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&p->last_ev, hipEventDisableTiming) != hipSuccess)
         return DDL_E_HIP;
-    const Schedule &s = p->s;
-    int rc = DDL_OK;
-    if (p->mode == DDL_STEPWISE) {
-        std::vector<DevItem> items;
-        std::vector<uint32_t> prefix;
-        for (int st = 0; st < s.nsteps; ++st) {
-            p->item_base.push_back(items.size());
-            p->prefix_base.push_back(prefix.size());
-            items.insert(items.end(), s.items[st].begin(), s.items[st].end());
-            prefix.insert(prefix.end(), s.prefix[st].begin(), s.prefix[st].end());
+    for (Part &pt : p->parts) {
+        const Schedule &s = pt.s;
+        int rc = DDL_OK;
+        if (p->mode == DDL_STEPWISE) {
+            std::vector<DevItem> items;
+            std::vector<uint32_t> prefix;
+            for (int st = 0; st < s.nsteps; ++st) {
+                pt.item_base.push_back(items.size());
+                pt.prefix_base.push_back(prefix.size());
+                items.insert(items.end(), s.items[st].begin(), s.items[st].end());
+                prefix.insert(prefix.end(), s.prefix[st].begin(), s.prefix[st].end());
+            }
+            if ((rc = upload(&pt.d_items, items.data(), items.size())) ||
+                (rc = upload(&pt.d_prefix, prefix.data(), prefix.size())))
+                return rc;
         }
-        if ((rc = upload(&p->d_items, items.data(), items.size())) ||
-            (rc = upload(&p->d_prefix, prefix.data(), prefix.size())))
+        // the fused tables are small; stepwise plans keep them for the
+        // one-rank SGD step, which has no schedule step to ride on
+        if ((rc = upload(&pt.d_spans, s.spans.data(), s.spans.size())) ||
+            (rc = upload(&pt.d_span_prefix, s.span_prefix.data(), s.span_prefix.size())) ||
+            (rc = upload(&pt.d_span_of_tile, s.span_of_tile.data(), s.span_of_tile.size())) ||
+            (rc = upload(&pt.d_chains, s.chains.data(), s.chains.size())))
+            return rc;
+        if (p->mode == DDL_FUSED &&
+            ((rc = upload(&pt.d_bk_spans, s.bk_spans.data(), s.bk_spans.size())) ||
+             (rc = upload(&pt.d_bk_prefix, s.bk_prefix.data(), s.bk_prefix.size())) ||
+             (rc = upload(&pt.d_bk_of_tile, s.bk_of_tile.data(), s.bk_of_tile.size()))))
             return rc;
     }
-    // the fused tables are small; stepwise plans keep them for the one-rank
-    // SGD step, which has no schedule step to ride on
-    if ((rc = upload(&p->d_spans, s.spans.data(), s.spans.size())) ||
-        (rc = upload(&p->d_span_prefix, s.span_prefix.data(), s.span_prefix.size())) ||
-        (rc = upload(&p->d_span_of_tile, s.span_of_tile.data(), s.span_of_tile.size())) ||
-        (rc = upload(&p->d_chains, s.chains.data(), s.chains.size())))
-        return rc;
     return DDL_OK;
 }
 
@@ -172,12 +196,12 @@ constexpr uint32_t kMaxTilesPerLaunch = 1u << 23;
 // where they measured faster on MI355X: 40 ranks fp32 +5%, 16 ranks fp16
 // +5%; 16 ranks fp32 -3%, 8 ranks -3%.  The SGD variant always takes one
 // kernel.
-int fused_passes(ddl_plan p, bool sgd) {
-    if (sgd || p->s.P < 2)
+int fused_passes(ddl_plan p, const Schedule &s, bool sgd) {
+    if (sgd || s.P < 2)
         return 1;
     if (p->fused_passes)
         return p->fused_passes;
-    return p->s.P * fused_vecs_per_lane(p->s.esz) >= 32 ? 2 : 1;
+    return s.P * fused_vecs_per_lane(s.esz) >= 32 ? 2 : 1;
 }
 
 // Side streams event-gated groups alternate over.  Automatic: two for
@@ -192,11 +216,13 @@ int side_streams(ddl_plan p) {
         return p->nside;
     if (p->mode == DDL_STEPWISE)
         return 2;
-    const Schedule &s = p->s;
-    uint64_t total = 0;
-    for (const Bucket &b : s.buckets)
-        total += b.len;
-    const uint64_t mean_bytes = s.buckets.empty() ? 0 : total * s.esz / s.buckets.size();
+    uint64_t bytes = 0, count = 0;
+    for (const Part &pt : p->parts) {
+        for (const Bucket &b : pt.s.buckets)
+            bytes += b.len * (uint64_t)pt.s.esz;
+        count += pt.s.buckets.size();
+    }
+    const uint64_t mean_bytes = count ? bytes / count : 0;
     return mean_bytes < (4ull << 20) ? 2 : 1;
 }
 
@@ -219,6 +245,7 @@ struct Launcher {
     const RankPtrs &bufs;
     hipStream_t stream;
     const SgdArgs *sgd;  // null for the plain all-reduce
+    Part *pt = nullptr;  // the element type of the current group
     std::vector<Bucket> runs;
 
     int bracket_begin(int kind) {
@@ -246,13 +273,13 @@ struct Launcher {
     }
 
     int step(int st, uint32_t lo, uint32_t hi) {
-        const Schedule &s = p->s;
+        const Schedule &s = pt->s;
         if (lo == hi)
             return DDL_OK;
         const uint32_t *pre = s.prefix[st].data();
         StepArgs a;
-        a.items = p->d_items + p->item_base[st];
-        a.prefix = p->d_prefix + p->prefix_base[st];
+        a.items = pt->d_items + pt->item_base[st];
+        a.prefix = pt->d_prefix + pt->prefix_base[st];
         a.item_lo = lo;
         a.item_hi = hi;
         a.divisor = (float)s.P;
@@ -276,16 +303,16 @@ struct Launcher {
     // over their spans and then the broadcast over the runs of memory they
     // cover
     int fused(int b0, int b1) {
-        const Schedule &s = p->s;
+        const Schedule &s = pt->s;
         const uint32_t lo = s.span_at[b0], hi = s.span_at[b1];
         if (lo == hi)
             return DDL_OK;
         const uint32_t *pre = s.span_prefix.data();
         FusedArgs a;
-        a.spans = p->d_spans;
-        a.prefix = p->d_span_prefix;
-        a.tile_span = p->d_span_of_tile;
-        a.chains = p->d_chains;
+        a.spans = pt->d_spans;
+        a.prefix = pt->d_span_prefix;
+        a.tile_span = pt->d_span_of_tile;
+        a.chains = pt->d_chains;
         a.span_lo = lo;
         a.span_hi = hi;
         a.P = s.P;
@@ -293,7 +320,7 @@ struct Launcher {
         a.mean = s.op == DDL_MEAN;
         a.divisor = (float)s.P;
         a.anchor = s.fused_anchor;
-        const bool two = fused_passes(p, sgd != nullptr) == 2;
+        const bool two = fused_passes(p, s, sgd != nullptr) == 2;
         for (uint32_t t = pre[lo]; t < pre[hi]; t += kMaxTilesPerLaunch) {
             const uint32_t tiles = std::min(kMaxTilesPerLaunch, pre[hi] - t);
             a.tile_base = t;
@@ -323,6 +350,7 @@ struct Launcher {
         }
         runs.resize(runs.empty() ? 0 : m + 1);
         BcastArgs bc;
+        std::memset(&bc, 0, sizeof(bc));
         bc.P = s.P;
         bc.ranks_per_group = bcast_ranks_per_group(s.P, s.esz);
         bc.ngroups = (s.P - 1 + bc.ranks_per_group - 1) / bc.ranks_per_group;
@@ -330,7 +358,27 @@ struct Launcher {
         // multiples of max_elems, which keeps the tiles' anchoring (the
         // broadcast always anchors: its runs are whole buckets)
         const uint64_t tile = fused_tile_elems(s.esz);
-        const uint64_t max_elems = (uint64_t)(0xffffffu / (uint32_t)bc.ngroups) * tile;
+        const uint32_t max_tiles = 0xffffffu / (uint32_t)bc.ngroups;
+        const uint64_t max_elems = (uint64_t)max_tiles * tile;
+        if (runs.size() > 1) {
+            // not one run of memory: one launch over the buckets' table
+            bc.spans = pt->d_bk_spans;
+            bc.prefix = pt->d_bk_prefix;
+            bc.tile_span = pt->d_bk_of_tile;
+            const uint32_t *bp = s.bk_prefix.data();
+            for (uint32_t t = bp[b0]; t < bp[b1]; t += max_tiles) {
+                bc.tile_base = t;
+                bc.tile_end = std::min(bp[b1], t + max_tiles);
+                int rc = bracket_begin(DDL_K_BROADCAST);
+                if (rc)
+                    return rc;
+                if (launch_bcast(s.dtype, bufs, bc, stream) != hipSuccess)
+                    return DDL_E_HIP;
+                if ((rc = bracket_end()))
+                    return rc;
+            }
+            return DDL_OK;
+        }
         for (const Bucket &r : runs) {
             for (uint64_t o = r.off; o < r.off + r.len; o = (o / max_elems + 1) * max_elems) {
                 bc.off = o;
@@ -350,7 +398,7 @@ struct Launcher {
 
     // every launch of buckets [b0, b1)
     int group(int b0, int b1) {
-        const Schedule &s = p->s;
+        const Schedule &s = pt->s;
         if (p->mode == DDL_FUSED || (sgd && s.P == 1))
             return fused(b0, b1);
         for (int st = 0; st < s.nsteps; ++st) {
@@ -364,16 +412,19 @@ struct Launcher {
 
 int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stream_,
                    void *done_event, const SgdArgs *sgd) {
-    const Schedule &s = p->s;
-    for (int r = 0; r < s.P; ++r) {
-        if (!bufs[r] && s.n)
+    const int P = p->parts[0].s.P;
+    bool any_elems = false;
+    for (const Part &pt : p->parts)
+        any_elems = any_elems || pt.s.n > 0;
+    for (int r = 0; r < P; ++r) {
+        if (!bufs[r] && any_elems)
             return DDL_E_NULL;
         if ((uintptr_t)bufs[r] % kVecBytes)
             return DDL_E_ALIGN;
     }
     if (sgd) {
         for (int r = 0; r < sgd->nweights; ++r) {
-            if (!sgd->w.p[r] && s.n)
+            if (!sgd->w.p[r] && any_elems)
                 return DDL_E_NULL;
             if ((uintptr_t)sgd->w.p[r] % kVecBytes)
                 return DDL_E_ALIGN;
@@ -393,11 +444,11 @@ int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stre
     }
     RankPtrs rp;
     std::memset(&rp, 0, sizeof(rp));
-    for (int r = 0; r < s.P; ++r)
+    for (int r = 0; r < P; ++r)
         rp.p[r] = bufs[r];
 
     hipStream_t cs = static_cast<hipStream_t>(stream_);
-    const int nb = (int)s.buckets.size();
+    const int nb = (int)p->order.size();
     bool any_event = false;
     for (int b = 0; ready && b < nb; ++b)
         any_event = any_event || ready[b] != nullptr;
@@ -406,18 +457,22 @@ int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stre
         return DDL_E_HIP;
 
     Launcher L{p, rp, ls, sgd};
-    const size_t esz = (size_t)s.esz;
+    auto bucket_bytes = [&](int i) {
+        const Part &pt = p->parts[p->order[i].first];
+        return (size_t)pt.s.buckets[p->order[i].second].len * (size_t)pt.s.esz;
+    };
     int b0 = 0, g = 0, used = 0;
+    std::vector<std::pair<int, int>> range(p->parts.size());
     while (b0 < nb) {
         // the group: equal events, then (with a threshold) more buckets
         // until it holds coalesce_bytes per rank
         void *ev0 = ready ? ready[b0] : nullptr;
         int b1 = b0 + 1;
-        size_t bytes = s.buckets[b0].len * esz;
+        size_t bytes = bucket_bytes(b0);
         while (b1 < nb) {
             void *ev = ready ? ready[b1] : nullptr;
             if (ev == ev0 || (p->coalesce_bytes && bytes < p->coalesce_bytes)) {
-                bytes += s.buckets[b1].len * esz;
+                bytes += bucket_bytes(b1);
                 ++b1;
             } else {
                 break;
@@ -439,9 +494,25 @@ int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stre
                 last = ev;
             }
         }
-        int rc = L.group(b0, b1);
-        if (rc)
-            return rc;
+        // one pass (or one step sequence) per element type in the group:
+        // the buckets of one type are numbered in list order, so those in
+        // the group are a contiguous range of its part
+        for (auto &r : range)
+            r = {-1, -1};
+        for (int b = b0; b < b1; ++b) {
+            auto &r = range[p->order[b].first];
+            if (r.first < 0)
+                r.first = p->order[b].second;
+            r.second = p->order[b].second + 1;
+        }
+        for (size_t q = 0; q < p->parts.size(); ++q) {
+            if (range[q].first < 0)
+                continue;
+            L.pt = &p->parts[q];
+            int rc = L.group(range[q].first, range[q].second);
+            if (rc)
+                return rc;
+        }
         b0 = b1;
         ++g;
     }
@@ -538,7 +609,10 @@ int ddl_plan_create(ddl_plan *out, int P, size_t n, ddl_dtype dtype, ddl_op op,
         return DDL_E_NOMEM;
     int rc;
     try {
-        rc = build_schedule(p->s, P, n, dtype, op, *topo, buckets, nbuckets);
+        p->parts.resize(1);
+        rc = build_schedule(p->parts[0].s, P, n, dtype, op, *topo, buckets, nbuckets);
+        for (int b = 0; !rc && b < (int)p->parts[0].s.buckets.size(); ++b)
+            p->order.emplace_back(0, b);
     } catch (const std::bad_alloc &) {
         rc = DDL_E_NOMEM;
     } catch (...) {
@@ -548,6 +622,81 @@ int ddl_plan_create(ddl_plan *out, int P, size_t n, ddl_dtype dtype, ddl_op op,
         delete p;
         return rc;
     }
+    p->mode = mode;
+    *out = p;
+    return DDL_OK;
+}
+
+int ddl_plan_create_typed(ddl_plan *out, int P, size_t nbytes, ddl_op op, const ddl_topo *topo,
+                          const ddl_typed_bucket *buckets, int nbuckets, ddl_mode mode) {
+    if (!out || !topo || (nbuckets > 0 && !buckets))
+        return DDL_E_NULL;
+    *out = nullptr;
+    if (mode != DDL_STEPWISE && mode != DDL_FUSED)
+        return DDL_E_ARG;
+    if (nbuckets < 0 || (nbuckets == 0 && nbytes > 0))
+        return DDL_E_BUCKETS;
+    // validate in bytes: element-aligned, in range, tiling [0, nbytes)
+    std::vector<std::pair<uint64_t, uint64_t>> spans;
+    for (int b = 0; b < nbuckets; ++b) {
+        const ddl_typed_bucket &t = buckets[b];
+        if (t.dtype != DDL_F32 && t.dtype != DDL_F16)
+            return DDL_E_ARG;
+        const uint64_t esz = t.dtype == DDL_F32 ? 4 : 2;
+        if (t.byte_offset % esz || t.byte_offset > nbytes ||
+            t.count > (nbytes - t.byte_offset) / esz)
+            return DDL_E_BUCKETS;
+        if (t.count)
+            spans.emplace_back(t.byte_offset, t.count * esz);
+    }
+    std::sort(spans.begin(), spans.end());
+    uint64_t at = 0;
+    for (const auto &sp : spans) {
+        if (sp.first != at)
+            return DDL_E_BUCKETS;
+        at += sp.second;
+    }
+    if (at != nbytes)
+        return DDL_E_BUCKETS;
+    ddl_plan p = new (std::nothrow) ddl_plan_s;
+    if (!p)
+        return DDL_E_NOMEM;
+    int rc = DDL_OK;
+    try {
+        // one part per element type present, buckets in list order
+        int part_of[2] = {-1, -1};
+        std::vector<ddl_bucket> lists[2];
+        for (int b = 0; b < nbuckets; ++b) {
+            const ddl_typed_bucket &t = buckets[b];
+            const uint64_t esz = t.dtype == DDL_F32 ? 4 : 2;
+            if (part_of[t.dtype] < 0) {
+                part_of[t.dtype] = (int)p->parts.size();
+                p->parts.emplace_back();
+            }
+            p->order.emplace_back(part_of[t.dtype], (int)lists[t.dtype].size());
+            lists[t.dtype].push_back({(size_t)(t.byte_offset / esz), t.count, nullptr});
+        }
+        if (p->parts.empty()) {  // nbytes == 0: an empty binary32 part
+            p->parts.emplace_back();
+            part_of[DDL_F32] = 0;
+        }
+        for (int d = 0; d < 2 && !rc; ++d) {
+            if (part_of[d] < 0)
+                continue;
+            const uint64_t esz = d == DDL_F32 ? 4 : 2;
+            rc = build_schedule(p->parts[part_of[d]].s, P, nbytes / esz, d, op, *topo,
+                                lists[d].data(), (int)lists[d].size(), false);
+        }
+    } catch (const std::bad_alloc &) {
+        rc = DDL_E_NOMEM;
+    } catch (...) {
+        rc = DDL_E_ARG;
+    }
+    if (rc) {
+        delete p;
+        return rc;
+    }
+    p->typed = true;
     p->mode = mode;
     *out = p;
     return DDL_OK;
@@ -570,7 +719,7 @@ int ddl_plan_execute_sgd(ddl_plan plan, void *const *bufs, void *const *weights,
                          void *done_event) {
     if (!plan || !bufs || !weights)
         return DDL_E_NULL;
-    if (nweights != 1 && nweights != plan->s.P)
+    if (plan->typed || (nweights != 1 && nweights != plan->parts[0].s.P))
         return DDL_E_ARG;
     if (!keep_grads && plan->mode != DDL_FUSED)
         return DDL_E_ARG;
@@ -623,12 +772,17 @@ int ddl_allreduce(void *const *bufs, int P, size_t n, ddl_dtype dtype, ddl_op op
 int ddl_plan_traffic(ddl_plan plan, size_t *sent, size_t *hbm_bytes) {
     if (!plan)
         return DDL_E_NULL;
-    const Schedule &s = plan->s;
-    if (sent)
-        for (int r = 0; r < s.P; ++r)
-            sent[r] = (size_t)s.sent[r];
+    const int P = plan->parts[0].s.P;
+    size_t hbm = 0;
+    for (int r = 0; sent && r < P; ++r)
+        sent[r] = 0;
+    for (const Part &pt : plan->parts) {
+        for (int r = 0; sent && r < P; ++r)
+            sent[r] += (size_t)pt.s.sent[r];
+        hbm += (size_t)(plan->mode == DDL_FUSED ? pt.s.fused_bytes : pt.s.step_bytes);
+    }
     if (hbm_bytes)
-        *hbm_bytes = (size_t)(plan->mode == DDL_FUSED ? s.fused_bytes : s.step_bytes);
+        *hbm_bytes = hbm;
     return DDL_OK;
 }
 
@@ -767,23 +921,25 @@ int ddl_plan_get_fused_passes(ddl_plan plan, int *passes) {
     if (!plan || !passes)
         return DDL_E_NULL;
     std::lock_guard<std::mutex> lk(plan->mu);
-    *passes = plan->mode == DDL_FUSED ? fused_passes(plan, false) : 0;
+    // typed plans: the form of the first element type's buckets
+    *passes = plan->mode == DDL_FUSED ? fused_passes(plan, plan->parts[0].s, false) : 0;
     return DDL_OK;
 }
 
 int ddl_plan_num_steps(ddl_plan plan, int *steps) {
     if (!plan || !steps)
         return DDL_E_NULL;
-    *steps = plan->s.nsteps;
+    *steps = plan->parts[0].s.nsteps;  // the same for every element type
     return DDL_OK;
 }
 
 int ddl_plan_step_kind(ddl_plan plan, int step, int *kind) {
     if (!plan || !kind)
         return DDL_E_NULL;
-    if (step < 0 || step >= plan->s.nsteps)
+    const Schedule &s = plan->parts[0].s;
+    if (step < 0 || step >= s.nsteps)
         return DDL_E_ARG;
-    *kind = plan->s.step_kind[step];
+    *kind = s.step_kind[step];
     return DDL_OK;
 }
 
@@ -791,8 +947,11 @@ int ddl_plan_step_items(ddl_plan plan, int step, int bucket, ddl_step_item *out,
                         int *count) {
     if (!plan || !count)
         return DDL_E_NULL;
-    const Schedule &s = plan->s;
-    if (step < 0 || step >= s.nsteps || bucket < 0 || bucket >= (int)s.buckets.size())
+    if (bucket < 0 || bucket >= (int)plan->order.size())
+        return DDL_E_ARG;
+    const Schedule &s = plan->parts[plan->order[bucket].first].s;
+    bucket = plan->order[bucket].second;
+    if (step < 0 || step >= s.nsteps)
         return DDL_E_ARG;
     const uint32_t lo = s.item_at[step][bucket], hi = s.item_at[step][bucket + 1];
     *count = (int)(hi - lo);
@@ -813,9 +972,10 @@ int ddl_plan_fused_spans(ddl_plan plan, int bucket, size_t *offset, size_t *coun
                          int cap, int *nspans, int *group) {
     if (!plan || !nspans)
         return DDL_E_NULL;
-    const Schedule &s = plan->s;
-    if (bucket < 0 || bucket >= (int)s.buckets.size())
+    if (bucket < 0 || bucket >= (int)plan->order.size())
         return DDL_E_ARG;
+    const Schedule &s = plan->parts[plan->order[bucket].first].s;
+    bucket = plan->order[bucket].second;
     const uint32_t lo = s.span_at[bucket], hi = s.span_at[bucket + 1];
     *nspans = (int)(hi - lo);
     if (group)

@@ -212,7 +212,7 @@ bool tiles_prefix(const std::vector<std::pair<uint64_t, uint64_t>> &ranges, uint
 }  // namespace
 
 int build_schedule(Schedule &s, int P, uint64_t n, int dtype, int op, const ddl_topo &topo,
-                   const ddl_bucket *buckets, int nbuckets) {
+                   const ddl_bucket *buckets, int nbuckets, bool exact) {
     if (P < 1 || P > DDL_MAX_RANKS)
         return DDL_E_ARG;
     if (dtype != DDL_F32 && dtype != DDL_F16)
@@ -279,11 +279,11 @@ int build_schedule(Schedule &s, int P, uint64_t n, int dtype, int op, const ddl_
                   [](const Bucket &a, const Bucket &b) { return a.off < b.off; });
         uint64_t at = 0;
         for (const Bucket &bk : sorted) {
-            if (bk.off != at)
+            if (exact ? bk.off != at : bk.off < at)
                 return DDL_E_BUCKETS;
-            at += bk.len;
+            at = bk.off + bk.len;
         }
-        if (at != n)
+        if (exact && at != n)
             return DDL_E_BUCKETS;
     }
     const int nb = (int)s.buckets.size();
@@ -347,6 +347,17 @@ int build_schedule(Schedule &s, int P, uint64_t n, int dtype, int op, const ddl_
     for (size_t i = 0; i < s.spans.size(); ++i)
         for (uint32_t t = s.span_prefix[i]; t < s.span_prefix[i + 1]; ++t)
             s.span_of_tile[t] = (uint32_t)i;
+    ranges.clear();
+    for (const Bucket &b : s.buckets) {
+        s.bk_spans.push_back({b.off, b.len, 0u, b.off % s.q == 0 ? (uint32_t)kItemAligned : 0u});
+        ranges.emplace_back(b.off, b.len);
+    }
+    if (!tiles_prefix(ranges, fused_tile_elems(s.esz), true, s.bk_prefix))
+        return DDL_E_ARG;
+    s.bk_of_tile.resize(s.bk_prefix.back());
+    for (size_t i = 0; i < s.buckets.size(); ++i)
+        for (uint32_t t = s.bk_prefix[i]; t < s.bk_prefix[i + 1]; ++t)
+            s.bk_of_tile[t] = (uint32_t)i;
     if (!check_schedule(s))
         return DDL_E_ARG;  // cannot happen for the schedules above
     return DDL_OK;

@@ -45,6 +45,13 @@ struct Schedule {
     std::vector<uint32_t> span_prefix;   // tile prefix, nspans+1
     std::vector<uint32_t> span_of_tile;  // [t] the span fused tile t belongs to
     bool fused_anchor = false;           // fused tiles anchored (ddl_internal.h)
+
+    // broadcast tables (two-kernel fused form, groups whose buckets are not
+    // one contiguous run): a DevSpan per bucket (chain unused), its anchored
+    // fused-tile prefix, and the bucket of every such tile
+    std::vector<DevSpan> bk_spans;
+    std::vector<uint32_t> bk_prefix;
+    std::vector<uint32_t> bk_of_tile;
     std::vector<uint8_t> chains;
 
     // accounting
@@ -58,8 +65,11 @@ struct Schedule {
 void split_segment(uint64_t L, int m, uint64_t q, std::vector<uint64_t> &b);
 
 // Validates the arguments and builds every table.  Returns a DDL_* code.
+// exact: the buckets must tile [0, n) exactly; otherwise (one element type
+// of a plan with typed buckets) they must only be disjoint and in range.
 int build_schedule(Schedule &s, int P, uint64_t n, int dtype, int op,
-                   const ddl_topo &topo, const ddl_bucket *buckets, int nbuckets);
+                   const ddl_topo &topo, const ddl_bucket *buckets, int nbuckets,
+                   bool exact = true);
 
 // Proves the tables race-free: within one step no element of any rank that
 // one item writes is read or written by another item.  Returns true if so.

@@ -52,6 +52,23 @@ def resnet50_param_sizes():
     return out
 
 
+def resnet50_mixed_typed_buckets():
+    """Typed buckets (byte offset, count, dtype) of a mixed-precision
+    ResNet-50 gradient: the convolution and fc weights in binary16, the
+    BatchNorm weights and biases and the fc bias in binary32.  Tensors are
+    packed in registration order (every size is a multiple of 8 elements, so
+    every offset is a multiple of 16 bytes) and issued output layer first.
+    Returns (buckets, nbytes)."""
+    out, at = [], 0
+    for name, cnt in resnet50_param_sizes():
+        f32 = ".bn" in name or name.startswith("bn") or "downsample.1" in name \
+            or name.endswith(".bias")
+        dt = "f32" if f32 else "f16"
+        out.append((at, cnt, dt))
+        at += cnt * (4 if f32 else 2)
+    return out[::-1], at
+
+
 def reverse_layer_buckets(sizes):
     """One bucket per tensor, tensors laid out in registration order, buckets
     issued in reverse (output layer first)."""

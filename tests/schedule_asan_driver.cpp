@@ -130,6 +130,13 @@ int main(int argc, char **argv) {
             if (covered != s.buckets[b].len)
                 return fail("spans tile the bucket", P, n, topo.kind);
         }
+        if (s.bk_of_tile.size() != s.bk_prefix.back() || s.bk_spans.size() != s.buckets.size())
+            return fail("broadcast bucket tables", P, n, topo.kind);
+        for (size_t t = 0; t < s.bk_of_tile.size(); ++t) {
+            const uint32_t i = s.bk_of_tile[t];
+            if (i >= s.buckets.size() || s.bk_prefix[i] > t || t >= s.bk_prefix[i + 1])
+                return fail("tile -> bucket table", P, n, topo.kind);
+        }
         if (s.span_of_tile.size() != s.span_prefix.back())
             return fail("one table entry per fused tile", P, n, topo.kind);
         for (size_t t = 0; t < s.span_of_tile.size(); ++t) {

@@ -292,3 +292,48 @@ def test_schedule_generator_under_sanitizers(tmp_path):
     out = subprocess.run([str(exe), "400"], capture_output=True, text=True, timeout=600)
     assert out.returncode == 0, out.stdout + out.stderr
     assert "ok 400 cases" in out.stdout
+
+
+def test_typed_plan_validation_and_tables():
+    """Plans with typed buckets (byte offsets, a dtype per bucket): argument
+    checks, and each bucket's tables equal a plain plan's of its dtype."""
+    P = 6
+    layout = [(0, 1000, "f32"), (4000, 2048, "f16"), (8096, 7, "f32"), (8124, 3, "f16"),
+              (8130, 500, "f16")]
+    nbytes = 8130 + 1000
+    plan = ddl.Plan.typed(P, nbytes, "mean", ddl.topo("ring"), layout)
+    for b, (off, cnt, dt) in enumerate(layout):
+        esz = 4 if dt == "f32" else 2
+        spans, group = plan.fused_spans(b)
+        ref = ddl.Plan(P, off // esz + cnt, dt, "mean", ddl.topo("ring"),
+                       [(0, off // esz), (off // esz, cnt)] if off else [(0, cnt)])
+        want, _ = ref.fused_spans(1 if off else 0)
+        assert spans == want, b
+        items = plan.step_items(3, b)
+        assert items == ref.step_items(3, 1 if off else 0), b
+        ref.destroy()
+    sent, hbm = plan.traffic()
+    assert hbm == 2 * P * nbytes
+    assert sum(sent) == 2 * (P - 1) * sum(c for _, c, _ in layout)
+    plan.destroy()
+    bad = [
+        [(0, 1000, "f32"), (4002, 2047, "f16")],     # gap
+        [(0, 1001, "f32"), (4000, 2048, "f16")],     # overlap
+        [(2, 1000, "f32"), (4002, 2048, "f16")],     # f32 offset not a multiple of 4
+        [(0, 1000, "f32"), (4000, 2049, "f16")],     # past the end
+    ]
+    for bl in bad:
+        with pytest.raises(ddl.DDLError) as e:
+            ddl.Plan.typed(P, 8096, "sum", ddl.topo("ring"), bl)
+        assert e.value.code == -3, bl
+    with pytest.raises(ddl.DDLError) as e:
+        ddl.Plan.typed(P, 8, "sum", ddl.topo("ring"), [(0, 2, 7)])
+    assert e.value.code == -2
+    # no SGD on typed plans
+    import ctypes
+    plan = ddl.Plan.typed(P, 4000, "sum", ddl.topo("ring"), [(0, 1000, "f32")])
+    bufs = (ctypes.c_void_p * P)(*[16 * (r + 1) for r in range(P)])
+    w = (ctypes.c_void_p * 1)(4096)
+    assert ddl.lib().ddl_plan_execute_sgd(plan.handle, bufs, w, 1, 0.1, 1, None, None,
+                                          None) == -2
+    plan.destroy()
