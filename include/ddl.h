@@ -258,7 +258,10 @@ typedef enum {
      * (default 4); the adds keep the schedule's order */
     DDL_TUNE_FUSED_BATCH = 4,
     DDL_TUNE_REDUCE_BATCH = 5,
-    DDL_TUNE_COUNT = 6
+    /* two-kernel form: consecutive tiles each broadcast workgroup copies
+     * (default 1; at most 64) */
+    DDL_TUNE_BCAST_TILES = 6,
+    DDL_TUNE_COUNT = 7
 } ddl_tune_knob;
 int ddl_set_tuning(int knob, int value);
 int ddl_get_tuning(int knob, int *value);

@@ -142,6 +142,7 @@ struct BcastArgs {
     int ranks_per_group;
     int ngroups;
     int aligned;
+    int tiles_per_group;  // consecutive tiles one workgroup copies
 };
 
 // The SGD step fused into the all-reduce's epilogue: binary32 weight

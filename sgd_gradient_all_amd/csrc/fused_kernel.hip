@@ -308,22 +308,23 @@ void fused_reduce_kernel(RankPtrs bufs, FusedArgs a) {
 // table is read, so a workgroup's first access is the load of the values
 // it copies.
 // ---------------------------------------------------------------------------
+// One tile of the broadcast: tile q of the run (or table tile q past
+// tile_base) to ranks r0 .. r1.
 template <class E>
-__global__ __launch_bounds__(kBlock) void bcast_kernel(RankPtrs bufs, BcastArgs a) {
+__device__ __forceinline__ void bcast_tile(const RankPtrs &bufs, const BcastArgs &a, uint64_t q,
+                                           int r0, int r1) {
     using T = typename E::T;
     using V = typename E::V;
     constexpr int U = fused_vecs_per_lane(sizeof(T));
     constexpr uint64_t kTile = fused_tile_elems(sizeof(T));
     constexpr uint64_t kStride = (uint64_t)kBlock * E::N;
     const uint32_t tid = threadIdx.x;
-    const uint32_t ng = (uint32_t)a.ngroups;
-    const int grp = (int)(blockIdx.x % ng);
-    uint64_t off = a.off, len = a.len, j = blockIdx.x / ng;
+    uint64_t off = a.off, len = a.len, j = q;
     bool aligned = a.aligned != 0;
     if (a.spans) {
-        const uint32_t tile = a.tile_base + (uint32_t)j;
-        if (tile >= a.tile_end)
+        if (q >= (uint64_t)(a.tile_end - a.tile_base))
             return;
+        const uint32_t tile = a.tile_base + (uint32_t)q;
         const uint32_t i = a.tile_span[tile];
         const DevSpan sp = a.spans[i];
         off = sp.off;
@@ -336,8 +337,6 @@ __global__ __launch_bounds__(kBlock) void bcast_kernel(RankPtrs bufs, BcastArgs 
         return;
     const uint64_t base = tile_lo(off, sh, kTile, j);
     const uint32_t cnt = (uint32_t)(tile_hi(off, len, sh, kTile, j) - base);
-    const int r0 = 1 + grp * a.ranks_per_group;
-    const int r1 = min(a.P, r0 + a.ranks_per_group);
     const T DDL_GLOBAL *home =
         reinterpret_cast<const T DDL_GLOBAL *>(reinterpret_cast<uint64_t>(bufs.p[0]));
     uint32_t done = 0;
@@ -369,6 +368,19 @@ __global__ __launch_bounds__(kBlock) void bcast_kernel(RankPtrs bufs, BcastArgs 
         for (int r = r0; r < r1; ++r)
             static_cast<T *>(bufs.p[r])[e] = x;
     }
+}
+
+// Workgroup b: rank group g = b % ngroups, tiles (b / ngroups) * tpg ...
+// + tpg - 1 (tpg = tiles_per_group).
+template <class E>
+__global__ __launch_bounds__(kBlock) void bcast_kernel(RankPtrs bufs, BcastArgs a) {
+    const uint32_t ng = (uint32_t)a.ngroups;
+    const int grp = (int)(blockIdx.x % ng);
+    const int r0 = 1 + grp * a.ranks_per_group;
+    const int r1 = min(a.P, r0 + a.ranks_per_group);
+    const uint64_t q0 = (uint64_t)(blockIdx.x / ng) * (uint64_t)a.tiles_per_group;
+    for (int k = 0; k < a.tiles_per_group; ++k)
+        bcast_tile<E>(bufs, a, q0 + (uint64_t)k, r0, r1);
 }
 
 }  // namespace
@@ -452,8 +464,11 @@ int launch_bcast(int dtype, const RankPtrs &bufs, const BcastArgs &a, void *stre
     const uint64_t tile = fused_tile_elems(dtype == DDL_F32 ? 4 : 2);
     const uint64_t tiles = a.spans ? (uint64_t)(a.tile_end - a.tile_base)
                                    : tile_count(a.len, tile_shift(a.off, tile, true), tile);
-    const uint64_t blocks = tiles * (uint64_t)a.ngroups;
-    if (a.ngroups < 1 || a.ranks_per_group < 1 || blocks * kBlock > 0xffffffffull)
+    if (a.ngroups < 1 || a.ranks_per_group < 1 || a.tiles_per_group < 1)
+        return (int)hipErrorInvalidValue;
+    const uint64_t blocks =
+        (tiles + (uint64_t)a.tiles_per_group - 1) / (uint64_t)a.tiles_per_group * (uint64_t)a.ngroups;
+    if (blocks * kBlock > 0xffffffffull)
         return (int)hipErrorInvalidValue;
     if (blocks == 0)
         return (int)hipSuccess;
