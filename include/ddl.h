@@ -190,9 +190,12 @@ int ddl_allreduce(void *const *bufs, int P, size_t n, ddl_dtype dtype, ddl_op op
  * elements each rank sends over the whole schedule, 2 (P-1)/P * n for a ring
  * when P*q divides every bucket (Patarasuk & Yuan's bandwidth-optimal
  * count; the Baidu article's "1.2 GB gradient -> about 2.4 GB sent and
- * received").  hbm_bytes (NULL allowed): the HBM bytes the plan's kernels
- * read plus write per execution -- 2 P n s for DDL_FUSED, 5 (P-1) n s for
- * DDL_STEPWISE (3 L s per reduce-scatter step, 2 L s per all-gather step). */
+ * received").  hbm_bytes (NULL allowed): the algorithmic bytes the plan's
+ * kernels read plus write per execution -- 2 P n s for DDL_FUSED (every
+ * rank's input read once, its result written once; the two-kernel form
+ * re-reads the n s bytes of results from the device caches on top, which
+ * this count leaves out), 5 (P-1) n s for DDL_STEPWISE (3 L s per
+ * reduce-scatter step, 2 L s per all-gather step). */
 int ddl_plan_traffic(ddl_plan plan, size_t *sent_elems_per_rank, size_t *hbm_bytes);
 
 /* Free the plan.  Returns DDL_E_BUSY, and frees nothing, while work the plan
