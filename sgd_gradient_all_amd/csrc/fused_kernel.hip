@@ -13,8 +13,11 @@
 //    and writes the result to rank 0 only, through the cache; then
 //    bcast_kernel copies rank 0's result, still cache-resident, to ranks
 //    1..P-1.  HBM then sees a read phase and a write phase instead of reads
-//    and writes interleaved, which is faster from 16 ranks on (measured on
-//    MI355X: 40 ranks +13..+32%, 16 ranks +7..+20%, 8 ranks -4..-7%).
+//    and writes interleaved.  Measured on MI355X in paired runs: 40 ranks
+//    binary32 +5..+18% (the spread is the physical placement of the
+//    buffers, to which the two-kernel form is far less sensitive), 16 ranks
+//    binary16 +5%, 16 ranks binary32 -3..+7%, 8 ranks -3%.  Plans choose
+//    the form (plan.cpp, fused_passes).
 #include "device_common.h"
 
 namespace ddl {
@@ -82,7 +85,7 @@ __device__ __forceinline__ void st_stream(void *p, V v) {
 // divided by P for the mean, and written once to each rank.
 //
 // The rank addresses, in chain order, are staged in LDS before the first
-// store, so the data loads never wait behind a table load.
+// load, so the data loads never wait behind a table load.
 // ---------------------------------------------------------------------------
 template <class E>
 struct Chain {
@@ -103,9 +106,8 @@ struct Chain {
 // Sums of U element vectors -- e + u * kBlock * N, u < U -- over the chain.
 // The ranks go in batches of kB from the first one; every load of a
 // batch is issued before the batch's adds.  In a partial last batch the
-// missing slots
-// re-load the batch's last rank (a line already in flight) and their adds
-// are skipped, which keeps every load unconditional.  Ungrouped (rings): one
+// missing slots re-load the batch's last rank (a line already in flight) and
+// their adds are skipped, which keeps every load unconditional.  Ungrouped (rings): one
 // chain of P entries.  Grouped (torus): chains of `group` entries, then
 // their sums.
 template <class E, bool kGrouped, bool kNt, int U, int kB>
@@ -302,11 +304,11 @@ void fused_reduce_kernel(RankPtrs bufs, FusedArgs a) {
 
 // ---------------------------------------------------------------------------
 // broadcast: the second kernel of the two-kernel form.  Workgroup b copies
-// anchored tile b / ngroups -- of the run [off, off + len), or of the bucket
-// table -- from rank 0 to ranks 1 + g * ranks_per_group ... (at most P - 1),
-// g = b % ngroups.  The copy is of the bits: no arithmetic.  In run mode no
-// table is read, so a workgroup's first access is the load of the values
-// it copies.
+// tiles_per_group anchored tiles from tile (b / ngroups) * tiles_per_group
+// on -- of the run [off, off + len), or of the bucket table -- from rank 0
+// to ranks 1 + g * ranks_per_group ... (at most P - 1), g = b % ngroups.
+// The copy is of the bits: no arithmetic.  In run mode no table is read, so
+// a workgroup's first access is the load of the values it copies.
 // ---------------------------------------------------------------------------
 // One tile of the broadcast: tile q of the run (or table tile q past
 // tile_base) to ranks r0 .. r1.

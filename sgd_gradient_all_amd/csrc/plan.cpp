@@ -3,10 +3,12 @@
 // The dispatcher issues buckets in list order -- output layer first, so the
 // all-reduce of the gradients back-propagation finishes first can overlap the
 // rest of it (Baidu Ring-Allreduce article, part 4, opening paragraphs).  A
-// bucket with a ready event waits for it on the plan's side stream; buckets
-// whose events are equal (NULL included) share one group of launches, so a
-// step of all of them is one kernel.  With no event at all the work goes on
-// the caller's stream directly.
+// bucket with a ready event waits for it on a side stream of the plan;
+// consecutive buckets whose events are equal (NULL included) share one group
+// of launches, so a step of all of them is one kernel.  With no event at all
+// the work goes on the caller's stream directly.  A plan with typed buckets
+// holds one schedule per element type, and a group runs one pass (or step
+// sequence) per type it holds.
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>

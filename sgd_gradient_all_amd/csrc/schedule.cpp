@@ -19,6 +19,11 @@
 //    the last phase that reduces) also divides by P.
 // Every piece of a segment starts on a multiple of q = 16 B / element size
 // when the segment does, which keeps the kernels on dwordx4 accesses.
+//
+// The generator also lays out the kernels' tile tables: the tile prefix of
+// every step's items and of the fused spans (tiles anchored at multiples of
+// the tile size when the ranges average two tiles or more), the fused tile
+// -> span table, and the broadcast's per-bucket tables.
 #include "schedule.h"
 
 #include <algorithm>
