@@ -264,7 +264,12 @@ typedef enum {
     /* two-kernel form: consecutive tiles each broadcast workgroup copies
      * (default 1; at most 64) */
     DDL_TUNE_BCAST_TILES = 6,
-    DDL_TUNE_COUNT = 7
+    /* two-kernel form: deal the broadcast's workgroups so that all rank
+     * groups of a tile run on one of this many accelerator dies (8 on
+     * MI355X), which fetches the tile's values into that die's L2 once;
+     * 0 or 1 = plain order (default) */
+    DDL_TUNE_BCAST_XCD = 7,
+    DDL_TUNE_COUNT = 8
 } ddl_tune_knob;
 int ddl_set_tuning(int knob, int value);
 int ddl_get_tuning(int knob, int *value);

@@ -143,6 +143,7 @@ struct BcastArgs {
     int ngroups;
     int aligned;
     int tiles_per_group;  // consecutive tiles one workgroup copies
+    int nxcd;             // > 1: all rank groups of a tile block on one die
 };
 
 // The SGD step fused into the all-reduce's epilogue: binary32 weight

@@ -373,14 +373,25 @@ __device__ __forceinline__ void bcast_tile(const RankPtrs &bufs, const BcastArgs
 }
 
 // Workgroup b: rank group g = b % ngroups, tiles (b / ngroups) * tpg ...
-// + tpg - 1 (tpg = tiles_per_group).
+// + tpg - 1 (tpg = tiles_per_group).  With nxcd > 1 the workgroups are
+// dealt so that all rank groups of a tile block run on one accelerator die
+// (workgroup b runs on die b % nxcd), which then fetches the block's values
+// into its L2 once instead of once per die.
 template <class E>
 __global__ __launch_bounds__(kBlock) void bcast_kernel(RankPtrs bufs, BcastArgs a) {
     const uint32_t ng = (uint32_t)a.ngroups;
-    const int grp = (int)(blockIdx.x % ng);
-    const int r0 = 1 + grp * a.ranks_per_group;
+    uint32_t qb, grp;
+    if (a.nxcd > 1) {
+        const uint32_t x = blockIdx.x % (uint32_t)a.nxcd, jj = blockIdx.x / (uint32_t)a.nxcd;
+        qb = x + (uint32_t)a.nxcd * (jj / ng);
+        grp = jj % ng;
+    } else {
+        qb = blockIdx.x / ng;
+        grp = blockIdx.x % ng;
+    }
+    const int r0 = 1 + (int)grp * a.ranks_per_group;
     const int r1 = min(a.P, r0 + a.ranks_per_group);
-    const uint64_t q0 = (uint64_t)(blockIdx.x / ng) * (uint64_t)a.tiles_per_group;
+    const uint64_t q0 = (uint64_t)qb * (uint64_t)a.tiles_per_group;
     for (int k = 0; k < a.tiles_per_group; ++k)
         bcast_tile<E>(bufs, a, q0 + (uint64_t)k, r0, r1);
 }
@@ -468,8 +479,11 @@ int launch_bcast(int dtype, const RankPtrs &bufs, const BcastArgs &a, void *stre
                                    : tile_count(a.len, tile_shift(a.off, tile, true), tile);
     if (a.ngroups < 1 || a.ranks_per_group < 1 || a.tiles_per_group < 1)
         return (int)hipErrorInvalidValue;
+    const uint64_t qblocks = (tiles + (uint64_t)a.tiles_per_group - 1) / (uint64_t)a.tiles_per_group;
     const uint64_t blocks =
-        (tiles + (uint64_t)a.tiles_per_group - 1) / (uint64_t)a.tiles_per_group * (uint64_t)a.ngroups;
+        a.nxcd > 1 ? (qblocks + (uint64_t)a.nxcd - 1) / (uint64_t)a.nxcd * (uint64_t)a.nxcd *
+                         (uint64_t)a.ngroups
+                   : qblocks * (uint64_t)a.ngroups;
     if (blocks * kBlock > 0xffffffffull)
         return (int)hipErrorInvalidValue;
     if (blocks == 0)

@@ -29,7 +29,7 @@ using namespace ddl;
 constexpr int kMaxSideStreams = 4;
 
 // process-wide tuning knobs (ddl_set_tuning); -1 = default
-std::atomic<int> g_tune[DDL_TUNE_COUNT] = {-1, -1, -1, -1, -1, -1, -1};
+std::atomic<int> g_tune[DDL_TUNE_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1};
 constexpr int kTuneDefault[DDL_TUNE_COUNT] = {
     0,   // DDL_TUNE_BCAST_RANKS: automatic
     1,   // DDL_TUNE_REDUCE_NT_LOAD: on
@@ -38,6 +38,7 @@ constexpr int kTuneDefault[DDL_TUNE_COUNT] = {
     1,   // DDL_TUNE_FUSED_BATCH
     4,   // DDL_TUNE_REDUCE_BATCH
     1,   // DDL_TUNE_BCAST_TILES
+    0,   // DDL_TUNE_BCAST_XCD: off
 };
 
 namespace ddl {
@@ -358,11 +359,14 @@ struct Launcher {
         bc.ranks_per_group = bcast_ranks_per_group(s.P, s.esz);
         bc.ngroups = (s.P - 1 + bc.ranks_per_group - 1) / bc.ranks_per_group;
         bc.tiles_per_group = std::max(1, std::min(tuning(DDL_TUNE_BCAST_TILES), 64));
+        bc.nxcd = std::max(1, std::min(tuning(DDL_TUNE_BCAST_XCD), 64));
         // a grid holds at most 2^32 - 1 work-items: runs are cut at
         // multiples of max_elems, which keeps the tiles' anchoring (the
         // broadcast always anchors: its runs are whole buckets)
         const uint64_t tile = fused_tile_elems(s.esz);
-        const uint32_t max_tiles = 0xffffffu / (uint32_t)bc.ngroups;  // tiles_per_group >= 1
+        // (the die-dealt order pads the last nxcd-block: keep headroom)
+        const uint32_t max_tiles = 0xffffffu / (uint32_t)(bc.ngroups * bc.nxcd) *
+                                   (uint32_t)bc.nxcd;
         const uint64_t max_elems = (uint64_t)max_tiles * tile;
         if (runs.size() > 1) {
             // not one run of memory: one launch over the buckets' table

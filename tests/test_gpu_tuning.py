@@ -31,6 +31,7 @@ SETTINGS = ([("fused_batch", b) for b in (2, 4, 8)] +
             [("reduce_batch", b) for b in (1, 2, 8)] +
             [("bcast_ranks", g) for g in (1, 3, 100)] +
             [("bcast_tiles", t) for t in (2, 5)] +
+            [("bcast_xcd", 8), ("bcast_xcd", 3)] +
             [("reduce_nt_load", 0), ("fused_nt_load_max_p", 1000), ("anchor", 1),
              ("anchor", 2)])
 
