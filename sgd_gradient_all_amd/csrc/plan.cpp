@@ -11,6 +11,8 @@
 // sequence) per type it holds.
 #include <hip/hip_runtime_api.h>
 
+#include <limits.h>
+
 #include <algorithm>
 #include <atomic>
 #include <cstring>
@@ -28,9 +30,9 @@ using namespace ddl;
 
 constexpr int kMaxSideStreams = 4;
 
-// process-wide tuning knobs (ddl_set_tuning); -1 = default
-std::atomic<int> g_tune[DDL_TUNE_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1};
-constexpr int kTuneDefault[DDL_TUNE_COUNT] = {
+// process-wide tuning knobs (ddl_set_tuning), stored as value + 1 so that
+// the zero-initialised array means "every knob at its default"
+constexpr int kTuneDefault[] = {
     0,   // DDL_TUNE_BCAST_RANKS: automatic
     1,   // DDL_TUNE_REDUCE_NT_LOAD: on
     24,  // DDL_TUNE_FUSED_NT_LOAD_MAX_P
@@ -40,13 +42,16 @@ constexpr int kTuneDefault[DDL_TUNE_COUNT] = {
     1,   // DDL_TUNE_BCAST_TILES
     0,   // DDL_TUNE_BCAST_XCD: off
 };
+static_assert(sizeof(kTuneDefault) / sizeof(kTuneDefault[0]) == DDL_TUNE_COUNT,
+              "one default per knob");
+std::atomic<int> g_tune[DDL_TUNE_COUNT];
 
 namespace ddl {
 int tuning(int knob) {
     if (knob < 0 || knob >= DDL_TUNE_COUNT)
         return 0;
     const int v = g_tune[knob].load(std::memory_order_relaxed);
-    return v < 0 ? kTuneDefault[knob] : v;
+    return v == 0 ? kTuneDefault[knob] : v - 1;
 }
 }  // namespace ddl
 constexpr int kLaunchKinds = DDL_K_COUNT;
@@ -902,7 +907,7 @@ int ddl_plan_profile_read(ddl_plan plan, double *total_ms, int *launches, double
 int ddl_set_tuning(int knob, int value) {
     if (knob < 0 || knob >= DDL_TUNE_COUNT)
         return DDL_E_ARG;
-    g_tune[knob].store(value < 0 ? -1 : value);
+    g_tune[knob].store(value < 0 ? 0 : (value == INT_MAX ? INT_MAX : value + 1));
     return DDL_OK;
 }
 
