@@ -498,7 +498,28 @@ def cpu_baseline(args, w, topo, torch, ddl, synth, np):
                       f"same algorithmic bytes as the GPU figure",
             "seconds": round(secs, 2),
             "host_cpus": os.cpu_count(),
+            "host": host_info(),
             "bytes_differing_from_gpu": mismatched}
+
+
+def host_info():
+    """CPU model, usable CPUs and memory of the host the oracle ran on."""
+    info = {"usable_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
+            else os.cpu_count()}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal"):
+                    info["ram_gb"] = round(int(line.split()[1]) / 2**20, 1)
+                    break
+    except OSError:
+        pass
+    return info
 
 
 if __name__ == "__main__":
