@@ -229,8 +229,7 @@ int ddl_plan_set_side_streams(ddl_plan plan, int n);
  * passes = 2: a reduce kernel reads every rank and writes the result to rank
  * 0, then a broadcast kernel copies it from rank 0 to ranks 1..P-1 while it
  * is still in the device caches, so HBM serves a read phase and then a write
- * phase.  passes = 0 (default): automatic, two kernels when P times the
- * vectors each lane streams (1 for binary32, 2 for binary16) is at least 32.
+ * phase.  passes = 0 (default): automatic, two kernels from 16 ranks on.
  * The results are bit-identical either way; only the speed differs.
  * Returns DDL_E_ARG for other values.  Takes effect at the next execute.
  * ddl_plan_get_fused_passes reports the form the next plain execute uses
@@ -245,7 +244,7 @@ int ddl_plan_get_fused_passes(ddl_plan plan, int *passes);
  * DDL_E_ARG for an unknown knob. */
 typedef enum {
     /* two-kernel form: ranks each broadcast workgroup writes; 0 = automatic
-     * (2 from 32 ranks on; below, 3 for binary16 and 7 for binary32) */
+     * (2 from 32 ranks on, 7 below) */
     DDL_TUNE_BCAST_RANKS = 0,
     /* two-kernel form: 1 = the reduce kernel's loads are non-temporal
      * (default), 0 = cached */

@@ -201,16 +201,16 @@ constexpr uint32_t kMaxTilesPerLaunch = 1u << 23;
 
 // Form of the fused pass: one kernel, or a reduce kernel that writes rank 0
 // and a broadcast kernel (see fused_kernel.hip).  Automatic: two kernels
-// when each lane streams at least 32 vectors (P times the vectors per lane),
-// where they measured faster on MI355X: 40 ranks fp32 +5%, 16 ranks fp16
-// +5%; 16 ranks fp32 -3%, 8 ranks -3%.  The SGD variant always takes one
-// kernel.
+// from 16 ranks on, where they measured faster on MI355X (paired, six
+// repeats): 40 ranks fp32 +5..+18%, 16 ranks fp32 ResNet-50 multi-ring
+// +7.3%, 16 ranks fp16 torus +5.8%; 8 ranks -3%.  The SGD variant always
+// takes one kernel.
 int fused_passes(ddl_plan p, const Schedule &s, bool sgd) {
     if (sgd || s.P < 2)
         return 1;
     if (p->fused_passes)
         return p->fused_passes;
-    return s.P * fused_vecs_per_lane(s.esz) >= 32 ? 2 : 1;
+    return s.P >= 16 ? 2 : 1;
 }
 
 // Side streams event-gated groups alternate over.  Automatic: two for
@@ -237,16 +237,16 @@ int side_streams(ddl_plan p) {
 
 // Ranks one broadcast workgroup writes (knob DDL_TUNE_BCAST_RANKS, 0 =
 // automatic).  Measured on MI355X (paired runs): 40 ranks fp32, two (5.45
-// TB/s; 4 within 1%, all 39 -4%, one -7%); 16 ranks fp16, three (5.47
-// against 5.35 with all 15); 16 ranks fp32, seven (5.51 against 5.26 with
-// all 15; the order of 7 and 15 changed between boxes).
-int bcast_ranks_per_group(int P, int esz) {
+// TB/s; 4 within 1%, all 39 -4%, one -7%); 16 ranks, seven (fp32 5.66
+// against 5.58 with three and 5.47 with all 15; fp16 5.48 against 5.40 and
+// 5.38).
+int bcast_ranks_per_group(int P) {
     const int v = tuning(DDL_TUNE_BCAST_RANKS);
     if (v > 0)
         return std::min(v, std::max(P - 1, 1));
     if (P >= 32)
         return 2;
-    return std::min(esz == 2 ? 3 : 7, std::max(P - 1, 1));
+    return std::min(7, std::max(P - 1, 1));
 }
 
 struct Launcher {
@@ -361,7 +361,7 @@ struct Launcher {
         BcastArgs bc;
         std::memset(&bc, 0, sizeof(bc));
         bc.P = s.P;
-        bc.ranks_per_group = bcast_ranks_per_group(s.P, s.esz);
+        bc.ranks_per_group = bcast_ranks_per_group(s.P);
         bc.ngroups = (s.P - 1 + bc.ranks_per_group - 1) / bc.ranks_per_group;
         bc.tiles_per_group = std::max(1, std::min(tuning(DDL_TUNE_BCAST_TILES), 64));
         bc.nxcd = std::max(1, std::min(tuning(DDL_TUNE_BCAST_XCD), 64));

@@ -226,14 +226,12 @@ def test_plan_create_needs_no_gpu():
 
 
 def test_fused_pass_form_setting():
-    # host-only: the automatic form is two kernels when P x vectors per lane
-    # (1 for f32, 2 for f16) reaches 32 (fused plans only); explicit 1 and 2
-    # stick; anything else is rejected
-    for P, dt, mode, want in ((8, "f32", "fused", 1), (16, "f32", "fused", 1),
-                              (31, "f32", "fused", 1), (32, "f32", "fused", 2),
-                              (40, "f32", "fused", 2), (15, "f16", "fused", 1),
-                              (16, "f16", "fused", 2), (1, "f32", "fused", 1),
-                              (40, "f32", "stepwise", 0)):
+    # host-only: the automatic form is two kernels from 16 ranks on (fused
+    # plans only); explicit 1 and 2 stick; anything else is rejected
+    for P, dt, mode, want in ((8, "f32", "fused", 1), (15, "f32", "fused", 1),
+                              (16, "f32", "fused", 2), (40, "f32", "fused", 2),
+                              (15, "f16", "fused", 1), (16, "f16", "fused", 2),
+                              (1, "f32", "fused", 1), (40, "f32", "stepwise", 0)):
         plan = ddl.Plan(P, 4096, dt, "mean", ddl.topo("ring"), None, mode)
         assert plan.fused_passes() == want, (P, dt, mode)
         if mode == "fused" and P > 1:
