@@ -294,16 +294,30 @@ def extras(args, w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_b
     plan.set_profiling(True)
     step_once()
     torch.cuda.synchronize()
-    kms, launches, _ = plan.profile_read()
+    kinds = plan.profile_read_kinds()
+    launches = sum(v[1] for v in kinds.values())
+    kms = sum(v[0] for v in kinds.values())
     # launches of different buckets overlap on the side streams, so the sum
-    # of their durations is not the step time: report the average launch
+    # of their durations is not the step time: report the average launch,
+    # and per step kernel its algorithmic bytes per launch over its average
+    # duration (3 L s per reduce-scatter launch, 2 L s per all-gather one)
+    kernel_rows = {}
+    for kind, share in (("reduce", 3), ("gather", 2)):
+        tot, cnt, mx = kinds[kind]
+        if cnt:
+            nb = share * sbytes / 5 / cnt   # the step bytes split 3 : 2
+            kernel_rows[kind + "_step_kernel"] = {
+                "launches_per_step": cnt, "avg_launch_us": round(tot / cnt * 1e3, 2),
+                "max_launch_us": round(mx * 1e3, 2), "algorithmic_bytes_per_launch": int(nb),
+                "GBps": round(nb / (tot / cnt * 1e-3) / 1e9, 1)}
     out["stepwise"] = {"ms_per_step": round(sms, 3),
                        "graph_ms_per_step": round(gms, 3),
                        "hbm_GBps": round(sbytes / (sms * 1e-3) / 1e9, 1),
                        "fused_floor_equiv_GBps": round(fused_bytes / (sms * 1e-3) / 1e9, 1),
                        "bytes_per_step": sbytes,
                        "launches_per_step": launches,
-                       "avg_launch_us": round(kms / max(launches, 1) * 1e3, 2)}
+                       "avg_launch_us": round(kms / max(launches, 1) * 1e3, 2),
+                       **kernel_rows}
     plan.destroy()
     log(f"bench: stepwise {out['stepwise']}")
 
