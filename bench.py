@@ -378,7 +378,39 @@ def extras(args, w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_b
 
     out["sgd"] = sgd_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_ms)
     out["typed"] = typed_leg(main_stream, torch, ddl, synth)
+    out["per_gpu_step"] = per_gpu_step_leg(w, main_stream, torch, ddl)
     return out
+
+
+def per_gpu_step_leg(w, main_stream, torch, ddl):
+    """One GPU's share of a real ring step: a chunk of the workload's bucket
+    (L / P elements) added into, or copied over, one neighbour's -- timed as
+    the step kernels of a two-rank ring over two such chunks (each of its
+    steps holds two pairs, one per rank: two GPUs' shares in one launch)."""
+    L = (w.bucket_list()[0][1] + w.P - 1) // w.P
+    L = (L + 3) // 4 * 4
+    tdt = torch.float32 if w.dtype == "f32" else torch.float16
+    bufs = [torch.ones(2 * L, dtype=tdt, device="cuda") for _ in range(2)]
+    plan = ddl.Plan(2, 2 * L, w.dtype, "sum", ddl.topo("ring"), None, "stepwise")
+    plan.execute(bufs, stream=main_stream)
+    torch.cuda.synchronize()
+    plan.set_profiling(True)
+    plan.profile_read_kinds()
+    reps = 200
+    for _ in range(reps):
+        plan.execute(bufs, stream=main_stream)
+    torch.cuda.synchronize()
+    k = plan.profile_read_kinds()
+    plan.destroy()
+    esz = 4 if w.dtype == "f32" else 2
+    res = {"chunk_elements": L, "chunks_per_launch": 2}
+    for kind, nbytes in (("reduce", 2 * 3 * L * esz), ("gather", 2 * 2 * L * esz)):
+        tot, cnt, _ = k[kind]
+        us = tot / cnt * 1e3
+        res[kind] = {"avg_launch_us": round(us, 2), "bytes": nbytes,
+                     "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+    log(f"bench: per-GPU step {res}")
+    return res
 
 
 def typed_leg(main_stream, torch, ddl, synth):
