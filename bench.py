@@ -291,15 +291,17 @@ def extras(args, w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_b
     torch.cuda.synchronize()
     gms = t0.elapsed_time(t1) / steps
     del graph
+    # the per-kernel figures come from one profiled step on a single side
+    # stream: overlapping launches would stretch each one's duration
+    plan.set_side_streams(1)
     plan.set_profiling(True)
     step_once()
     torch.cuda.synchronize()
     kinds = plan.profile_read_kinds()
+    plan.set_side_streams(0)
     launches = sum(v[1] for v in kinds.values())
     kms = sum(v[0] for v in kinds.values())
-    # launches of different buckets overlap on the side streams, so the sum
-    # of their durations is not the step time: report the average launch,
-    # and per step kernel its algorithmic bytes per launch over its average
+    # per step kernel: its algorithmic bytes per launch over its average
     # duration (3 L s per reduce-scatter launch, 2 L s per all-gather one)
     kernel_rows = {}
     for kind, share in (("reduce", 3), ("gather", 2)):
