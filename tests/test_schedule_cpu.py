@@ -90,9 +90,9 @@ def _div(a, P, dtype):
     return (a.astype(np.float32) / np.float32(P)).astype(np.float16)
 
 
-def interpret_steps(plan, bufs, nbuckets, dtype):
+def interpret_steps(plan, bufs, nbuckets, dtype, which=None):
     steps = plan.num_steps()
-    for b in range(nbuckets):
+    for b in (range(nbuckets) if which is None else which):
         for s in range(steps):
             kind = plan.step_kind(s)
             items = plan.step_items(s, b)
@@ -110,9 +110,9 @@ def interpret_steps(plan, bufs, nbuckets, dtype):
                     bufs[dst][off:off + cnt] = data
 
 
-def interpret_fused(plan, bufs, nbuckets, dtype, mean):
+def interpret_fused(plan, bufs, nbuckets, dtype, mean, which=None):
     P = len(bufs)
-    for b in range(nbuckets):
+    for b in (range(nbuckets) if which is None else which):
         spans, group = plan.fused_spans(b)
         for off, cnt, chain in spans:
             acc = None
@@ -182,6 +182,58 @@ def test_tables_replay_to_the_oracle(case, op):
         else:
             assert hbm == 5 * (P - 1) * n * esz
         plan.destroy()
+
+
+def test_typed_tables_replay_to_the_oracle():
+    """A plan with typed buckets: each bucket's tables, replayed on the
+    dtype's view of the byte buffers, give the oracle's walk of that bucket
+    alone (binary32 and binary16 buckets interleaved, ragged)."""
+    rng = np.random.default_rng(5)
+    for P, kind, k, rows, cols in ((5, "ring", 1, 0, 0), (8, "multiring", 3, 0, 0),
+                                   (6, "torus2d", 1, 2, 3)):
+        layout, at = [], 0
+        for _ in range(7):
+            dt = "f16" if rng.random() < 0.5 else "f32"
+            esz = 4 if dt == "f32" else 2
+            if at % esz:
+                off, cnt, pdt = layout[-1]
+                layout[-1] = (off, cnt + 1, pdt)
+                at += 2
+            cnt = int(rng.integers(1, 300))
+            layout.append((at, cnt, dt))
+            at += cnt * esz
+        layout = layout[::-1]
+        nbytes = at
+        pad = (nbytes + 3) // 4 * 4
+        g = [rng.integers(0, 256, pad, dtype=np.uint8) for _ in range(P)]
+        # finite values: random bytes can make NaNs, whose payloads may differ
+        for off, cnt, dt in layout:
+            npdt = np.float32 if dt == "f32" else np.float16
+            for r in range(P):
+                g[r][off:off + cnt * np.dtype(npdt).itemsize] = \
+                    rng.standard_normal(cnt).astype(npdt).view(np.uint8)
+        t = ddl.topo(kind, k, rows, cols)
+        for mode in ("stepwise", "fused"):
+            plan = ddl.Plan.typed(P, nbytes, "mean", t, layout, mode)
+            bufs = [x.copy() for x in g]
+            for b, (off, cnt, dt) in enumerate(layout):
+                npdt = np.float32 if dt == "f32" else np.float16
+                views = [x[:pad // np.dtype(npdt).itemsize * np.dtype(npdt).itemsize]
+                         .view(npdt) for x in bufs]
+                if mode == "stepwise":
+                    interpret_steps(plan, views, len(layout), npdt, which=[b])
+                else:
+                    interpret_fused(plan, views, len(layout), npdt, True, which=[b])
+            plan.destroy()
+            for off, cnt, dt in layout:
+                npdt = np.float32 if dt == "f32" else np.float16
+                nb = cnt * np.dtype(npdt).itemsize
+                seg = [x[off:off + nb].view(npdt).copy() for x in g]
+                kinds = {"ring": orc.RING, "multiring": orc.MULTIRING, "torus2d": orc.TORUS2D}
+                orc.allreduce(seg, op=orc.MEAN, kind=kinds[kind], k=k, rows=rows, cols=cols)
+                for r in range(P):
+                    assert bufs[r][off:off + nb].tobytes() == seg[r].view(np.uint8).tobytes(), \
+                        (kind, mode, off, dt, r)
 
 
 def test_step_counts_and_kinds():
