@@ -553,3 +553,46 @@ def test_several_side_streams(nside):
         for r in range(w.P):
             assert bitwise_equal(out[r], ref[r]), (mode, r)
         assert bitwise_equal(snap.cpu().numpy(), ref[2])
+
+
+@pytest.mark.parametrize("mode", ["stepwise", "fused2"])
+def test_graph_capture_with_bucket_events_and_side_streams(mode):
+    """Capture with a ready event per bucket (recorded inside the capture),
+    so the work forks onto the plan's side streams (two, automatically, for
+    stepwise plans) and joins back; every replay gives the oracle's bits."""
+    say(f"case graph capture with events {mode}")
+    w = Workload("graph-ev", 8, 12 * 40_000, "f32", "mean", "ring", dist="normal", sigma=1e-2,
+                 seed=24, buckets=[(i * 40_000, 40_000) for i in reversed(range(12))])
+    g = host_inputs(w)
+    ref = [x.copy() for x in g]
+    oracle_full(w, ref)
+    src = to_device(g)
+    bufs = [t.clone() for t in src]
+    plan = make_plan(w, mode)
+    events = [torch.cuda.Event() for _ in w.bucket_list()]
+    main = torch.cuda.current_stream()
+    for e in events:
+        e.record(main)
+    plan.execute(bufs, events=events, stream=main)   # binds the plan
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(main)
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            for e in events:
+                e.record(s)
+            plan.execute(bufs, events=events, stream=s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for b, x in zip(bufs, src):
+            b.copy_(x)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        out = [b.cpu().numpy() for b in bufs]
+        for r in (0, 3, 7):
+            assert bitwise_equal(out[r], ref[r]), (mode, rep, r)
+    del graph
+    torch.cuda.synchronize()
+    plan.destroy()
