@@ -46,6 +46,10 @@ def lib():
         L.ddl_oracle_sum_f64.restype = i32
         L.ddl_oracle_sgd.argtypes = [ctypes.POINTER(vp), i32, vp, u64, i32, ctypes.c_float]
         L.ddl_oracle_sgd.restype = i32
+        L.ddl_oracle_lars.argtypes = [ctypes.POINTER(vp), i32, vp, ctypes.POINTER(u64),
+                                      ctypes.POINTER(u64), i32, i32, ctypes.c_float,
+                                      ctypes.c_double, ctypes.c_double, vp]
+        L.ddl_oracle_lars.restype = i32
         L.ddl_oracle_split.argtypes = [u64, i32, u64, ctypes.POINTER(u64)]
         L.ddl_oracle_split.restype = None
         for name in ("ddl_oracle_f16_to_f32", "ddl_oracle_f32_to_f16"):
@@ -160,6 +164,22 @@ def sgd(weights, y, lr):
                           float(lr))
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
+
+
+def lars(weights, y, layers, lr, coeff=0.01, eps=1e-6):
+    """In place: the LARS step of every layer (offset, count) on every float32
+    array in weights; returns the per-layer rates lr * trust (float32)."""
+    L = lib()
+    for w in weights:
+        assert w.dtype == np.float32 and w.flags.c_contiguous and w.shape == y.shape
+    ptrs = (ctypes.c_void_p * len(weights))(*[w.ctypes.data for w in weights])
+    rates = np.zeros(max(1, len(layers)), dtype=np.float32)
+    rc = L.ddl_oracle_lars(ptrs, len(weights), y.ctypes.data, _u64(o for o, _ in layers),
+                           _u64(c for _, c in layers), len(layers), _dtype_code(y.dtype),
+                           float(lr), float(coeff), float(eps), rates.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return rates[:len(layers)]
 
 
 def split(L_, m, q):

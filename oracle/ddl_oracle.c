@@ -38,14 +38,33 @@
  * any copy, so every rank receives the same bits.
  *
  * After the all-reduce, ddl_oracle_sgd is the plain SGD step w = w - lr*y
- * that synchronous SGD takes with the averaged gradient.
+ * that synchronous SGD takes with the averaged gradient, and ddl_oracle_lars
+ * the layer-wise adaptive step the Sony article trains with ("训练设置": LARS,
+ * its reference 9, coefficient 0.01, eps 1e-6; the formula itself is not on
+ * the page).  LARS as You, Gitman and Ginsburg publish it scales each layer's
+ * learning rate by a trust ratio coeff * ||w|| / ||grad||; the reading taken
+ * (no weight decay or momentum is stated, so neither is applied):
+ *
+ *   per layer l:  W = sum of w_0[e]^2, G = sum of y[e]^2 over the layer,
+ *                 in binary64 (each square of a binary32 value is exact),
+ *                 element by element in index order;
+ *   trust = coeff * sqrt(W) / (sqrt(G) + eps)   if W > 0 and G > 0,
+ *           1                                    otherwise (a zero layer
+ *                                                 would never move);
+ *   rate  = binary32(lr * trust), one rounding from binary64;
+ *   every replica: w_r[e] = w_r[e] - rate * y[e], the SGD step with rate.
+ *
+ * The norms use replica 0: synchronous SGD keeps every replica identical.
+ * All rates are taken from the weights before any of them is updated.
  *
  * Parity pins (tests/test_oracle_*.py): closed forms, exact small-integer
  * sums, hand-worked adversarial examples of the chain order, rank identity,
  * the traffic identity and the pages' "about 2.4 GB", reductions between the
  * three schedules, exhaustive binary16 conversion and addition against numpy,
- * and fp64 error bounds.  No function here is "parity unpinned"; the
- * association order itself is this reading of an omitted passage.
+ * and fp64 error bounds; for LARS, closed-form rates, the gradient-scale
+ * invariance, the zero-layer fallback to the plain SGD step and exact
+ * rational norms on small layers.  No function here is "parity unpinned";
+ * the association order itself is this reading of an omitted passage.
  *
  * Build: plain C11, -O2 -ffp-contract=off, no fast-math, SSE scalar floats.
  * The MXCSR flush-to-zero / denormals-are-zero bits are cleared for the
@@ -451,6 +470,54 @@ int ddl_oracle_sgd(float *const *weights, int nweights, const void *y, uint64_t 
         }
     }
     fpenv_leave(env);
+    return 0;
+}
+
+int ddl_oracle_lars(float *const *weights, int nweights, const void *y,
+                    const uint64_t *layer_off, const uint64_t *layer_len, int nlayers,
+                    int dtype, float lr, double coeff, double eps, float *rates_out)
+{
+    if (nweights < 1 || !weights || nlayers < 0 || (nlayers > 0 && (!layer_off || !layer_len)))
+        return -1;
+    if (!(coeff >= 0.0) || !(eps >= 0.0) || coeff > 1e300 || eps > 1e300)
+        return -1;
+    for (int l = 0; l < nlayers; ++l)
+        if (layer_len[l] && (!y || !weights[0]))
+            return -1;
+    float *rate = malloc(sizeof(float) * (size_t)(nlayers > 0 ? nlayers : 1));
+    if (!rate)
+        return -1;
+    unsigned int env = fpenv_enter();
+    /* every layer's rate, from the weights as they are before the step */
+    for (int l = 0; l < nlayers; ++l) {
+        double W = 0.0, G = 0.0;
+        for (uint64_t e = layer_off[l]; e < layer_off[l] + layer_len[l]; ++e) {
+            double w = (double)weights[0][e];
+            double g = dtype == ORC_F32 ? (double)((const float *)y)[e]
+                                        : (double)h2f(((const uint16_t *)y)[e]);
+            W += w * w;
+            G += g * g;
+        }
+        double trust = 1.0;
+        if (W > 0.0 && G > 0.0)
+            trust = coeff * sqrt(W) / (sqrt(G) + eps);
+        rate[l] = (float)((double)lr * trust);
+        if (rates_out)
+            rates_out[l] = rate[l];
+    }
+    /* then the SGD step of every layer with its own rate */
+    for (int l = 0; l < nlayers; ++l) {
+        for (int r = 0; r < nweights; ++r) {
+            for (uint64_t e = layer_off[l]; e < layer_off[l] + layer_len[l]; ++e) {
+                float g = dtype == ORC_F32 ? ((const float *)y)[e]
+                                           : h2f(((const uint16_t *)y)[e]);
+                float step = rate[l] * g;
+                weights[r][e] = weights[r][e] - step;
+            }
+        }
+    }
+    fpenv_leave(env);
+    free(rate);
     return 0;
 }
 

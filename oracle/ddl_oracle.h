@@ -18,7 +18,8 @@
  *    and Fig. 2: GPUs on a 2D grid; reduce-scatter, all-reduce, all-gather in
  *    horizontal and vertical rings.
  *  - Same article, "训练设置" (training settings): the gradient exchange is
- *    done in half precision (FP16).
+ *    done in half precision (FP16), and the weights are updated with LARS
+ *    (coefficient 0.01, eps 1e-6).
  *
  * Parity status of each function is in the header comment of ddl_oracle.c.
  */
@@ -71,6 +72,22 @@ int ddl_oracle_allreduce(void *const *bufs, int P, uint64_t n, int dtype, int op
  * weights: nweights binary32 host arrays; y: count elements of dtype. */
 int ddl_oracle_sgd(float *const *weights, int nweights, const void *y, uint64_t count,
                    int dtype, float lr);
+
+/* LARS step after the all-reduce (Sony article, "训练设置": LARS, reference
+ * 9 there, coefficient 0.01, eps 1e-6; the update is You, Gitman and
+ * Ginsburg's layer-wise trust ratio without weight decay or momentum).
+ * Layer l covers elements [layer_off[l], layer_off[l] + layer_len[l]).  For
+ * each layer, from replica 0's weights and the all-reduced gradient y:
+ *     W = sum w_0[e]^2, G = sum y[e]^2       (binary64, index order)
+ *     trust = coeff * sqrt(W) / (sqrt(G) + eps), or 1 if W or G is 0
+ *     rate = binary32(lr * trust)
+ * then every replica takes w_r[e] = w_r[e] - rate * y[e] (binary32, the
+ * product rounded before the difference).  All rates are computed before
+ * any weight changes.  rates_out: NULL or nlayers floats.  Returns -1 for
+ * bad arguments (negative or non-finite coeff or eps), touching nothing. */
+int ddl_oracle_lars(float *const *weights, int nweights, const void *y,
+                    const uint64_t *layer_off, const uint64_t *layer_len, int nlayers,
+                    int dtype, float lr, double coeff, double eps, float *rates_out);
 
 /* The plain definition: out[e] = sum over ranks of g_r[e] in binary64,
  * divided by P for ORC_MEAN.  Reference for tolerance checks. */
