@@ -179,6 +179,34 @@ int ddl_plan_execute_sgd(ddl_plan plan, void *const *bufs, void *const *weights,
                          float lr, int keep_grads, void *const *ready_events, void *stream,
                          void *done_event);
 
+/* The all-reduce followed by a LARS step (Sony ResNet-50 article, "训练设置":
+ * the weights are updated with LARS, coefficient 0.01 and eps 1e-6; the
+ * page omits the formula, taken here from You, Gitman and Ginsburg's
+ * layer-wise adaptive rate scaling without weight decay or momentum).  Each
+ * bucket is a layer.  Once the bucket is all-reduced (bufs end with the
+ * result, as after ddl_plan_execute), from replica 0's weights w and the
+ * reduced gradient y over the bucket:
+ *     trust = coeff * ||w|| / (||y|| + eps)   (1 if ||w|| or ||y|| is 0)
+ *     rate  = binary32(lr * trust)            (norms and trust in binary64)
+ * and every replica takes w[e] = w[e] - rate * y[e] as in
+ * ddl_plan_execute_sgd.  Replicas of a synchronous step are identical, so
+ * replica 0's norm serves all of them.
+ *  weights     as for ddl_plan_execute_sgd (nweights 1 or P).
+ *  coeff, eps  the trust coefficient and eps (the page: 0.01 and 1e-6);
+ *              finite and >= 0, else DDL_E_ARG.
+ *  rates_out   NULL, or device memory for nbuckets binary32 values that
+ *              receive each bucket's rate (bucket list order).
+ * The norms are sums of squares in binary64, deterministic but not in index
+ * order, so a rate can differ from an index-order evaluation when lr * trust
+ * lies within about 1e-13 (relative) of a binary32 rounding boundary.  The
+ * first call allocates 16 bytes per tile of the plan's buckets (a tile is
+ * 1024 binary32 or 4096 binary16 elements) plus 4 per bucket, once.
+ * DDL_E_ARG for a plan with typed buckets or another nweights.  Other
+ * arguments and the asynchrony are those of ddl_plan_execute. */
+int ddl_plan_execute_lars(ddl_plan plan, void *const *bufs, void *const *weights, int nweights,
+                          float lr, double coeff, double eps, float *rates_out,
+                          void *const *ready_events, void *stream, void *done_event);
+
 /* One-shot form: looks up (or builds and caches) the plan for these
  * arguments -- the cache key is everything except the buffers and events --
  * and executes it with the buckets' ready_event fields.  Thread-safe. */
@@ -288,14 +316,18 @@ int ddl_plan_profile_read_kinds(ddl_plan plan, double *total_ms, int *launches,
 
 /* ---- schedule introspection (host-only; used by the tests) ------------- */
 /* Kernel launches: a reduce-scatter step, an all-gather step, the one-kernel
- * fused pass, and the two kernels of the two-kernel fused pass. */
+ * fused pass, the two kernels of the two-kernel fused pass, and the three
+ * kernels of the LARS step (norms, rates, update). */
 typedef enum {
     DDL_K_REDUCE = 0,
     DDL_K_GATHER = 1,
     DDL_K_FUSED = 2,
     DDL_K_FUSED_REDUCE = 3,
     DDL_K_BROADCAST = 4,
-    DDL_K_COUNT = 5
+    DDL_K_LARS_NORM = 5,
+    DDL_K_LARS_RATE = 6,
+    DDL_K_LARS_UPDATE = 7,
+    DDL_K_COUNT = 8
 } ddl_launch_kind;
 
 /* One pair transfer of one step: rank dst combines elements

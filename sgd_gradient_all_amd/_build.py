@@ -10,7 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libddl.so")
 SOURCES = [os.path.join(HERE, "csrc", f)
-           for f in ("schedule.cpp", "plan.cpp", "step_kernels.hip", "fused_kernel.hip")]
+           for f in ("schedule.cpp", "plan.cpp", "step_kernels.hip", "fused_kernel.hip",
+                     "lars_kernels.hip")]
 
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
              "-Wall", "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",

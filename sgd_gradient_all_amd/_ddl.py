@@ -11,8 +11,12 @@ DDL_SUM, DDL_MEAN = 0, 1
 DDL_RING, DDL_MULTIRING, DDL_TORUS2D = 0, 1, 2
 DDL_STEPWISE, DDL_FUSED = 0, 1
 DDL_K_REDUCE, DDL_K_GATHER, DDL_K_FUSED, DDL_K_FUSED_REDUCE, DDL_K_BROADCAST = 0, 1, 2, 3, 4
-DDL_K_COUNT = 5
-LAUNCH_KINDS = ("reduce", "gather", "fused", "fused_reduce", "broadcast")
+DDL_K_LARS_NORM, DDL_K_LARS_RATE, DDL_K_LARS_UPDATE = 5, 6, 7
+DDL_K_COUNT = 8
+LAUNCH_KINDS = ("reduce", "gather", "fused", "fused_reduce", "broadcast", "lars_norm",
+                "lars_rate", "lars_update")
+# LARS as the Sony ResNet-50 article trains with it: coefficient and eps
+LARS_COEFF, LARS_EPS = 0.01, 1e-6
 
 _DTYPES = {"f32": DDL_F32, "f16": DDL_F16, "float32": DDL_F32, "float16": DDL_F16}
 _OPS = {"sum": DDL_SUM, "mean": DDL_MEAN}
@@ -72,6 +76,9 @@ def lib():
                                i32, vp, vp], i32),
             "ddl_plan_execute_sgd": ([vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32,
                                       ctypes.c_float, i32, ctypes.POINTER(vp), vp, vp], i32),
+            "ddl_plan_execute_lars": ([vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32,
+                                       ctypes.c_float, ctypes.c_double, ctypes.c_double,
+                                       vp, ctypes.POINTER(vp), vp, vp], i32),
             "ddl_plan_traffic": ([vp, ctypes.POINTER(sz), ctypes.POINTER(sz)], i32),
             "ddl_plan_destroy": ([vp], i32),
             "ddl_cache_clear": ([], i32),
@@ -239,6 +246,22 @@ class Plan:
         _check(lib().ddl_plan_execute_sgd(self.handle, _bufs(bufs), _bufs(weights), len(weights),
                                           float(lr), 1 if keep_grads else 0, ev, _ptr(stream),
                                           _ptr(done_event)), "ddl_plan_execute_sgd")
+
+    def execute_lars(self, bufs, weights, lr, coeff=LARS_COEFF, eps=LARS_EPS, rates_out=None,
+                     events=None, stream=None, done_event=None):
+        """All-reduce, then the LARS step of every bucket (a layer): rate =
+        lr * coeff * ||w|| / (||y|| + eps), w = w - rate * y on every replica.
+        rates_out: None or device memory (pointer or tensor) for one float32
+        per bucket."""
+        if len(bufs) != self.P:
+            raise ValueError(f"expected {self.P} buffers, got {len(bufs)}")
+        ev = None
+        if events is not None:
+            ev = (ctypes.c_void_p * max(1, len(events)))(*[_ptr(e) for e in events])
+        _check(lib().ddl_plan_execute_lars(self.handle, _bufs(bufs), _bufs(weights),
+                                           len(weights), float(lr), float(coeff), float(eps),
+                                           _ptr(rates_out), ev, _ptr(stream),
+                                           _ptr(done_event)), "ddl_plan_execute_lars")
 
     def traffic(self):
         sent = (ctypes.c_size_t * self.P)()

@@ -158,6 +158,26 @@ struct SgdArgs {
     int keep_grads;
 };
 
+// The LARS step after the all-reduce, layer = bucket (lars_kernels.hip):
+// per-tile binary64 sums of squares, per-bucket rates, then the SGD step of
+// every replica with its bucket's rate.  The tiles are the buckets' anchored
+// tiles of fused_tile_elems elements (Schedule::bk_spans, bk_prefix,
+// bk_of_tile).
+struct LarsArgs {
+    const DevSpan *spans;          // one per bucket
+    const uint32_t *prefix;        // [i] first tile of bucket i, nbuckets + 1
+    const uint32_t *tile_span;     // [t] bucket of tile t
+    const void *y;                 // the reduced gradient: rank 0's buffer
+    uint32_t tile_base, tile_end;  // norm and update launches: these tiles
+    uint32_t bucket_lo, bucket_hi; // rate launch: these buckets
+    double *partial;               // [2t], [2t+1]: sums of w_0^2 and y^2 over tile t
+    float *rate;                   // [i] the rate of bucket i
+    float *rate_out;               // null, or the caller's copy of rate
+    float lr;
+    int nweights;
+    double coeff, eps;
+};
+
 // Current value of a ddl_tune_knob (its default unless ddl_set_tuning set it).
 int tuning(int knob);
 
@@ -168,5 +188,9 @@ int launch_step(int dtype, int kind, int vpl, const RankPtrs &bufs, const StepAr
 int launch_fused(int dtype, const RankPtrs &bufs, const FusedArgs &a, const SgdArgs *sgd,
                  bool home, uint32_t tiles, void *stream);
 int launch_bcast(int dtype, const RankPtrs &bufs, const BcastArgs &a, void *stream);
+// kind: DDL_K_LARS_NORM or DDL_K_LARS_UPDATE (blocks = tiles from
+// a.tile_base), DDL_K_LARS_RATE (blocks = buckets from a.bucket_lo).
+int launch_lars(int dtype, int kind, const RankPtrs &w, const LarsArgs &a, uint32_t blocks,
+                void *stream);
 
 }  // namespace ddl

@@ -70,6 +70,8 @@ struct Part {
     DevSpan *d_bk_spans = nullptr;
     uint32_t *d_bk_prefix = nullptr;
     uint32_t *d_bk_of_tile = nullptr;
+    double *d_lars_partial = nullptr;  // LARS: two sums per bucket-table tile
+    float *d_lars_rate = nullptr;      // LARS: one rate per bucket
 };
 
 struct ddl_plan_s {
@@ -131,6 +133,8 @@ void release_device(ddl_plan p) {
         (void)hipFree(pt.d_bk_spans);
         (void)hipFree(pt.d_bk_prefix);
         (void)hipFree(pt.d_bk_of_tile);
+        (void)hipFree(pt.d_lars_partial);
+        (void)hipFree(pt.d_lars_rate);
         pt = Part{std::move(pt.s)};
     }
     for (hipEvent_t e : p->prof)
@@ -178,16 +182,15 @@ int bind_device(ddl_plan p, int dev) {
                 return rc;
         }
         // the fused tables are small; stepwise plans keep them for the
-        // one-rank SGD step, which has no schedule step to ride on
+        // one-rank SGD step, which has no schedule step to ride on, and the
+        // bucket tables for the broadcast and the LARS step
         if ((rc = upload(&pt.d_spans, s.spans.data(), s.spans.size())) ||
             (rc = upload(&pt.d_span_prefix, s.span_prefix.data(), s.span_prefix.size())) ||
             (rc = upload(&pt.d_span_of_tile, s.span_of_tile.data(), s.span_of_tile.size())) ||
-            (rc = upload(&pt.d_chains, s.chains.data(), s.chains.size())))
-            return rc;
-        if (p->mode == DDL_FUSED &&
-            ((rc = upload(&pt.d_bk_spans, s.bk_spans.data(), s.bk_spans.size())) ||
-             (rc = upload(&pt.d_bk_prefix, s.bk_prefix.data(), s.bk_prefix.size())) ||
-             (rc = upload(&pt.d_bk_of_tile, s.bk_of_tile.data(), s.bk_of_tile.size()))))
+            (rc = upload(&pt.d_chains, s.chains.data(), s.chains.size())) ||
+            (rc = upload(&pt.d_bk_spans, s.bk_spans.data(), s.bk_spans.size())) ||
+            (rc = upload(&pt.d_bk_prefix, s.bk_prefix.data(), s.bk_prefix.size())) ||
+            (rc = upload(&pt.d_bk_of_tile, s.bk_of_tile.data(), s.bk_of_tile.size())))
             return rc;
     }
     return DDL_OK;
@@ -249,11 +252,21 @@ int bcast_ranks_per_group(int P) {
     return std::min(7, std::max(P - 1, 1));
 }
 
+// The LARS step's arguments of one call (ddl_plan_execute_lars).
+struct LarsCall {
+    RankPtrs w;
+    int nweights;
+    float lr;
+    double coeff, eps;
+    float *rates_out;
+};
+
 struct Launcher {
     ddl_plan p;
     const RankPtrs &bufs;
     hipStream_t stream;
     const SgdArgs *sgd;  // null for the plain all-reduce
+    const LarsCall *lars = nullptr;  // the LARS step after the all-reduce
     Part *pt = nullptr;  // the element type of the current group
     std::vector<Bucket> runs;
 
@@ -409,22 +422,86 @@ struct Launcher {
         return DDL_OK;
     }
 
+    // the LARS step of buckets [b0, b1), once their all-reduce is enqueued:
+    // the norms of every tile, the rate of every bucket, the update
+    int lars_step(int b0, int b1) {
+        const Schedule &s = pt->s;
+        LarsArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.spans = pt->d_bk_spans;
+        a.prefix = pt->d_bk_prefix;
+        a.tile_span = pt->d_bk_of_tile;
+        a.y = bufs.p[0];
+        a.partial = pt->d_lars_partial;
+        a.rate = pt->d_lars_rate;
+        a.rate_out = lars->rates_out;
+        a.lr = lars->lr;
+        a.nweights = lars->nweights;
+        a.coeff = lars->coeff;
+        a.eps = lars->eps;
+        a.bucket_lo = (uint32_t)b0;
+        a.bucket_hi = (uint32_t)b1;
+        const uint32_t *bp = s.bk_prefix.data();
+        auto tiles = [&](int kind) {
+            for (uint32_t t = bp[b0]; t < bp[b1]; t += kMaxTilesPerLaunch) {
+                a.tile_base = t;
+                a.tile_end = std::min(bp[b1], t + kMaxTilesPerLaunch);
+                int rc = bracket_begin(kind);
+                if (rc)
+                    return rc;
+                if (launch_lars(s.dtype, kind, lars->w, a, a.tile_end - t, stream) != hipSuccess)
+                    return (int)DDL_E_HIP;
+                if ((rc = bracket_end()))
+                    return rc;
+            }
+            return (int)DDL_OK;
+        };
+        int rc = tiles(DDL_K_LARS_NORM);
+        if (rc || b1 == b0)
+            return rc;
+        if ((rc = bracket_begin(DDL_K_LARS_RATE)))
+            return rc;
+        if (launch_lars(s.dtype, DDL_K_LARS_RATE, lars->w, a, (uint32_t)(b1 - b0), stream) !=
+            hipSuccess)
+            return DDL_E_HIP;
+        if ((rc = bracket_end()))
+            return rc;
+        return tiles(DDL_K_LARS_UPDATE);
+    }
+
     // every launch of buckets [b0, b1)
     int group(int b0, int b1) {
         const Schedule &s = pt->s;
-        if (p->mode == DDL_FUSED || (sgd && s.P == 1))
-            return fused(b0, b1);
-        for (int st = 0; st < s.nsteps; ++st) {
-            int rc = step(st, s.item_at[st][b0], s.item_at[st][b1]);
-            if (rc)
-                return rc;
+        int rc = DDL_OK;
+        if (p->mode == DDL_FUSED || (sgd && s.P == 1)) {
+            rc = fused(b0, b1);
+        } else {
+            for (int st = 0; st < s.nsteps && !rc; ++st)
+                rc = step(st, s.item_at[st][b0], s.item_at[st][b1]);
         }
-        return DDL_OK;
+        if (rc || !lars)
+            return rc;
+        return lars_step(b0, b1);
     }
 };
 
+// Device memory of the LARS step, allocated by a plan's first LARS call.
+int ensure_lars(ddl_plan p) {
+    for (Part &pt : p->parts) {
+        if (pt.d_lars_partial)
+            continue;
+        const size_t tiles = std::max<size_t>(1, pt.s.bk_prefix.empty() ? 0 : pt.s.bk_prefix.back());
+        const size_t nb = std::max<size_t>(1, pt.s.buckets.size());
+        if (hipMalloc((void **)&pt.d_lars_partial, 2 * tiles * sizeof(double)) != hipSuccess)
+            return DDL_E_NOMEM;
+        if (hipMalloc((void **)&pt.d_lars_rate, nb * sizeof(float)) != hipSuccess)
+            return DDL_E_NOMEM;
+    }
+    return DDL_OK;
+}
+
 int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stream_,
-                   void *done_event, const SgdArgs *sgd) {
+                   void *done_event, const SgdArgs *sgd, const LarsCall *lars = nullptr) {
     const int P = p->parts[0].s.P;
     bool any_elems = false;
     for (const Part &pt : p->parts)
@@ -435,13 +512,17 @@ int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stre
         if ((uintptr_t)bufs[r] % kVecBytes)
             return DDL_E_ALIGN;
     }
-    if (sgd) {
-        for (int r = 0; r < sgd->nweights; ++r) {
-            if (!sgd->w.p[r] && any_elems)
-                return DDL_E_NULL;
-            if ((uintptr_t)sgd->w.p[r] % kVecBytes)
-                return DDL_E_ALIGN;
-        }
+    for (int r = 0; sgd && r < sgd->nweights; ++r) {
+        if (!sgd->w.p[r] && any_elems)
+            return DDL_E_NULL;
+        if ((uintptr_t)sgd->w.p[r] % kVecBytes)
+            return DDL_E_ALIGN;
+    }
+    for (int r = 0; lars && r < lars->nweights; ++r) {
+        if (!lars->w.p[r] && any_elems)
+            return DDL_E_NULL;
+        if ((uintptr_t)lars->w.p[r] % kVecBytes)
+            return DDL_E_ALIGN;
     }
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
@@ -454,6 +535,11 @@ int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stre
         }
     } else if (p->device != dev) {
         return DDL_E_DEVICE;
+    }
+    if (lars) {
+        int rc = ensure_lars(p);
+        if (rc)
+            return rc;
     }
     RankPtrs rp;
     std::memset(&rp, 0, sizeof(rp));
@@ -469,7 +555,7 @@ int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stre
     if (any_event && hipEventRecord(p->call_ev, cs) != hipSuccess)
         return DDL_E_HIP;
 
-    Launcher L{p, rp, ls, sgd};
+    Launcher L{p, rp, ls, sgd, lars};
     auto bucket_bytes = [&](int i) {
         const Part &pt = p->parts[p->order[i].first];
         return (size_t)pt.s.buckets[p->order[i].second].len * (size_t)pt.s.esz;
@@ -746,6 +832,33 @@ int ddl_plan_execute_sgd(ddl_plan plan, void *const *bufs, void *const *weights,
     std::lock_guard<std::mutex> lk(plan->mu);
     try {
         return execute_locked(plan, bufs, ready_events, stream, done_event, &g);
+    } catch (...) {
+        return DDL_E_NOMEM;
+    }
+}
+
+int ddl_plan_execute_lars(ddl_plan plan, void *const *bufs, void *const *weights, int nweights,
+                          float lr, double coeff, double eps, float *rates_out,
+                          void *const *ready_events, void *stream, void *done_event) {
+    if (!plan || !bufs || !weights)
+        return DDL_E_NULL;
+    if (plan->typed || (nweights != 1 && nweights != plan->parts[0].s.P))
+        return DDL_E_ARG;
+    // finite and >= 0 (NaN fails both comparisons)
+    if (!(coeff >= 0.0 && coeff <= 1e300) || !(eps >= 0.0 && eps <= 1e300))
+        return DDL_E_ARG;
+    LarsCall c;
+    std::memset(&c, 0, sizeof(c));
+    for (int r = 0; r < nweights; ++r)
+        c.w.p[r] = weights[r];
+    c.nweights = nweights;
+    c.lr = lr;
+    c.coeff = coeff;
+    c.eps = eps;
+    c.rates_out = rates_out;
+    std::lock_guard<std::mutex> lk(plan->mu);
+    try {
+        return execute_locked(plan, bufs, ready_events, stream, done_event, nullptr, &c);
     } catch (...) {
         return DDL_E_NOMEM;
     }

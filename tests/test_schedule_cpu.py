@@ -329,6 +329,35 @@ def test_sgd_argument_validation_before_any_gpu_call():
         plan.destroy()
 
 
+def test_lars_argument_validation_before_any_gpu_call():
+    import ctypes
+    P = 4
+    nan, inf = float("nan"), float("inf")
+    plan = ddl.Plan(P, 1000, "f32", "mean", ddl.topo("ring"), None, "fused")
+    bufs = (ctypes.c_void_p * P)(*[16 * (r + 1) for r in range(P)])
+    for nweights, coeff, eps, wofs, want in ((2, 0.01, 1e-6, 0, -2), (0, 0.01, 1e-6, 0, -2),
+                                             (1, -0.01, 1e-6, 0, -2), (1, 0.01, -1e-6, 0, -2),
+                                             (1, nan, 1e-6, 0, -2), (1, 0.01, nan, 0, -2),
+                                             (1, inf, 1e-6, 0, -2), (P, 0.01, inf, 0, -2),
+                                             (P, 0.01, 1e-6, 4, -4), (1, 0.01, 1e-6, 8, -4)):
+        w = (ctypes.c_void_p * max(1, nweights))(
+            *[4096 * (r + 1) + wofs for r in range(max(1, nweights))])
+        rc = ddl.lib().ddl_plan_execute_lars(plan.handle, bufs, w, nweights, 0.1, coeff, eps,
+                                             None, None, None, None)
+        assert rc == want, (nweights, coeff, eps, wofs, rc)
+    w = (ctypes.c_void_p * 1)(4096)
+    assert ddl.lib().ddl_plan_execute_lars(plan.handle, bufs, None, 1, 0.1, 0.01, 1e-6, None,
+                                           None, None, None) == -1
+    assert ddl.lib().ddl_plan_execute_lars(None, bufs, w, 1, 0.1, 0.01, 1e-6, None, None, None,
+                                           None) == -1
+    plan.destroy()
+    # no LARS on typed plans
+    plan = ddl.Plan.typed(P, 4000, "sum", ddl.topo("ring"), [(0, 1000, "f32")])
+    assert ddl.lib().ddl_plan_execute_lars(plan.handle, bufs, w, 1, 0.1, 0.01, 1e-6, None,
+                                           None, None, None) == -2
+    plan.destroy()
+
+
 def test_schedule_generator_under_sanitizers(tmp_path):
     """The host schedule generator, built with AddressSanitizer and
     UndefinedBehaviorSanitizer (g++, host code only), through random
