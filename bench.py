@@ -22,6 +22,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "achieved HBM GB/s and % of peak per all-reduce (300M fp32, P=40 ring)"
+LEGS = ("stepwise", "overlap", "sgd", "lars", "typed", "per_gpu_step")
 PEAK_HBM_GBPS = 8000.0
 # committed counter summaries: one file per form of the fused pass
 TRAFFIC_FILES = {1: ("fused_kernel", "hbm_bytes_per_launch"),
@@ -71,13 +72,19 @@ def main():
                     help="fused pass form: 0 the plan's choice, 1 one kernel, "
                          "2 reduce + broadcast kernels")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the step-by-step and overlap measurements")
+                    help="skip every side measurement (--legs)")
+    ap.add_argument("--legs", default=",".join(LEGS),
+                    help="comma-separated side measurements to run, of: " + ", ".join(LEGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-buckets", type=int, default=64,
                     help="buckets of the workload the CPU oracle is timed on")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run one plain device copy of this size (counter calibration)")
     args = ap.parse_args()
+    args.legs = [] if args.no_extras else [x for x in args.legs.split(",") if x]
+    for leg in args.legs:
+        if leg not in LEGS:
+            ap.error(f"unknown leg {leg!r}; known: {', '.join(LEGS)}")
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -236,7 +243,7 @@ def main():
         result["calib_copy_bytes"] = 2 * nel * 4
         del a, b
 
-    if not args.no_extras:
+    if args.legs:
         result.update(extras(args, w, bufs, topo, buckets, main_stream, torch, ddl, synth,
                              hbm_bytes, ms))
 
@@ -248,8 +255,27 @@ def main():
 
 def extras(args, w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_bytes, fused_ms):
     out = {}
-    # the step-by-step schedule on the same buffers: timed without per-launch
-    # events, then one profiled pass for the kernel-side figure
+    if "stepwise" in args.legs:
+        out["stepwise"] = stepwise_leg(w, bufs, topo, buckets, main_stream, torch, ddl,
+                                       fused_bytes)
+    if "overlap" in args.legs and w.side_stream:
+        out["overlap"] = overlap_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth,
+                                     fused_bytes, fused_ms)
+    if "sgd" in args.legs:
+        out["sgd"] = sgd_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_ms)
+    if "lars" in args.legs:
+        out["lars"] = lars_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_ms)
+    if "typed" in args.legs:
+        out["typed"] = typed_leg(main_stream, torch, ddl, synth)
+    if "per_gpu_step" in args.legs:
+        out["per_gpu_step"] = per_gpu_step_leg(w, main_stream, torch, ddl)
+    return out
+
+
+def stepwise_leg(w, bufs, topo, buckets, main_stream, torch, ddl, fused_bytes):
+    """The step-by-step schedule on the same buffers: timed without
+    per-launch events, replayed from a HIP graph, then one profiled pass for
+    the kernel-side figures."""
     plan = ddl.Plan(w.P, w.n, w.dtype, w.op, topo, buckets, "stepwise")
     _, sbytes = plan.traffic()
     evs = [torch.cuda.Event() for _ in buckets] if w.side_stream else None
@@ -312,7 +338,7 @@ def extras(args, w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_b
                 "launches_per_step": cnt, "avg_launch_us": round(tot / cnt * 1e3, 2),
                 "max_launch_us": round(mx * 1e3, 2), "algorithmic_bytes_per_launch": int(nb),
                 "GBps": round(nb / (tot / cnt * 1e-3) / 1e9, 1)}
-    out["stepwise"] = {"ms_per_step": round(sms, 3),
+    res = {"ms_per_step": round(sms, 3),
                        "graph_ms_per_step": round(gms, 3),
                        "hbm_GBps": round(sbytes / (sms * 1e-3) / 1e9, 1),
                        "fused_floor_equiv_GBps": round(fused_bytes / (sms * 1e-3) / 1e9, 1),
@@ -321,67 +347,65 @@ def extras(args, w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_b
                        "avg_launch_us": round(kms / max(launches, 1) * 1e3, 2),
                        **kernel_rows}
     plan.destroy()
-    log(f"bench: stepwise {out['stepwise']}")
+    log(f"bench: stepwise {res}")
+    return res
 
-    if w.side_stream:
-        # overlap with a streaming compute kernel standing in for the rest of
-        # back-propagation: 0.925 x the all-reduce's bytes (the Baidu
-        # article's ~370 ms compute vs ~400 ms communication), in one slice
-        # per bucket; bucket b waits for slice b
-        nb = len(buckets)
-        comp_elems = int(0.925 * fused_bytes / 8) // (4 * nb) * (4 * nb)
-        free = torch.cuda.mem_get_info()[0]
-        if comp_elems * 4 > free * 0.9:
-            comp_elems = int(free * 0.9 / 4) // (4 * nb) * (4 * nb)
-        scratch = torch.zeros(comp_elems, dtype=torch.float32, device="cuda")
-        per = comp_elems // nb
-        cs = main_stream.cuda_stream
 
-        def compute_slices(evs):
-            for i in range(nb):
-                synth.stream_compute(scratch.data_ptr() + 4 * i * per, per, 1.0, 0.0, cs)
-                if evs is not None:
-                    evs[i].record(main_stream)
+def overlap_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_bytes, fused_ms):
+    """Overlap with a streaming compute kernel standing in for the rest of
+    back-propagation: 0.925 x the all-reduce's bytes (the Baidu article's
+    ~370 ms compute vs ~400 ms communication), in one slice per bucket;
+    bucket b waits for slice b."""
+    nb = len(buckets)
+    comp_elems = int(0.925 * fused_bytes / 8) // (4 * nb) * (4 * nb)
+    free = torch.cuda.mem_get_info()[0]
+    if comp_elems * 4 > free * 0.9:
+        comp_elems = int(free * 0.9 / 4) // (4 * nb) * (4 * nb)
+    scratch = torch.zeros(comp_elems, dtype=torch.float32, device="cuda")
+    per = comp_elems // nb
+    cs = main_stream.cuda_stream
 
-        plan = ddl.Plan(w.P, w.n, w.dtype, w.op, topo, buckets, "fused")
-        evs = [torch.cuda.Event() for _ in buckets]
+    def compute_slices(evs):
+        for i in range(nb):
+            synth.stream_compute(scratch.data_ptr() + 4 * i * per, per, 1.0, 0.0, cs)
+            if evs is not None:
+                evs[i].record(main_stream)
+
+    plan = ddl.Plan(w.P, w.n, w.dtype, w.op, topo, buckets, "fused")
+    evs = [torch.cuda.Event() for _ in buckets]
+    compute_slices(None)
+    torch.cuda.synchronize()
+    reps = 3
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(main_stream)
+    for _ in range(reps):
         compute_slices(None)
-        torch.cuda.synchronize()
-        reps = 3
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record(main_stream)
-        for _ in range(reps):
-            compute_slices(None)
-        t1.record(main_stream)
-        torch.cuda.synchronize()
-        t_comp = t0.elapsed_time(t1) / reps
+    t1.record(main_stream)
+    torch.cuda.synchronize()
+    t_comp = t0.elapsed_time(t1) / reps
+    compute_slices(evs)
+    plan.execute(bufs, events=evs, stream=main_stream)
+    torch.cuda.synchronize()
+    t0.record(main_stream)
+    for _ in range(reps):
         compute_slices(evs)
         plan.execute(bufs, events=evs, stream=main_stream)
-        torch.cuda.synchronize()
-        t0.record(main_stream)
-        for _ in range(reps):
-            compute_slices(evs)
-            plan.execute(bufs, events=evs, stream=main_stream)
-        t1.record(main_stream)
-        torch.cuda.synchronize()
-        t_both = t0.elapsed_time(t1) / reps
-        comp_bytes = 2 * 4 * comp_elems
-        out["overlap"] = {
-            "t_allreduce_ms": round(fused_ms, 3), "t_compute_ms": round(t_comp, 3),
-            "t_both_ms": round(t_both, 3),
-            "overlap_efficiency": round((fused_ms + t_comp - t_both) / min(fused_ms, t_comp), 3),
-            "combined_hbm_GBps": round((fused_bytes + comp_bytes) / (t_both * 1e-3) / 1e9, 1),
-            "compute_bytes": comp_bytes,
-        }
-        plan.destroy()
-        del scratch
-        torch.cuda.empty_cache()
-        log(f"bench: overlap {out['overlap']}")
-
-    out["sgd"] = sgd_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_ms)
-    out["typed"] = typed_leg(main_stream, torch, ddl, synth)
-    out["per_gpu_step"] = per_gpu_step_leg(w, main_stream, torch, ddl)
-    return out
+    t1.record(main_stream)
+    torch.cuda.synchronize()
+    t_both = t0.elapsed_time(t1) / reps
+    comp_bytes = 2 * 4 * comp_elems
+    res = {
+        "t_allreduce_ms": round(fused_ms, 3), "t_compute_ms": round(t_comp, 3),
+        "t_both_ms": round(t_both, 3),
+        "overlap_efficiency": round((fused_ms + t_comp - t_both) / min(fused_ms, t_comp), 3),
+        "combined_hbm_GBps": round((fused_bytes + comp_bytes) / (t_both * 1e-3) / 1e9, 1),
+        "compute_bytes": comp_bytes,
+    }
+    plan.destroy()
+    del scratch
+    torch.cuda.empty_cache()
+    log(f"bench: overlap {res}")
+    return res
 
 
 def per_gpu_step_leg(w, main_stream, torch, ddl):
@@ -504,6 +528,77 @@ def sgd_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_ms):
     del weights
     torch.cuda.empty_cache()
     log(f"bench: sgd {res}")
+    return res
+
+
+def lars_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_ms):
+    """The LARS step after the all-reduce (every bucket a layer; the Sony
+    article's coefficient 0.01 and eps 1e-6), one weight replica per rank
+    (one shared replica when HBM is short): the whole step's time, and each
+    LARS kernel's average launch against its algorithmic bytes, from one
+    profiled step."""
+    lr = 0.01
+    esz = 4 if w.dtype == "f32" else 2
+    free = torch.cuda.mem_get_info()[0]
+    nrep = w.P if w.P * w.n * 4 < 0.8 * free else 1
+    weights = [torch.empty(w.n, dtype=torch.float32, device="cuda") for _ in range(nrep)]
+    for t in weights:
+        synth.fill_device(t.data_ptr(), w.n, synth.F32, "uniform", 77, 0)
+    rates = torch.zeros(len(buckets), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event() for _ in buckets] if w.side_stream else None
+    plan = ddl.Plan(w.P, w.n, w.dtype, w.op, topo, buckets, "fused")
+    _, ar_bytes = plan.traffic()
+
+    def one():
+        if evs:
+            for e in evs:
+                e.record(main_stream)
+        plan.execute_lars(bufs, weights, lr, rates_out=rates, events=evs, stream=main_stream)
+
+    one()
+    torch.cuda.synchronize()
+    reps = 3
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(main_stream)
+    for _ in range(reps):
+        one()
+    t1.record(main_stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    # algorithmic bytes: the all-reduce; the norms read y and w_0 (s + 4 per
+    # element); the update reads y and reads and writes every replica
+    # (s + 8 nrep); the rates read 16 bytes per tile
+    norm_b, upd_b = (esz + 4) * w.n, (esz + 8 * nrep) * w.n
+    nbytes = ar_bytes + norm_b + upd_b
+    plan.set_profiling(True)
+    plan.profile_read_kinds()
+    one()
+    torch.cuda.synchronize()
+    kinds = plan.profile_read_kinds()
+    plan.destroy()
+    res = {"replicas": nrep, "lr": lr, "coeff": ddl.LARS_COEFF, "eps": ddl.LARS_EPS,
+           "layers": len(buckets), "ms": round(ms, 3),
+           "hbm_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes": nbytes,
+           "over_allreduce_ms": round(ms - fused_ms, 3)}
+    for kind, total_b in (("lars_norm", norm_b), ("lars_update", upd_b)):
+        tot, cnt, mx = kinds[kind]
+        if cnt:
+            nb = total_b / cnt
+            res[kind + "_kernel"] = {"launches_per_step": cnt,
+                                     "avg_launch_us": round(tot / cnt * 1e3, 2),
+                                     "max_launch_us": round(mx * 1e3, 2),
+                                     "algorithmic_bytes_per_launch": int(nb),
+                                     "GBps": round(nb / (tot / cnt * 1e-3) / 1e9, 1)}
+    tot, cnt, _ = kinds["lars_rate"]
+    if cnt:
+        res["lars_rate_kernel"] = {"launches_per_step": cnt,
+                                   "avg_launch_us": round(tot / cnt * 1e3, 2)}
+    r = rates.cpu()
+    res["rate_range"] = [float(r.min()), float(r.max())]
+    del weights
+    torch.cuda.empty_cache()
+    log(f"bench: lars {res}")
     return res
 
 

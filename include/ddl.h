@@ -296,7 +296,13 @@ typedef enum {
      * MI355X), which fetches the tile's values into that die's L2 once;
      * 0 or 1 = plain order (default) */
     DDL_TUNE_BCAST_XCD = 7,
-    DDL_TUNE_COUNT = 8
+    /* LARS update: weight replicas each workgroup steps (default 2); 0 =
+     * all of them in one workgroup */
+    DDL_TUNE_LARS_REPS = 8,
+    /* LARS update: replicas whose loads each lane issues before their stores
+     * (1, 2, 4 or 8; default 4) */
+    DDL_TUNE_LARS_BATCH = 9,
+    DDL_TUNE_COUNT = 10
 } ddl_tune_knob;
 int ddl_set_tuning(int knob, int value);
 int ddl_get_tuning(int knob, int *value);

@@ -178,7 +178,8 @@ def ddl_cache_clear():
 
 
 TUNE = {"bcast_ranks": 0, "reduce_nt_load": 1, "fused_nt_load_max_p": 2, "anchor": 3,
-        "fused_batch": 4, "reduce_batch": 5, "bcast_tiles": 6, "bcast_xcd": 7}
+        "fused_batch": 4, "reduce_batch": 5, "bcast_tiles": 6, "bcast_xcd": 7,
+        "lars_reps": 8, "lars_batch": 9}
 
 
 def set_tuning(knob, value):

@@ -175,6 +175,8 @@ struct LarsArgs {
     float *rate_out;               // null, or the caller's copy of rate
     float lr;
     int nweights;
+    int reps_per_group;            // update: replicas each workgroup steps
+    int ngroups;                   // update: workgroups per tile
     double coeff, eps;
 };
 

@@ -41,6 +41,8 @@ constexpr int kTuneDefault[] = {
     4,   // DDL_TUNE_REDUCE_BATCH
     1,   // DDL_TUNE_BCAST_TILES
     0,   // DDL_TUNE_BCAST_XCD: off
+    2,   // DDL_TUNE_LARS_REPS
+    4,   // DDL_TUNE_LARS_BATCH
 };
 static_assert(sizeof(kTuneDefault) / sizeof(kTuneDefault[0]) == DDL_TUNE_COUNT,
               "one default per knob");
@@ -437,6 +439,12 @@ struct Launcher {
         a.rate_out = lars->rates_out;
         a.lr = lars->lr;
         a.nweights = lars->nweights;
+        // replicas per update workgroup: measured on MI355X, 40 replicas x
+        // 18.75 MB buckets, paired: 2 per workgroup 279 us per launch, 1
+        // 287, 4 297, 8 291, all 40 302 (load batch 1-8 within 1% at 2)
+        const int g = tuning(DDL_TUNE_LARS_REPS);
+        a.reps_per_group = g > 0 ? std::min(g, lars->nweights) : lars->nweights;
+        a.ngroups = (lars->nweights + a.reps_per_group - 1) / a.reps_per_group;
         a.coeff = lars->coeff;
         a.eps = lars->eps;
         a.bucket_lo = (uint32_t)b0;

@@ -146,6 +146,23 @@ def test_lars_events_two_calls_and_zero_layers(mode, passes):
     assert got[1] == np.float32(0.2) and got[3] == np.float32(0.2)
 
 
+@pytest.fixture
+def restore_knobs():
+    yield
+    for k in ("lars_reps", "lars_batch"):
+        ddl.set_tuning(k, -1)
+
+
+@pytest.mark.parametrize("knob,value", [("lars_reps", g) for g in (0, 1, 3, 7, 100)] +
+                         [("lars_batch", b) for b in (1, 2, 8)], ids=lambda v: str(v))
+def test_lars_knobs(knob, value, restore_knobs):
+    # the update's replica split and load batch change launch shapes only
+    ddl.set_tuning(knob, value)
+    for w in (CASES[2], CASES[5]):
+        say(f"case lars knob {knob}={value} {w.name}")
+        run_case(w, "fused", 0, False)
+
+
 def test_lars_page_constants_closed_form():
     # every rank holds 2^-10 (64 elements per rank, 4 ranks, mean): y = 2^-10
     # exactly, ||y|| = 2^-7; weights 1.5: ||w|| = 12.  With the page's
