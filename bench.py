@@ -581,7 +581,7 @@ def lars_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_ms):
            "layers": len(buckets), "ms": round(ms, 3),
            "hbm_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes": nbytes,
            "over_allreduce_ms": round(ms - fused_ms, 3)}
-    for kind, total_b in (("lars_norm", norm_b), ("lars_update", upd_b)):
+    for kind, total_b in (("lars_norm", norm_b), ("update", upd_b)):
         tot, cnt, mx = kinds[kind]
         if cnt:
             nb = total_b / cnt

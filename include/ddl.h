@@ -171,8 +171,10 @@ int ddl_plan_execute(ddl_plan plan, void *const *bufs, void *const *ready_events
  *              leaves them.  0 (DDL_FUSED plans only): bufs are left as they
  *              were -- the reduced gradient is consumed by the update and
  *              never written, saving P writes per element.
- * In DDL_STEPWISE plans the owner of each chunk updates at the add that
- * completes the sum and every other rank when the all-gather delivers it.
+ * In DDL_FUSED plans the update rides in the one-kernel pass's epilogue, or
+ * follows the two-kernel pass (ddl_plan_set_fused_passes).  In DDL_STEPWISE
+ * plans the owner of each chunk updates at the add that completes the sum and
+ * every other rank when the all-gather delivers it.
  * Other arguments and the asynchrony are those of ddl_plan_execute.
  * DDL_E_ARG for any other nweights, or keep_grads == 0 on a stepwise plan. */
 int ddl_plan_execute_sgd(ddl_plan plan, void *const *bufs, void *const *weights, int nweights,
@@ -252,12 +254,16 @@ int ddl_plan_set_coalesce_bytes(ddl_plan plan, size_t bytes);
  * under 4 MB per rank (short launches whose ramps overlap), else 1. */
 int ddl_plan_set_side_streams(ddl_plan plan, int n);
 
-/* Form of a fused plan's pass (fused mode only; the SGD variant always uses
- * the first).  passes = 1: one kernel reads every rank and writes every rank.
- * passes = 2: a reduce kernel reads every rank and writes the result to rank
- * 0, then a broadcast kernel copies it from rank 0 to ranks 1..P-1 while it
- * is still in the device caches, so HBM serves a read phase and then a write
- * phase.  passes = 0 (default): automatic, two kernels from 16 ranks on.
+/* Form of a fused plan's pass (fused mode only).  passes = 1: one kernel
+ * reads every rank and writes every rank (with the SGD step, it also updates
+ * the weights).  passes = 2: a reduce kernel reads every rank and writes the
+ * result to rank 0, then a broadcast kernel copies it from rank 0 to ranks
+ * 1..P-1 while it is still in the device caches, so HBM serves a read phase
+ * and then a write phase; with the SGD step an update kernel then steps the
+ * weights from rank 0's result (without kept gradients the reduce kernel
+ * writes to a scratch buffer of n elements instead, allocated by the first
+ * such call, and nothing is broadcast).  passes = 0 (default): automatic,
+ * two kernels from 16 ranks on.
  * The results are bit-identical either way; only the speed differs.
  * Returns DDL_E_ARG for other values.  Takes effect at the next execute.
  * ddl_plan_get_fused_passes reports the form the next plain execute uses
@@ -296,12 +302,13 @@ typedef enum {
      * MI355X), which fetches the tile's values into that die's L2 once;
      * 0 or 1 = plain order (default) */
     DDL_TUNE_BCAST_XCD = 7,
-    /* LARS update: weight replicas each workgroup steps (default 2); 0 =
-     * all of them in one workgroup */
-    DDL_TUNE_LARS_REPS = 8,
-    /* LARS update: replicas whose loads each lane issues before their stores
-     * (1, 2, 4 or 8; default 4) */
-    DDL_TUNE_LARS_BATCH = 9,
+    /* update kernel (the LARS step, and the SGD step of the two-kernel
+     * form): weight replicas each workgroup steps (default 2); 0 = all of
+     * them in one workgroup */
+    DDL_TUNE_UPDATE_REPS = 8,
+    /* update kernel: replicas whose loads each lane issues before their
+     * stores (1, 2, 4 or 8; default 4) */
+    DDL_TUNE_UPDATE_BATCH = 9,
     DDL_TUNE_COUNT = 10
 } ddl_tune_knob;
 int ddl_set_tuning(int knob, int value);
@@ -322,8 +329,9 @@ int ddl_plan_profile_read_kinds(ddl_plan plan, double *total_ms, int *launches,
 
 /* ---- schedule introspection (host-only; used by the tests) ------------- */
 /* Kernel launches: a reduce-scatter step, an all-gather step, the one-kernel
- * fused pass, the two kernels of the two-kernel fused pass, and the three
- * kernels of the LARS step (norms, rates, update). */
+ * fused pass, the two kernels of the two-kernel fused pass, the LARS step's
+ * norms and rates, and the weight update (of the LARS step, and of the SGD
+ * step in the two-kernel form). */
 typedef enum {
     DDL_K_REDUCE = 0,
     DDL_K_GATHER = 1,
@@ -332,7 +340,7 @@ typedef enum {
     DDL_K_BROADCAST = 4,
     DDL_K_LARS_NORM = 5,
     DDL_K_LARS_RATE = 6,
-    DDL_K_LARS_UPDATE = 7,
+    DDL_K_UPDATE = 7,
     DDL_K_COUNT = 8
 } ddl_launch_kind;
 

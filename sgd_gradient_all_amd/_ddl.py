@@ -11,10 +11,10 @@ DDL_SUM, DDL_MEAN = 0, 1
 DDL_RING, DDL_MULTIRING, DDL_TORUS2D = 0, 1, 2
 DDL_STEPWISE, DDL_FUSED = 0, 1
 DDL_K_REDUCE, DDL_K_GATHER, DDL_K_FUSED, DDL_K_FUSED_REDUCE, DDL_K_BROADCAST = 0, 1, 2, 3, 4
-DDL_K_LARS_NORM, DDL_K_LARS_RATE, DDL_K_LARS_UPDATE = 5, 6, 7
+DDL_K_LARS_NORM, DDL_K_LARS_RATE, DDL_K_UPDATE = 5, 6, 7
 DDL_K_COUNT = 8
 LAUNCH_KINDS = ("reduce", "gather", "fused", "fused_reduce", "broadcast", "lars_norm",
-                "lars_rate", "lars_update")
+                "lars_rate", "update")
 # LARS as the Sony ResNet-50 article trains with it: coefficient and eps
 LARS_COEFF, LARS_EPS = 0.01, 1e-6
 
@@ -179,7 +179,7 @@ def ddl_cache_clear():
 
 TUNE = {"bcast_ranks": 0, "reduce_nt_load": 1, "fused_nt_load_max_p": 2, "anchor": 3,
         "fused_batch": 4, "reduce_batch": 5, "bcast_tiles": 6, "bcast_xcd": 7,
-        "lars_reps": 8, "lars_batch": 9}
+        "update_reps": 8, "update_batch": 9}
 
 
 def set_tuning(knob, value):

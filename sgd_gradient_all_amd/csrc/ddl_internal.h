@@ -122,6 +122,8 @@ struct FusedArgs {
     int mean;        // divide by P at the end
     float divisor;
     int anchor;      // tiles anchored at multiples of the tile size
+    void *home;      // reduce kernel: where the result goes (rank 0's buffer,
+                     // or a scratch buffer of n elements)
 };
 
 // Arguments of one broadcast launch (second kernel of the two-kernel fused
@@ -171,7 +173,8 @@ struct LarsArgs {
     uint32_t tile_base, tile_end;  // norm and update launches: these tiles
     uint32_t bucket_lo, bucket_hi; // rate launch: these buckets
     double *partial;               // [2t], [2t+1]: sums of w_0^2 and y^2 over tile t
-    float *rate;                   // [i] the rate of bucket i
+    float *rate;                   // [i] the rate of bucket i; null: lr for all
+                                   // (the plain SGD step)
     float *rate_out;               // null, or the caller's copy of rate
     float lr;
     int nweights;
@@ -190,7 +193,7 @@ int launch_step(int dtype, int kind, int vpl, const RankPtrs &bufs, const StepAr
 int launch_fused(int dtype, const RankPtrs &bufs, const FusedArgs &a, const SgdArgs *sgd,
                  bool home, uint32_t tiles, void *stream);
 int launch_bcast(int dtype, const RankPtrs &bufs, const BcastArgs &a, void *stream);
-// kind: DDL_K_LARS_NORM or DDL_K_LARS_UPDATE (blocks = tiles from
+// kind: DDL_K_LARS_NORM or DDL_K_UPDATE (blocks = tiles from
 // a.tile_base), DDL_K_LARS_RATE (blocks = buckets from a.bucket_lo).
 int launch_lars(int dtype, int kind, const RankPtrs &w, const LarsArgs &a, uint32_t blocks,
                 void *stream);

@@ -10,9 +10,10 @@
 //  - one kernel (fused_kernel): each workgroup reads its tile from all P
 //    ranks and writes the result to all P ranks;
 //  - two kernels over the same tiles: fused_reduce_kernel reads all P ranks
-//    and writes the result to rank 0 only, through the cache; then
-//    bcast_kernel copies rank 0's result, still cache-resident, to ranks
-//    1..P-1.  HBM then sees a read phase and a write phase instead of reads
+//    and writes the result to rank 0 only (or, for an SGD step that leaves
+//    the gradients as they were, to a scratch buffer), through the cache;
+//    then bcast_kernel copies rank 0's result, still cache-resident, to
+//    ranks 1..P-1.  HBM then sees a read phase and a write phase instead of reads
 //    and writes interleaved.  Measured on MI355X in paired runs: 40 ranks
 //    binary32 +5..+18% (the spread is the physical placement of the
 //    buffers, to which the two-kernel form is far less sensitive), 16 ranks
@@ -169,23 +170,25 @@ __device__ __forceinline__ void sgd_all(const SgdArgs *g, uint64_t e,
         }
 }
 
-// Stores of the reduced vectors v[0..U) of element e to rank 0 only, with
-// ordinary (cached) stores: the broadcast kernel that follows re-reads them.
+// Stores of the reduced vectors v[0..U) of element e to the home buffer
+// only (rank 0's, or a scratch buffer when the gradients must stay as they
+// were), with ordinary (cached) stores: the kernel that follows re-reads
+// them.
 template <class E, int U>
-__device__ __forceinline__ void store_home(const RankPtrs &bufs, uint64_t e,
+__device__ __forceinline__ void store_home(void *home, uint64_t e,
                                            const typename E::V (&v)[U]) {
     using T = typename E::T;
     using V = typename E::V;
     constexpr uint64_t kStride = (uint64_t)kBlock * E::N;
     V DDL_GLOBAL *h = reinterpret_cast<V DDL_GLOBAL *>(
-        reinterpret_cast<uint64_t>(bufs.p[0]) + e * sizeof(T));
+        reinterpret_cast<uint64_t>(home) + e * sizeof(T));
 #pragma unroll
     for (int u = 0; u < U; ++u)
         h[u * (kStride / E::N)] = v[u];
 }
 
-// kHome: write the result to rank 0 only (the first kernel of the two-kernel
-// form); otherwise to every rank.
+// kHome: write the result to the home buffer only (the first kernel of the
+// two-kernel form); otherwise to every rank.
 template <class E, bool kGrouped, bool kNt, bool kSgd, bool kHome, int kB>
 __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs &a,
                                            const SgdArgs *g) {
@@ -227,7 +230,7 @@ __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs
                     for (int u = 0; u < U; ++u)
                         acc[u] = E::div(acc[u], a.divisor);
                 if (kHome)
-                    store_home<E, U>(bufs, e, acc);
+                    store_home<E, U>(a.home, e, acc);
                 else if (!kSgd || g->keep_grads)
                     store_all<E, U>(bufs, P, e, acc);
                 if (kSgd)
@@ -240,7 +243,7 @@ __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs
                     if (a.mean)
                         acc[0] = E::div(acc[0], a.divisor);
                     if (kHome)
-                        store_home<E, 1>(bufs, e, acc);
+                        store_home<E, 1>(a.home, e, acc);
                     else if (!kSgd || g->keep_grads)
                         store_all<E, 1>(bufs, P, e, acc);
                     if (kSgd)
@@ -266,7 +269,7 @@ __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs
             if (a.mean)
                 acc = E::div1(acc, a.divisor);
             if (kHome)
-                static_cast<T *>(bufs.p[0])[e] = acc;
+                static_cast<T *>(a.home)[e] = acc;
             else if (!kSgd || g->keep_grads)
                 for (int r = 0; r < P; ++r)
                     static_cast<T *>(bufs.p[r])[e] = acc;

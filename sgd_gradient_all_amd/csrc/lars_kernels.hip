@@ -18,7 +18,7 @@
 //    the two partial sums of the tile;
 //  - lars_rate_kernel: one workgroup per bucket adds its tiles' partials
 //    and writes rate = binary32(lr * trust), trust in binary64;
-//  - lars_update_kernel: each tile takes ceil(nweights / G) workgroups, each
+//  - update_kernel: each tile takes ceil(nweights / G) workgroups, each
 //    loading y and stepping G replicas with the bucket's rate (G = 2 by
 //    default: measured on MI355X with 40 replicas, 8% faster than one
 //    workgroup stepping all of them; the extra loads of y hit the cache).
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(kBlock) void lars_rate_kernel(LarsArgs a) {
 // stores, so a wave keeps kRB requests in flight.
 // ---------------------------------------------------------------------------
 template <class E, int kRB>
-__global__ __launch_bounds__(kBlock) void lars_update_kernel(RankPtrs w, LarsArgs a) {
+__global__ __launch_bounds__(kBlock) void update_kernel(RankPtrs w, LarsArgs a) {
     using T = typename E::T;
     using V = typename E::V;
     using Wv = typename E::W;
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(kBlock) void lars_update_kernel(RankPtrs w, LarsArg
     const int rb = (int)(blockIdx.x % ng) * a.reps_per_group;
     const int nw = min(a.nweights, rb + a.reps_per_group);
     const TileRange tr = tile_range<sizeof(T)>(a, t);
-    const float rate = a.rate[tr.bucket];
+    const float rate = a.rate ? a.rate[tr.bucket] : a.lr;
     const T *y = static_cast<const T *>(a.y);
     const uint32_t tid = threadIdx.x;
     uint32_t done = 0;
@@ -254,10 +254,10 @@ template <class E>
 void launch_update(dim3 grid, hipStream_t s, const RankPtrs &w, const LarsArgs &a, int batch) {
     const dim3 block(kBlock);
     switch (batch) {
-    case 1: hipLaunchKernelGGL((lars_update_kernel<E, 1>), grid, block, 0, s, w, a); break;
-    case 2: hipLaunchKernelGGL((lars_update_kernel<E, 2>), grid, block, 0, s, w, a); break;
-    case 8: hipLaunchKernelGGL((lars_update_kernel<E, 8>), grid, block, 0, s, w, a); break;
-    default: hipLaunchKernelGGL((lars_update_kernel<E, 4>), grid, block, 0, s, w, a); break;
+    case 1: hipLaunchKernelGGL((update_kernel<E, 1>), grid, block, 0, s, w, a); break;
+    case 2: hipLaunchKernelGGL((update_kernel<E, 2>), grid, block, 0, s, w, a); break;
+    case 8: hipLaunchKernelGGL((update_kernel<E, 8>), grid, block, 0, s, w, a); break;
+    default: hipLaunchKernelGGL((update_kernel<E, 4>), grid, block, 0, s, w, a); break;
     }
 }
 
@@ -279,16 +279,16 @@ int launch_lars(int dtype, int kind, const RankPtrs &w, const LarsArgs &a, uint3
     case DDL_K_LARS_RATE:
         hipLaunchKernelGGL(lars_rate_kernel, grid, block, 0, s, a);
         break;
-    case DDL_K_LARS_UPDATE: {
+    case DDL_K_UPDATE: {
         // blocks counts tiles; every tile takes ngroups workgroups
         if (a.ngroups < 1 || a.reps_per_group < 1 ||
             (uint64_t)blocks * (uint64_t)a.ngroups * kBlock > 0xffffffffull)
             return (int)hipErrorInvalidValue;
         const dim3 ugrid(blocks * (uint32_t)a.ngroups);
         if (dtype == DDL_F32)
-            launch_update<F32>(ugrid, s, w, a, tuning(DDL_TUNE_LARS_BATCH));
+            launch_update<F32>(ugrid, s, w, a, tuning(DDL_TUNE_UPDATE_BATCH));
         else
-            launch_update<F16>(ugrid, s, w, a, tuning(DDL_TUNE_LARS_BATCH));
+            launch_update<F16>(ugrid, s, w, a, tuning(DDL_TUNE_UPDATE_BATCH));
         break;
     }
     default:

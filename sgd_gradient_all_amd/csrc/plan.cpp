@@ -41,8 +41,8 @@ constexpr int kTuneDefault[] = {
     4,   // DDL_TUNE_REDUCE_BATCH
     1,   // DDL_TUNE_BCAST_TILES
     0,   // DDL_TUNE_BCAST_XCD: off
-    2,   // DDL_TUNE_LARS_REPS
-    4,   // DDL_TUNE_LARS_BATCH
+    2,   // DDL_TUNE_UPDATE_REPS
+    4,   // DDL_TUNE_UPDATE_BATCH
 };
 static_assert(sizeof(kTuneDefault) / sizeof(kTuneDefault[0]) == DDL_TUNE_COUNT,
               "one default per knob");
@@ -74,6 +74,8 @@ struct Part {
     uint32_t *d_bk_of_tile = nullptr;
     double *d_lars_partial = nullptr;  // LARS: two sums per bucket-table tile
     float *d_lars_rate = nullptr;      // LARS: one rate per bucket
+    void *d_sgd_home = nullptr;        // SGD without kept gradients, two-kernel
+                                       // form: the reduced values (n elements)
 };
 
 struct ddl_plan_s {
@@ -137,6 +139,7 @@ void release_device(ddl_plan p) {
         (void)hipFree(pt.d_bk_of_tile);
         (void)hipFree(pt.d_lars_partial);
         (void)hipFree(pt.d_lars_rate);
+        (void)hipFree(pt.d_sgd_home);
         pt = Part{std::move(pt.s)};
     }
     for (hipEvent_t e : p->prof)
@@ -208,10 +211,14 @@ constexpr uint32_t kMaxTilesPerLaunch = 1u << 23;
 // and a broadcast kernel (see fused_kernel.hip).  Automatic: two kernels
 // from 16 ranks on, where they measured faster on MI355X (paired, six
 // repeats): 40 ranks fp32 +5..+18%, 16 ranks fp32 ResNet-50 multi-ring
-// +7.3%, 16 ranks fp16 torus +5.8%; 8 ranks -3%.  The SGD variant always
-// takes one kernel.
+// +7.3%, 16 ranks fp16 torus +5.8%; 8 ranks -3%.  With the SGD step, the
+// one-kernel form updates the weights in its epilogue; the two-kernel form
+// reduces (to rank 0, or to a scratch buffer when the gradients are not
+// kept), broadcasts (when they are), then runs the update kernel with the
+// constant rate lr.
 int fused_passes(ddl_plan p, const Schedule &s, bool sgd) {
-    if (sgd || s.P < 2)
+    (void)sgd;
+    if (s.P < 2)
         return 1;
     if (p->fused_passes)
         return p->fused_passes;
@@ -325,7 +332,7 @@ struct Launcher {
 
     // the fused pass of buckets [b0, b1): one kernel, or the reduce kernel
     // over their spans and then the broadcast over the runs of memory they
-    // cover
+    // cover (and, with the SGD step, the update kernel)
     int fused(int b0, int b1) {
         const Schedule &s = pt->s;
         const uint32_t lo = s.span_at[b0], hi = s.span_at[b1];
@@ -345,6 +352,10 @@ struct Launcher {
         a.divisor = (float)s.P;
         a.anchor = s.fused_anchor;
         const bool two = fused_passes(p, s, sgd != nullptr) == 2;
+        // two-kernel SGD without kept gradients: the results go to the
+        // plan's scratch buffer, and the gradient buffers stay as they were
+        const bool scratch = two && sgd && !sgd->keep_grads;
+        a.home = scratch ? pt->d_sgd_home : bufs.p[0];
         for (uint32_t t = pre[lo]; t < pre[hi]; t += kMaxTilesPerLaunch) {
             const uint32_t tiles = std::min(kMaxTilesPerLaunch, pre[hi] - t);
             a.tile_base = t;
@@ -352,13 +363,23 @@ struct Launcher {
             int rc = bracket_begin(two ? DDL_K_FUSED_REDUCE : DDL_K_FUSED);
             if (rc)
                 return rc;
-            if (launch_fused(s.dtype, bufs, a, sgd, two, tiles, stream) != hipSuccess)
+            if (launch_fused(s.dtype, bufs, a, two ? nullptr : sgd, two, tiles, stream) !=
+                hipSuccess)
                 return DDL_E_HIP;
             if ((rc = bracket_end()))
                 return rc;
         }
         if (!two)
             return DDL_OK;
+        int rc = scratch ? DDL_OK : broadcast(b0, b1);
+        if (rc || !sgd)
+            return rc;
+        return update(b0, b1, a.home, nullptr, sgd->lr, sgd->w, sgd->nweights);
+    }
+
+    // the broadcast of buckets [b0, b1) from rank 0 to ranks 1..P-1
+    int broadcast(int b0, int b1) {
+        const Schedule &s = pt->s;
         runs.clear();
         for (int b = b0; b < b1; ++b)
             if (s.buckets[b].len)
@@ -424,57 +445,72 @@ struct Launcher {
         return DDL_OK;
     }
 
-    // the LARS step of buckets [b0, b1), once their all-reduce is enqueued:
-    // the norms of every tile, the rate of every bucket, the update
-    int lars_step(int b0, int b1) {
-        const Schedule &s = pt->s;
+    // Arguments of the update and LARS kernels over buckets [b0, b1): y the
+    // reduced values, rate null for the constant rate lr
+    LarsArgs update_args(int b0, int b1, const void *y, float *rate, float lr, int nweights) {
         LarsArgs a;
         std::memset(&a, 0, sizeof(a));
         a.spans = pt->d_bk_spans;
         a.prefix = pt->d_bk_prefix;
         a.tile_span = pt->d_bk_of_tile;
-        a.y = bufs.p[0];
-        a.partial = pt->d_lars_partial;
-        a.rate = pt->d_lars_rate;
-        a.rate_out = lars->rates_out;
-        a.lr = lars->lr;
-        a.nweights = lars->nweights;
+        a.y = y;
+        a.rate = rate;
+        a.lr = lr;
+        a.nweights = nweights;
         // replicas per update workgroup: measured on MI355X, 40 replicas x
         // 18.75 MB buckets, paired: 2 per workgroup 279 us per launch, 1
         // 287, 4 297, 8 291, all 40 302 (load batch 1-8 within 1% at 2)
-        const int g = tuning(DDL_TUNE_LARS_REPS);
-        a.reps_per_group = g > 0 ? std::min(g, lars->nweights) : lars->nweights;
-        a.ngroups = (lars->nweights + a.reps_per_group - 1) / a.reps_per_group;
-        a.coeff = lars->coeff;
-        a.eps = lars->eps;
+        const int g = tuning(DDL_TUNE_UPDATE_REPS);
+        a.reps_per_group = g > 0 ? std::min(g, nweights) : nweights;
+        a.ngroups = (nweights + a.reps_per_group - 1) / a.reps_per_group;
         a.bucket_lo = (uint32_t)b0;
         a.bucket_hi = (uint32_t)b1;
-        const uint32_t *bp = s.bk_prefix.data();
-        auto tiles = [&](int kind) {
-            for (uint32_t t = bp[b0]; t < bp[b1]; t += kMaxTilesPerLaunch) {
-                a.tile_base = t;
-                a.tile_end = std::min(bp[b1], t + kMaxTilesPerLaunch);
-                int rc = bracket_begin(kind);
-                if (rc)
-                    return rc;
-                if (launch_lars(s.dtype, kind, lars->w, a, a.tile_end - t, stream) != hipSuccess)
-                    return (int)DDL_E_HIP;
-                if ((rc = bracket_end()))
-                    return rc;
-            }
-            return (int)DDL_OK;
-        };
-        int rc = tiles(DDL_K_LARS_NORM);
+        return a;
+    }
+
+    // one launch kind over the bucket-table tiles of buckets [b0, b1)
+    int table_tiles(int kind, int b0, int b1, LarsArgs &a, const RankPtrs &w) {
+        const uint32_t *bp = pt->s.bk_prefix.data();
+        for (uint32_t t = bp[b0]; t < bp[b1]; t += kMaxTilesPerLaunch) {
+            a.tile_base = t;
+            a.tile_end = std::min(bp[b1], t + kMaxTilesPerLaunch);
+            int rc = bracket_begin(kind);
+            if (rc)
+                return rc;
+            if (launch_lars(pt->s.dtype, kind, w, a, a.tile_end - t, stream) != hipSuccess)
+                return DDL_E_HIP;
+            if ((rc = bracket_end()))
+                return rc;
+        }
+        return DDL_OK;
+    }
+
+    // w = w - rate * y on every replica over buckets [b0, b1)
+    int update(int b0, int b1, const void *y, float *rate, float lr, const RankPtrs &w,
+               int nweights) {
+        LarsArgs a = update_args(b0, b1, y, rate, lr, nweights);
+        return table_tiles(DDL_K_UPDATE, b0, b1, a, w);
+    }
+
+    // the LARS step of buckets [b0, b1), once their all-reduce is enqueued:
+    // the norms of every tile, the rate of every bucket, the update
+    int lars_step(int b0, int b1) {
+        LarsArgs a = update_args(b0, b1, bufs.p[0], pt->d_lars_rate, lars->lr, lars->nweights);
+        a.partial = pt->d_lars_partial;
+        a.rate_out = lars->rates_out;
+        a.coeff = lars->coeff;
+        a.eps = lars->eps;
+        int rc = table_tiles(DDL_K_LARS_NORM, b0, b1, a, lars->w);
         if (rc || b1 == b0)
             return rc;
         if ((rc = bracket_begin(DDL_K_LARS_RATE)))
             return rc;
-        if (launch_lars(s.dtype, DDL_K_LARS_RATE, lars->w, a, (uint32_t)(b1 - b0), stream) !=
+        if (launch_lars(pt->s.dtype, DDL_K_LARS_RATE, lars->w, a, (uint32_t)(b1 - b0), stream) !=
             hipSuccess)
             return DDL_E_HIP;
         if ((rc = bracket_end()))
             return rc;
-        return tiles(DDL_K_LARS_UPDATE);
+        return table_tiles(DDL_K_UPDATE, b0, b1, a, lars->w);
     }
 
     // every launch of buckets [b0, b1)
@@ -492,6 +528,18 @@ struct Launcher {
         return lars_step(b0, b1);
     }
 };
+
+// The scratch buffer of two-kernel SGD without kept gradients (n elements
+// per part), allocated by the first such call.
+int ensure_sgd_home(ddl_plan p) {
+    for (Part &pt : p->parts) {
+        if (pt.d_sgd_home || pt.s.n == 0)
+            continue;
+        if (hipMalloc(&pt.d_sgd_home, (size_t)pt.s.n * (size_t)pt.s.esz) != hipSuccess)
+            return DDL_E_NOMEM;
+    }
+    return DDL_OK;
+}
 
 // Device memory of the LARS step, allocated by a plan's first LARS call.
 int ensure_lars(ddl_plan p) {
@@ -546,6 +594,12 @@ int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stre
     }
     if (lars) {
         int rc = ensure_lars(p);
+        if (rc)
+            return rc;
+    }
+    if (sgd && !sgd->keep_grads && p->mode == DDL_FUSED &&
+        fused_passes(p, p->parts[0].s, true) == 2) {
+        int rc = ensure_sgd_home(p);
         if (rc)
             return rc;
     }

@@ -149,12 +149,12 @@ def test_lars_events_two_calls_and_zero_layers(mode, passes):
 @pytest.fixture
 def restore_knobs():
     yield
-    for k in ("lars_reps", "lars_batch"):
+    for k in ("update_reps", "update_batch"):
         ddl.set_tuning(k, -1)
 
 
-@pytest.mark.parametrize("knob,value", [("lars_reps", g) for g in (0, 1, 3, 7, 100)] +
-                         [("lars_batch", b) for b in (1, 2, 8)], ids=lambda v: str(v))
+@pytest.mark.parametrize("knob,value", [("update_reps", g) for g in (0, 1, 3, 7, 100)] +
+                         [("update_batch", b) for b in (1, 2, 8)], ids=lambda v: str(v))
 def test_lars_knobs(knob, value, restore_knobs):
     # the update's replica split and load batch change launch shapes only
     ddl.set_tuning(knob, value)

@@ -44,10 +44,15 @@ def expected(w, weights0, lr):
 
 
 @pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
-@pytest.mark.parametrize("mode,keep", [("fused", True), ("fused", False), ("stepwise", True)])
+@pytest.mark.parametrize("mode,keep,passes", [("fused", True, 1), ("fused", False, 1),
+                                              ("fused", True, 2), ("fused", False, 2),
+                                              ("stepwise", True, 0)], ids=lambda v: str(v))
 @pytest.mark.parametrize("shared", [False, True])
-def test_sgd_bitwise(w, mode, keep, shared):
-    say(f"case sgd {w.name} mode={mode} keep={keep} shared={shared}")
+def test_sgd_bitwise(w, mode, keep, passes, shared):
+    # passes 1: the update in the one-kernel pass's epilogue; 2: reduce
+    # (to rank 0, or to the plan's scratch buffer without kept gradients),
+    # broadcast, then the update kernel
+    say(f"case sgd {w.name} mode={mode} keep={keep} passes={passes} shared={shared}")
     lr = 0.0125
     rng = np.random.default_rng(w.seed)
     nrep = 1 if shared else w.P
@@ -57,7 +62,7 @@ def test_sgd_bitwise(w, mode, keep, shared):
     weights = [torch.from_numpy(x).cuda() for x in w0]
     plan = ddl.Plan(w.P, w.n, w.dtype, w.op, ddl_topo(w), w.bucket_list(), mode)
     if mode == "fused":
-        plan.set_fused_passes(2)   # ignored by the SGD variant (one kernel)
+        plan.set_fused_passes(passes)
     plan.execute_sgd(bufs, weights, lr, keep_grads=keep)
     torch.cuda.synchronize()
     plan.destroy()
@@ -69,9 +74,12 @@ def test_sgd_bitwise(w, mode, keep, shared):
         assert got.tobytes() == (y[r] if keep else g[r]).tobytes(), (w.name, r)
 
 
-def test_sgd_headline_sampled():
-    """40 ranks x 300M fp32, 64 event-gated buckets, one replica per rank:
-    sampled elements against the oracle, every replica identical."""
+@pytest.mark.parametrize("keep", [True, False])
+def test_sgd_headline_sampled(keep):
+    """40 ranks x 300M fp32, 64 event-gated buckets, one replica per rank, in
+    the form bench.py times (two kernels and the update kernel): sampled
+    elements against the oracle, every replica identical, and without kept
+    gradients the buffers untouched."""
     w = WORKLOADS["ring_p40_300m_64b"]
     lr = 0.01
     say("case sgd headline: inputs")
@@ -86,9 +94,10 @@ def test_sgd_headline_sampled():
     events = [torch.cuda.Event() for _ in w.bucket_list()]
     for e in events:
         e.record(stream)
-    say("case sgd headline: fused all-reduce + SGD")
+    say(f"case sgd headline: fused all-reduce + SGD keep={keep}")
     plan = ddl.Plan(w.P, w.n, w.dtype, w.op, ddl_topo(w), w.bucket_list(), "fused")
-    plan.execute_sgd(bufs, weights, lr, keep_grads=True, events=events, stream=stream)
+    assert plan.fused_passes() == 2
+    plan.execute_sgd(bufs, weights, lr, keep_grads=keep, events=events, stream=stream)
     torch.cuda.synchronize()
     plan.destroy()
     assert all(torch.equal(weights[0].view(torch.int32), t.view(torch.int32))
@@ -103,6 +112,10 @@ def test_sgd_headline_sampled():
     got = weights[w.P // 3][it].cpu().numpy()
     assert got.tobytes() == want.tobytes()
     got_y = bufs[w.P - 1][it].cpu().numpy()
-    assert got_y.tobytes() == y.tobytes()
+    if keep:
+        assert got_y.tobytes() == y.tobytes()
+    else:
+        g = synth.gather_host(idx, synth.F32, w.dist, w.seed, w.P - 1, sigma=w.sigma)
+        assert got_y.tobytes() == g.tobytes()
     del bufs, weights
     torch.cuda.empty_cache()
