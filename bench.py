@@ -262,9 +262,11 @@ def extras(args, w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_b
         out["overlap"] = overlap_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth,
                                      fused_bytes, fused_ms)
     if "sgd" in args.legs:
-        out["sgd"] = sgd_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_ms)
+        out["sgd"] = sgd_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_ms,
+                             args.passes)
     if "lars" in args.legs:
-        out["lars"] = lars_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_ms)
+        out["lars"] = lars_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_ms,
+                               args.passes)
     if "typed" in args.legs:
         out["typed"] = typed_leg(main_stream, torch, ddl, synth)
     if "per_gpu_step" in args.legs:
@@ -475,7 +477,7 @@ def typed_leg(main_stream, torch, ddl, synth):
     return res
 
 
-def sgd_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_ms):
+def sgd_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_ms, passes=0):
     """The SGD step fused into the all-reduce's epilogue, against the
     all-reduce followed by a separate update of every replica."""
     lr = 0.01
@@ -488,8 +490,9 @@ def sgd_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_ms):
     torch.cuda.synchronize()
     evs = [torch.cuda.Event() for _ in buckets] if w.side_stream else None
     plan = ddl.Plan(w.P, w.n, w.dtype, w.op, topo, buckets, "fused")
+    plan.set_fused_passes(passes)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    res = {"replicas": nrep, "lr": lr}
+    res = {"replicas": nrep, "lr": lr, "fused_passes": plan.fused_passes()}
     for keep in (True, False):
         def one():
             if evs:
@@ -531,7 +534,7 @@ def sgd_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_ms):
     return res
 
 
-def lars_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_ms):
+def lars_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_ms, passes=0):
     """The LARS step after the all-reduce (every bucket a layer; the Sony
     article's coefficient 0.01 and eps 1e-6), one weight replica per rank
     (one shared replica when HBM is short): the whole step's time, and each
@@ -548,6 +551,7 @@ def lars_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_ms):
     torch.cuda.synchronize()
     evs = [torch.cuda.Event() for _ in buckets] if w.side_stream else None
     plan = ddl.Plan(w.P, w.n, w.dtype, w.op, topo, buckets, "fused")
+    plan.set_fused_passes(passes)
     _, ar_bytes = plan.traffic()
 
     def one():
@@ -578,6 +582,7 @@ def lars_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_ms):
     kinds = plan.profile_read_kinds()
     plan.destroy()
     res = {"replicas": nrep, "lr": lr, "coeff": ddl.LARS_COEFF, "eps": ddl.LARS_EPS,
+           "fused_passes": passes or "auto",
            "layers": len(buckets), "ms": round(ms, 3),
            "hbm_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes": nbytes,
            "over_allreduce_ms": round(ms - fused_ms, 3)}
