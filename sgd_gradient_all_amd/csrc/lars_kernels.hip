@@ -24,8 +24,10 @@
 //    workgroup stepping all of them; the extra loads of y hit the cache).
 // HBM: the norms read y and w_0 (s + 4 bytes per element), the update reads
 // y and reads and writes every replica (s + 8 nweights); the partials are
-// 16 bytes per tile.  Both streaming kernels are HBM-bound; the counters
-// read 1.00x these bytes for both.
+// 16 bytes per tile.  Both streaming kernels are HBM-bound.  Measured with
+// rocprofv3 counters on MI355X (40 replicas): the norm kernel moves 1.01x
+// its bytes, the update kernel 1.09x -- each accelerator die fetches y once
+// for the replica groups of a tile that run on it.
 //
 // The sums' association order (per lane in element order, then a fixed
 // tree over the workgroup, then the tiles of a bucket in a fixed tree) is
