@@ -175,7 +175,10 @@ int ddl_plan_execute(ddl_plan plan, void *const *bufs, void *const *ready_events
  * follows the two-kernel pass (ddl_plan_set_fused_passes).  In DDL_STEPWISE
  * plans the owner of each chunk updates at the add that completes the sum and
  * every other rank when the all-gather delivers it.
- * Other arguments and the asynchrony are those of ddl_plan_execute.
+ * Other arguments and the asynchrony are those of ddl_plan_execute.  Calls
+ * with keep_grads == 0 in the two-kernel form share the plan's scratch
+ * buffer: two such calls on one plan that may run at the same time on the
+ * device race; order them.
  * DDL_E_ARG for any other nweights, or keep_grads == 0 on a stepwise plan. */
 int ddl_plan_execute_sgd(ddl_plan plan, void *const *bufs, void *const *weights, int nweights,
                          float lr, int keep_grads, void *const *ready_events, void *stream,
@@ -203,6 +206,9 @@ int ddl_plan_execute_sgd(ddl_plan plan, void *const *bufs, void *const *weights,
  * lies within about 1e-13 (relative) of a binary32 rounding boundary.  The
  * first call allocates 16 bytes per tile of the plan's buckets (a tile is
  * 1024 binary32 or 4096 binary16 elements) plus 4 per bucket, once.
+ * The partial sums and rates are the plan's: two LARS calls on one plan that
+ * may run at the same time on the device (different streams, no ordering
+ * event) race; order them.
  * DDL_E_ARG for a plan with typed buckets or another nweights.  Other
  * arguments and the asynchrony are those of ddl_plan_execute. */
 int ddl_plan_execute_lars(ddl_plan plan, void *const *bufs, void *const *weights, int nweights,

@@ -239,3 +239,75 @@ def test_lars_headline_buckets():
                    want_r, y[0], [(0, c)], ("headline", i))
     del bufs, weights
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("kind,mode,passes", [("lars", "fused", 2), ("lars", "fused", 1),
+                                              ("lars", "stepwise", 0), ("sgd_keep", "fused", 2),
+                                              ("sgd_drop", "fused", 2)], ids=lambda v: str(v))
+def test_graph_capture_lars_and_sgd(kind, mode, passes):
+    """The LARS step and the two-kernel SGD step captured into a HIP graph
+    (after one eager call has bound the plan and allocated its scratch)
+    replay to the oracle's result, replay after replay, with the inputs and
+    weights restored eagerly in between."""
+    say(f"case graph capture {kind} {mode} passes={passes}")
+    w = Workload("graph-lars", 16, 16 * 65_536, "f32", "mean", "multiring", k=4, dist="normal",
+                 sigma=1e-2, seed=58, buckets=[(i * 65_536, 65_536) for i in reversed(range(16))])
+    lr = 0.05
+    layers = w.bucket_list()
+    rng = np.random.default_rng(w.seed)
+    w0 = (rng.standard_normal(w.n) * 0.1).astype(np.float32)
+    g = host_inputs(w)
+    y = [x.copy() for x in g]
+    oracle_full(w, y)
+    want_w = [w0.copy() for _ in range(w.P)]
+    if kind == "lars":
+        want_rates = orc.lars(want_w, y[0], layers, lr)
+    else:
+        orc.sgd(want_w, y[0], lr)
+    src = [torch.from_numpy(x).cuda() for x in g]
+    wsrc = torch.from_numpy(w0).cuda()
+    bufs = [t.clone() for t in src]
+    weights = [wsrc.clone() for _ in range(w.P)]
+    rates = torch.zeros(len(layers), dtype=torch.float32, device="cuda")
+    plan = ddl.Plan(w.P, w.n, w.dtype, w.op, ddl_topo(w), layers, mode)
+    if mode == "fused":
+        plan.set_fused_passes(passes)
+
+    def call(stream):
+        if kind == "lars":
+            plan.execute_lars(bufs, weights, lr, rates_out=rates, stream=stream)
+        else:
+            plan.execute_sgd(bufs, weights, lr, keep_grads=kind == "sgd_keep", stream=stream)
+
+    call(torch.cuda.current_stream())   # binds the plan, allocates its scratch
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            call(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for b, x in zip(bufs, src):
+            b.copy_(x)
+        for t in weights:
+            t.copy_(wsrc)
+        rates.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        want_g = g if kind == "sgd_drop" else y
+        for r in (0, 7, 15):
+            assert bufs[r].cpu().numpy().tobytes() == want_g[r].tobytes(), (kind, rep, r)
+        if kind == "lars":
+            got_rates = rates.cpu().numpy()
+            for r in (0, 15):
+                check_lars(weights[r].cpu().numpy(), want_w[r], got_rates, want_rates, y[0],
+                           layers, (kind, rep, r))
+        else:
+            for r in (0, 15):
+                assert weights[r].cpu().numpy().tobytes() == want_w[r].tobytes(), (kind, rep, r)
+    del graph
+    torch.cuda.synchronize()
+    plan.destroy()
