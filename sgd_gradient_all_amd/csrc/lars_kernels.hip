@@ -282,15 +282,23 @@ int launch_lars(int dtype, int kind, const RankPtrs &w, const LarsArgs &a, uint3
         hipLaunchKernelGGL(lars_rate_kernel, grid, block, 0, s, a);
         break;
     case DDL_K_UPDATE: {
-        // blocks counts tiles; every tile takes ngroups workgroups
-        if (a.ngroups < 1 || a.reps_per_group < 1 ||
-            (uint64_t)blocks * (uint64_t)a.ngroups * kBlock > 0xffffffffull)
+        // blocks counts tiles; every tile takes ngroups workgroups, and a
+        // grid holds at most 2^32 - 1 work-items: cut into several launches
+        if (a.ngroups < 1 || a.reps_per_group < 1)
             return (int)hipErrorInvalidValue;
-        const dim3 ugrid(blocks * (uint32_t)a.ngroups);
-        if (dtype == DDL_F32)
-            launch_update<F32>(ugrid, s, w, a, tuning(DDL_TUNE_UPDATE_BATCH));
-        else
-            launch_update<F16>(ugrid, s, w, a, tuning(DDL_TUNE_UPDATE_BATCH));
+        const uint32_t per = 0xffffffffu / (uint32_t)kBlock / (uint32_t)a.ngroups;
+        if (per == 0)
+            return (int)hipErrorInvalidValue;
+        const int batch = tuning(DDL_TUNE_UPDATE_BATCH);
+        for (uint32_t t0 = 0; t0 < blocks; t0 += per) {
+            LarsArgs b = a;
+            b.tile_base = a.tile_base + t0;
+            const dim3 ugrid(min(per, blocks - t0) * (uint32_t)a.ngroups);
+            if (dtype == DDL_F32)
+                launch_update<F32>(ugrid, s, w, b, batch);
+            else
+                launch_update<F16>(ugrid, s, w, b, batch);
+        }
         break;
     }
     default:
