@@ -1,0 +1,117 @@
+"""GPU parity over seeded random configurations.
+
+Each case draws a rank count, a topology (ring or multi-ring with random
+ring orders, or a torus grid), an element type, an op, a ragged bucket list
+in a random issue order (empty buckets and offsets that are not multiples of
+16 bytes included), ready events shared by runs of consecutive buckets, a
+coalescing threshold, a side-stream count and an execution form (one-kernel
+or two-kernel fused pass, or step by step).  Every element of every rank is
+compared bit for bit with the oracle's walk of the same schedule.
+"""
+import numpy as np
+import pytest
+
+import oracle as orc
+import sgd_gradient_all_amd as ddl
+import synth
+
+from _helpers import say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+NCASES = 48
+
+
+def draw(seed):
+    rng = np.random.default_rng(1000 + seed)
+    P = int(rng.choice([1, 2, 3, 4, 5, 7, 8, 12, 16, 24, 40]))
+    dtype = str(rng.choice(["f32", "f16"]))
+    op = str(rng.choice(["sum", "mean"]))
+    kind = str(rng.choice(["ring", "multiring", "torus2d"]))
+    k, rows, cols, order = 1, 0, 0, None
+    if kind == "torus2d":
+        divs = [r for r in range(1, P + 1) if P % r == 0]
+        rows = int(rng.choice(divs))
+        cols = P // rows
+    else:
+        if kind == "multiring":
+            k = int(rng.integers(1, 6))
+        if rng.random() < 0.6:
+            order = np.concatenate([rng.permutation(P) for _ in range(k)]).astype(np.int32)
+    nb = int(rng.integers(1, 12))
+    sizes = []
+    for _ in range(nb):
+        r = rng.random()
+        if r < 0.1:
+            sizes.append(0)
+        elif r < 0.4:
+            sizes.append(int(rng.integers(1, 200)))
+        elif r < 0.8:
+            sizes.append(int(rng.integers(200, 20_000)))
+        else:
+            sizes.append(int(rng.integers(20_000, 150_000)))
+    offs = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(int).tolist()
+    buckets = [(int(o), int(c)) for o, c in zip(offs, sizes)]
+    perm = rng.permutation(nb)
+    buckets = [buckets[i] for i in perm]
+    n = int(sum(sizes))
+    # runs of consecutive buckets share one event; some buckets get none
+    ev_of, cur = [], 0
+    for b in range(nb):
+        if b and rng.random() < 0.5:
+            cur += 1
+        ev_of.append(None if rng.random() < 0.15 else cur)
+    use_events = rng.random() < 0.7
+    form = str(rng.choice(["fused1", "fused2", "stepwise"]))
+    coalesce = int(rng.choice([0, 0, 4096, 1 << 20]))
+    nside = int(rng.integers(0, 5))
+    return dict(P=P, dtype=dtype, op=op, kind=kind, k=k, rows=rows, cols=cols, order=order,
+                buckets=buckets, n=n, ev_of=ev_of if use_events else None, form=form,
+                coalesce=coalesce, nside=nside, seed=seed)
+
+
+@pytest.mark.parametrize("seed", range(NCASES))
+def test_random_configuration(seed):
+    c = draw(seed)
+    say(f"case random {seed}: P={c['P']} {c['dtype']} {c['op']} {c['kind']} k={c['k']} "
+        f"grid={c['rows']}x{c['cols']} n={c['n']} buckets={len(c['buckets'])} "
+        f"form={c['form']} events={c['ev_of'] is not None} coalesce={c['coalesce']} "
+        f"side={c['nside']}")
+    P, n = c["P"], c["n"]
+    sdt = synth.F32 if c["dtype"] == "f32" else synth.F16
+    g = [synth.fill_host(n, sdt, "normal", 500 + c["seed"], r, sigma=1e-2) for r in range(P)]
+    want = [x.copy() for x in g]
+    kinds = {"ring": orc.RING, "multiring": orc.MULTIRING, "torus2d": orc.TORUS2D}
+    orc.allreduce(want, op=orc.SUM if c["op"] == "sum" else orc.MEAN, kind=kinds[c["kind"]],
+                  k=c["k"], rows=c["rows"], cols=c["cols"], ring_order=c["order"],
+                  buckets=c["buckets"])
+    bufs = [torch.from_numpy(x).cuda() for x in g]
+    topo = ddl.topo(c["kind"], c["k"], c["rows"], c["cols"],
+                    ring_order=None if c["order"] is None else c["order"].tolist())
+    mode = "stepwise" if c["form"] == "stepwise" else "fused"
+    plan = ddl.Plan(P, n, c["dtype"], c["op"], topo, c["buckets"], mode)
+    if mode == "fused":
+        plan.set_fused_passes(1 if c["form"] == "fused1" else 2)
+    plan.set_coalesce_bytes(c["coalesce"])
+    plan.set_side_streams(c["nside"])
+    stream = torch.cuda.current_stream()
+    events = None
+    if c["ev_of"] is not None:
+        pool = {}
+        events = []
+        for e in c["ev_of"]:
+            if e is None:
+                events.append(None)
+            else:
+                if e not in pool:
+                    pool[e] = torch.cuda.Event()
+                    pool[e].record(stream)
+                events.append(pool[e])
+    plan.execute(bufs, events=events, stream=stream)
+    torch.cuda.synchronize()
+    plan.destroy()
+    for r in range(P):
+        got = bufs[r].cpu().numpy()
+        assert got.tobytes() == want[r].tobytes(), (seed, r)
