@@ -115,3 +115,75 @@ def test_random_configuration(seed):
     for r in range(P):
         got = bufs[r].cpu().numpy()
         assert got.tobytes() == want[r].tobytes(), (seed, r)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_sgd_and_lars(seed):
+    """The SGD step (kept or dropped gradients) or the LARS step on a drawn
+    configuration, with shared or per-rank weight replicas; SGD bit for bit,
+    LARS to the tolerance of tests/test_gpu_lars.py."""
+    from test_gpu_lars import check_lars
+    c = draw(100 + seed)
+    rng = np.random.default_rng(7000 + seed)
+    step = str(rng.choice(["sgd_keep", "sgd_drop", "lars"]))
+    if step == "sgd_drop" and c["form"] == "stepwise":
+        c["form"] = "fused2"
+    shared = bool(rng.random() < 0.4)
+    lr = float(rng.choice([0.01, 0.1, 0.5]))
+    say(f"case random {step} {seed}: P={c['P']} {c['dtype']} {c['op']} {c['kind']} "
+        f"k={c['k']} grid={c['rows']}x{c['cols']} n={c['n']} buckets={len(c['buckets'])} "
+        f"form={c['form']} shared={shared} events={c['ev_of'] is not None}")
+    P, n = c["P"], c["n"]
+    sdt = synth.F32 if c["dtype"] == "f32" else synth.F16
+    g = [synth.fill_host(n, sdt, "normal", 800 + seed, r, sigma=1e-2) for r in range(P)]
+    w0 = (rng.standard_normal(n) * 0.1).astype(np.float32)
+    nrep = 1 if shared else P
+    y = [x.copy() for x in g]
+    kinds = {"ring": orc.RING, "multiring": orc.MULTIRING, "torus2d": orc.TORUS2D}
+    orc.allreduce(y, op=orc.SUM if c["op"] == "sum" else orc.MEAN, kind=kinds[c["kind"]],
+                  k=c["k"], rows=c["rows"], cols=c["cols"], ring_order=c["order"],
+                  buckets=c["buckets"])
+    want_w = [w0.copy() for _ in range(nrep)]
+    if step == "lars":
+        want_rates = orc.lars(want_w, y[0], c["buckets"], lr)
+    else:
+        orc.sgd(want_w, y[0], lr)
+    bufs = [torch.from_numpy(x).cuda() for x in g]
+    weights = [torch.from_numpy(w0.copy()).cuda() for _ in range(nrep)]
+    rates = torch.zeros(max(1, len(c["buckets"])), dtype=torch.float32, device="cuda")
+    topo = ddl.topo(c["kind"], c["k"], c["rows"], c["cols"],
+                    ring_order=None if c["order"] is None else c["order"].tolist())
+    mode = "stepwise" if c["form"] == "stepwise" else "fused"
+    plan = ddl.Plan(P, n, c["dtype"], c["op"], topo, c["buckets"], mode)
+    if mode == "fused":
+        plan.set_fused_passes(1 if c["form"] == "fused1" else 2)
+    plan.set_side_streams(c["nside"])
+    stream = torch.cuda.current_stream()
+    events = None
+    if c["ev_of"] is not None:
+        pool, events = {}, []
+        for e in c["ev_of"]:
+            if e is None:
+                events.append(None)
+            else:
+                if e not in pool:
+                    pool[e] = torch.cuda.Event()
+                    pool[e].record(stream)
+                events.append(pool[e])
+    if step == "lars":
+        plan.execute_lars(bufs, weights, lr, rates_out=rates, events=events, stream=stream)
+    else:
+        plan.execute_sgd(bufs, weights, lr, keep_grads=step == "sgd_keep", events=events,
+                         stream=stream)
+    torch.cuda.synchronize()
+    plan.destroy()
+    want_g = g if step == "sgd_drop" else y
+    for r in range(P):
+        assert bufs[r].cpu().numpy().tobytes() == want_g[r].tobytes(), (seed, "grads", r)
+    for r in range(nrep):
+        got = weights[r].cpu().numpy()
+        if step == "lars":
+            check_lars(got, want_w[r], rates.cpu().numpy(), want_rates, y[0], c["buckets"],
+                       (seed, r))
+        else:
+            assert got.tobytes() == want_w[r].tobytes(), (seed, "weights", r)
