@@ -269,11 +269,14 @@ int ddl_plan_set_side_streams(ddl_plan plan, int n);
  * weights from rank 0's result (without kept gradients the reduce kernel
  * writes to a scratch buffer of n elements instead, allocated by the first
  * such call, and nothing is broadcast).  passes = 0 (default): automatic,
- * two kernels from 16 ranks on.
+ * per group: two kernels from 16 ranks on for groups of at least 200 MB
+ * summed over the ranks (400 MB for binary16), one kernel otherwise (short
+ * passes are launch-bound, and the second launch costs more than it saves).
  * The results are bit-identical either way; only the speed differs.
  * Returns DDL_E_ARG for other values.  Takes effect at the next execute.
- * ddl_plan_get_fused_passes reports the form the next plain execute uses
- * (0 for a stepwise plan). */
+ * ddl_plan_get_fused_passes reports the form of one group holding all the
+ * plan's buckets, as in a call without ready events (0 for a stepwise
+ * plan). */
 int ddl_plan_set_fused_passes(ddl_plan plan, int passes);
 int ddl_plan_get_fused_passes(ddl_plan plan, int *passes);
 

@@ -207,22 +207,28 @@ int bind_device(ddl_plan p, int dev) {
 // A grid holds at most 2^32 - 1 work-items in x: cut bigger launches.
 constexpr uint32_t kMaxTilesPerLaunch = 1u << 23;
 
-// Form of the fused pass: one kernel, or a reduce kernel that writes rank 0
-// and a broadcast kernel (see fused_kernel.hip).  Automatic: two kernels
-// from 16 ranks on, where they measured faster on MI355X (paired, six
-// repeats): 40 ranks fp32 +5..+18%, 16 ranks fp32 ResNet-50 multi-ring
-// +7.3%, 16 ranks fp16 torus +5.8%; 8 ranks -3%.  With the SGD step, the
-// one-kernel form updates the weights in its epilogue; the two-kernel form
-// reduces (to rank 0, or to a scratch buffer when the gradients are not
-// kept), broadcasts (when they are), then runs the update kernel with the
-// constant rate lr.
-int fused_passes(ddl_plan p, const Schedule &s, bool sgd) {
-    (void)sgd;
+// Form of the fused pass of a group of `elems` elements per rank: one
+// kernel, or a reduce kernel that writes rank 0 and a broadcast kernel (see
+// fused_kernel.hip).  Automatic: two kernels from 16 ranks on, for groups
+// of at least 200 MB over all ranks (binary32; 400 MB binary16).  Measured
+// on MI355X: whole workloads (paired, six repeats) 40 ranks fp32 +5..+18%,
+// 16 ranks fp32 ResNet-50 multi-ring +7.3%, 16 ranks fp16 torus (818 MB)
+// +5.8%; 8 ranks -3%.  By group size, one bucket per call: 40 ranks fp32
+// two kernels win from 8 MB per rank (-7%), lose at 4 MB (+4%) and below;
+// 16 ranks fp32 win from 16 MB (-3%), lose at 8 MB (+4%) and below (+16..19%,
+// launch-bound); 16 ranks fp16 still lose at 16 MB (+8%).  With the SGD
+// step, the one-kernel form updates the weights in its epilogue; the
+// two-kernel form reduces (to rank 0, or to a scratch buffer when the
+// gradients are not kept), broadcasts (when they are), then runs the update
+// kernel with the constant rate lr.
+constexpr uint64_t kTwoKernelMinBytes = 200ull << 20;
+int fused_passes(ddl_plan p, const Schedule &s, uint64_t elems) {
     if (s.P < 2)
         return 1;
     if (p->fused_passes)
         return p->fused_passes;
-    return s.P >= 16 ? 2 : 1;
+    const uint64_t min_bytes = kTwoKernelMinBytes * (s.esz == 4 ? 1 : 2);
+    return s.P >= 16 && (uint64_t)s.P * elems * (uint64_t)s.esz >= min_bytes ? 2 : 1;
 }
 
 // Side streams event-gated groups alternate over.  Automatic: two for
@@ -351,7 +357,10 @@ struct Launcher {
         a.mean = s.op == DDL_MEAN;
         a.divisor = (float)s.P;
         a.anchor = s.fused_anchor;
-        const bool two = fused_passes(p, s, sgd != nullptr) == 2;
+        uint64_t elems = 0;
+        for (int b = b0; b < b1; ++b)
+            elems += s.buckets[b].len;
+        const bool two = fused_passes(p, s, elems) == 2;
         // two-kernel SGD without kept gradients: the results go to the
         // plan's scratch buffer, and the gradient buffers stay as they were
         const bool scratch = two && sgd && !sgd->keep_grads;
@@ -598,7 +607,7 @@ int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stre
             return rc;
     }
     if (sgd && !sgd->keep_grads && p->mode == DDL_FUSED &&
-        fused_passes(p, p->parts[0].s, true) == 2) {
+        fused_passes(p, p->parts[0].s, p->parts[0].s.n) == 2) {
         int rc = ensure_sgd_home(p);
         if (rc)
             return rc;
@@ -1109,8 +1118,13 @@ int ddl_plan_get_fused_passes(ddl_plan plan, int *passes) {
     if (!plan || !passes)
         return DDL_E_NULL;
     std::lock_guard<std::mutex> lk(plan->mu);
-    // typed plans: the form of the first element type's buckets
-    *passes = plan->mode == DDL_FUSED ? fused_passes(plan, plan->parts[0].s, false) : 0;
+    // the form of one group holding all the buckets (of the first element
+    // type, for typed plans)
+    const Schedule &s = plan->parts[0].s;
+    uint64_t all = 0;
+    for (const Bucket &b : s.buckets)
+        all += b.len;
+    *passes = plan->mode == DDL_FUSED ? fused_passes(plan, s, all) : 0;
     return DDL_OK;
 }
 

@@ -278,14 +278,26 @@ def test_plan_create_needs_no_gpu():
 
 
 def test_fused_pass_form_setting():
-    # host-only: the automatic form is two kernels from 16 ranks on (fused
-    # plans only); explicit 1 and 2 stick; anything else is rejected
-    for P, dt, mode, want in ((8, "f32", "fused", 1), (15, "f32", "fused", 1),
-                              (16, "f32", "fused", 2), (40, "f32", "fused", 2),
-                              (15, "f16", "fused", 1), (16, "f16", "fused", 2),
-                              (1, "f32", "fused", 1), (40, "f32", "stepwise", 0)):
-        plan = ddl.Plan(P, 4096, dt, "mean", ddl.topo("ring"), None, mode)
-        assert plan.fused_passes() == want, (P, dt, mode)
+    # host-only: the automatic form is two kernels from 16 ranks on for
+    # groups of at least 200 MB over all ranks (400 MB for binary16), one
+    # kernel otherwise (fused plans only); explicit 1 and 2 stick; anything
+    # else is rejected.  Thresholds: 16 ranks binary32 3,276,800 elements per
+    # rank, 40 ranks 1,310,720, 16 ranks binary16 13,107,200.
+    big32, big16 = 200 << 20, 400 << 20
+    for P, n, dt, mode, want in ((8, 1 << 26, "f32", "fused", 1),
+                                 (15, 1 << 26, "f32", "fused", 1),
+                                 (16, big32 // 64, "f32", "fused", 2),
+                                 (16, big32 // 64 - 1, "f32", "fused", 1),
+                                 (40, big32 // 160, "f32", "fused", 2),
+                                 (40, big32 // 160 - 1, "f32", "fused", 1),
+                                 (40, 4096, "f32", "fused", 1),
+                                 (15, 1 << 26, "f16", "fused", 1),
+                                 (16, big16 // 32, "f16", "fused", 2),
+                                 (16, big16 // 32 - 1, "f16", "fused", 1),
+                                 (1, 4096, "f32", "fused", 1),
+                                 (40, 4096, "f32", "stepwise", 0)):
+        plan = ddl.Plan(P, n, dt, "mean", ddl.topo("ring"), None, mode)
+        assert plan.fused_passes() == want, (P, n, dt, mode)
         if mode == "fused" and P > 1:
             for v in (1, 2):
                 plan.set_fused_passes(v)
