@@ -94,6 +94,10 @@ struct ddl_plan_s {
     hipStream_t side[kMaxSideStreams] = {};
     hipEvent_t side_done[kMaxSideStreams] = {};
     hipEvent_t call_ev = nullptr, last_ev = nullptr;
+    // typed plans: a group's smaller element-type passes run on part_side,
+    // forked from and joined back into the group's stream
+    hipStream_t part_side = nullptr;
+    hipEvent_t part_fork = nullptr, part_join = nullptr;
     bool in_flight = false;
 
     // profiling
@@ -148,6 +152,14 @@ void release_device(ddl_plan p) {
         (void)hipEventDestroy(p->call_ev);
     if (p->last_ev)
         (void)hipEventDestroy(p->last_ev);
+    if (p->part_fork)
+        (void)hipEventDestroy(p->part_fork);
+    if (p->part_join)
+        (void)hipEventDestroy(p->part_join);
+    if (p->part_side)
+        (void)hipStreamDestroy(p->part_side);
+    p->call_ev = p->last_ev = p->part_fork = p->part_join = nullptr;
+    p->part_side = nullptr;
     for (int i = 0; i < kMaxSideStreams; ++i) {
         if (p->side_done[i])
             (void)hipEventDestroy(p->side_done[i]);
@@ -169,6 +181,11 @@ int bind_device(ddl_plan p, int dev) {
             return DDL_E_HIP;
     if (hipEventCreateWithFlags(&p->call_ev, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&p->last_ev, hipEventDisableTiming) != hipSuccess)
+        return DDL_E_HIP;
+    if (p->parts.size() > 1 &&
+        (hipStreamCreateWithFlags(&p->part_side, hipStreamNonBlocking) != hipSuccess ||
+         hipEventCreateWithFlags(&p->part_fork, hipEventDisableTiming) != hipSuccess ||
+         hipEventCreateWithFlags(&p->part_join, hipEventDisableTiming) != hipSuccess))
         return DDL_E_HIP;
     for (Part &pt : p->parts) {
         const Schedule &s = pt.s;
@@ -675,13 +692,48 @@ int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stre
                 r.first = p->order[b].second;
             r.second = p->order[b].second + 1;
         }
+        // with more than one element type in the group, the largest part
+        // runs on the group's stream and the others on the plan's part
+        // stream at the same time (the small binary32 tensors of a mixed
+        // gradient are latency-bound: alone they leave the device idle)
+        int big = -1, nparts = 0;
+        size_t big_bytes = 0;
         for (size_t q = 0; q < p->parts.size(); ++q) {
             if (range[q].first < 0)
                 continue;
+            const Part &pq = p->parts[q];
+            size_t bytes_q = 0;
+            for (int b = range[q].first; b < range[q].second; ++b)
+                bytes_q += (size_t)pq.s.buckets[b].len * (size_t)pq.s.esz;
+            if (big < 0 || bytes_q > big_bytes) {
+                big = (int)q;
+                big_bytes = bytes_q;
+            }
+            ++nparts;
+        }
+        const hipStream_t gs = L.stream;
+        if (nparts > 1 && (hipEventRecord(p->part_fork, gs) != hipSuccess ||
+                           hipStreamWaitEvent(p->part_side, p->part_fork, 0) != hipSuccess))
+            return DDL_E_HIP;
+        for (size_t q = 0; q < p->parts.size(); ++q) {
+            if (range[q].first < 0 || (nparts > 1 && (int)q == big))
+                continue;
             L.pt = &p->parts[q];
+            L.stream = nparts > 1 ? p->part_side : gs;
             int rc = L.group(range[q].first, range[q].second);
             if (rc)
                 return rc;
+        }
+        if (nparts > 1) {
+            if (hipEventRecord(p->part_join, p->part_side) != hipSuccess)
+                return DDL_E_HIP;
+            L.pt = &p->parts[big];
+            L.stream = gs;
+            int rc = L.group(range[big].first, range[big].second);
+            if (rc)
+                return rc;
+            if (hipStreamWaitEvent(gs, p->part_join, 0) != hipSuccess)
+                return DDL_E_HIP;
         }
         b0 = b1;
         ++g;
