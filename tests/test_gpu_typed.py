@@ -126,3 +126,78 @@ def test_resnet50_mixed_precision_full_size():
         for r in (0, 7, P - 1):
             assert dev[r].cpu().numpy().tobytes() == want[r].tobytes(), (mode, r)
         del dev
+
+
+def _paired_events(segs, stream):
+    """One ready event per pair of consecutive buckets: groups of two
+    buckets, often of two element types, whose passes run side by side."""
+    evs = [torch.cuda.Event() for _ in range((len(segs) + 1) // 2)]
+    for e in evs:
+        e.record(stream)
+    return [evs[b // 2] for b in range(len(segs))]
+
+
+@pytest.mark.parametrize("mode", ["fused1", "fused2", "stepwise"])
+def test_typed_mixed_groups_on_side_streams(mode):
+    """Groups that hold both element types: the smaller type's pass runs on
+    the plan's part stream beside the larger one's; every byte checked."""
+    P, tk, nb, mx = CASES[1]
+    segs, nbytes = layout(300, 14, mx)
+    say(f"case typed mixed groups P={P} buckets={len(segs)} mode={mode}")
+    host = fill(P, segs, nbytes, 17)
+    want = expected(P, segs, host, "mean", "multiring", 4, 0, 0)
+    dev = [torch.zeros(nbytes + 16, dtype=torch.uint8, device="cuda") for _ in range(P)]
+    for d, h in zip(dev, host):
+        d[:nbytes].copy_(torch.from_numpy(h))
+    plan = ddl.Plan.typed(P, nbytes, "mean", ddl.topo(**tk), segs,
+                          "stepwise" if mode == "stepwise" else "fused")
+    if mode != "stepwise":
+        plan.set_fused_passes(1 if mode == "fused1" else 2)
+    stream = torch.cuda.current_stream()
+    plan.execute(dev, events=_paired_events(segs, stream), stream=stream)
+    torch.cuda.synchronize()
+    plan.destroy()
+    for r in range(P):
+        assert dev[r][:nbytes].cpu().numpy().tobytes() == want[r].tobytes(), (mode, r)
+
+
+@pytest.mark.parametrize("mode", ["fused2", "stepwise"])
+@pytest.mark.parametrize("gated", [False, True])
+def test_typed_graph_capture_and_replay(mode, gated):
+    """A typed plan's execution captured into a HIP graph (the element-type
+    passes forked onto the part stream and joined back inside the capture)
+    replays to the oracle's bytes, replay after replay, with the inputs
+    restored eagerly in between."""
+    P, tk, nb, mx = CASES[2]
+    segs, nbytes = layout(301, 10, mx)
+    say(f"case typed graph P={P} buckets={len(segs)} mode={mode} gated={gated}")
+    host = fill(P, segs, nbytes, 19)
+    want = expected(P, segs, host, "mean", "torus2d", 1, 4, 4)
+    src = [torch.zeros(nbytes + 16, dtype=torch.uint8, device="cuda") for _ in range(P)]
+    for d, h in zip(src, host):
+        d[:nbytes].copy_(torch.from_numpy(h))
+    dev = [t.clone() for t in src]
+    plan = ddl.Plan.typed(P, nbytes, "mean", ddl.topo(**tk), segs,
+                          "stepwise" if mode == "stepwise" else "fused")
+    if mode != "stepwise":
+        plan.set_fused_passes(2)
+    plan.execute(dev, stream=torch.cuda.current_stream())   # binds the plan
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            plan.execute(dev, events=_paired_events(segs, s) if gated else None, stream=s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for d, x in zip(dev, src):
+            d.copy_(x)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for r in (0, 5, P - 1):
+            assert dev[r][:nbytes].cpu().numpy().tobytes() == want[r].tobytes(), (mode, rep, r)
+    del graph
+    torch.cuda.synchronize()
+    plan.destroy()
