@@ -264,6 +264,58 @@ def test_workload_full_size_sampled(name):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("dtype,P,n", [("f16", 3, (1 << 32) + 4099), ("f32", 2, (1 << 31) + 13)])
+def test_element_indices_beyond_32_bits(dtype, P, n):
+    """Buffers of more than 2^32 (binary16) or 2^31 (binary32) elements per
+    rank, so element indices and byte offsets pass 32 bits: sampled elements
+    (chunk edges, the 2^31 and 2^32 boundaries, the ragged tail) against the
+    oracle, every rank bit-identical, and the stepwise walk and both fused
+    forms bit-identical everywhere."""
+    half = (n // 2) // 8 * 8
+    w = Workload("beyond32", P, n, dtype, "mean", "ring", dist="normal", sigma=1e-2, seed=97,
+                 buckets=[(half, n - half), (0, half)])
+    need = 2 * P * n * w.esize
+    if torch.cuda.mem_get_info()[0] < need + (4 << 30):
+        pytest.skip(f"needs {need >> 30} GiB of device memory")
+    say(f"case beyond 32 bits: {dtype} P={P} n={n}: device inputs")
+    bufs = device_inputs(w)
+    copy = [b.clone() for b in bufs]
+    iv = torch.int32 if dtype == "f32" else torch.int16
+    plan = ddl.Plan(P, n, dtype, "mean", ddl_topo(w), w.bucket_list(), "fused")
+    say(f"case beyond 32 bits: {dtype} fused, {plan.fused_passes()} kernel(s)")
+    plan.execute(bufs)
+    torch.cuda.synchronize()
+    assert ranks_identical(bufs)
+    idx = set(sample_indices(w, 1500, seed=3).tolist())
+    for edge in (1 << 31, 1 << 32, half, n):
+        idx.update(e for e in range(edge - 2, edge + 2) if 0 <= e < n)
+    idx = np.array(sorted(idx), dtype=np.uint64)
+    want, _ = oracle_at(w, idx)
+    it = torch.from_numpy(idx.astype(np.int64)).cuda()
+    for r in range(P):
+        assert bitwise_equal(bufs[r][it].cpu().numpy(), want), (dtype, r)
+    other = 3 - plan.fused_passes()
+    plan.destroy()
+    say(f"case beyond 32 bits: {dtype} stepwise")
+    plan = ddl.Plan(P, n, dtype, "mean", ddl_topo(w), w.bucket_list(), "stepwise")
+    plan.execute(copy)
+    torch.cuda.synchronize()
+    plan.destroy()
+    assert all(torch.equal(a.view(iv), b.view(iv)) for a, b in zip(bufs, copy))
+    say(f"case beyond 32 bits: {dtype} fused, {other} kernel(s)")
+    for r, b in enumerate(copy):
+        synth.fill_device(b.data_ptr(), n, synth_dtype(dtype), w.dist, w.seed, r, sigma=w.sigma)
+    torch.cuda.synchronize()
+    plan = ddl.Plan(P, n, dtype, "mean", ddl_topo(w), w.bucket_list(), "fused")
+    plan.set_fused_passes(other)
+    plan.execute(copy)
+    torch.cuda.synchronize()
+    plan.destroy()
+    assert all(torch.equal(a.view(iv), b.view(iv)) for a, b in zip(bufs, copy))
+    del bufs, copy
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------------------
 # dispatcher: ready events gate buckets
 # ---------------------------------------------------------------------------
