@@ -217,7 +217,9 @@ int ddl_plan_execute_lars(ddl_plan plan, void *const *bufs, void *const *weights
 
 /* One-shot form: looks up (or builds and caches) the plan for these
  * arguments -- the cache key is everything except the buffers and events --
- * and executes it with the buckets' ready_event fields.  Thread-safe. */
+ * and executes it with the buckets' ready_event fields.  Thread-safe.  The
+ * cache holds at most 64 plans: a new one first destroys the least recently
+ * used plan that has no work in flight. */
 int ddl_allreduce(void *const *bufs, int P, size_t n, ddl_dtype dtype, ddl_op op,
                   const ddl_topo *topo, const ddl_bucket *buckets, int nbuckets,
                   ddl_mode mode, void *stream, void *done_event);
@@ -240,6 +242,9 @@ int ddl_plan_destroy(ddl_plan plan);
 
 /* Drop every plan ddl_allreduce cached (DDL_E_BUSY if one is in flight). */
 int ddl_cache_clear(void);
+
+/* Number of plans ddl_allreduce holds in its cache. */
+int ddl_cache_count(size_t *count);
 
 /* Static text for a DDL_* code. */
 const char *ddl_strerror(int code);

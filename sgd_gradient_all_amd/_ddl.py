@@ -82,6 +82,7 @@ def lib():
             "ddl_plan_traffic": ([vp, ctypes.POINTER(sz), ctypes.POINTER(sz)], i32),
             "ddl_plan_destroy": ([vp], i32),
             "ddl_cache_clear": ([], i32),
+            "ddl_cache_count": ([ctypes.POINTER(sz)], i32),
             "ddl_strerror": ([i32], ctypes.c_char_p),
             "ddl_plan_set_coalesce_bytes": ([vp, sz], i32),
             "ddl_plan_set_side_streams": ([vp, i32], i32),
@@ -175,6 +176,13 @@ def ddl_allreduce(bufs, n, dtype="f32", op="sum", topology=None, buckets=None,
 
 def ddl_cache_clear():
     _check(lib().ddl_cache_clear(), "ddl_cache_clear")
+
+
+def ddl_cache_count():
+    """Plans ddl_allreduce holds in its cache (at most 64)."""
+    n = ctypes.c_size_t(0)
+    _check(lib().ddl_cache_count(ctypes.byref(n)), "ddl_cache_count")
+    return n.value
 
 
 TUNE = {"bcast_ranks": 0, "reduce_nt_load": 1, "fused_nt_load_max_p": 2, "anchor": 3,

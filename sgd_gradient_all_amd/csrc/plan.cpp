@@ -773,8 +773,41 @@ bool busy(ddl_plan p) {
 // ---------------------------------------------------------------------------
 // plan cache of ddl_allreduce
 // ---------------------------------------------------------------------------
+// At most kCacheMax plans are kept; making room destroys the least recently
+// used plan that has no work in flight.
+constexpr size_t kCacheMax = 64;
+struct CacheEntry {
+    ddl_plan plan;
+    uint64_t used;  // g_cache_tick at the last call
+};
 std::mutex g_cache_mu;
-std::map<std::string, ddl_plan> g_cache;
+std::map<std::string, CacheEntry> g_cache;
+uint64_t g_cache_tick = 0;
+
+// Destroys least recently used idle plans until fewer than kCacheMax remain
+// (or every remaining plan is busy).  Caller holds g_cache_mu, which every
+// call on a cached plan also holds, so an idle plan stays idle meanwhile.
+void cache_make_room() {
+    while (g_cache.size() >= kCacheMax) {
+        auto victim = g_cache.end();
+        for (auto it = g_cache.begin(); it != g_cache.end(); ++it) {
+            if (victim != g_cache.end() && it->second.used >= victim->second.used)
+                continue;
+            std::lock_guard<std::mutex> pl(it->second.plan->mu);
+            if (!busy(it->second.plan))
+                victim = it;
+        }
+        if (victim == g_cache.end())
+            return;
+        ddl_plan p = victim->second.plan;
+        g_cache.erase(victim);
+        {
+            std::lock_guard<std::mutex> pl(p->mu);
+            release_device(p);
+        }
+        delete p;
+    }
+}
 
 void put(std::string &k, const void *p, size_t n) { k.append((const char *)p, n); }
 
@@ -992,6 +1025,9 @@ int ddl_allreduce(void *const *bufs, int P, size_t n, ddl_dtype dtype, ddl_op op
                   ddl_mode mode, void *stream, void *done_event) {
     if (!bufs || !topo || (nbuckets > 0 && !buckets))
         return DDL_E_NULL;
+    // the key reads P (or k * P) ring-order entries: range-check them first
+    if (P < 1 || P > DDL_MAX_RANKS || (topo->kind == DDL_MULTIRING && topo->k < 1))
+        return DDL_E_ARG;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         return DDL_E_HIP;
@@ -1002,12 +1038,14 @@ int ddl_allreduce(void *const *bufs, int P, size_t n, ddl_dtype dtype, ddl_op op
             cache_key(dev, P, n, dtype, op, *topo, buckets, std::max(nbuckets, 0), mode);
         auto it = g_cache.find(key);
         if (it != g_cache.end()) {
-            p = it->second;
+            p = it->second.plan;
+            it->second.used = ++g_cache_tick;
         } else {
             int rc = ddl_plan_create(&p, P, n, dtype, op, topo, buckets, nbuckets, mode);
             if (rc)
                 return rc;
-            g_cache[key] = p;
+            cache_make_room();
+            g_cache.emplace(key, CacheEntry{p, ++g_cache_tick});
         }
         std::vector<void *> ev(std::max(nbuckets, 0), nullptr);
         for (int b = 0; b < nbuckets; ++b)
@@ -1051,15 +1089,23 @@ int ddl_plan_destroy(ddl_plan plan) {
 int ddl_cache_clear(void) {
     std::lock_guard<std::mutex> lk(g_cache_mu);
     for (auto &kv : g_cache) {
-        std::lock_guard<std::mutex> pl(kv.second->mu);
-        if (busy(kv.second))
+        std::lock_guard<std::mutex> pl(kv.second.plan->mu);
+        if (busy(kv.second.plan))
             return DDL_E_BUSY;
     }
     for (auto &kv : g_cache) {
-        release_device(kv.second);
-        delete kv.second;
+        release_device(kv.second.plan);
+        delete kv.second.plan;
     }
     g_cache.clear();
+    return DDL_OK;
+}
+
+int ddl_cache_count(size_t *count) {
+    if (!count)
+        return DDL_E_NULL;
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    *count = g_cache.size();
     return DDL_OK;
 }
 

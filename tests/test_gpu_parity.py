@@ -402,6 +402,31 @@ def test_plan_reuse_and_cache():
     ddl.ddl_cache_clear()
 
 
+def test_plan_cache_is_bounded():
+    """ddl_allreduce keeps at most 64 plans: 80 distinct shapes in a row all
+    give the closed-form result, the cache never holds more than 64 plans, a
+    repeated shape reuses its plan, and clearing empties it."""
+    say("case plan cache bound")
+    ddl.ddl_cache_clear()
+    assert ddl.ddl_cache_count() == 0
+    P = 3
+    for i in range(80):
+        n = 4096 + 8 * i
+        bufs = [torch.full((n,), float(r + 1), device="cuda") for r in range(P)]
+        ddl.ddl_allreduce(bufs, n, "f32", "sum", ddl.topo("ring"))
+        torch.cuda.synchronize()
+        for b in bufs:
+            assert bool((b == 6.0).all()), (i, n)
+        assert ddl.ddl_cache_count() == min(i + 1, 64), i
+    bufs = [torch.full((4096 + 8 * 79,), 1.0, device="cuda") for _ in range(P)]
+    ddl.ddl_allreduce(bufs, bufs[0].numel(), "f32", "sum", ddl.topo("ring"))
+    torch.cuda.synchronize()
+    assert ddl.ddl_cache_count() == 64
+    assert bool((bufs[1] == 3.0).all())
+    ddl.ddl_cache_clear()
+    assert ddl.ddl_cache_count() == 0
+
+
 # ---------------------------------------------------------------------------
 # dispatcher: grouping threshold, stream semantics, busy plans; edge shapes
 # ---------------------------------------------------------------------------

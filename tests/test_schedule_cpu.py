@@ -429,3 +429,20 @@ def test_typed_plan_validation_and_tables():
     assert ddl.lib().ddl_plan_execute_sgd(plan.handle, bufs, w, 1, 0.1, 1, None, None,
                                           None) == -2
     plan.destroy()
+
+
+def test_oneshot_rejects_bad_rank_counts_before_reading_ring_orders():
+    """ddl_allreduce range-checks P (and k) before it reads the ring order
+    into its cache key: a negative or too-large P with a ring order is
+    DDL_E_ARG, not a read far past the caller's array."""
+    import ctypes
+    order = (ctypes.c_int * 4)(0, 1, 2, 3)
+    bufs = (ctypes.c_void_p * 4)(*[16 * (r + 1) for r in range(4)])
+    for P, kind, k in ((-1, 0, 1), (0, 0, 1), (ddl.DDL_MAX_RANKS + 1, 0, 1), (4, 1, 0), (4, 1, -3)):
+        t = ddl.topo("ring") if kind == 0 else ddl.topo("multiring", 1)
+        t.kind, t.k = kind, k
+        t.ring_order = ctypes.cast(order, ctypes.POINTER(ctypes.c_int))
+        rc = ddl.lib().ddl_allreduce(bufs, P, 100, 0, 0, ctypes.byref(t), None, 0, 1, None, None)
+        assert rc == -2, (P, kind, k, rc)
+    n = ctypes.c_size_t(99)
+    assert ddl.lib().ddl_cache_count(ctypes.byref(n)) == 0 and n.value == 0
