@@ -126,6 +126,22 @@ struct FusedArgs {
                      // or a scratch buffer of n elements)
 };
 
+// Spans of at most kTinySpanMax elements are "tiny": a group made only of
+// them (the BatchNorm and bias tensors of a ResNet, split over rings and
+// ranks into pieces of a few elements) runs one wave per span, one element
+// per lane, instead of one workgroup per span.
+constexpr uint32_t kTinySpanMax = 64;
+struct TinyArgs {
+    const DevSpan *spans;
+    const uint32_t *tiny;  // span indices of the tiny spans, in span order
+    const uint8_t *chains;
+    uint32_t lo, hi;       // entries [lo, hi) of tiny
+    int P;
+    int group;             // chain entries per group (as FusedArgs)
+    int mean;
+    float divisor;
+};
+
 // Arguments of one broadcast launch (second kernel of the two-kernel fused
 // form): rank 0's values are copied to ranks 1..P-1, ranks_per_group of
 // them per workgroup, so each tile of fused_tile_elems elements takes
@@ -193,6 +209,7 @@ int launch_step(int dtype, int kind, int vpl, const RankPtrs &bufs, const StepAr
 int launch_fused(int dtype, const RankPtrs &bufs, const FusedArgs &a, const SgdArgs *sgd,
                  bool home, uint32_t tiles, void *stream);
 int launch_bcast(int dtype, const RankPtrs &bufs, const BcastArgs &a, void *stream);
+int launch_tiny(int dtype, const RankPtrs &bufs, const TinyArgs &a, void *stream);
 // kind: DDL_K_LARS_NORM or DDL_K_UPDATE (blocks = tiles from
 // a.tile_base), DDL_K_LARS_RATE (blocks = buckets from a.bucket_lo).
 int launch_lars(int dtype, int kind, const RankPtrs &w, const LarsArgs &a, uint32_t blocks,

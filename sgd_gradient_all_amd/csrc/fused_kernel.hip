@@ -399,6 +399,56 @@ __global__ __launch_bounds__(kBlock) void bcast_kernel(RankPtrs bufs, BcastArgs 
         bcast_tile<E>(bufs, a, q0 + (uint64_t)k, r0, r1);
 }
 
+// ---------------------------------------------------------------------------
+// tiny spans: a group made only of spans of at most kTinySpanMax elements.
+// Wave w of workgroup b takes tiny span lo + 4 b + w, lane l its element l:
+// the chain is walked in the span's order (groups of `group` entries, then
+// the group sums), the mean applied, and the result written to every rank,
+// exactly as the one-kernel pass does.  Loads go out kTinyBatch at a time
+// ahead of their adds.  No barrier: whole waves and lanes may leave early.
+// ---------------------------------------------------------------------------
+constexpr int kTinyBatch = 8;
+
+template <class E>
+__global__ __launch_bounds__(kBlock) void tiny_kernel(RankPtrs bufs, TinyArgs a) {
+    using T = typename E::T;
+    const uint32_t t = a.lo + blockIdx.x * (uint32_t)(kBlock / 64) + (threadIdx.x >> 6);
+    if (t >= a.hi)
+        return;
+    const DevSpan sp = a.spans[a.tiny[t]];
+    const uint32_t lane = threadIdx.x & 63u;
+    if (lane >= sp.len)
+        return;
+    const uint64_t e = sp.off + lane;
+    const uint8_t *ch = a.chains + sp.chain_off;
+    const int P = a.P;
+    T acc = 0, gacc = 0;
+    int pos = 0;
+    bool first_group = true;
+    for (int b = 0; b < P; b += kTinyBatch) {
+        T x[kTinyBatch];
+#pragma unroll
+        for (int j = 0; j < kTinyBatch; ++j)
+            if (b + j < P)
+                x[j] = *(reinterpret_cast<const T DDL_GLOBAL *>(
+                             reinterpret_cast<uint64_t>(bufs.p[ch[b + j]])) + e);
+#pragma unroll
+        for (int j = 0; j < kTinyBatch; ++j)
+            if (b + j < P) {
+                gacc = pos == 0 ? x[j] : E::add1(gacc, x[j]);
+                if (++pos == a.group) {
+                    acc = first_group ? gacc : E::add1(acc, gacc);
+                    first_group = false;
+                    pos = 0;
+                }
+            }
+    }
+    if (a.mean)
+        acc = E::div1(acc, a.divisor);
+    for (int r = 0; r < P; ++r)
+        static_cast<T *>(bufs.p[r])[e] = acc;
+}
+
 }  // namespace
 
 namespace {
@@ -472,6 +522,19 @@ int launch_fused(int dtype, const RankPtrs &bufs, const FusedArgs &a, const SgdA
         else
             launch_e<F16, false>(grid, s, bufs, a, sgd, home);
     }
+    return (int)hipGetLastError();
+}
+
+int launch_tiny(int dtype, const RankPtrs &bufs, const TinyArgs &a, void *stream) {
+    if (a.hi <= a.lo)
+        return (int)hipSuccess;
+    constexpr uint32_t kWaves = kBlock / 64;
+    const dim3 grid((a.hi - a.lo + kWaves - 1) / kWaves), block(kBlock);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dtype == DDL_F32)
+        hipLaunchKernelGGL((tiny_kernel<F32>), grid, block, 0, s, bufs, a);
+    else
+        hipLaunchKernelGGL((tiny_kernel<F16>), grid, block, 0, s, bufs, a);
     return (int)hipGetLastError();
 }
 

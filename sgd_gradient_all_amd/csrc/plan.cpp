@@ -69,6 +69,7 @@ struct Part {
     uint32_t *d_span_prefix = nullptr;
     uint32_t *d_span_of_tile = nullptr;
     uint8_t *d_chains = nullptr;
+    uint32_t *d_tiny = nullptr;
     DevSpan *d_bk_spans = nullptr;
     uint32_t *d_bk_prefix = nullptr;
     uint32_t *d_bk_of_tile = nullptr;
@@ -138,6 +139,7 @@ void release_device(ddl_plan p) {
         (void)hipFree(pt.d_span_prefix);
         (void)hipFree(pt.d_span_of_tile);
         (void)hipFree(pt.d_chains);
+        (void)hipFree(pt.d_tiny);
         (void)hipFree(pt.d_bk_spans);
         (void)hipFree(pt.d_bk_prefix);
         (void)hipFree(pt.d_bk_of_tile);
@@ -210,6 +212,7 @@ int bind_device(ddl_plan p, int dev) {
             (rc = upload(&pt.d_span_prefix, s.span_prefix.data(), s.span_prefix.size())) ||
             (rc = upload(&pt.d_span_of_tile, s.span_of_tile.data(), s.span_of_tile.size())) ||
             (rc = upload(&pt.d_chains, s.chains.data(), s.chains.size())) ||
+            (rc = upload(&pt.d_tiny, s.tiny.data(), s.tiny.size())) ||
             (rc = upload(&pt.d_bk_spans, s.bk_spans.data(), s.bk_spans.size())) ||
             (rc = upload(&pt.d_bk_prefix, s.bk_prefix.data(), s.bk_prefix.size())) ||
             (rc = upload(&pt.d_bk_of_tile, s.bk_of_tile.data(), s.bk_of_tile.size())))
@@ -378,6 +381,25 @@ struct Launcher {
         for (int b = b0; b < b1; ++b)
             elems += s.buckets[b].len;
         const bool two = fused_passes(p, s, elems) == 2;
+        if (!two && !sgd && s.tiny_prefix[hi] - s.tiny_prefix[lo] == hi - lo) {
+            // every span of the group is tiny: one wave per span
+            TinyArgs ta;
+            ta.spans = pt->d_spans;
+            ta.tiny = pt->d_tiny;
+            ta.chains = pt->d_chains;
+            ta.lo = s.tiny_prefix[lo];
+            ta.hi = s.tiny_prefix[hi];
+            ta.P = s.P;
+            ta.group = s.group;
+            ta.mean = s.op == DDL_MEAN;
+            ta.divisor = (float)s.P;
+            int rc = bracket_begin(DDL_K_FUSED);
+            if (rc)
+                return rc;
+            if (launch_tiny(s.dtype, bufs, ta, stream) != hipSuccess)
+                return DDL_E_HIP;
+            return bracket_end();
+        }
         // two-kernel SGD without kept gradients: the results go to the
         // plan's scratch buffer, and the gradient buffers stay as they were
         const bool scratch = two && sgd && !sgd->keep_grads;

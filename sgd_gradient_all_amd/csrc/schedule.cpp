@@ -352,6 +352,13 @@ int build_schedule(Schedule &s, int P, uint64_t n, int dtype, int op, const ddl_
     for (size_t i = 0; i < s.spans.size(); ++i)
         for (uint32_t t = s.span_prefix[i]; t < s.span_prefix[i + 1]; ++t)
             s.span_of_tile[t] = (uint32_t)i;
+    s.tiny_prefix.assign(s.spans.size() + 1, 0);
+    for (size_t i = 0; i < s.spans.size(); ++i) {
+        const bool tiny = s.spans[i].len <= kTinySpanMax;
+        if (tiny)
+            s.tiny.push_back((uint32_t)i);
+        s.tiny_prefix[i + 1] = s.tiny_prefix[i] + (tiny ? 1u : 0u);
+    }
     ranges.clear();
     for (const Bucket &b : s.buckets) {
         s.bk_spans.push_back({b.off, b.len, 0u, b.off % s.q == 0 ? (uint32_t)kItemAligned : 0u});

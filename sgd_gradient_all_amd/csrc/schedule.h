@@ -45,6 +45,8 @@ struct Schedule {
     std::vector<uint32_t> span_prefix;   // tile prefix, nspans+1
     std::vector<uint32_t> span_of_tile;  // [t] the span fused tile t belongs to
     bool fused_anchor = false;           // fused tiles anchored (ddl_internal.h)
+    std::vector<uint32_t> tiny;          // spans of <= kTinySpanMax elements, in order
+    std::vector<uint32_t> tiny_prefix;   // tiny spans before span i, nspans+1
 
     // broadcast tables (two-kernel fused form, groups whose buckets are not
     // one contiguous run): a DevSpan per bucket (chain unused), its anchored

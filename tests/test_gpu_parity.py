@@ -116,6 +116,54 @@ def test_small_bitwise(w, mode, op):
         assert bitwise_equal(out[r], ref[r]), (w.name, mode, op, r)
 
 
+TINY_TOPOS = [
+    ("ring40", 40, dict(topo="ring")),
+    ("mring16k4", 16, dict(topo="multiring", k=4)),
+    ("torus4x4", 16, dict(topo="torus2d", rows=4, cols=4)),
+    ("torus2x3", 6, dict(topo="torus2d", rows=2, cols=3)),
+]
+
+
+@pytest.mark.parametrize("name,P,tk", TINY_TOPOS, ids=[t[0] for t in TINY_TOPOS])
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("op", ["sum", "mean"])
+@pytest.mark.parametrize("gated", [True, False])
+def test_tiny_spans_one_wave_each(name, P, tk, dtype, op, gated):
+    """Buckets whose every span has at most 64 elements (one to a few
+    elements per rank chunk) run one wave per span when a group holds only
+    them; groups mixing them with larger spans take the tiled pass.  With one
+    ready event per bucket every group is one bucket; without events the
+    whole list is one mixed group.  Every element of every rank against the
+    oracle, in the automatic (one-kernel) fused form and stepwise."""
+    sizes = [1, 2, 7, 17, 64, 100, 333, 1000, 4096, 4100, 5000, 20000]
+    buckets, at = [], 0
+    for c in sizes:
+        buckets.append((at, c))
+        at += c
+    w = Workload(f"tiny-{name}", P, at, dtype, op, tk["topo"], k=tk.get("k", 1),
+                 rows=tk.get("rows", 0), cols=tk.get("cols", 0), dist="normal", sigma=1e-2,
+                 seed=71, buckets=buckets[::-1])
+    say(f"case tiny spans {name} {dtype} {op} gated={gated}")
+    g = host_inputs(w)
+    ref = [x.copy() for x in g]
+    oracle_full(w, ref)
+    stream = torch.cuda.current_stream()
+    for mode in ("fused", "stepwise"):
+        bufs = to_device(g)
+        events = None
+        if gated:
+            events = [torch.cuda.Event() for _ in buckets]
+            for e in events:
+                e.record(stream)
+        plan = make_plan(w, mode)
+        plan.execute(bufs, events=events, stream=stream)
+        torch.cuda.synchronize()
+        plan.destroy()
+        out = to_host(bufs)
+        for r in range(P):
+            assert bitwise_equal(out[r], ref[r]), (name, dtype, op, gated, mode, r)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 def test_subnormals_and_specials(dtype):
     say(f"case subnormals/specials {dtype}")
