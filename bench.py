@@ -22,7 +22,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "achieved HBM GB/s and % of peak per all-reduce (300M fp32, P=40 ring)"
-LEGS = ("stepwise", "overlap", "sgd", "lars", "typed", "per_gpu_step")
+LEGS = ("stepwise", "overlap", "sgd", "lars", "typed", "per_gpu_step", "configs")
 PEAK_HBM_GBPS = 8000.0
 # committed counter summaries: one file per form of the fused pass
 TRAFFIC_FILES = {1: ("fused_kernel", "hbm_bytes_per_launch"),
@@ -269,8 +269,58 @@ def extras(args, w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_b
                                args.passes)
     if "typed" in args.legs:
         out["typed"] = typed_leg(main_stream, torch, ddl, synth)
+    if "configs" in args.legs:
+        out["configs"] = configs_leg(w, main_stream, torch, ddl, synth)
     if "per_gpu_step" in args.legs:
         out["per_gpu_step"] = per_gpu_step_leg(w, main_stream, torch, ddl)
+    return out
+
+
+def configs_leg(head, main_stream, torch, ddl, synth):
+    """The other workloads, each in its plan's default fused form on fresh
+    inputs: ms per all-reduce and HBM GB/s over its algorithmic bytes (the
+    4-rank 2^20 case fits the caches, so its figure is not an HBM one)."""
+    from synth.workloads import WORKLOADS
+    out = {}
+    for name, w in WORKLOADS.items():
+        if name == head.name:
+            continue
+        tdt = torch.float32 if w.dtype == "f32" else torch.float16
+        sdt = synth.F32 if w.dtype == "f32" else synth.F16
+        bufs = [torch.empty(w.n, dtype=tdt, device="cuda") for _ in range(w.P)]
+        for r, b in enumerate(bufs):
+            synth.fill_device(b.data_ptr(), w.n, sdt, w.dist, w.seed, r, sigma=w.sigma)
+        torch.cuda.synchronize()
+        buckets = w.bucket_list()
+        evs = [torch.cuda.Event() for _ in buckets] if w.side_stream else None
+        plan = ddl.Plan(w.P, w.n, w.dtype, w.op, ddl.topo(w.topo, w.k, w.rows, w.cols),
+                        buckets, "fused")
+        _, nbytes = plan.traffic()
+        reps = 10 if nbytes > (4 << 30) else 50
+
+        def run(k):
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record(main_stream)
+            for _ in range(k):
+                if evs:
+                    for e in evs:
+                        e.record(main_stream)
+                plan.execute(bufs, events=evs, stream=main_stream)
+            t1.record(main_stream)
+            torch.cuda.synchronize()
+            return t0.elapsed_time(t1) / k
+
+        run(3)
+        ms = run(reps)
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"ms": round(ms, 4), "hbm_GBps": round(gbps, 1),
+                     "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
+                     "fused_passes": plan.fused_passes(), "bytes": nbytes,
+                     "cache_resident": nbytes < (256 << 20)}
+        plan.destroy()
+        del bufs
+        torch.cuda.empty_cache()
+    log(f"bench: configs {out}")
     return out
 
 
