@@ -94,7 +94,11 @@ struct ddl_plan_s {
     int device = -1;        // bound at first execution
     hipStream_t side[kMaxSideStreams] = {};
     hipEvent_t side_done[kMaxSideStreams] = {};
-    hipEvent_t call_ev = nullptr, last_ev = nullptr;
+    hipEvent_t call_ev = nullptr;
+    // the end of the latest call on each stream a call ended on: calls on
+    // one stream complete in order, calls on different streams need one
+    // event each, or a plan could be freed under an earlier call's kernels
+    std::vector<std::pair<hipStream_t, hipEvent_t>> last_ev;
     // typed plans: a group's smaller element-type passes run on part_side,
     // forked from and joined back into the group's stream
     hipStream_t part_side = nullptr;
@@ -152,15 +156,16 @@ void release_device(ddl_plan p) {
         (void)hipEventDestroy(e);
     if (p->call_ev)
         (void)hipEventDestroy(p->call_ev);
-    if (p->last_ev)
-        (void)hipEventDestroy(p->last_ev);
+    for (auto &se : p->last_ev)
+        (void)hipEventDestroy(se.second);
+    p->last_ev.clear();
     if (p->part_fork)
         (void)hipEventDestroy(p->part_fork);
     if (p->part_join)
         (void)hipEventDestroy(p->part_join);
     if (p->part_side)
         (void)hipStreamDestroy(p->part_side);
-    p->call_ev = p->last_ev = p->part_fork = p->part_join = nullptr;
+    p->call_ev = p->part_fork = p->part_join = nullptr;
     p->part_side = nullptr;
     for (int i = 0; i < kMaxSideStreams; ++i) {
         if (p->side_done[i])
@@ -181,8 +186,7 @@ int bind_device(ddl_plan p, int dev) {
         if (hipStreamCreateWithFlags(&p->side[i], hipStreamNonBlocking) != hipSuccess ||
             hipEventCreateWithFlags(&p->side_done[i], hipEventDisableTiming) != hipSuccess)
             return DDL_E_HIP;
-    if (hipEventCreateWithFlags(&p->call_ev, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&p->last_ev, hipEventDisableTiming) != hipSuccess)
+    if (hipEventCreateWithFlags(&p->call_ev, hipEventDisableTiming) != hipSuccess)
         return DDL_E_HIP;
     if (p->parts.size() > 1 &&
         (hipStreamCreateWithFlags(&p->part_side, hipStreamNonBlocking) != hipSuccess ||
@@ -772,7 +776,18 @@ int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stre
     }
     if (done_event && hipEventRecord(static_cast<hipEvent_t>(done_event), ls) != hipSuccess)
         return DDL_E_HIP;
-    if (hipEventRecord(p->last_ev, ls) != hipSuccess)
+    hipEvent_t *last = nullptr;
+    for (auto &se : p->last_ev)
+        if (se.first == ls)
+            last = &se.second;
+    if (!last) {
+        hipEvent_t e;
+        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
+            return DDL_E_HIP;
+        p->last_ev.emplace_back(ls, e);
+        last = &p->last_ev.back().second;
+    }
+    if (hipEventRecord(*last, ls) != hipSuccess)
         return DDL_E_HIP;
     p->in_flight = true;
     return DDL_OK;
@@ -784,9 +799,11 @@ bool busy(ddl_plan p) {
     int cur = 0;
     (void)hipGetDevice(&cur);
     (void)hipSetDevice(p->device);
-    const hipError_t q = hipEventQuery(p->last_ev);
+    bool pending = false;
+    for (auto &se : p->last_ev)
+        pending = pending || hipEventQuery(se.second) == hipErrorNotReady;
     (void)hipSetDevice(cur);
-    if (q == hipErrorNotReady)
+    if (pending)
         return true;
     p->in_flight = false;
     return false;

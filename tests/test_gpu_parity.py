@@ -561,6 +561,35 @@ def test_destroy_with_work_in_flight_is_busy():
     assert bool((bufs[5] == P).all())
 
 
+def test_busy_tracks_every_stream_a_plan_ran_on():
+    """One plan, two calls on two streams: the first queued behind several
+    milliseconds of other work, the second free to finish at once.  Once the
+    second has finished the plan is still busy with the first, so destroy
+    refuses (DDL_E_BUSY) until that one is done too."""
+    say("case busy over two streams")
+    P, n = 8, 1 << 20
+    bufs_a = [torch.ones(n, device="cuda") for _ in range(P)]
+    bufs_b = [torch.full((n,), 2.0, device="cuda") for _ in range(P)]
+    scratch = torch.zeros(1 << 28, device="cuda")
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    plan = ddl.Plan(P, n, "f32", "sum", ddl.topo("ring"))
+    plan.execute(bufs_b, stream=torch.cuda.current_stream())   # binds the plan
+    for b in bufs_b:
+        b.fill_(2.0)
+    torch.cuda.synchronize()
+    for _ in range(8):   # keep stream a busy for several milliseconds
+        synth.stream_compute(scratch.data_ptr(), scratch.numel(), 1.0, 0.0, sa.cuda_stream)
+    plan.execute(bufs_a, stream=sa)
+    plan.execute(bufs_b, stream=sb)
+    sb.synchronize()
+    assert bool((bufs_b[3] == 2.0 * P).all())
+    rc = ddl.lib().ddl_plan_destroy(plan.handle)
+    assert rc == -7
+    torch.cuda.synchronize()
+    plan.destroy()
+    assert bool((bufs_a[5] == P).all())
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 def test_max_ranks(dtype):
     say(f"case 128 ranks {dtype}")
