@@ -67,7 +67,12 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ring_p40_300m_64b")
-    ap.add_argument("--mode", default="fused", choices=["fused", "stepwise"])
+    ap.add_argument("--mode", default=os.environ.get("DDL_MODE", "fused"),
+                    choices=["fused", "stepwise"], help="default: $DDL_MODE, else fused")
+    ap.add_argument("--coalesce-bytes", type=int,
+                    default=int(os.environ.get("DDL_COALESCE", "0")),
+                    help="the headline plan's grouping threshold in bytes per rank "
+                         "(ddl_plan_set_coalesce_bytes; default: $DDL_COALESCE, else 0)")
     ap.add_argument("--passes", type=int, default=0, choices=[0, 1, 2],
                     help="fused pass form: 0 the plan's choice, 1 one kernel, "
                          "2 reduce + broadcast kernels")
@@ -141,6 +146,8 @@ def main():
     plan_build_ms = (time.perf_counter() - t_plan) * 1e3
     if args.mode == "fused":
         plan.set_fused_passes(args.passes)
+    if args.coalesce_bytes:
+        plan.set_coalesce_bytes(args.coalesce_bytes)
     passes = plan.fused_passes()
     _, hbm_bytes = plan.traffic()
     evs = make_events()
@@ -209,6 +216,7 @@ def main():
         "config": {"workload": w.name, "P": w.P, "n": w.n, "topology": w.topo, "k": w.k,
                    "rows": w.rows, "cols": w.cols, "op": w.op, "buckets": len(buckets),
                    "side_stream": w.side_stream, "mode": args.mode,
+                   "coalesce_bytes": args.coalesce_bytes,
                    "fused_passes": passes, "bytes_per_step": hbm_bytes},
         "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "bus_bw_GBps": round(bus_bw, 2),
