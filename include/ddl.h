@@ -40,8 +40,10 @@
  * of bucket issue order, and identical on every rank.
  *
  * Ownership: the caller owns the buffers (device memory, in place), streams
- * and events.  A plan owns its host and device tables and one side stream;
- * it allocates device memory once, on its first execution, never per call.
+ * and events.  A plan owns its host and device tables, its side streams and
+ * events; it allocates device memory once, on its first execution (the LARS
+ * step and two-kernel SGD without kept gradients add a buffer each on their
+ * first call), never per call.
  *
  * Errors: every entry point returns DDL_OK (0) or a negative DDL_E_* code;
  * arguments are validated before anything is enqueued, so a failed call
