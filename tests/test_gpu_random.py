@@ -8,6 +8,8 @@ coalescing threshold, a side-stream count and an execution form (one-kernel
 or two-kernel fused pass, or step by step).  Every element of every rank is
 compared bit for bit with the oracle's walk of the same schedule.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -21,7 +23,9 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-NCASES = 48
+# more cases on request: DDL_RANDOM_CASES / DDL_RANDOM_STEP_CASES
+NCASES = int(os.environ.get("DDL_RANDOM_CASES", "48"))
+NSTEP_CASES = int(os.environ.get("DDL_RANDOM_STEP_CASES", "24"))
 
 
 def draw(seed):
@@ -117,7 +121,7 @@ def test_random_configuration(seed):
         assert got.tobytes() == want[r].tobytes(), (seed, r)
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(NSTEP_CASES))
 def test_random_sgd_and_lars(seed):
     """The SGD step (kept or dropped gradients) or the LARS step on a drawn
     configuration, with shared or per-rank weight replicas; SGD bit for bit,
