@@ -191,3 +191,66 @@ def test_random_sgd_and_lars(seed):
                        (seed, r))
         else:
             assert got.tobytes() == want_w[r].tobytes(), (seed, "weights", r)
+
+
+NTYPED_CASES = int(os.environ.get("DDL_RANDOM_TYPED_CASES", "16"))
+
+
+@pytest.mark.parametrize("seed", range(NTYPED_CASES))
+def test_random_typed_configuration(seed):
+    """Plans whose buckets carry their own element type: a drawn topology and
+    form over a random mixed layout (binary16 and binary32 buckets, odd
+    binary16 counts, empty buckets), with or without shared ready events;
+    every byte against the oracle's walk of each bucket alone."""
+    from test_gpu_typed import expected, fill
+    c = draw(3000 + seed)
+    rng = np.random.default_rng(9000 + seed)
+    P = c["P"]
+    segs, at = [], 0
+    for _ in range(int(rng.integers(1, 14))):
+        dt = "f16" if rng.random() < 0.5 else "f32"
+        esz = 4 if dt == "f32" else 2
+        if at % esz:
+            off, cnt, pdt = segs[-1]
+            segs[-1] = (off, cnt + 1, pdt)
+            at += 2
+        r = rng.random()
+        cnt = 0 if r < 0.08 else int(rng.integers(1, 300 if r < 0.4 else 60_000))
+        segs.append((at, cnt, dt))
+        at += cnt * esz
+    if at % 4:   # keep the total a whole number of binary32 elements
+        off, cnt, pdt = segs[-1]
+        segs[-1] = (off, cnt + 1, pdt)
+        at += 2
+    order = list(rng.permutation(len(segs)))
+    segs = [segs[i] for i in order]
+    nbytes = at
+    tk = {"kind": c["kind"], "k": c["k"], "rows": c["rows"], "cols": c["cols"]}
+    say(f"case random typed {seed}: P={P} {c['kind']} k={c['k']} grid={c['rows']}x{c['cols']} "
+        f"buckets={len(segs)} bytes={nbytes} form={c['form']} events={c['ev_of'] is not None}")
+    host = fill(P, segs, nbytes, 60 + seed)
+    want = expected(P, segs, host, c["op"], c["kind"], c["k"], c["rows"], c["cols"])
+    dev = [torch.zeros(nbytes + 16, dtype=torch.uint8, device="cuda") for _ in range(P)]
+    for d, h in zip(dev, host):
+        d[:nbytes].copy_(torch.from_numpy(h))
+    mode = "stepwise" if c["form"] == "stepwise" else "fused"
+    plan = ddl.Plan.typed(P, nbytes, c["op"],
+                          ddl.topo(tk["kind"], tk["k"], tk["rows"], tk["cols"]), segs, mode)
+    if mode == "fused":
+        plan.set_fused_passes(1 if c["form"] == "fused1" else 2)
+    plan.set_side_streams(c["nside"])
+    stream = torch.cuda.current_stream()
+    events = None
+    if rng.random() < 0.7:
+        pool, events = {}, []
+        for b in range(len(segs)):
+            key = b // int(rng.integers(1, 4))
+            if key not in pool:
+                pool[key] = torch.cuda.Event()
+                pool[key].record(stream)
+            events.append(pool[key])
+    plan.execute(dev, events=events, stream=stream)
+    torch.cuda.synchronize()
+    plan.destroy()
+    for r in range(P):
+        assert dev[r][:nbytes].cpu().numpy().tobytes() == want[r].tobytes(), (seed, r)
