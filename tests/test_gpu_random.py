@@ -28,9 +28,11 @@ NCASES = int(os.environ.get("DDL_RANDOM_CASES", "48"))
 NSTEP_CASES = int(os.environ.get("DDL_RANDOM_STEP_CASES", "24"))
 
 
-def draw(seed):
-    rng = np.random.default_rng(1000 + seed)
-    P = int(rng.choice([1, 2, 3, 4, 5, 7, 8, 12, 16, 24, 40]))
+def draw(seed, wide=False):
+    """wide: rank counts up to 128 and buckets up to 2M elements."""
+    rng = np.random.default_rng((5000 if wide else 1000) + seed)
+    P = int(rng.choice([1, 2, 3, 4, 5, 7, 8, 12, 16, 24, 40] +
+                       ([48, 64, 96, 100, 127, 128] if wide else [])))
     dtype = str(rng.choice(["f32", "f16"]))
     op = str(rng.choice(["sum", "mean"]))
     kind = str(rng.choice(["ring", "multiring", "torus2d"]))
@@ -55,7 +57,7 @@ def draw(seed):
         elif r < 0.8:
             sizes.append(int(rng.integers(200, 20_000)))
         else:
-            sizes.append(int(rng.integers(20_000, 150_000)))
+            sizes.append(int(rng.integers(20_000, 2_000_000 if wide else 150_000)))
     offs = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(int).tolist()
     buckets = [(int(o), int(c)) for o, c in zip(offs, sizes)]
     perm = rng.permutation(nb)
@@ -76,9 +78,14 @@ def draw(seed):
                 coalesce=coalesce, nside=nside, seed=seed)
 
 
-@pytest.mark.parametrize("seed", range(NCASES))
+NWIDE_CASES = int(os.environ.get("DDL_RANDOM_WIDE_CASES", "4"))
+
+
+@pytest.mark.parametrize("seed", [("base", s) for s in range(NCASES)] +
+                         [("wide", s) for s in range(NWIDE_CASES)], ids=str)
 def test_random_configuration(seed):
-    c = draw(seed)
+    kind_, seed = seed
+    c = draw(seed, wide=kind_ == "wide")
     say(f"case random {seed}: P={c['P']} {c['dtype']} {c['op']} {c['kind']} k={c['k']} "
         f"grid={c['rows']}x{c['cols']} n={c['n']} buckets={len(c['buckets'])} "
         f"form={c['form']} events={c['ev_of'] is not None} coalesce={c['coalesce']} "
