@@ -221,7 +221,8 @@ int ddl_plan_execute_lars(ddl_plan plan, void *const *bufs, void *const *weights
  * arguments -- the cache key is everything except the buffers and events --
  * and executes it with the buckets' ready_event fields.  Thread-safe.  The
  * cache holds at most 64 plans: a new one first destroys the least recently
- * used plan that has no work in flight. */
+ * used plan that has no work in flight (freeing its device tables, which
+ * waits for the device like any hipFree). */
 int ddl_allreduce(void *const *bufs, int P, size_t n, ddl_dtype dtype, ddl_op op,
                   const ddl_topo *topo, const ddl_bucket *buckets, int nbuckets,
                   ddl_mode mode, void *stream, void *done_event);
