@@ -349,6 +349,18 @@ class Plan:
             _check(lib().ddl_plan_destroy(self.handle), "ddl_plan_destroy")
             self.handle = None
 
+    def try_destroy(self):
+        """ddl_plan_destroy that reports work in flight instead of raising:
+        returns 0 once the plan is freed, DDL_E_BUSY (-7) while it is not."""
+        if not self.handle:
+            return 0
+        rc = lib().ddl_plan_destroy(self.handle)
+        if rc == 0:
+            self.handle = None
+        elif rc != -7:
+            _check(rc, "ddl_plan_destroy")
+        return rc
+
     def __del__(self):
         try:
             if self.handle:

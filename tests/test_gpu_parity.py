@@ -5,6 +5,8 @@ Bit-exact comparison of every element at sizes the oracle walks in seconds
 properties at the full workload sizes, in the launch configuration the
 benchmark times.  Every test names its case on stdout before touching the GPU.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -21,6 +23,8 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 TORCH_DT = {"f32": torch.float32, "f16": torch.float16}
+# launches that the runtime serialises complete before the launch call returns
+SERIALISED = os.environ.get("AMD_SERIALIZE_KERNEL", "0") not in ("", "0")
 
 
 def to_device(arrs):
@@ -554,8 +558,9 @@ def test_destroy_with_work_in_flight_is_busy():
         synth.stream_compute(scratch.data_ptr(), scratch.numel(), 1.0, 0.0, stream.cuda_stream)
     plan = ddl.Plan(P, n, "f32", "sum", ddl.topo("ring"))
     plan.execute(bufs, stream=stream)
-    rc = ddl.lib().ddl_plan_destroy(plan.handle)
-    assert rc == -7
+    rc = plan.try_destroy()
+    # with launches serialised (AMD_SERIALIZE_KERNEL) nothing is ever in flight
+    assert rc == -7 or (SERIALISED and rc == 0)
     torch.cuda.synchronize()
     plan.destroy()
     assert bool((bufs[5] == P).all())
@@ -583,8 +588,8 @@ def test_busy_tracks_every_stream_a_plan_ran_on():
     plan.execute(bufs_b, stream=sb)
     sb.synchronize()
     assert bool((bufs_b[3] == 2.0 * P).all())
-    rc = ddl.lib().ddl_plan_destroy(plan.handle)
-    assert rc == -7
+    rc = plan.try_destroy()
+    assert rc == -7 or (SERIALISED and rc == 0)
     torch.cuda.synchronize()
     plan.destroy()
     assert bool((bufs_a[5] == P).all())
