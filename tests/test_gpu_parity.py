@@ -479,6 +479,46 @@ def test_plan_cache_is_bounded():
     assert ddl.ddl_cache_count() == 0
 
 
+def test_oneshot_from_several_threads():
+    """ddl_allreduce from four host threads at once, each on its own stream,
+    cycling through 20 shapes of its own (80 in all, so the 64-plan cache
+    evicts while other threads' work is in flight): every call gives the
+    closed form, and no plan is freed under running work."""
+    import threading
+    say("case one-shot from four threads")
+    ddl.ddl_cache_clear()
+    P, errors = 3, []
+
+    def worker(t):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for i in range(40):
+                    n = 4096 + 8 * (t * 1000 + i % 20)
+                    bufs = [torch.full((n,), float(r + 1), device="cuda") for r in range(P)]
+                    ddl.ddl_allreduce(bufs, n, "f32", "sum", ddl.topo("ring"), stream=s)
+                    if i % 7 == 0:
+                        s.synchronize()
+                        if not all(bool((b == 6.0).all()) for b in bufs):
+                            errors.append((t, i, "values"))
+                s.synchronize()
+                if not all(bool((b == 6.0).all()) for b in bufs):
+                    errors.append((t, "last", "values"))
+        except Exception as e:   # surfaced below
+            errors.append((t, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=120)
+    assert not any(th.is_alive() for th in threads)
+    torch.cuda.synchronize()
+    assert not errors, errors
+    assert ddl.ddl_cache_count() <= 64
+    ddl.ddl_cache_clear()
+
+
 # ---------------------------------------------------------------------------
 # dispatcher: grouping threshold, stream semantics, busy plans; edge shapes
 # ---------------------------------------------------------------------------
