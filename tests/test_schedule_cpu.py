@@ -446,3 +446,24 @@ def test_oneshot_rejects_bad_rank_counts_before_reading_ring_orders():
         assert rc == -2, (P, kind, k, rc)
     n = ctypes.c_size_t(99)
     assert ddl.lib().ddl_cache_count(ctypes.byref(n)) == 0 and n.value == 0
+
+
+def test_plan_layer_under_sanitizers(tmp_path):
+    """The plan layer's host code (plan.cpp with schedule.cpp), built with
+    AddressSanitizer and UndefinedBehaviorSanitizer (g++, host code only),
+    against a fake device whose memory is host memory: random plain and typed
+    plans through every entry point, each kernel launch's tile ranges checked
+    against the tables it indexes, and every allocation, stream and event
+    released."""
+    exe = tmp_path / "plan_asan"
+    csrc = os.path.join(ROOT, "sgd_gradient_all_amd", "csrc")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=undefined", "-D__HIP_PLATFORM_AMD__",
+                    "-I", "/opt/rocm/include", "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "plan_asan_driver.cpp"),
+                    os.path.join(csrc, "plan.cpp"), os.path.join(csrc, "schedule.cpp"),
+                    "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe), "150"], capture_output=True, text=True, timeout=600,
+                         env=dict(os.environ, ASAN_OPTIONS="detect_leaks=1"))
+    assert out.returncode == 0, out.stdout[-3000:] + out.stderr[-3000:]
+    assert "ok 150 cases" in out.stdout
