@@ -350,7 +350,9 @@ def test_mean_is_correctly_rounded_division():
 
 def test_mean_f16_division_correctly_rounded():
     x = np.arange(0, 0x7c00, dtype=np.uint16)  # all finite non-negative halfs
-    for P in (2, 3, 5, 7, 10, 16, 40):
+    # 14, 26, 28, 30, 56, 82 and 102 are rank counts where a binary32
+    # reciprocal multiply, rounded to binary16, differs from the division
+    for P in (2, 3, 5, 7, 10, 14, 16, 26, 28, 30, 40, 56, 82, 102):
         got = orc.f16_div(x, P)
         want = (x.view(np.float16).astype(np.float64) / P).astype(np.float16).view(np.uint16)
         assert np.array_equal(got, want), P
