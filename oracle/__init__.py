@@ -12,7 +12,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ddl_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# DDL_ORACLE_LIB: load another build of ddl_oracle.c (the mutation tests plant
+# mistakes in scratch copies and check that the pins catch them)
+_LIB_PATH = os.environ.get("DDL_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 F32, F16 = 0, 1
 SUM, MEAN = 0, 1
