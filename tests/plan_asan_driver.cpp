@@ -23,129 +23,7 @@
 
 #include "../sgd_gradient_all_amd/csrc/ddl_internal.h"
 
-// ---------------------------------------------------------------------------
-// fake device
-// ---------------------------------------------------------------------------
-static long g_live_allocs = 0, g_live_streams = 0, g_live_events = 0;
-
-extern "C" {
-hipError_t hipMalloc(void **p, size_t n) {
-    *p = std::malloc(n ? n : 1);
-    ++g_live_allocs;
-    return *p ? hipSuccess : hipErrorOutOfMemory;
-}
-hipError_t hipFree(void *p) {
-    if (p) {
-        std::free(p);
-        --g_live_allocs;
-    }
-    return hipSuccess;
-}
-hipError_t hipMemcpy(void *d, const void *s, size_t n, hipMemcpyKind) {
-    std::memcpy(d, s, n);
-    return hipSuccess;
-}
-hipError_t hipGetDevice(int *d) {
-    *d = 0;
-    return hipSuccess;
-}
-hipError_t hipSetDevice(int) { return hipSuccess; }
-hipError_t hipStreamCreateWithFlags(hipStream_t *s, unsigned) {
-    *s = reinterpret_cast<hipStream_t>(new int(1));
-    ++g_live_streams;
-    return hipSuccess;
-}
-hipError_t hipStreamDestroy(hipStream_t s) {
-    delete reinterpret_cast<int *>(s);
-    --g_live_streams;
-    return hipSuccess;
-}
-hipError_t hipEventCreate(hipEvent_t *e) {
-    *e = reinterpret_cast<hipEvent_t>(new int(2));
-    ++g_live_events;
-    return hipSuccess;
-}
-hipError_t hipEventCreateWithFlags(hipEvent_t *e, unsigned) { return hipEventCreate(e); }
-hipError_t hipEventDestroy(hipEvent_t e) {
-    delete reinterpret_cast<int *>(e);
-    --g_live_events;
-    return hipSuccess;
-}
-hipError_t hipEventRecord(hipEvent_t e, hipStream_t) {
-    return *reinterpret_cast<int *>(e) == 2 ? hipSuccess : hipErrorInvalidValue;
-}
-hipError_t hipStreamWaitEvent(hipStream_t, hipEvent_t e, unsigned) {
-    // caller events are tokens of this driver too (value 2)
-    return *reinterpret_cast<int *>(e) == 2 ? hipSuccess : hipErrorInvalidValue;
-}
-hipError_t hipEventQuery(hipEvent_t) { return hipSuccess; }
-hipError_t hipEventSynchronize(hipEvent_t) { return hipSuccess; }
-hipError_t hipEventElapsedTime(float *ms, hipEvent_t, hipEvent_t) {
-    *ms = 0.f;
-    return hipSuccess;
-}
-}
-
-// ---------------------------------------------------------------------------
-// launchers: argument checks instead of kernels
-// ---------------------------------------------------------------------------
-static long g_launches = 0;
-static void fail(const char *what) {
-    std::printf("FAILED: %s\n", what);
-    std::exit(1);
-}
-namespace ddl {
-int launch_step(int, int, int vpl, const RankPtrs &, const StepArgs &a, const SgdArgs *,
-                uint32_t tiles, void *) {
-    if (!a.items || !a.prefix || tiles == 0 || (vpl != 1 && vpl != 2 && vpl != 4))
-        fail("step launch arguments");
-    if (a.prefix[a.item_lo] > a.tile_base || a.tile_base + tiles > a.prefix[a.item_hi])
-        fail("step launch tiles outside the step's items");
-    ++g_launches;
-    return 0;
-}
-int launch_fused(int, const RankPtrs &, const FusedArgs &a, const SgdArgs *, bool home,
-                 uint32_t tiles, void *) {
-    if (!a.spans || !a.prefix || !a.tile_span || !a.chains || tiles == 0 ||
-        a.tile_end - a.tile_base != tiles || (home && !a.home))
-        fail("fused launch arguments");
-    if (a.prefix[a.span_lo] > a.tile_base || a.tile_end > a.prefix[a.span_hi])
-        fail("fused launch tiles outside the group's spans");
-    for (uint32_t t = a.tile_base; t < a.tile_end; t += 97) {
-        const uint32_t i = a.tile_span[t];
-        if (i < a.span_lo || i >= a.span_hi || a.prefix[i] > t || t >= a.prefix[i + 1])
-            fail("tile -> span table");
-    }
-    ++g_launches;
-    return 0;
-}
-int launch_bcast(int, const RankPtrs &, const BcastArgs &a, void *) {
-    if (a.ranks_per_group < 1 || a.ngroups < 1 || a.tiles_per_group < 1 ||
-        1 + (a.ngroups - 1) * a.ranks_per_group >= a.P)
-        fail("broadcast launch arguments");
-    if (a.spans && (a.tile_end <= a.tile_base || !a.prefix || !a.tile_span))
-        fail("broadcast table launch");
-    if (!a.spans && a.len == 0)
-        fail("empty broadcast run");
-    ++g_launches;
-    return 0;
-}
-int launch_tiny(int, const RankPtrs &, const TinyArgs &a, void *) {
-    if (!a.spans || !a.tiny || !a.chains || a.hi <= a.lo)
-        fail("tiny launch arguments");
-    for (uint32_t t = a.lo; t < a.hi; ++t)
-        if (a.spans[a.tiny[t]].len > kTinySpanMax || a.spans[a.tiny[t]].len == 0)
-            fail("tiny span length");
-    ++g_launches;
-    return 0;
-}
-int launch_lars(int, int, const RankPtrs &, const LarsArgs &a, uint32_t blocks, void *) {
-    if (blocks == 0 || !a.spans || !a.prefix)
-        fail("LARS launch arguments");
-    ++g_launches;
-    return 0;
-}
-}  // namespace ddl
+#include "fake_device.inc"
 
 // ---------------------------------------------------------------------------
 // random cases
