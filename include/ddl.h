@@ -94,7 +94,9 @@ typedef struct ddl_plan_s *ddl_plan;
 enum {
     DDL_OK = 0,
     DDL_E_NULL = -1,     /* a required pointer is NULL */
-    DDL_E_ARG = -2,      /* P, n, dtype, op, mode or topology out of range */
+    DDL_E_ARG = -2,      /* P, n, dtype, op, mode or topology out of range;
+                            or a plan handle that no create call returned or
+                            that ddl_plan_destroy has freed */
     DDL_E_BUCKETS = -3,  /* buckets do not tile [0, n) exactly */
     DDL_E_ALIGN = -4,    /* a rank buffer is not 16-byte aligned */
     DDL_E_HIP = -5,      /* a HIP runtime call failed */
@@ -158,6 +160,11 @@ int ddl_plan_create_typed(ddl_plan *out, int P, size_t nbytes, ddl_op op,
  * buffers race. */
 int ddl_plan_execute(ddl_plan plan, void *const *bufs, void *const *ready_events,
                      void *stream, void *done_event);
+/* HIP graph capture: every execute entry point may be captured on the
+ * caller's stream once the plan has run eagerly on the device (its first
+ * call allocates and uploads its tables, as does the first LARS call and
+ * the first two-kernel SGD call without kept gradients).  The graph then
+ * holds the plan's table addresses: see ddl_plan_destroy. */
 
 /* The all-reduce followed by the SGD step it serves, fused into the
  * reduction's epilogue (the Baidu article, "总结": the all-reduce averages
@@ -221,8 +228,9 @@ int ddl_plan_execute_lars(ddl_plan plan, void *const *bufs, void *const *weights
  * arguments -- the cache key is everything except the buffers and events --
  * and executes it with the buckets' ready_event fields.  Thread-safe.  The
  * cache holds at most 64 plans: a new one first destroys the least recently
- * used plan that has no work in flight (freeing its device tables, which
- * waits for the device like any hipFree). */
+ * used plan that has no work in flight and was never captured into a HIP
+ * graph (freeing its device tables, which waits for the device like any
+ * hipFree). */
 int ddl_allreduce(void *const *bufs, int P, size_t n, ddl_dtype dtype, ddl_op op,
                   const ddl_topo *topo, const ddl_bucket *buckets, int nbuckets,
                   ddl_mode mode, void *stream, void *done_event);
@@ -240,10 +248,20 @@ int ddl_allreduce(void *const *bufs, int P, size_t n, ddl_dtype dtype, ddl_op op
 int ddl_plan_traffic(ddl_plan plan, size_t *sent_elems_per_rank, size_t *hbm_bytes);
 
 /* Free the plan.  Returns DDL_E_BUSY, and frees nothing, while work the plan
- * enqueued has not completed. */
+ * enqueued has not completed; DDL_E_ARG for a handle that is not a live plan
+ * (destroyed already, or never created), which is checked against the
+ * library's registry of live plans before anything is touched, so a second
+ * destroy or a call on a destroyed handle is an error code, not a use of freed
+ * memory.
+ * HIP graphs: an execution captured into a HIP graph (see ddl_plan_execute)
+ * keeps the addresses of the plan's device tables in the graph, and the
+ * library cannot see the graph's replays.  A plan must outlive every graph
+ * and graph executable made from a capture of it: destroy those first. */
 int ddl_plan_destroy(ddl_plan plan);
 
-/* Drop every plan ddl_allreduce cached (DDL_E_BUSY if one is in flight). */
+/* Drop every plan ddl_allreduce cached (DDL_E_BUSY if one is in flight).
+ * Plans whose execution was captured into a HIP graph stay cached until the
+ * process ends: a replay of the graph may still read them. */
 int ddl_cache_clear(void);
 
 /* Number of plans ddl_allreduce holds in its cache. */
@@ -332,11 +350,15 @@ int ddl_set_tuning(int knob, int value);
 int ddl_get_tuning(int knob, int *value);
 
 /* ---- measurement -------------------------------------------------------- *
- * With profiling on, every kernel launch is bracketed by a pair of HIP events
- * on the stream it is launched on.  ddl_plan_profile_read waits for the last
- * of them and reports, for all launches since the previous read, the sum of
- * their durations (ms), their number and the longest one; then it starts a
- * new count.  Costs a few microseconds per launch. */
+ * With profiling on, kernel launches are bracketed by a pair of HIP events
+ * on the stream they are launched on: enable = 1 brackets every launch;
+ * enable = m > 1 brackets the launches of every m-th group of buckets (the
+ * groups counted across calls from this setting on), so that a timed run is
+ * barely slowed; 0 turns it off; negative values are DDL_E_ARG.
+ * ddl_plan_profile_read waits for the last of them and reports, for all
+ * bracketed launches since the previous read, the sum of their durations
+ * (ms), their number and the longest one; then it starts a new count.
+ * Costs a few microseconds per bracketed launch. */
 int ddl_plan_set_profiling(ddl_plan plan, int enable);
 int ddl_plan_profile_read(ddl_plan plan, double *total_ms, int *launches, double *max_ms);
 /* The same, per launch kind: each argument (or NULL) is an array of

@@ -1,6 +1,8 @@
 """ctypes binding of include/ddl.h.  Argument marshalling only."""
+import atexit
 import ctypes
 import os
+import threading
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libddl.so")
@@ -201,11 +203,37 @@ def get_tuning(knob):
     return v.value
 
 
+# Handles of Plans garbage-collected while their work was still in flight
+# (ddl_plan_destroy answered DDL_E_BUSY): destroyed later, when the next
+# Plan is made or executed, or at exit, instead of being leaked.
+_pending = []
+_pending_lock = threading.RLock()  # __del__ may run inside _reap
+
+
+def _reap():
+    """Destroy the pending handles whose work has completed; returns how many
+    are still pending."""
+    with _pending_lock:
+        if not _pending:
+            return 0
+        keep = []
+        for h in _pending:
+            rc = lib().ddl_plan_destroy(h)
+            if rc == -7:  # DDL_E_BUSY: still in flight
+                keep.append(h)
+        _pending[:] = keep
+        return len(keep)
+
+
+atexit.register(_reap)
+
+
 class Plan:
     """Owner of a ddl_plan (ddl_plan_create / execute / traffic / destroy)."""
 
     def __init__(self, P, n, dtype="f32", op="sum", topology=None, buckets=None,
                  mode="fused"):
+        _reap()
         self.P, self.n = P, n
         self.nbuckets = len(buckets) if buckets is not None else (1 if n else 0)
         t = topology if topology is not None else topo()
@@ -220,6 +248,7 @@ class Plan:
     def typed(cls, P, nbytes, op="sum", topology=None, buckets=(), mode="fused"):
         """A plan whose buckets carry their own dtype: buckets is a list of
         (byte_offset, count, dtype) in issue order (ddl_plan_create_typed)."""
+        _reap()
         self = cls.__new__(cls)
         self.P, self.n, self.nbuckets = P, nbytes, len(buckets)
         self.handle = None
@@ -235,6 +264,8 @@ class Plan:
         return self
 
     def execute(self, bufs, events=None, stream=None, done_event=None):
+        if _pending:
+            _reap()
         if len(bufs) != self.P:
             raise ValueError(f"expected {self.P} buffers, got {len(bufs)}")
         ev = None
@@ -294,7 +325,10 @@ class Plan:
         return v.value
 
     def set_profiling(self, on=True):
-        _check(lib().ddl_plan_set_profiling(self.handle, 1 if on else 0), "set_profiling")
+        """True/1: bracket every launch with HIP events; an int m > 1: the
+        launches of every m-th bucket group; False/0: off."""
+        v = int(on) if not isinstance(on, bool) else (1 if on else 0)
+        _check(lib().ddl_plan_set_profiling(self.handle, v), "set_profiling")
 
     def profile_read(self):
         tot, mx = ctypes.c_double(), ctypes.c_double()
@@ -363,8 +397,12 @@ class Plan:
 
     def __del__(self):
         try:
-            if self.handle:
-                lib().ddl_plan_destroy(self.handle)
+            h = getattr(self, "handle", None)
+            if h:
+                self.handle = None
+                if lib().ddl_plan_destroy(h) == -7:  # busy: destroy it later
+                    with _pending_lock:
+                        _pending.append(h)
         except Exception:
             pass
 

@@ -29,6 +29,9 @@
 using namespace ddl;
 
 constexpr int kMaxSideStreams = 4;
+// Events a plan makes when it binds, for the completion tracking of the
+// first caller streams it is executed on.
+constexpr int kSpareEvents = 8;
 
 // process-wide tuning knobs (ddl_set_tuning), stored as value + 1 so that
 // the zero-initialised array means "every knob at its default"
@@ -103,10 +106,23 @@ struct ddl_plan_s {
     // forked from and joined back into the group's stream
     hipStream_t part_side = nullptr;
     hipEvent_t part_fork = nullptr, part_join = nullptr;
+    // events made at binding for last_ev entries of streams first seen later
+    // (the allocation-free entry point creates none)
+    std::vector<hipEvent_t> spare_ev;
     bool in_flight = false;
+    // an execution was enqueued on a stream under HIP graph capture: the
+    // graph holds the addresses of this plan's tables, and its replays are
+    // invisible to the event queries of busy(), so the one-shot cache never
+    // destroys such a plan
+    bool captured = false;
+    // freed by ddl_plan_destroy: a call that looked the handle up before the
+    // destroy finds this under the plan's mutex and enqueues nothing
+    bool dead = false;
 
-    // profiling
+    // profiling: every launch of every prof_stride-th group is bracketed
     bool profiling = false;
+    int prof_stride = 1;
+    uint64_t prof_group = 0;        // groups seen since profiling was set
     std::vector<hipEvent_t> prof;   // pairs (start, end)
     std::vector<int> prof_kind;     // ddl_launch_kind of each pair
     int prof_used = 0;
@@ -159,6 +175,9 @@ void release_device(ddl_plan p) {
     for (auto &se : p->last_ev)
         (void)hipEventDestroy(se.second);
     p->last_ev.clear();
+    for (hipEvent_t e : p->spare_ev)
+        (void)hipEventDestroy(e);
+    p->spare_ev.clear();
     if (p->part_fork)
         (void)hipEventDestroy(p->part_fork);
     if (p->part_join)
@@ -188,6 +207,12 @@ int bind_device(ddl_plan p, int dev) {
             return DDL_E_HIP;
     if (hipEventCreateWithFlags(&p->call_ev, hipEventDisableTiming) != hipSuccess)
         return DDL_E_HIP;
+    for (int i = 0; i < kSpareEvents; ++i) {
+        hipEvent_t e;
+        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
+            return DDL_E_HIP;
+        p->spare_ev.push_back(e);
+    }
     if (p->parts.size() > 1 &&
         (hipStreamCreateWithFlags(&p->part_side, hipStreamNonBlocking) != hipSuccess ||
          hipEventCreateWithFlags(&p->part_fork, hipEventDisableTiming) != hipSuccess ||
@@ -298,6 +323,9 @@ struct LarsCall {
     float lr;
     double coeff, eps;
     float *rates_out;
+    // the partial sums and rates, when not the plan's own buffers
+    double *partial;
+    float *rate;
 };
 
 struct Launcher {
@@ -308,9 +336,10 @@ struct Launcher {
     const LarsCall *lars = nullptr;  // the LARS step after the all-reduce
     Part *pt = nullptr;  // the element type of the current group
     std::vector<Bucket> runs;
+    bool prof = false;   // bracket the launches of the current group
 
     int bracket_begin(int kind) {
-        if (!p->profiling)
+        if (!prof)
             return DDL_OK;
         if ((size_t)(2 * p->prof_used + 2) > p->prof.size()) {
             hipEvent_t a, b;
@@ -325,7 +354,7 @@ struct Launcher {
                                                                                : DDL_E_HIP;
     }
     int bracket_end() {
-        if (!p->profiling)
+        if (!prof)
             return DDL_OK;
         if (hipEventRecord(p->prof[2 * p->prof_used + 1], stream) != hipSuccess)
             return DDL_E_HIP;
@@ -547,8 +576,9 @@ struct Launcher {
     // the LARS step of buckets [b0, b1), once their all-reduce is enqueued:
     // the norms of every tile, the rate of every bucket, the update
     int lars_step(int b0, int b1) {
-        LarsArgs a = update_args(b0, b1, bufs.p[0], pt->d_lars_rate, lars->lr, lars->nweights);
-        a.partial = pt->d_lars_partial;
+        LarsArgs a = update_args(b0, b1, bufs.p[0], lars->rate ? lars->rate : pt->d_lars_rate,
+                                 lars->lr, lars->nweights);
+        a.partial = lars->partial ? lars->partial : pt->d_lars_partial;
         a.rate_out = lars->rates_out;
         a.coeff = lars->coeff;
         a.eps = lars->eps;
@@ -608,6 +638,25 @@ int ensure_lars(ddl_plan p) {
     return DDL_OK;
 }
 
+// The event that records the end of the latest call on stream ls: an
+// existing entry, else one of the events made at binding, else (unless the
+// caller may not allocate) a new one.  Null on failure.
+hipEvent_t *last_event(ddl_plan p, hipStream_t ls, bool may_create = true) {
+    for (auto &se : p->last_ev)
+        if (se.first == ls)
+            return &se.second;
+    hipEvent_t e = nullptr;
+    if (!p->spare_ev.empty()) {
+        e = p->spare_ev.back();
+        p->spare_ev.pop_back();
+    } else if (!may_create ||
+               hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+        return nullptr;
+    }
+    p->last_ev.emplace_back(ls, e);
+    return &p->last_ev.back().second;
+}
+
 int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stream_,
                    void *done_event, const SgdArgs *sgd, const LarsCall *lars = nullptr) {
     const int P = p->parts[0].s.P;
@@ -661,6 +710,16 @@ int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stre
         rp.p[r] = bufs[r];
 
     hipStream_t cs = static_cast<hipStream_t>(stream_);
+    // under HIP graph capture the graph keeps this plan's table addresses
+    // for its replays (a stream the runtime cannot query counts as not
+    // capturing; its error is cleared so that no launch reports it)
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(cs, &cap) != hipSuccess) {
+        (void)hipGetLastError();
+        cap = hipStreamCaptureStatusNone;
+    }
+    if (cap == hipStreamCaptureStatusActive)
+        p->captured = true;
     const int nb = (int)p->order.size();
     bool any_event = false;
     for (int b = 0; ready && b < nb; ++b)
@@ -677,6 +736,7 @@ int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stre
     int b0 = 0, g = 0, used = 0;
     std::vector<std::pair<int, int>> range(p->parts.size());
     while (b0 < nb) {
+        L.prof = p->profiling && p->prof_group++ % (uint64_t)p->prof_stride == 0;
         // the group: equal events, then (with a threshold) more buckets
         // until it holds coalesce_bytes per rank
         void *ev0 = ready ? ready[b0] : nullptr;
@@ -776,17 +836,9 @@ int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stre
     }
     if (done_event && hipEventRecord(static_cast<hipEvent_t>(done_event), ls) != hipSuccess)
         return DDL_E_HIP;
-    hipEvent_t *last = nullptr;
-    for (auto &se : p->last_ev)
-        if (se.first == ls)
-            last = &se.second;
-    if (!last) {
-        hipEvent_t e;
-        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
-            return DDL_E_HIP;
-        p->last_ev.emplace_back(ls, e);
-        last = &p->last_ev.back().second;
-    }
+    hipEvent_t *last = last_event(p, ls);
+    if (!last)
+        return DDL_E_HIP;
     if (hipEventRecord(*last, ls) != hipSuccess)
         return DDL_E_HIP;
     p->in_flight = true;
@@ -816,15 +868,19 @@ bool busy(ddl_plan p) {
 // used plan that has no work in flight.
 constexpr size_t kCacheMax = 64;
 struct CacheEntry {
-    ddl_plan plan;
+    std::shared_ptr<ddl_plan_s> plan;
     uint64_t used;  // g_cache_tick at the last call
 };
+// The cache and the registry below are never destroyed: their plans hold
+// HIP streams, events and device memory, which must not be released by
+// static destructors after the HIP runtime has shut down at process exit.
 std::mutex g_cache_mu;
-std::map<std::string, CacheEntry> g_cache;
+std::map<std::string, CacheEntry> &g_cache = *new std::map<std::string, CacheEntry>;
 uint64_t g_cache_tick = 0;
 
 // Destroys least recently used idle plans until fewer than kCacheMax remain
-// (or every remaining plan is busy).  Caller holds g_cache_mu, which every
+// (or every remaining plan is busy or was captured into a HIP graph, whose
+// replays may still read its tables).  Caller holds g_cache_mu, which every
 // call on a cached plan also holds, so an idle plan stays idle meanwhile.
 void cache_make_room() {
     while (g_cache.size() >= kCacheMax) {
@@ -833,19 +889,72 @@ void cache_make_room() {
             if (victim != g_cache.end() && it->second.used >= victim->second.used)
                 continue;
             std::lock_guard<std::mutex> pl(it->second.plan->mu);
-            if (!busy(it->second.plan))
+            if (!it->second.plan->captured && !busy(it->second.plan.get()))
                 victim = it;
         }
         if (victim == g_cache.end())
             return;
-        ddl_plan p = victim->second.plan;
-        g_cache.erase(victim);
-        {
-            std::lock_guard<std::mutex> pl(p->mu);
-            release_device(p);
-        }
-        delete p;
+        g_cache.erase(victim);  // the last reference: the plan is freed
     }
+}
+
+// ---------------------------------------------------------------------------
+// handles
+// ---------------------------------------------------------------------------
+// Plans handed to callers (ddl_plan_create, ddl_plan_create_typed) are
+// registered here until ddl_plan_destroy; every entry point looks its
+// handle up, so a stale or foreign handle is an argument error, not a use
+// of freed memory.  The one-shot cache's plans are never handed out and are
+// not registered.
+void free_plan(ddl_plan_s *p) {
+    release_device(p);
+    delete p;
+}
+std::mutex g_live_mu;
+std::map<const ddl_plan_s *, std::shared_ptr<ddl_plan_s>> &g_live =
+    *new std::map<const ddl_plan_s *, std::shared_ptr<ddl_plan_s>>;
+
+int register_plan(ddl_plan p, ddl_plan *out) {
+    std::shared_ptr<ddl_plan_s> sp(p, free_plan);
+    std::lock_guard<std::mutex> lk(g_live_mu);
+    g_live.emplace(p, std::move(sp));
+    *out = p;
+    return DDL_OK;
+}
+
+// A live plan, its mutex held.  Members are released in reverse order: the
+// lock, then the reference (which frees the plan if ddl_plan_destroy let go
+// of it meanwhile).
+struct PlanRef {
+    std::shared_ptr<ddl_plan_s> sp;
+    std::unique_lock<std::mutex> lk;
+    int rc = DDL_OK;
+    ddl_plan_s *operator->() const { return sp.get(); }
+    ddl_plan get() const { return sp.get(); }
+};
+
+PlanRef acquire(ddl_plan h) {
+    PlanRef r;
+    if (!h) {
+        r.rc = DDL_E_NULL;
+        return r;
+    }
+    {
+        std::lock_guard<std::mutex> lk(g_live_mu);
+        auto it = g_live.find(h);
+        if (it == g_live.end()) {
+            r.rc = DDL_E_ARG;
+            return r;
+        }
+        r.sp = it->second;
+    }
+    r.lk = std::unique_lock<std::mutex>(r.sp->mu);
+    if (r.sp->dead) {
+        r.lk.unlock();
+        r.sp.reset();
+        r.rc = DDL_E_ARG;
+    }
+    return r;
 }
 
 void put(std::string &k, const void *p, size_t n) { k.append((const char *)p, n); }
@@ -890,9 +999,13 @@ const char *ddl_strerror(int code) {
     }
 }
 
-int ddl_plan_create(ddl_plan *out, int P, size_t n, ddl_dtype dtype, ddl_op op,
-                    const ddl_topo *topo, const ddl_bucket *buckets, int nbuckets,
-                    ddl_mode mode) {
+}  // extern "C"
+
+namespace {
+
+// A plan for ddl_plan_create and the one-shot cache, not yet registered.
+int create_plan(ddl_plan *out, int P, size_t n, ddl_dtype dtype, ddl_op op,
+                const ddl_topo *topo, const ddl_bucket *buckets, int nbuckets, ddl_mode mode) {
     if (!out || !topo)
         return DDL_E_NULL;
     *out = nullptr;
@@ -919,6 +1032,25 @@ int ddl_plan_create(ddl_plan *out, int P, size_t n, ddl_dtype dtype, ddl_op op,
     p->mode = mode;
     *out = p;
     return DDL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ddl_plan_create(ddl_plan *out, int P, size_t n, ddl_dtype dtype, ddl_op op,
+                    const ddl_topo *topo, const ddl_bucket *buckets, int nbuckets,
+                    ddl_mode mode) {
+    ddl_plan p = nullptr;
+    const int rc = create_plan(&p, P, n, dtype, op, topo, buckets, nbuckets, mode);
+    if (rc)
+        return rc;
+    try {
+        return register_plan(p, out);
+    } catch (...) {
+        delete p;
+        return DDL_E_NOMEM;
+    }
 }
 
 int ddl_plan_create_typed(ddl_plan *out, int P, size_t nbytes, ddl_op op, const ddl_topo *topo,
@@ -992,17 +1124,23 @@ int ddl_plan_create_typed(ddl_plan *out, int P, size_t nbytes, ddl_op op, const 
     }
     p->typed = true;
     p->mode = mode;
-    *out = p;
-    return DDL_OK;
+    try {
+        return register_plan(p, out);
+    } catch (...) {
+        delete p;
+        return DDL_E_NOMEM;
+    }
 }
 
 int ddl_plan_execute(ddl_plan plan, void *const *bufs, void *const *ready_events,
                      void *stream, void *done_event) {
     if (!plan || !bufs)
         return DDL_E_NULL;
-    std::lock_guard<std::mutex> lk(plan->mu);
     try {
-        return execute_locked(plan, bufs, ready_events, stream, done_event, nullptr);
+        PlanRef r = acquire(plan);
+        if (r.rc)
+            return r.rc;
+        return execute_locked(r.get(), bufs, ready_events, stream, done_event, nullptr);
     } catch (...) {
         return DDL_E_NOMEM;
     }
@@ -1013,50 +1151,65 @@ int ddl_plan_execute_sgd(ddl_plan plan, void *const *bufs, void *const *weights,
                          void *done_event) {
     if (!plan || !bufs || !weights)
         return DDL_E_NULL;
-    if (plan->typed || (nweights != 1 && nweights != plan->parts[0].s.P))
-        return DDL_E_ARG;
-    if (!keep_grads && plan->mode != DDL_FUSED)
-        return DDL_E_ARG;
-    SgdArgs g;
-    std::memset(&g, 0, sizeof(g));
-    for (int r = 0; r < nweights; ++r)
-        g.w.p[r] = weights[r];
-    g.lr = lr;
-    g.nweights = nweights;
-    g.keep_grads = keep_grads ? 1 : 0;
-    std::lock_guard<std::mutex> lk(plan->mu);
     try {
-        return execute_locked(plan, bufs, ready_events, stream, done_event, &g);
+        PlanRef r = acquire(plan);
+        if (r.rc)
+            return r.rc;
+        if (r->typed || (nweights != 1 && nweights != r->parts[0].s.P))
+            return DDL_E_ARG;
+        if (!keep_grads && r->mode != DDL_FUSED)
+            return DDL_E_ARG;
+        SgdArgs g;
+        std::memset(&g, 0, sizeof(g));
+        for (int i = 0; i < nweights; ++i)
+            g.w.p[i] = weights[i];
+        g.lr = lr;
+        g.nweights = nweights;
+        g.keep_grads = keep_grads ? 1 : 0;
+        return execute_locked(r.get(), bufs, ready_events, stream, done_event, &g);
     } catch (...) {
         return DDL_E_NOMEM;
     }
 }
 
-int ddl_plan_execute_lars(ddl_plan plan, void *const *bufs, void *const *weights, int nweights,
-                          float lr, double coeff, double eps, float *rates_out,
-                          void *const *ready_events, void *stream, void *done_event) {
+namespace {
+
+int execute_lars(ddl_plan plan, void *const *bufs, void *const *weights, int nweights, float lr,
+                 double coeff, double eps, float *rates_out, void *const *ready_events,
+                 void *stream, void *done_event) {
     if (!plan || !bufs || !weights)
         return DDL_E_NULL;
-    if (plan->typed || (nweights != 1 && nweights != plan->parts[0].s.P))
-        return DDL_E_ARG;
-    // finite and >= 0 (NaN fails both comparisons)
-    if (!(coeff >= 0.0 && coeff <= 1e300) || !(eps >= 0.0 && eps <= 1e300))
-        return DDL_E_ARG;
-    LarsCall c;
-    std::memset(&c, 0, sizeof(c));
-    for (int r = 0; r < nweights; ++r)
-        c.w.p[r] = weights[r];
-    c.nweights = nweights;
-    c.lr = lr;
-    c.coeff = coeff;
-    c.eps = eps;
-    c.rates_out = rates_out;
-    std::lock_guard<std::mutex> lk(plan->mu);
     try {
-        return execute_locked(plan, bufs, ready_events, stream, done_event, nullptr, &c);
+        PlanRef r = acquire(plan);
+        if (r.rc)
+            return r.rc;
+        if (r->typed || (nweights != 1 && nweights != r->parts[0].s.P))
+            return DDL_E_ARG;
+        // finite and >= 0 (NaN fails both comparisons)
+        if (!(coeff >= 0.0 && coeff <= 1e300) || !(eps >= 0.0 && eps <= 1e300))
+            return DDL_E_ARG;
+        LarsCall c;
+        std::memset(&c, 0, sizeof(c));
+        for (int i = 0; i < nweights; ++i)
+            c.w.p[i] = weights[i];
+        c.nweights = nweights;
+        c.lr = lr;
+        c.coeff = coeff;
+        c.eps = eps;
+        c.rates_out = rates_out;
+        return execute_locked(r.get(), bufs, ready_events, stream, done_event, nullptr, &c);
     } catch (...) {
         return DDL_E_NOMEM;
     }
+}
+
+}  // namespace
+
+int ddl_plan_execute_lars(ddl_plan plan, void *const *bufs, void *const *weights, int nweights,
+                          float lr, double coeff, double eps, float *rates_out,
+                          void *const *ready_events, void *stream, void *done_event) {
+    return execute_lars(plan, bufs, weights, nweights, lr, coeff, eps, rates_out, ready_events,
+                        stream, done_event);
 }
 
 int ddl_allreduce(void *const *bufs, int P, size_t n, ddl_dtype dtype, ddl_op op,
@@ -1070,42 +1223,47 @@ int ddl_allreduce(void *const *bufs, int P, size_t n, ddl_dtype dtype, ddl_op op
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         return DDL_E_HIP;
-    ddl_plan p = nullptr;
     try {
         std::lock_guard<std::mutex> lk(g_cache_mu);
         const std::string key =
             cache_key(dev, P, n, dtype, op, *topo, buckets, std::max(nbuckets, 0), mode);
+        std::shared_ptr<ddl_plan_s> sp;
         auto it = g_cache.find(key);
         if (it != g_cache.end()) {
-            p = it->second.plan;
+            sp = it->second.plan;
             it->second.used = ++g_cache_tick;
         } else {
-            int rc = ddl_plan_create(&p, P, n, dtype, op, topo, buckets, nbuckets, mode);
+            ddl_plan p = nullptr;
+            int rc = create_plan(&p, P, n, dtype, op, topo, buckets, nbuckets, mode);
             if (rc)
                 return rc;
+            sp = std::shared_ptr<ddl_plan_s>(p, free_plan);
             cache_make_room();
-            g_cache.emplace(key, CacheEntry{p, ++g_cache_tick});
+            g_cache.emplace(key, CacheEntry{sp, ++g_cache_tick});
         }
         std::vector<void *> ev(std::max(nbuckets, 0), nullptr);
         for (int b = 0; b < nbuckets; ++b)
             ev[b] = buckets[b].ready_event;
-        return ddl_plan_execute(p, bufs, nbuckets ? ev.data() : nullptr, stream, done_event);
+        std::lock_guard<std::mutex> pl(sp->mu);
+        return execute_locked(sp.get(), bufs, nbuckets ? ev.data() : nullptr, stream, done_event,
+                              nullptr);
     } catch (...) {
         return DDL_E_NOMEM;
     }
 }
 
 int ddl_plan_traffic(ddl_plan plan, size_t *sent, size_t *hbm_bytes) {
-    if (!plan)
-        return DDL_E_NULL;
-    const int P = plan->parts[0].s.P;
+    PlanRef r = acquire(plan);
+    if (r.rc)
+        return r.rc;
+    const int P = r->parts[0].s.P;
     size_t hbm = 0;
-    for (int r = 0; sent && r < P; ++r)
-        sent[r] = 0;
-    for (const Part &pt : plan->parts) {
-        for (int r = 0; sent && r < P; ++r)
-            sent[r] += (size_t)pt.s.sent[r];
-        hbm += (size_t)(plan->mode == DDL_FUSED ? pt.s.fused_bytes : pt.s.step_bytes);
+    for (int i = 0; sent && i < P; ++i)
+        sent[i] = 0;
+    for (const Part &pt : r->parts) {
+        for (int i = 0; sent && i < P; ++i)
+            sent[i] += (size_t)pt.s.sent[i];
+        hbm += (size_t)(r->mode == DDL_FUSED ? pt.s.fused_bytes : pt.s.step_bytes);
     }
     if (hbm_bytes)
         *hbm_bytes = hbm;
@@ -1115,13 +1273,22 @@ int ddl_plan_traffic(ddl_plan plan, size_t *sent, size_t *hbm_bytes) {
 int ddl_plan_destroy(ddl_plan plan) {
     if (!plan)
         return DDL_E_NULL;
+    std::shared_ptr<ddl_plan_s> sp;
     {
-        std::lock_guard<std::mutex> lk(plan->mu);
-        if (busy(plan))
+        std::lock_guard<std::mutex> lk(g_live_mu);
+        auto it = g_live.find(plan);
+        if (it == g_live.end())
+            return DDL_E_ARG;  // never created, or destroyed already
+        std::lock_guard<std::mutex> pl(it->second->mu);
+        if (busy(it->second.get()))
             return DDL_E_BUSY;
-        release_device(plan);
+        it->second->dead = true;
+        sp = std::move(it->second);
+        g_live.erase(it);
     }
-    delete plan;
+    // frees the plan now, or when a call that looked it up before the
+    // destroy (and then found it dead) lets go of it
+    sp.reset();
     return DDL_OK;
 }
 
@@ -1129,14 +1296,12 @@ int ddl_cache_clear(void) {
     std::lock_guard<std::mutex> lk(g_cache_mu);
     for (auto &kv : g_cache) {
         std::lock_guard<std::mutex> pl(kv.second.plan->mu);
-        if (busy(kv.second.plan))
+        if (!kv.second.plan->captured && busy(kv.second.plan.get()))
             return DDL_E_BUSY;
     }
-    for (auto &kv : g_cache) {
-        release_device(kv.second.plan);
-        delete kv.second.plan;
-    }
-    g_cache.clear();
+    // plans captured into a HIP graph stay: a replay may still read them
+    for (auto it = g_cache.begin(); it != g_cache.end();)
+        it = it->second.plan->captured ? std::next(it) : g_cache.erase(it);
     return DDL_OK;
 }
 
@@ -1149,10 +1314,10 @@ int ddl_cache_count(size_t *count) {
 }
 
 int ddl_plan_set_coalesce_bytes(ddl_plan plan, size_t bytes) {
-    if (!plan)
-        return DDL_E_NULL;
-    std::lock_guard<std::mutex> lk(plan->mu);
-    plan->coalesce_bytes = bytes;
+    PlanRef r = acquire(plan);
+    if (r.rc)
+        return r.rc;
+    r->coalesce_bytes = bytes;
     return DDL_OK;
 }
 
@@ -1161,32 +1326,41 @@ int ddl_plan_set_side_streams(ddl_plan plan, int n) {
         return DDL_E_NULL;
     if (n < 0 || n > kMaxSideStreams)
         return DDL_E_ARG;
-    std::lock_guard<std::mutex> lk(plan->mu);
-    plan->nside = n;
+    PlanRef r = acquire(plan);
+    if (r.rc)
+        return r.rc;
+    r->nside = n;
     return DDL_OK;
 }
 
 int ddl_plan_set_profiling(ddl_plan plan, int enable) {
     if (!plan)
         return DDL_E_NULL;
-    std::lock_guard<std::mutex> lk(plan->mu);
-    plan->profiling = enable != 0;
+    if (enable < 0)
+        return DDL_E_ARG;
+    PlanRef r = acquire(plan);
+    if (r.rc)
+        return r.rc;
+    r->profiling = enable != 0;
+    r->prof_stride = enable > 1 ? enable : 1;
+    r->prof_group = 0;
     return DDL_OK;
 }
 
 int ddl_plan_profile_read_kinds(ddl_plan plan, double *total_ms, int *launches,
                                 double *max_ms) {
-    if (!plan)
-        return DDL_E_NULL;
-    std::lock_guard<std::mutex> lk(plan->mu);
+    PlanRef r = acquire(plan);
+    if (r.rc)
+        return r.rc;
+    ddl_plan_s *const p = r.get();
     double tot[kLaunchKinds] = {}, mx[kLaunchKinds] = {};
     int cnt[kLaunchKinds] = {};
-    for (int i = 0; i < plan->prof_used; ++i) {
+    for (int i = 0; i < p->prof_used; ++i) {
         float ms = 0;
-        if (hipEventSynchronize(plan->prof[2 * i + 1]) != hipSuccess ||
-            hipEventElapsedTime(&ms, plan->prof[2 * i], plan->prof[2 * i + 1]) != hipSuccess)
+        if (hipEventSynchronize(p->prof[2 * i + 1]) != hipSuccess ||
+            hipEventElapsedTime(&ms, p->prof[2 * i], p->prof[2 * i + 1]) != hipSuccess)
             return DDL_E_HIP;
-        const int k = plan->prof_kind[i];
+        const int k = p->prof_kind[i];
         tot[k] += ms;
         mx[k] = std::max(mx[k], (double)ms);
         ++cnt[k];
@@ -1199,7 +1373,7 @@ int ddl_plan_profile_read_kinds(ddl_plan plan, double *total_ms, int *launches,
         if (max_ms)
             max_ms[k] = mx[k];
     }
-    plan->prof_used = 0;
+    p->prof_used = 0;
     return DDL_OK;
 }
 
@@ -1246,36 +1420,46 @@ int ddl_plan_set_fused_passes(ddl_plan plan, int passes) {
         return DDL_E_NULL;
     if (passes < 0 || passes > 2)
         return DDL_E_ARG;
-    std::lock_guard<std::mutex> lk(plan->mu);
-    plan->fused_passes = passes;
+    PlanRef r = acquire(plan);
+    if (r.rc)
+        return r.rc;
+    r->fused_passes = passes;
     return DDL_OK;
 }
 
 int ddl_plan_get_fused_passes(ddl_plan plan, int *passes) {
     if (!plan || !passes)
         return DDL_E_NULL;
-    std::lock_guard<std::mutex> lk(plan->mu);
+    PlanRef r = acquire(plan);
+    if (r.rc)
+        return r.rc;
     // the form of one group holding all the buckets (of the first element
     // type, for typed plans)
-    const Schedule &s = plan->parts[0].s;
+    const Schedule &s = r->parts[0].s;
     uint64_t all = 0;
     for (const Bucket &b : s.buckets)
         all += b.len;
-    *passes = plan->mode == DDL_FUSED ? fused_passes(plan, s, all) : 0;
+    *passes = r->mode == DDL_FUSED ? fused_passes(r.get(), s, all) : 0;
     return DDL_OK;
 }
 
 int ddl_plan_num_steps(ddl_plan plan, int *steps) {
     if (!plan || !steps)
         return DDL_E_NULL;
-    *steps = plan->parts[0].s.nsteps;  // the same for every element type
+    PlanRef r = acquire(plan);
+    if (r.rc)
+        return r.rc;
+    *steps = r->parts[0].s.nsteps;  // the same for every element type
     return DDL_OK;
 }
 
 int ddl_plan_step_kind(ddl_plan plan, int step, int *kind) {
     if (!plan || !kind)
         return DDL_E_NULL;
-    const Schedule &s = plan->parts[0].s;
+    PlanRef r = acquire(plan);
+    if (r.rc)
+        return r.rc;
+    const Schedule &s = r->parts[0].s;
     if (step < 0 || step >= s.nsteps)
         return DDL_E_ARG;
     *kind = s.step_kind[step];
@@ -1286,10 +1470,13 @@ int ddl_plan_step_items(ddl_plan plan, int step, int bucket, ddl_step_item *out,
                         int *count) {
     if (!plan || !count)
         return DDL_E_NULL;
-    if (bucket < 0 || bucket >= (int)plan->order.size())
+    PlanRef r = acquire(plan);
+    if (r.rc)
+        return r.rc;
+    if (bucket < 0 || bucket >= (int)r->order.size())
         return DDL_E_ARG;
-    const Schedule &s = plan->parts[plan->order[bucket].first].s;
-    bucket = plan->order[bucket].second;
+    const Schedule &s = r->parts[r->order[bucket].first].s;
+    bucket = r->order[bucket].second;
     if (step < 0 || step >= s.nsteps)
         return DDL_E_ARG;
     const uint32_t lo = s.item_at[step][bucket], hi = s.item_at[step][bucket + 1];
@@ -1311,10 +1498,13 @@ int ddl_plan_fused_spans(ddl_plan plan, int bucket, size_t *offset, size_t *coun
                          int cap, int *nspans, int *group) {
     if (!plan || !nspans)
         return DDL_E_NULL;
-    if (bucket < 0 || bucket >= (int)plan->order.size())
+    PlanRef r = acquire(plan);
+    if (r.rc)
+        return r.rc;
+    if (bucket < 0 || bucket >= (int)r->order.size())
         return DDL_E_ARG;
-    const Schedule &s = plan->parts[plan->order[bucket].first].s;
-    bucket = plan->order[bucket].second;
+    const Schedule &s = r->parts[r->order[bucket].first].s;
+    bucket = r->order[bucket].second;
     const uint32_t lo = s.span_at[bucket], hi = s.span_at[bucket + 1];
     *nspans = (int)(hi - lo);
     if (group)

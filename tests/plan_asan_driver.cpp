@@ -36,6 +36,106 @@ static int check(int rc, const char *what) {
     return rc;
 }
 
+static void expect(int rc, int want, const char *what) {
+    if (rc != want) {
+        std::printf("FAILED: %s returned %d, expected %d\n", what, rc, want);
+        std::exit(1);
+    }
+}
+
+// A destroyed handle, a second destroy, and a pointer that was never a
+// plan are argument errors: the handle is looked up in the library's
+// registry of live plans before anything is touched.
+static void stale_handles() {
+    ddl_topo ring = {DDL_RING, 1, 0, 0, nullptr};
+    const size_t n = 4096;
+    std::vector<void *> bufs(4);
+    for (auto &b : bufs)
+        b = std::aligned_alloc(16, n * 4);
+    hipStream_t s;
+    (void)hipStreamCreateWithFlags(&s, 0);
+    ddl_plan plan = nullptr;
+    check(ddl_plan_create(&plan, 4, n, DDL_F32, DDL_SUM, &ring, nullptr, 0, DDL_FUSED), "create");
+    check(ddl_plan_execute(plan, bufs.data(), nullptr, s, nullptr), "execute");
+    check(ddl_plan_destroy(plan), "destroy");
+    expect(ddl_plan_destroy(plan), DDL_E_ARG, "second destroy");
+    expect(ddl_plan_execute(plan, bufs.data(), nullptr, s, nullptr), DDL_E_ARG,
+           "execute after destroy");
+    std::vector<void *> w(bufs);
+    expect(ddl_plan_execute_sgd(plan, bufs.data(), w.data(), 4, 0.1f, 1, nullptr, s, nullptr),
+           DDL_E_ARG, "SGD after destroy");
+    expect(ddl_plan_execute_lars(plan, bufs.data(), w.data(), 4, 0.1f, 0.01, 1e-6, nullptr,
+                                 nullptr, s, nullptr),
+           DDL_E_ARG, "LARS after destroy");
+    size_t hbm = 0;
+    expect(ddl_plan_traffic(plan, nullptr, &hbm), DDL_E_ARG, "traffic after destroy");
+    expect(ddl_plan_set_coalesce_bytes(plan, 1), DDL_E_ARG, "coalesce after destroy");
+    expect(ddl_plan_set_profiling(plan, 1), DDL_E_ARG, "profiling after destroy");
+    int v = 0;
+    expect(ddl_plan_num_steps(plan, &v), DDL_E_ARG, "num_steps after destroy");
+    // an address that never was a plan
+    int junk[64] = {};
+    ddl_plan fake = reinterpret_cast<ddl_plan>(junk);
+    expect(ddl_plan_destroy(fake), DDL_E_ARG, "destroy of a foreign pointer");
+    expect(ddl_plan_execute(fake, bufs.data(), nullptr, s, nullptr), DDL_E_ARG,
+           "execute of a foreign pointer");
+    expect(ddl_plan_destroy(nullptr), DDL_E_NULL, "destroy of NULL");
+    (void)hipStreamDestroy(s);
+    for (auto &b : bufs)
+        std::free(b);
+}
+
+// The one-shot cache makes room by destroying idle plans, but never one
+// whose execution was captured into a HIP graph: the graph's replays read
+// its tables.  ddl_cache_clear keeps those too.
+static void captured_plans_stay_cached() {
+    ddl_topo ring = {DDL_RING, 1, 0, 0, nullptr};
+    const size_t n = 10000;
+    std::vector<void *> bufs(8);
+    for (auto &b : bufs)
+        b = std::aligned_alloc(16, (n + 64) * 4);
+    hipStream_t s;
+    (void)hipStreamCreateWithFlags(&s, 0);
+    // a stream under capture (fake: its token holds kCapturingStream)
+    hipStream_t cap = reinterpret_cast<hipStream_t>(new int(kCapturingStream));
+    for (int mode = 0; mode < 2; ++mode) {
+        ddl_bucket all = {0, n, nullptr};
+        check(ddl_allreduce(bufs.data(), 8, n, DDL_F32, DDL_MEAN, &ring, &all, 1, (ddl_mode)mode,
+                            s, nullptr),
+              "eager call before the capture");
+        check(ddl_allreduce(bufs.data(), 8, n, DDL_F32, DDL_MEAN, &ring, &all, 1, (ddl_mode)mode,
+                            cap, nullptr),
+              "captured call");
+    }
+    if (g_captured_tables.empty())
+        fail("no launch was enqueued on the capturing stream");
+    // 150 other shapes push the cache past its bound many times over
+    for (int i = 0; i < 150; ++i) {
+        ddl_bucket all = {0, n - 1 - (size_t)i, nullptr};
+        check(ddl_allreduce(bufs.data(), 8, all.count, DDL_F32, DDL_SUM, &ring, &all, 1,
+                            DDL_FUSED, s, nullptr),
+              "one-shot call");
+    }
+    size_t cached = 0;
+    check(ddl_cache_count(&cached), "cache count");
+    if (cached > 64)
+        fail("cache above its bound");
+    for (const void *t : g_captured_tables)
+        if (!live_address(t))
+            fail("a captured plan's tables were freed by the cache");
+    check(ddl_cache_clear(), "cache clear with captured plans");
+    check(ddl_cache_count(&cached), "cache count");
+    if (cached != 2)
+        fail("ddl_cache_clear dropped a captured plan, or kept another one");
+    for (const void *t : g_captured_tables)
+        if (!live_address(t))
+            fail("ddl_cache_clear freed a captured plan's tables");
+    delete reinterpret_cast<int *>(cap);
+    (void)hipStreamDestroy(s);
+    for (auto &b : bufs)
+        std::free(b);
+}
+
 int main(int argc, char **argv) {
     const int ncases = argc > 1 ? std::atoi(argv[1]) : 200;
     std::mt19937_64 rng(12345);
@@ -172,10 +272,12 @@ int main(int argc, char **argv) {
             std::free(raw[r]);
     }
     check(ddl_cache_clear(), "cache clear");
+    stale_handles();
     if (g_live_allocs || g_live_streams || g_live_events)
         std::printf("FAILED: leaked %ld allocations, %ld streams, %ld events\n", g_live_allocs,
                     g_live_streams, g_live_events),
             std::exit(1);
+    captured_plans_stay_cached();
     std::printf("ok %d cases, %ld launches checked\n", ncases, g_launches);
     return 0;
 }

@@ -54,6 +54,36 @@ def _create_rc(P, n, dtype=0, op=0, kind=0, k=1, rows=0, cols=0, order=None, buc
     return rc
 
 
+def test_stale_and_foreign_handles_are_argument_errors():
+    """Every entry point looks its handle up among the live plans first: a
+    second destroy, a call on a destroyed plan and a pointer that never was
+    a plan return DDL_E_ARG instead of touching freed memory (no GPU is
+    needed: each fails before any device work)."""
+    import ctypes
+    L = ddl.lib()
+    plan = ddl.Plan(4, 1000, "f32", "sum", ddl.topo("ring"))
+    h = plan.handle
+    assert L.ddl_plan_destroy(h) == 0
+    plan.handle = None
+    bufs = (ctypes.c_void_p * 4)(*[256 * (r + 1) for r in range(4)])
+    n = ctypes.c_int()
+    hbm = ctypes.c_size_t()
+    assert L.ddl_plan_destroy(h) == -2
+    assert L.ddl_plan_execute(h, bufs, None, None, None) == -2
+    assert L.ddl_plan_execute_sgd(h, bufs, bufs, 4, 0.1, 1, None, None, None) == -2
+    assert L.ddl_plan_execute_lars(h, bufs, bufs, 4, 0.1, 0.01, 1e-6, None, None, None,
+                                   None) == -2
+    assert L.ddl_plan_traffic(h, None, ctypes.byref(hbm)) == -2
+    assert L.ddl_plan_num_steps(h, ctypes.byref(n)) == -2
+    assert L.ddl_plan_set_coalesce_bytes(h, 1) == -2
+    assert L.ddl_plan_set_profiling(h, 1) == -2
+    junk = (ctypes.c_char * 512)()
+    foreign = ctypes.cast(junk, ctypes.c_void_p)
+    assert L.ddl_plan_destroy(foreign) == -2
+    assert L.ddl_plan_execute(foreign, bufs, None, None, None) == -2
+    assert L.ddl_plan_destroy(None) == -1
+
+
 def test_argument_validation():
     assert _create_rc(4, 100) == 0
     assert _create_rc(0, 100) == -2
