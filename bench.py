@@ -6,10 +6,16 @@ fp32 gradients each, 48 GB, 64 equal buckets issued last-first, each gated
 by its own ready event on the library's side stream), inputs resident in HBM.
 Prints one JSON line: achieved HBM GB/s (the algorithmic bytes of the fused
 pass, every rank's input read once and its result written once, over the
-step time), the roofline of the dominant kernel from HIP events around each
-of its launches, the CPU oracle timed on a bounded sample of the same
-workload, and side measurements (step-by-step mode, overlap with a streaming
-compute kernel).
+step time); the roofline of the dominant kernel from the kernels' own
+durations in the committed rocprofv3 summary of the same form (taken on the
+current sources), with the live figure from HIP events around the launches
+of every m-th bucket group of a second run of the timed steps beside it (no
+fraction when the kernels' time would exceed the steps' wall time); the CPU
+oracle
+timed on a bounded sample of the same workload; and side measurements (the
+other workloads, step-by-step mode in both forms, small buckets with one
+ready event each, overlap with a streaming compute kernel, the SGD and LARS
+steps, typed buckets, one GPU's real per-step shape).
 """
 import argparse
 import hashlib
@@ -22,7 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "achieved HBM GB/s and % of peak per all-reduce (300M fp32, P=40 ring)"
-LEGS = ("stepwise", "overlap", "sgd", "lars", "typed", "per_gpu_step", "configs")
+LEGS = ("configs", "stepwise", "latency", "overlap", "sgd", "lars", "typed", "per_gpu_step")
 PEAK_HBM_GBPS = 8000.0
 # committed counter summaries: one file per form of the fused pass
 TRAFFIC_FILES = {1: ("fused_kernel", "hbm_bytes_per_launch"),
@@ -37,8 +43,8 @@ def kernel_source_hash():
     """Hash of the fused pass's sources (kernels, launch configuration, tile
     tables): counter figures taken on another version are not reported."""
     h = hashlib.sha256()
-    for name in ("fused_kernel.hip", "device_common.h", "ddl_internal.h", "plan.cpp",
-                 "schedule.cpp"):
+    for name in ("fused_kernel.hip", "step_kernels.hip", "device_common.h", "ddl_internal.h",
+                 "plan.cpp", "schedule.cpp"):
         with open(os.path.join(ROOT, "sgd_gradient_all_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -59,6 +65,113 @@ def measured_traffic(workload, mode, passes):
     if rec.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     return rec.get(key)
+
+
+# committed rocprofv3 kernel-trace summaries: the stem of the file by form of
+# the hot path, and the kernels whose average durations add up to one unit
+TRACE_FILES = {"fused2": ("fused_pass", ("fused_reduce_kernel", "bcast_kernel")),
+               "fused1": ("fused_kernel", ("fused_kernel",)),
+               "walk": ("walk_kernel", ("walk_kernel",)),
+               "steps": ("step_kernel", ("step_kernel",))}
+
+
+def committed_trace(form, workload, bytes_per_unit):
+    """The rocprofv3 average kernel durations of this form and workload from
+    the committed summary (profiles/<stem>_<workload>_trace.json), the
+    roofline fraction they give, and whether they were taken on the current
+    kernel sources."""
+    stem, names = TRACE_FILES[form]
+    path = os.path.join(ROOT, "profiles", f"{stem}_{workload}_trace.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    ks = rec.get("kernels", {})
+    if not all(n in ks for n in names):
+        return None
+    avg_us = sum(ks[n]["avg_us"] for n in names)
+    achieved = bytes_per_unit / (avg_us * 1e-6) / 1e9
+    return {"file": os.path.relpath(path.replace("_trace.json", ".md"), ROOT),
+            "avg_unit_us": round(avg_us, 2),
+            "per_kernel_avg_us": {n: ks[n]["avg_us"] for n in names},
+            "achieved": round(achieved, 2), "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "source_matches": rec.get("kernel_source_sha256_16") == kernel_source_hash()}
+
+
+def roofline_of(args, w, passes, hbm_bytes, ms, ms_prof, kinds, per_step):
+    """Roofline of the dominant kernel: the algorithmic bytes of one unit (a
+    launch; in the fused pass's two-kernel form a reduce + broadcast pair)
+    over its average duration.  The duration is the kernels' own, from the
+    committed rocprofv3 summary of this form and workload when it was taken
+    on the current sources; the live HIP-event figure of the sampled timed
+    region stands beside it (and stands in for it otherwise).  A duration
+    whose units per step would exceed the step's wall time gives no
+    fraction."""
+    kernels = {}
+    if args.mode == "fused" and passes == 2:
+        form = "fused2"
+        red, bc = kinds["fused_reduce"], kinds["broadcast"]
+        units = per_step["fused_reduce"]
+        sampled = red[1]
+        avg_ms = red[0] / red[1] + bc[0] / bc[1]
+        kmax = red[2] + bc[2]
+        bytes_per_unit = hbm_bytes / units
+        rk = bytes_per_unit * (w.P + 1) / (2 * w.P)   # P reads + 1 write
+        bk = bytes_per_unit / 2                        # 1 read + P-1 writes
+        for name, (tot, cnt, mx), nb in (("fused_reduce_kernel", red, rk),
+                                          ("bcast_kernel", bc, bk)):
+            kernels[name] = {"launches_per_step": per_step[
+                                 "fused_reduce" if name.startswith("fused") else "broadcast"],
+                             "sampled_launches": cnt,
+                             "avg_launch_us": round(tot / cnt * 1e3, 2),
+                             "max_launch_us": round(mx * 1e3, 2),
+                             "algorithmic_bytes_per_launch": int(nb),
+                             "GBps": round(nb / (tot / cnt * 1e-3) / 1e9, 1)}
+        kernel_name = "fused pass: fused_reduce_kernel + bcast_kernel"
+    else:
+        if args.mode == "fused":
+            form, keys, kernel_name = "fused1", ("fused",), "fused_kernel"
+        elif per_step.get("walk"):
+            form, keys, kernel_name = "walk", ("walk",), "walk_kernel"
+        else:
+            form, keys, kernel_name = "steps", ("reduce", "gather"), "step_kernel"
+        units = sum(per_step[k] for k in keys)
+        sampled = sum(kinds[k][1] for k in keys)
+        avg_ms = sum(kinds[k][0] for k in keys) / max(sampled, 1)
+        kmax = max(kinds[k][2] for k in keys)
+        bytes_per_unit = hbm_bytes / units
+    ev_achieved = bytes_per_unit / (avg_ms * 1e-3) / 1e9
+    ev_kernel_ms = units * avg_ms
+    ev_ok = ev_kernel_ms <= ms and ev_kernel_ms <= ms_prof
+    events = {"avg_unit_us": round(avg_ms * 1e3, 2), "max_unit_us": round(kmax * 1e3, 2),
+              "achieved": round(ev_achieved, 2), "frac": round(ev_achieved / PEAK_HBM_GBPS, 4),
+              "kernel_ms_per_step": round(ev_kernel_ms, 4), "sampled_units": sampled,
+              "profiled_ms_per_step": round(ms_prof, 4), "fits_step_wall_time": ev_ok,
+              "timing": f"HIP event pairs around the launches of every {args.prof_stride}-th "
+                        f"bucket group, on the stream they run on, over {args.steps} timed "
+                        f"steps (each pair also holds its launch's dispatch)"}
+    rp = committed_trace(form, w.name, bytes_per_unit)
+    out = {"bound": "hbm", "kernel": kernel_name, "achieved": None, "peak": PEAK_HBM_GBPS,
+           "unit": "GB/s", "frac": None, "traffic": measured_traffic(w.name, args.mode, passes),
+           "units_per_step": units, "algorithmic_bytes_per_unit": int(bytes_per_unit)}
+    # the kernels' own durations, from the committed rocprofv3 summary of
+    # this form and workload taken on the current sources; else the events
+    if rp and rp["source_matches"] and units * rp["avg_unit_us"] * 1e-3 <= ms:
+        out.update(achieved=rp["achieved"], frac=rp["frac"], source="rocprof",
+                   avg_unit_us=rp["avg_unit_us"])
+        rp["event_over_rocprof"] = round(avg_ms * 1e3 / rp["avg_unit_us"], 4)
+    elif ev_ok:
+        out.update(achieved=events["achieved"], frac=events["frac"], source="events",
+                   avg_unit_us=events["avg_unit_us"])
+    else:
+        out["withheld"] = (f"no committed rocprofv3 summary of the current sources, and "
+                           f"{units} units x {avg_ms * 1e3:.2f} us (events) = "
+                           f"{ev_kernel_ms:.3f} ms exceeds the step's wall time "
+                           f"({ms:.3f} ms)")
+    if rp:
+        out["rocprof"] = rp
+    out["events"] = events
+    return out, kernels
 
 
 def main():
@@ -83,6 +196,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-buckets", type=int, default=64,
                     help="buckets of the workload the CPU oracle is timed on")
+    ap.add_argument("--prof-stride", type=int, default=8,
+                    help="the roofline's HIP events bracket the launches of every m-th "
+                         "bucket group of the timed steps (default 8)")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run one plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -157,46 +273,22 @@ def main():
     torch.cuda.synchronize()
     # timed region 1: the steps alone -> value, ms_per_step
     ms = run_steps(plan, evs, args.steps)
-    # timed region 2: the same steps with a HIP event pair around every
-    # launch, on the stream it is launched on -> the kernel's roofline
-    plan.set_profiling(True)
+    value = hbm_bytes / (ms * 1e-3) / 1e9
+    # launches per step, counted on one step with every launch bracketed
+    plan.set_profiling(1)
+    plan.profile_read()
+    run_steps(plan, evs, 1)
+    per_step = {k: v[1] for k, v in plan.profile_read_kinds().items()}
+    # timed region 2: the same steps with HIP event pairs around the launches
+    # of every prof_stride-th bucket group, on the stream they run on -> each
+    # kernel's average launch duration, with the steps barely slowed
+    plan.set_profiling(args.prof_stride)
     plan.profile_read()
     ms_prof = run_steps(plan, evs, args.steps)
     kinds = plan.profile_read_kinds()
-    value = hbm_bytes / (ms * 1e-3) / 1e9
-    kernels = {}
-    if passes == 2:
-        # the unit is one reduce + broadcast pair: the fused pass of a group,
-        # credited with the pass's algorithmic bytes (every rank's input read
-        # once, every rank's result written once); the reduced values the
-        # broadcast re-reads are counted in the per-kernel figures
-        red, bc = kinds["fused_reduce"], kinds["broadcast"]
-        launches = red[1]
-        avg_launch_ms = red[0] / red[1] + bc[0] / bc[1]
-        kmax = red[2] + bc[2]
-        bytes_per_launch = hbm_bytes / (launches / args.steps)
-        rk = bytes_per_launch * (w.P + 1) / (2 * w.P)   # P reads + 1 write
-        bk = bytes_per_launch / 2                        # 1 read + P-1 writes
-        for name, (tot, cnt, mx), nb in (("fused_reduce_kernel", red, rk),
-                                          ("bcast_kernel", bc, bk)):
-            kernels[name] = {"launches_per_step": cnt / args.steps,
-                             "avg_launch_us": round(tot / cnt * 1e3, 2),
-                             "max_launch_us": round(mx * 1e3, 2),
-                             "algorithmic_bytes_per_launch": int(nb),
-                             "GBps": round(nb / (tot / cnt * 1e-3) / 1e9, 1)}
-        kernel_name = "fused pass: fused_reduce_kernel + bcast_kernel"
-    else:
-        kms = sum(v[0] for v in kinds.values())
-        launches = sum(v[1] for v in kinds.values())
-        kmax = max(v[2] for v in kinds.values())
-        avg_launch_ms = kms / launches
-        bytes_per_launch = hbm_bytes / (launches / args.steps)
-        kernel_name = "fused_kernel" if args.mode == "fused" else "step_kernel"
-    launches_per_step = launches / args.steps
-    achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
-    log(f"bench: {ms:.3f} ms/step, {value:.1f} GB/s; {launches_per_step:.0f} "
-        f"{'passes' if passes == 2 else 'launches'}/step, avg {avg_launch_ms * 1e3:.1f} us, "
-        f"kernel-side {achieved:.1f} GB/s (profiled steps {ms_prof:.3f} ms) {kernels or ''}")
+    plan.set_profiling(0)
+    roofline, kernels = roofline_of(args, w, passes, hbm_bytes, ms, ms_prof, kinds, per_step)
+    log(f"bench: {ms:.3f} ms/step, {value:.1f} GB/s; roofline {roofline} {kernels or ''}")
     esize = 4 if w.dtype == "f32" else 2
     bus_bw = 2 * (w.P - 1) / w.P * w.n * esize / (ms * 1e-3) / 1e9
 
@@ -217,23 +309,11 @@ def main():
                    "rows": w.rows, "cols": w.cols, "op": w.op, "buckets": len(buckets),
                    "side_stream": w.side_stream, "mode": args.mode,
                    "coalesce_bytes": args.coalesce_bytes,
-                   "fused_passes": passes, "bytes_per_step": hbm_bytes},
+                   "fused_passes": passes, "step_form": plan.step_form(),
+                   "bytes_per_step": hbm_bytes},
         "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "bus_bw_GBps": round(bus_bw, 2),
-        "roofline": {
-            "bound": "hbm",
-            "kernel": kernel_name,
-            "achieved": round(achieved, 2),
-            "peak": PEAK_HBM_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBPS, 4),
-            "traffic": measured_traffic(w.name, args.mode, passes),
-            "launches_per_step": launches_per_step,
-            "avg_launch_us": round(avg_launch_ms * 1e3, 2),
-            "max_launch_us": round(kmax * 1e3, 2),
-            "algorithmic_bytes_per_launch": int(bytes_per_launch),
-            "profiled_ms_per_step": round(ms_prof, 4),
-        },
+        "roofline": roofline,
         **({"pass_kernels": kernels} if kernels else {}),
         "plan_build_ms": round(plan_build_ms, 2),
         "device": dev_name,
@@ -263,9 +343,15 @@ def main():
 
 def extras(args, w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_bytes, fused_ms):
     out = {}
+    # the other workloads first: their buffers then take the pages the
+    # process gets first, before the large legs below have churned HBM
+    if "configs" in args.legs:
+        out["configs"] = configs_leg(w, main_stream, torch, ddl, synth)
     if "stepwise" in args.legs:
         out["stepwise"] = stepwise_leg(w, bufs, topo, buckets, main_stream, torch, ddl,
                                        fused_bytes)
+    if "latency" in args.legs:
+        out["latency"] = latency_leg(main_stream, torch, ddl, synth)
     if "overlap" in args.legs and w.side_stream:
         out["overlap"] = overlap_leg(w, bufs, topo, buckets, main_stream, torch, ddl, synth,
                                      fused_bytes, fused_ms)
@@ -277,17 +363,18 @@ def extras(args, w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_b
                                args.passes)
     if "typed" in args.legs:
         out["typed"] = typed_leg(main_stream, torch, ddl, synth)
-    if "configs" in args.legs:
-        out["configs"] = configs_leg(w, main_stream, torch, ddl, synth)
     if "per_gpu_step" in args.legs:
         out["per_gpu_step"] = per_gpu_step_leg(w, main_stream, torch, ddl)
     return out
 
 
-def configs_leg(head, main_stream, torch, ddl, synth):
+def configs_leg(head, main_stream, torch, ddl, synth, allocations=3):
     """The other workloads, each in its plan's default fused form on fresh
     inputs: ms per all-reduce and HBM GB/s over its algorithmic bytes (the
-    4-rank 2^20 case fits the caches, so its figure is not an HBM one)."""
+    4-rank 2^20 case fits the caches, so its figure is not an HBM one).  Each
+    workload runs on `allocations` successive fresh allocations of its
+    buffers (the rate depends somewhat on the physical pages behind them);
+    the reported figure is their median, every allocation's is listed."""
     from synth.workloads import WORKLOADS
     out = {}
     for name, w in WORKLOADS.items():
@@ -295,50 +382,61 @@ def configs_leg(head, main_stream, torch, ddl, synth):
             continue
         tdt = torch.float32 if w.dtype == "f32" else torch.float16
         sdt = synth.F32 if w.dtype == "f32" else synth.F16
-        bufs = [torch.empty(w.n, dtype=tdt, device="cuda") for _ in range(w.P)]
-        for r, b in enumerate(bufs):
-            synth.fill_device(b.data_ptr(), w.n, sdt, w.dist, w.seed, r, sigma=w.sigma)
-        torch.cuda.synchronize()
-        buckets = w.bucket_list()
-        evs = [torch.cuda.Event() for _ in buckets] if w.side_stream else None
-        plan = ddl.Plan(w.P, w.n, w.dtype, w.op, ddl.topo(w.topo, w.k, w.rows, w.cols),
-                        buckets, "fused")
-        _, nbytes = plan.traffic()
-        reps = 10 if nbytes > (4 << 30) else 50
-
-        def run(k):
-            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            t0.record(main_stream)
-            for _ in range(k):
-                if evs:
-                    for e in evs:
-                        e.record(main_stream)
-                plan.execute(bufs, events=evs, stream=main_stream)
-            t1.record(main_stream)
+        runs = []
+        for _ in range(allocations):
+            bufs = [torch.empty(w.n, dtype=tdt, device="cuda") for _ in range(w.P)]
+            for r, b in enumerate(bufs):
+                synth.fill_device(b.data_ptr(), w.n, sdt, w.dist, w.seed, r, sigma=w.sigma)
             torch.cuda.synchronize()
-            return t0.elapsed_time(t1) / k
+            buckets = w.bucket_list()
+            evs = [torch.cuda.Event() for _ in buckets] if w.side_stream else None
+            plan = ddl.Plan(w.P, w.n, w.dtype, w.op, ddl.topo(w.topo, w.k, w.rows, w.cols),
+                            buckets, "fused")
+            _, nbytes = plan.traffic()
+            reps = 10 if nbytes > (4 << 30) else 50
 
-        run(3)
-        ms = run(reps)
+            def run(k):
+                t0 = torch.cuda.Event(enable_timing=True)
+                t1 = torch.cuda.Event(enable_timing=True)
+                t0.record(main_stream)
+                for _ in range(k):
+                    if evs:
+                        for e in evs:
+                            e.record(main_stream)
+                    plan.execute(bufs, events=evs, stream=main_stream)
+                t1.record(main_stream)
+                torch.cuda.synchronize()
+                return t0.elapsed_time(t1) / k
+
+            run(3)
+            runs.append(run(reps))
+            passes = plan.fused_passes()
+            plan.destroy()
+            del bufs
+            torch.cuda.empty_cache()
+        ms = sorted(runs)[len(runs) // 2]
         gbps = nbytes / (ms * 1e-3) / 1e9
         out[name] = {"ms": round(ms, 4), "hbm_GBps": round(gbps, 1),
                      "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
-                     "fused_passes": plan.fused_passes(), "bytes": nbytes,
+                     "ms_per_allocation": [round(x, 4) for x in runs],
+                     "fused_passes": passes, "bytes": nbytes,
                      "cache_resident": nbytes < (256 << 20)}
-        plan.destroy()
-        del bufs
-        torch.cuda.empty_cache()
     log(f"bench: configs {out}")
     return out
 
 
 def stepwise_leg(w, bufs, topo, buckets, main_stream, torch, ddl, fused_bytes):
-    """The step-by-step schedule on the same buffers: timed without
-    per-launch events, replayed from a HIP graph, then one profiled pass for
-    the kernel-side figures."""
+    """The step-by-step schedule on the same buffers, in both forms: one
+    kernel launch per schedule step (the per-GPU step kernels) and the
+    persistent step kernel (one launch per group, each workgroup walking
+    every step of its tile).  Each is timed without per-launch events; the
+    per-step form is also replayed from a HIP graph; one profiled step of
+    each (one side stream, so launches do not overlap) gives the kernel-side
+    figures: each kernel's average launch against its algorithmic bytes."""
     plan = ddl.Plan(w.P, w.n, w.dtype, w.op, topo, buckets, "stepwise")
     _, sbytes = plan.traffic()
     evs = [torch.cuda.Event() for _ in buckets] if w.side_stream else None
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     def step_once():
         if evs:
@@ -346,68 +444,212 @@ def stepwise_leg(w, bufs, topo, buckets, main_stream, torch, ddl, fused_bytes):
                 e.record(main_stream)
         plan.execute(bufs, events=evs, stream=main_stream)
 
-    step_once()
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    steps = 3
-    t0.record(main_stream)
-    for _ in range(steps):
+    def timed(steps):
+        t0.record(main_stream)
+        for _ in range(steps):
+            step_once()
+        t1.record(main_stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    res = {"bytes_per_step": sbytes, "default_form": plan.step_form()}
+    for form, label in ((1, "per_step_launches"), (2, "persistent")):
+        plan.set_step_form(form)
         step_once()
-    t1.record(main_stream)
-    torch.cuda.synchronize()
-    sms = t0.elapsed_time(t1) / steps
-    # the same execution captured once into a HIP graph and replayed: the
-    # thousands of step launches are then issued by one graph launch
-    graph = torch.cuda.CUDAGraph()
-    cap = torch.cuda.Stream()
-    cap.wait_stream(main_stream)
-    with torch.cuda.stream(cap):
-        with torch.cuda.graph(graph, stream=cap):
-            if evs:
-                for e in evs:
-                    e.record(cap)
-            plan.execute(bufs, events=evs, stream=cap)
-    torch.cuda.synchronize()
-    graph.replay()
-    torch.cuda.synchronize()
-    t0.record(main_stream)
-    for _ in range(steps):
-        graph.replay()
-    t1.record(main_stream)
-    torch.cuda.synchronize()
-    gms = t0.elapsed_time(t1) / steps
-    del graph
-    # the per-kernel figures come from one profiled step on a single side
-    # stream: overlapping launches would stretch each one's duration
-    plan.set_side_streams(1)
-    plan.set_profiling(True)
-    step_once()
-    torch.cuda.synchronize()
-    kinds = plan.profile_read_kinds()
-    plan.set_side_streams(0)
-    launches = sum(v[1] for v in kinds.values())
-    kms = sum(v[0] for v in kinds.values())
-    # per step kernel: its algorithmic bytes per launch over its average
-    # duration (3 L s per reduce-scatter launch, 2 L s per all-gather one)
-    kernel_rows = {}
-    for kind, share in (("reduce", 3), ("gather", 2)):
-        tot, cnt, mx = kinds[kind]
-        if cnt:
-            nb = share * sbytes / 5 / cnt   # the step bytes split 3 : 2
-            kernel_rows[kind + "_step_kernel"] = {
-                "launches_per_step": cnt, "avg_launch_us": round(tot / cnt * 1e3, 2),
-                "max_launch_us": round(mx * 1e3, 2), "algorithmic_bytes_per_launch": int(nb),
-                "GBps": round(nb / (tot / cnt * 1e-3) / 1e9, 1)}
-    res = {"ms_per_step": round(sms, 3),
-                       "graph_ms_per_step": round(gms, 3),
-                       "hbm_GBps": round(sbytes / (sms * 1e-3) / 1e9, 1),
-                       "fused_floor_equiv_GBps": round(fused_bytes / (sms * 1e-3) / 1e9, 1),
-                       "bytes_per_step": sbytes,
-                       "launches_per_step": launches,
-                       "avg_launch_us": round(kms / max(launches, 1) * 1e3, 2),
-                       **kernel_rows}
+        torch.cuda.synchronize()
+        sms = timed(3)
+        row = {"ms_per_step": round(sms, 3),
+               "hbm_GBps": round(sbytes / (sms * 1e-3) / 1e9, 1),
+               "pct_of_peak": round(100 * sbytes / (sms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+               "fused_floor_equiv_GBps": round(fused_bytes / (sms * 1e-3) / 1e9, 1)}
+        if form == 1:
+            # captured once into a HIP graph and replayed: the thousands of
+            # step launches are then issued by one graph launch
+            graph = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream()
+            cap.wait_stream(main_stream)
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(graph, stream=cap):
+                    if evs:
+                        for e in evs:
+                            e.record(cap)
+                    plan.execute(bufs, events=evs, stream=cap)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            t0.record(main_stream)
+            for _ in range(3):
+                graph.replay()
+            t1.record(main_stream)
+            torch.cuda.synchronize()
+            row["graph_ms_per_step"] = round(t0.elapsed_time(t1) / 3, 3)
+            del graph
+            torch.cuda.synchronize()
+        # kernel-side figures: one profiled step on a single side stream
+        plan.set_side_streams(1)
+        plan.set_profiling(1)
+        step_once()
+        torch.cuda.synchronize()
+        kinds = plan.profile_read_kinds()
+        plan.set_profiling(0)
+        plan.set_side_streams(0)
+        row["launches_per_step"] = sum(v[1] for v in kinds.values())
+        shares = (("reduce", 3), ("gather", 2)) if form == 1 else (("walk", 5),)
+        for kind, share in shares:
+            tot, cnt, mx = kinds[kind]
+            if cnt:
+                nb = share * sbytes / 5 / cnt   # the step bytes split 3 : 2
+                name = "walk_kernel" if kind == "walk" else kind + "_step_kernel"
+                row[name] = {
+                    "launches_per_step": cnt, "avg_launch_us": round(tot / cnt * 1e3, 2),
+                    "max_launch_us": round(mx * 1e3, 2),
+                    "algorithmic_bytes_per_launch": int(nb),
+                    "GBps": round(nb / (tot / cnt * 1e-3) / 1e9, 1)}
+        res[label] = row
     plan.destroy()
     log(f"bench: stepwise {res}")
+    return res
+
+
+def latency_leg(main_stream, torch, ddl, synth, calls=4):
+    """Small buckets (IBM's latency/bandwidth trade-off): the ResNet-50
+    gradient over 16 ranks and 4 rings, binary32, each of its 161 tensors its
+    own bucket with its own ready event recorded as back-propagation would,
+    output layer first.  For the fused pass and both step forms, at grouping
+    thresholds 0 and 16 MB:
+      - gpu_ms: device time per all-reduce with the host ahead of the device
+        (a streaming kernel on the caller's stream holds the device while the
+        calls are enqueued; timed from its end), i.e. what the schedule costs
+        the device;
+      - eager_ms: back-to-back calls, event recording included, i.e. the rate
+        when the host issues nothing else (host-bound when the host is
+        slower than the device);
+      - graph_ms: the same call (event records and all) captured once into a
+        HIP graph and replayed back to back;
+      - host_ms: the host time of the library call itself.
+    Against the same all-reduce with no events (one group)."""
+    from synth.workloads import WORKLOADS
+    w = WORKLOADS["multiring_k4_p16_resnet50"]
+    bufs = [torch.empty(w.n, dtype=torch.float32, device="cuda") for _ in range(w.P)]
+    for r, b in enumerate(bufs):
+        synth.fill_device(b.data_ptr(), w.n, synth.F32, w.dist, w.seed, r, sigma=w.sigma)
+    buckets = w.bucket_list()
+    topo = ddl.topo(w.topo, w.k, w.rows, w.cols)
+    events = [torch.cuda.Event() for _ in buckets]
+    gate = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+    cs = main_stream.cuda_stream
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+
+    def hold(n):
+        for _ in range(n):
+            synth.stream_compute(gate.data_ptr(), gate.numel(), 1.0, 0.0, cs)
+
+    t0.record(main_stream)
+    hold(4)
+    t1.record(main_stream)
+    torch.cuda.synchronize()
+    hold_ms = t0.elapsed_time(t1) / 4
+
+    def run(plan, gated):
+        if gated:
+            for e in events:
+                e.record(main_stream)
+        plan.execute(bufs, events=events if gated else None, stream=main_stream)
+
+    def measure(plan, gated, graph_too):
+        run(plan, gated)
+        torch.cuda.synchronize()
+        # the library's own host time per call
+        host = []
+        for _ in range(calls):
+            if gated:
+                for e in events:
+                    e.record(main_stream)
+            h0 = time.perf_counter()
+            plan.execute(bufs, events=events if gated else None, stream=main_stream)
+            host.append(time.perf_counter() - h0)
+        torch.cuda.synchronize()
+        host_ms = sorted(host)[len(host) // 2] * 1e3
+        # back to back
+        t0.record(main_stream)
+        for _ in range(calls):
+            run(plan, gated)
+        t1.record(main_stream)
+        torch.cuda.synchronize()
+        eager = t0.elapsed_time(t1) / calls
+        # host ahead: the calls are enqueued behind a streaming kernel long
+        # enough to cover their host time
+        need = (eager * calls * 1.5 + 2.0) / max(hold_ms, 1e-3)
+        hold(int(need) + 1)
+        t0.record(main_stream)
+        h0 = time.perf_counter()
+        for _ in range(calls):
+            run(plan, gated)
+        host_all = (time.perf_counter() - h0) * 1e3
+        t1.record(main_stream)
+        torch.cuda.synchronize()
+        row = {"gpu_ms": round(t0.elapsed_time(t1) / calls, 4), "eager_ms": round(eager, 4),
+               "host_ms": round(host_ms, 4),
+               "host_ahead": bool(host_all < (int(need) + 1) * hold_ms)}
+        if graph_too:
+            graph = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream()
+            cap.wait_stream(main_stream)
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(graph, stream=cap):
+                    if gated:
+                        for e in events:
+                            e.record(cap)
+                    plan.execute(bufs, events=events if gated else None, stream=cap)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            t0.record(main_stream)
+            for _ in range(calls):
+                graph.replay()
+            t1.record(main_stream)
+            torch.cuda.synchronize()
+            row["graph_ms"] = round(t0.elapsed_time(t1) / calls, 4)
+            del graph
+            torch.cuda.synchronize()
+        return row
+
+    res = {"workload": w.name, "ranks": w.P, "tensors": len(buckets), "events": len(buckets),
+           "hold_kernel_ms": round(hold_ms, 3)}
+    plan = ddl.Plan(w.P, w.n, w.dtype, w.op, topo, buckets, "fused")
+    res["no_events_fused"] = measure(plan, False, False)
+    plan.destroy()
+    variants = [("fused", 0, 0, False), ("fused", 0, 16, False), ("fused", 0, 16, True),
+                ("stepwise", 2, 0, False), ("stepwise", 2, 16, True),
+                ("stepwise", 1, 0, False), ("stepwise", 1, 16, True)]
+    for mode, form, thr_mb, ordered in variants:
+        plan = ddl.Plan(w.P, w.n, w.dtype, w.op, topo, buckets, mode)
+        if mode == "stepwise":
+            plan.set_step_form(form)
+        plan.set_coalesce_bytes(thr_mb << 20)
+        # the events are recorded in list order on one stream, as
+        # back-propagation records them: the promise may be made
+        plan.set_ordered_events(ordered)
+        plan.set_profiling(1)
+        run(plan, True)
+        torch.cuda.synchronize()
+        launches = sum(v[1] for v in plan.profile_read_kinds().values())
+        plan.set_profiling(0)
+        key = (f"{mode}{'' if mode == 'fused' else '_form%d' % form}_coalesce_{thr_mb}mb"
+               f"{'_ordered' if ordered else ''}")
+        row = measure(plan, True, True)
+        row["launches"] = launches
+        res[key] = row
+        # captured plans must outlive the graph, which is gone by now
+        plan.destroy()
+    base = res["no_events_fused"]["gpu_ms"]
+    res["fused_per_tensor_events_over_no_events"] = {
+        k: round(res[k]["gpu_ms"] / base, 3)
+        for k in ("fused_coalesce_0mb", "fused_coalesce_16mb", "fused_coalesce_16mb_ordered")}
+    del bufs, gate
+    torch.cuda.empty_cache()
+    log(f"bench: latency {res}")
     return res
 
 
@@ -478,6 +720,7 @@ def per_gpu_step_leg(w, main_stream, torch, ddl):
     tdt = torch.float32 if w.dtype == "f32" else torch.float16
     bufs = [torch.ones(2 * L, dtype=tdt, device="cuda") for _ in range(2)]
     plan = ddl.Plan(2, 2 * L, w.dtype, "sum", ddl.topo("ring"), None, "stepwise")
+    plan.set_step_form(1)   # the per-step kernels, one launch per step
     plan.execute(bufs, stream=main_stream)
     torch.cuda.synchronize()
     plan.set_profiling(True)

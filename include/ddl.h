@@ -279,6 +279,18 @@ const char *ddl_strerror(int code);
  * for all their events before it starts.  Default 0. */
 int ddl_plan_set_coalesce_bytes(ddl_plan plan, size_t bytes);
 
+/* The caller's promise that it records the buckets' ready events in list
+ * order on one stream -- as back-propagation produces the gradients, output
+ * layer first (Baidu article, opening paragraphs) -- so that the completion
+ * of bucket b's event implies that of every earlier bucket's.  With
+ * ordered = 1 a group of buckets (coalesced up to ddl_plan_set_coalesce_bytes)
+ * waits only for the event of its last bucket that has one, instead of one
+ * wait per distinct event: each wait costs the device a few microseconds.
+ * Buckets without an event still wait for the caller's stream as of the
+ * call.  If the promise does not hold, a bucket may be reduced before its
+ * gradient is complete.  Default 0; DDL_E_ARG for values other than 0, 1. */
+int ddl_plan_set_ordered_events(ddl_plan plan, int ordered);
+
 /* Event-gated groups alternate over n side streams (1..4) in list order.
  * Buckets are independent all-reduces, so a group's kernels may run while
  * the previous group's drain; the results do not change.  n = 0 (default):
@@ -305,6 +317,26 @@ int ddl_plan_set_side_streams(ddl_plan plan, int n);
  * plan). */
 int ddl_plan_set_fused_passes(ddl_plan plan, int passes);
 int ddl_plan_get_fused_passes(ddl_plan plan, int *passes);
+
+/* Form of a stepwise plan's execution (stepwise mode only).
+ * form = 1: one kernel launch per schedule step, every pair of the step in
+ * that launch.  form = 2: one persistent launch per group of buckets.  Every
+ * dependency of the schedule is per element (a step reads element e of a
+ * rank only where an earlier step wrote element e), so each workgroup takes
+ * one tile of a chunk (torus: of a sub-chunk) and carries it through every
+ * reduce-scatter and all-gather step in schedule order, reading and writing
+ * the ranks' buffers at each step as the per-step launches do (the same
+ * bytes, the same results); no barrier spans workgroups.  This is the
+ * latency form for small buckets ("[论文解读] PowerAI DDL", ABSTRACT: the
+ * latency/bandwidth trade-off): 2 (P-1) launches become one.
+ * form = 0 (default): automatic, per group: persistent for groups of at most
+ * 8 MB per rank, one launch per step above.  With the SGD step
+ * (ddl_plan_execute_sgd) stepwise plans always launch per step.
+ * DDL_E_ARG for other values; takes effect at the next execute.
+ * ddl_plan_get_step_form reports the form of one group holding all the
+ * plan's buckets, as in a call without ready events (0 for a fused plan). */
+int ddl_plan_set_step_form(ddl_plan plan, int form);
+int ddl_plan_get_step_form(ddl_plan plan, int *form);
 
 /* ---- tuning ------------------------------------------------------------ *
  * Process-wide knobs of the fused pass's kernels, for benchmarks.  They
@@ -369,8 +401,9 @@ int ddl_plan_profile_read_kinds(ddl_plan plan, double *total_ms, int *launches,
 /* ---- schedule introspection (host-only; used by the tests) ------------- */
 /* Kernel launches: a reduce-scatter step, an all-gather step, the one-kernel
  * fused pass, the two kernels of the two-kernel fused pass, the LARS step's
- * norms and rates, and the weight update (of the LARS step, and of the SGD
- * step in the two-kernel form). */
+ * norms and rates, the weight update (of the LARS step, and of the SGD step
+ * in the two-kernel form), and the persistent step kernel of a stepwise
+ * group (ddl_plan_set_step_form). */
 typedef enum {
     DDL_K_REDUCE = 0,
     DDL_K_GATHER = 1,
@@ -380,7 +413,8 @@ typedef enum {
     DDL_K_LARS_NORM = 5,
     DDL_K_LARS_RATE = 6,
     DDL_K_UPDATE = 7,
-    DDL_K_COUNT = 8
+    DDL_K_WALK = 8,
+    DDL_K_COUNT = 9
 } ddl_launch_kind;
 
 /* One pair transfer of one step: rank dst combines elements

@@ -13,10 +13,10 @@ DDL_SUM, DDL_MEAN = 0, 1
 DDL_RING, DDL_MULTIRING, DDL_TORUS2D = 0, 1, 2
 DDL_STEPWISE, DDL_FUSED = 0, 1
 DDL_K_REDUCE, DDL_K_GATHER, DDL_K_FUSED, DDL_K_FUSED_REDUCE, DDL_K_BROADCAST = 0, 1, 2, 3, 4
-DDL_K_LARS_NORM, DDL_K_LARS_RATE, DDL_K_UPDATE = 5, 6, 7
-DDL_K_COUNT = 8
+DDL_K_LARS_NORM, DDL_K_LARS_RATE, DDL_K_UPDATE, DDL_K_WALK = 5, 6, 7, 8
+DDL_K_COUNT = 9
 LAUNCH_KINDS = ("reduce", "gather", "fused", "fused_reduce", "broadcast", "lars_norm",
-                "lars_rate", "update")
+                "lars_rate", "update", "walk")
 # LARS as the Sony ResNet-50 article trains with it: coefficient and eps
 LARS_COEFF, LARS_EPS = 0.01, 1e-6
 
@@ -88,10 +88,13 @@ def lib():
             "ddl_strerror": ([i32], ctypes.c_char_p),
             "ddl_plan_set_coalesce_bytes": ([vp, sz], i32),
             "ddl_plan_set_side_streams": ([vp, i32], i32),
+            "ddl_plan_set_ordered_events": ([vp, i32], i32),
             "ddl_plan_set_fused_passes": ([vp, i32], i32),
             "ddl_set_tuning": ([i32, i32], i32),
             "ddl_get_tuning": ([i32, ctypes.POINTER(i32)], i32),
             "ddl_plan_get_fused_passes": ([vp, ctypes.POINTER(i32)], i32),
+            "ddl_plan_set_step_form": ([vp, i32], i32),
+            "ddl_plan_get_step_form": ([vp, ctypes.POINTER(i32)], i32),
             "ddl_plan_profile_read_kinds": ([vp, ctypes.POINTER(ctypes.c_double),
                                              ctypes.POINTER(i32),
                                              ctypes.POINTER(ctypes.c_double)], i32),
@@ -312,6 +315,12 @@ class Plan:
     def set_coalesce_bytes(self, nbytes):
         _check(lib().ddl_plan_set_coalesce_bytes(self.handle, nbytes), "set_coalesce_bytes")
 
+    def set_ordered_events(self, ordered=True):
+        """Promise that the ready events are recorded in bucket list order on
+        one stream: a group then waits for its last event only."""
+        _check(lib().ddl_plan_set_ordered_events(self.handle, 1 if ordered else 0),
+               "set_ordered_events")
+
     def set_side_streams(self, n):
         _check(lib().ddl_plan_set_side_streams(self.handle, n), "set_side_streams")
 
@@ -322,6 +331,16 @@ class Plan:
     def fused_passes(self):
         v = ctypes.c_int()
         _check(lib().ddl_plan_get_fused_passes(self.handle, ctypes.byref(v)), "fused_passes")
+        return v.value
+
+    def set_step_form(self, form):
+        """Stepwise plans: 0 automatic, 1 one launch per schedule step, 2 one
+        persistent launch per group (each workgroup walks every step of a tile)."""
+        _check(lib().ddl_plan_set_step_form(self.handle, int(form)), "set_step_form")
+
+    def step_form(self):
+        v = ctypes.c_int()
+        _check(lib().ddl_plan_get_step_form(self.handle, ctypes.byref(v)), "step_form")
         return v.value
 
     def set_profiling(self, on=True):

@@ -210,6 +210,10 @@ int launch_fused(int dtype, const RankPtrs &bufs, const FusedArgs &a, const SgdA
                  bool home, uint32_t tiles, void *stream);
 int launch_bcast(int dtype, const RankPtrs &bufs, const BcastArgs &a, void *stream);
 int launch_tiny(int dtype, const RankPtrs &bufs, const TinyArgs &a, void *stream);
+// The persistent step kernel: tiles [a.tile_base, a.tile_base + tiles) of the
+// fused span table, every schedule step walked by the workgroup of a tile.
+int launch_walk(int dtype, const RankPtrs &bufs, const FusedArgs &a, uint32_t tiles,
+                void *stream);
 // kind: DDL_K_LARS_NORM or DDL_K_UPDATE (blocks = tiles from
 // a.tile_base), DDL_K_LARS_RATE (blocks = buckets from a.bucket_lo).
 int launch_lars(int dtype, int kind, const RankPtrs &w, const LarsArgs &a, uint32_t blocks,

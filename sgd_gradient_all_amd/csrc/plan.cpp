@@ -90,8 +90,12 @@ struct ddl_plan_s {
     bool typed = false;     // created with typed buckets (byte offsets)
     int mode = DDL_FUSED;
     size_t coalesce_bytes = 0;
+    // the caller records the ready events in list order on one stream: a
+    // group then waits for its last event only
+    bool ordered_events = false;
     int nside = 0;          // side streams event-gated groups alternate over (0 auto)
     int fused_passes = 0;   // 0 automatic, 1 one kernel, 2 reduce + broadcast
+    int step_form = 0;      // 0 automatic, 1 a launch per step, 2 persistent
 
     std::mutex mu;
     int device = -1;        // bound at first execution
@@ -280,6 +284,20 @@ int fused_passes(ddl_plan p, const Schedule &s, uint64_t elems) {
     return s.P >= 16 && (uint64_t)s.P * elems * (uint64_t)s.esz >= min_bytes ? 2 : 1;
 }
 
+// Form of a stepwise group of `elems` elements per rank: one launch per
+// schedule step (1), or one persistent launch whose workgroups each walk
+// every step of one tile (2).  Automatic: persistent for groups of at most
+// kPersistentMaxBytes per rank, where the 2 (P - 1) launches' dispatch
+// dominates.  The SGD step rides on the per-step launches.
+constexpr uint64_t kPersistentMaxBytes = 8ull << 20;
+int step_form(ddl_plan p, const Schedule &s, uint64_t elems, bool sgd) {
+    if (sgd)
+        return 1;
+    if (p->step_form)
+        return p->step_form;
+    return elems * (uint64_t)s.esz <= kPersistentMaxBytes ? 2 : 1;
+}
+
 // Side streams event-gated groups alternate over.  Automatic: two for
 // stepwise plans and for fused plans with small buckets, where the next
 // group's launches fill the previous group's ramp-down (measured on MI355X
@@ -382,6 +400,41 @@ struct Launcher {
                 return rc;
             if (launch_step(s.dtype, s.step_kind[st], s.step_vpl, bufs, a, sgd, tiles, stream) !=
                 hipSuccess)
+                return DDL_E_HIP;
+            if ((rc = bracket_end()))
+                return rc;
+        }
+        return DDL_OK;
+    }
+
+    // the persistent step kernel over the fused tiles of buckets [b0, b1)
+    int walk(int b0, int b1) {
+        const Schedule &s = pt->s;
+        const uint32_t lo = s.span_at[b0], hi = s.span_at[b1];
+        if (lo == hi)
+            return DDL_OK;
+        const uint32_t *pre = s.span_prefix.data();
+        FusedArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.spans = pt->d_spans;
+        a.prefix = pt->d_span_prefix;
+        a.tile_span = pt->d_span_of_tile;
+        a.chains = pt->d_chains;
+        a.span_lo = lo;
+        a.span_hi = hi;
+        a.P = s.P;
+        a.group = s.group;
+        a.mean = s.op == DDL_MEAN;
+        a.divisor = (float)s.P;
+        a.anchor = s.fused_anchor;
+        for (uint32_t t = pre[lo]; t < pre[hi]; t += kMaxTilesPerLaunch) {
+            const uint32_t tiles = std::min(kMaxTilesPerLaunch, pre[hi] - t);
+            a.tile_base = t;
+            a.tile_end = t + tiles;
+            int rc = bracket_begin(DDL_K_WALK);
+            if (rc)
+                return rc;
+            if (launch_walk(s.dtype, bufs, a, tiles, stream) != hipSuccess)
                 return DDL_E_HIP;
             if ((rc = bracket_end()))
                 return rc;
@@ -602,8 +655,14 @@ struct Launcher {
         if (p->mode == DDL_FUSED || (sgd && s.P == 1)) {
             rc = fused(b0, b1);
         } else {
-            for (int st = 0; st < s.nsteps && !rc; ++st)
-                rc = step(st, s.item_at[st][b0], s.item_at[st][b1]);
+            uint64_t elems = 0;
+            for (int b = b0; b < b1; ++b)
+                elems += s.buckets[b].len;
+            if (s.nsteps > 0 && step_form(p, s, elems, sgd != nullptr) == 2)
+                rc = walk(b0, b1);
+            else
+                for (int st = 0; st < s.nsteps && !rc; ++st)
+                    rc = step(st, s.item_at[st][b0], s.item_at[st][b1]);
         }
         if (rc || !lars)
             return rc;
@@ -758,9 +817,26 @@ int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stre
             L.stream = p->side[si];
             used = std::max(used, si + 1);
             void *last = reinterpret_cast<void *>(1);
-            for (int b = b0; b < b1; ++b) {
+            // with ordered events the last event of the group implies the
+            // earlier ones; buckets without an event still wait for the
+            // caller's stream as of the call
+            int from = b0;
+            if (p->ordered_events) {
+                int lastev = -1;
+                bool anynull = false;
+                for (int b = b0; b < b1; ++b) {
+                    if (ready[b])
+                        lastev = b;
+                    else
+                        anynull = true;
+                }
+                if (anynull && hipStreamWaitEvent(L.stream, p->call_ev, 0) != hipSuccess)
+                    return DDL_E_HIP;
+                from = lastev < 0 ? b1 : lastev;
+            }
+            for (int b = from; b < b1; ++b) {
                 void *ev = ready[b] ? ready[b] : static_cast<void *>(p->call_ev);
-                if (ev == last)
+                if (ev == last || (p->ordered_events && !ready[b]))
                     continue;
                 if (hipStreamWaitEvent(L.stream, static_cast<hipEvent_t>(ev), 0) != hipSuccess)
                     return DDL_E_HIP;
@@ -1321,6 +1397,18 @@ int ddl_plan_set_coalesce_bytes(ddl_plan plan, size_t bytes) {
     return DDL_OK;
 }
 
+int ddl_plan_set_ordered_events(ddl_plan plan, int ordered) {
+    if (!plan)
+        return DDL_E_NULL;
+    if (ordered != 0 && ordered != 1)
+        return DDL_E_ARG;
+    PlanRef r = acquire(plan);
+    if (r.rc)
+        return r.rc;
+    r->ordered_events = ordered != 0;
+    return DDL_OK;
+}
+
 int ddl_plan_set_side_streams(ddl_plan plan, int n) {
     if (!plan)
         return DDL_E_NULL;
@@ -1440,6 +1528,32 @@ int ddl_plan_get_fused_passes(ddl_plan plan, int *passes) {
     for (const Bucket &b : s.buckets)
         all += b.len;
     *passes = r->mode == DDL_FUSED ? fused_passes(r.get(), s, all) : 0;
+    return DDL_OK;
+}
+
+int ddl_plan_set_step_form(ddl_plan plan, int form) {
+    if (!plan)
+        return DDL_E_NULL;
+    if (form < 0 || form > 2)
+        return DDL_E_ARG;
+    PlanRef r = acquire(plan);
+    if (r.rc)
+        return r.rc;
+    r->step_form = form;
+    return DDL_OK;
+}
+
+int ddl_plan_get_step_form(ddl_plan plan, int *form) {
+    if (!plan || !form)
+        return DDL_E_NULL;
+    PlanRef r = acquire(plan);
+    if (r.rc)
+        return r.rc;
+    const Schedule &s = r->parts[0].s;
+    uint64_t all = 0;
+    for (const Bucket &b : s.buckets)
+        all += b.len;
+    *form = r->mode == DDL_STEPWISE ? step_form(r.get(), s, all, false) : 0;
     return DDL_OK;
 }
 

@@ -6,6 +6,9 @@
 // stores stay cached: the next step reads what this one wrote.
 #include "device_common.h"
 
+// global (address space 1) accesses from addresses kept in LDS
+#define DDL_STEP_GLOBAL __attribute__((address_space(1)))
+
 namespace ddl {
 namespace {
 
@@ -113,6 +116,137 @@ __global__ __launch_bounds__(kBlock) void step_sgd_kernel(RankPtrs bufs, StepArg
     step_body<E, kReduce, true, VPL>(bufs, a, &g);
 }
 
+// ---------------------------------------------------------------------------
+// persistent step kernel: one launch walks every schedule step of a group.
+//
+// Every dependency of the schedule is per element: the value that step t
+// writes to element e of a rank is read again only at element e, by a later
+// step.  So a workgroup that owns one tile of a fused span (a chunk, or a
+// torus sub-piece, whose elements all follow the same chain of ranks) can
+// run every step of the schedule over that tile by itself, in step order,
+// and each lane touches the same elements at every step -- it reads back
+// only what it wrote itself, so no barrier and no grid-wide wait is needed.
+// Each step still moves its data through memory exactly as the one-launch-
+// per-step path does (reduce: read the sender's and the receiver's element,
+// write the receiver's; copy: read the sender's, write the receiver's), so
+// the counted bytes are the stepwise ones, 5 (P-1) s per element.
+//
+// With the chain c[0..P) of the span in groups of C = `group` entries
+// (G = P / C groups; rings have one group of P):
+//   row reduce-scatter of each group g: c[gC+t+1] (+)= c[gC+t], t = 0..C-2
+//   column reduce-scatter: c[(t+1)C+C-1] (+)= c[tC+C-1], t = 0..G-2
+//   column all-gather: c[tC+C-1] = c[((t-1) mod G)C+C-1], t = 0..G-2
+//   row all-gather of each group: c[gC+t] = c[gC+(t-1) mod C], t = 0..C-2
+// with the mean fused into the add that completes the sum (the last column
+// add, or the last row add when G = 1).  For a ring, position x of the ring
+// is chain entry (x - c) mod P of chunk c, so these are the ring's steps;
+// for the torus, group g is row (d + g) mod rows of sub-piece d, and its
+// last entry is the rank of column (c - 1) mod cols that owns row piece c.
+// ---------------------------------------------------------------------------
+template <class V>
+__device__ __forceinline__ V ld_at(uint64_t addr) {
+    return *reinterpret_cast<const V DDL_STEP_GLOBAL *>(addr);
+}
+template <class V>
+__device__ __forceinline__ void st_at(uint64_t addr, V v) {
+    *reinterpret_cast<V DDL_STEP_GLOBAL *>(addr) = v;
+}
+
+// The walk of U values of type X (vectors, or single elements with U = 1)
+// at byte offsets off + u * stride of every rank, rank addresses in chain
+// order in c[].
+template <class E, class X, int U>
+__device__ __forceinline__ void walk_body(const uint64_t *c, int P, int C, bool mean,
+                                          float divisor, uint64_t off, uint64_t stride) {
+    const int G = P / C;
+    auto add = [](X a, X b) {
+        if constexpr (sizeof(X) == sizeof(typename E::V))
+            return E::add(a, b);
+        else
+            return E::add1(a, b);
+    };
+    auto div = [](X a, float d) {
+        if constexpr (sizeof(X) == sizeof(typename E::V))
+            return E::div(a, d);
+        else
+            return E::div1(a, d);
+    };
+    // reduce: dst (+)= src, then / P when last
+    auto reduce = [&](int src, int dst, bool last) {
+        X s[U], d[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            s[u] = ld_at<X>(c[src] + off + u * stride);
+            d[u] = ld_at<X>(c[dst] + off + u * stride);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            X r = add(d[u], s[u]);
+            if (last)
+                r = div(r, divisor);
+            st_at<X>(c[dst] + off + u * stride, r);
+        }
+    };
+    auto copy = [&](int src, int dst) {
+        X s[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            s[u] = ld_at<X>(c[src] + off + u * stride);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            st_at<X>(c[dst] + off + u * stride, s[u]);
+    };
+    for (int g = 0; g < G; ++g)
+        for (int t = 0; t + 1 < C; ++t)
+            reduce(g * C + t, g * C + t + 1, mean && G == 1 && t == C - 2);
+    for (int t = 0; t + 1 < G; ++t)
+        reduce(t * C + C - 1, (t + 1) * C + C - 1, mean && t == G - 2);
+    for (int t = 0; t + 1 < G; ++t)
+        copy(((t + G - 1) % G) * C + C - 1, t * C + C - 1);
+    for (int g = 0; g < G; ++g)
+        for (int t = 0; t + 1 < C; ++t)
+            copy(g * C + (t + C - 1) % C, g * C + t);
+}
+
+// Workgroup b walks tile tile_base + b of the fused span table.
+template <class E>
+__global__ __launch_bounds__(kBlock) void walk_kernel(RankPtrs bufs, FusedArgs a) {
+    using T = typename E::T;
+    using V = typename E::V;
+    constexpr int U = fused_vecs_per_lane(sizeof(T));
+    constexpr uint64_t kTile = fused_tile_elems(sizeof(T));
+    constexpr uint64_t kStride = (uint64_t)kBlock * E::N * sizeof(T);
+    __shared__ uint64_t c[DDL_MAX_RANKS];  // rank addresses, chain order
+    const int P = a.P;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t tile = a.tile_base + blockIdx.x;
+    const uint32_t i = a.tile_span[tile];
+    const DevSpan sp = a.spans[i];
+    for (int j = (int)tid; j < P; j += kBlock)
+        c[j] = reinterpret_cast<uint64_t>(bufs.p[a.chains[sp.chain_off + j]]);
+    __syncthreads();
+    const uint64_t j = tile - a.prefix[i];
+    const uint64_t sh = tile_shift(sp.off, kTile, a.anchor);
+    const uint64_t base = tile_lo(sp.off, sh, kTile, j);
+    const uint32_t cnt = (uint32_t)(tile_hi(sp.off, sp.len, sh, kTile, j) - base);
+    const bool mean = a.mean != 0;
+    uint32_t done = 0;
+    if (sp.flags & kItemAligned) {
+        const uint32_t nvec = cnt / E::N;
+        if (nvec == (uint32_t)(U * kBlock)) {
+            walk_body<E, V, U>(c, P, a.group, mean, a.divisor,
+                               (base + (uint64_t)tid * E::N) * sizeof(T), kStride);
+        } else {
+            for (uint32_t v = tid; v < nvec; v += kBlock)
+                walk_body<E, V, 1>(c, P, a.group, mean, a.divisor,
+                                   (base + (uint64_t)v * E::N) * sizeof(T), 0);
+        }
+        done = nvec * E::N;
+    }
+    for (uint32_t k = done + tid; k < cnt; k += kBlock)
+        walk_body<E, T, 1>(c, P, a.group, mean, a.divisor, (base + k) * sizeof(T), 0);
+}
+
 }  // namespace
 
 namespace {
@@ -148,6 +282,18 @@ void launch_e(int kind, int vpl, dim3 grid, hipStream_t s, const RankPtrs &bufs,
 }
 
 }  // namespace
+
+int launch_walk(int dtype, const RankPtrs &bufs, const FusedArgs &a, uint32_t tiles,
+                void *stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (tiles == 0)
+        return (int)hipSuccess;
+    if (dtype == DDL_F32)
+        hipLaunchKernelGGL((walk_kernel<F32>), dim3(tiles), dim3(kBlock), 0, s, bufs, a);
+    else
+        hipLaunchKernelGGL((walk_kernel<F16>), dim3(tiles), dim3(kBlock), 0, s, bufs, a);
+    return (int)hipGetLastError();
+}
 
 int launch_step(int dtype, int kind, int vpl, const RankPtrs &bufs, const StepArgs &a,
                 const SgdArgs *sgd, uint32_t tiles, void *stream) {

@@ -189,10 +189,13 @@ int main(int argc, char **argv) {
         hipStream_t s;
         (void)hipStreamCreateWithFlags(&s, 0);
         check(ddl_plan_set_side_streams(plan, uni(0, 4)), "side streams");
+        check(ddl_plan_set_ordered_events(plan, uni(0, 1)), "ordered events");
         check(ddl_plan_set_coalesce_bytes(plan, uni(0, 1) ? 0 : (size_t)uni(1, 1 << 22)),
               "coalesce");
         if (mode == DDL_FUSED)
             check(ddl_plan_set_fused_passes(plan, uni(0, 2)), "passes");
+        else
+            check(ddl_plan_set_step_form(plan, uni(0, 2)), "step form");
         check(ddl_plan_set_profiling(plan, uni(0, 1)), "profiling");
         for (int rep = 0; rep < 2; ++rep) {
             check(ddl_plan_execute(plan, bufs.data(), uni(0, 1) ? evp.data() : nullptr, s, ev[0]),

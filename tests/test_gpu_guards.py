@@ -72,7 +72,7 @@ def check_guards(w, allocs, what):
 
 
 @pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
-@pytest.mark.parametrize("mode", ["fused1", "fused2", "stepwise"])
+@pytest.mark.parametrize("mode", ["fused1", "fused2", "step1", "step2"])
 def test_guards_untouched_by_the_allreduce(w, mode):
     say(f"case guards {w.name} {mode}")
     g = host_inputs(w)
@@ -80,9 +80,12 @@ def test_guards_untouched_by_the_allreduce(w, mode):
     oracle_full(w, ref)
     allocs, views = guarded(w, g)
     torch.cuda.synchronize()
+    stepwise = mode.startswith("step")
     plan = ddl.Plan(w.P, w.n, w.dtype, w.op, ddl_topo(w), w.bucket_list(),
-                    "stepwise" if mode == "stepwise" else "fused")
-    if mode != "stepwise":
+                    "stepwise" if stepwise else "fused")
+    if stepwise:
+        plan.set_step_form(int(mode[-1]))
+    else:
         plan.set_fused_passes(1 if mode == "fused1" else 2)
     stream = torch.cuda.current_stream()
     events = [torch.cuda.Event() for _ in w.bucket_list()]

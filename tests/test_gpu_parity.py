@@ -48,21 +48,26 @@ def bitwise_equal(a, b):
 
 
 # "fused1" / "fused2": a fused plan forced to its one-kernel / two-kernel
-# form; "fused" leaves the form to the plan.
+# form; "fused" leaves the form to the plan.  "step1" / "step2": a stepwise
+# plan forced to one launch per step / the persistent step kernel;
+# "stepwise" leaves the form to the plan.
 PASSES = {"fused1": 1, "fused2": 2}
+STEP_FORMS = {"step1": 1, "step2": 2}
 
 
 def make_plan(w, mode, op=None):
     plan = ddl.Plan(w.P, w.n, w.dtype, op or w.op, ddl_topo(w), w.bucket_list(),
-                    "fused" if mode in PASSES else mode)
+                    "fused" if mode in PASSES else "stepwise" if mode in STEP_FORMS else mode)
     if mode in PASSES:
         plan.set_fused_passes(PASSES[mode])
+    if mode in STEP_FORMS:
+        plan.set_step_form(STEP_FORMS[mode])
     return plan
 
 
 def run_ddl(bufs, w, mode, op=None, plan_api=True, events=None, stream=None):
     t = ddl_topo(w)
-    if plan_api or mode in PASSES:
+    if plan_api or mode in PASSES or mode in STEP_FORMS:
         plan = make_plan(w, mode, op)
         plan.execute(bufs, events=events, stream=stream)
         torch.cuda.synchronize()
@@ -106,7 +111,7 @@ def small_cases():
 
 
 @pytest.mark.parametrize("w", small_cases(), ids=lambda w: w.name)
-@pytest.mark.parametrize("mode", ["fused1", "fused2", "stepwise"])
+@pytest.mark.parametrize("mode", ["fused1", "fused2", "step1", "step2"])
 @pytest.mark.parametrize("op", ["sum", "mean"])
 def test_small_bitwise(w, mode, op):
     say(f"case {w.name} mode={mode} op={op}")
@@ -152,7 +157,7 @@ def test_tiny_spans_one_wave_each(name, P, tk, dtype, op, gated):
     ref = [x.copy() for x in g]
     oracle_full(w, ref)
     stream = torch.cuda.current_stream()
-    for mode in ("fused", "stepwise"):
+    for mode in ("fused", "step1", "step2"):
         bufs = to_device(g)
         events = None
         if gated:
@@ -180,7 +185,7 @@ def test_subnormals_and_specials(dtype):
     g[2][9] = np.nan
     g[0][11], g[3][11] = np.inf, -np.inf
     w = Workload("sub", P, n, dtype, "mean", "ring")
-    for mode in ("fused1", "fused2", "stepwise"):
+    for mode in ("fused1", "fused2", "step1", "step2"):
         for op in ("sum", "mean"):
             ref = [x.copy() for x in g]
             oracle_full(w, ref, op=op)
@@ -198,7 +203,7 @@ def test_closed_form_rank_plus_one():
         say(f"case closed form {name}")
         bufs = [torch.full((w.n,), r + 1, dtype=TORCH_DT[w.dtype], device="cuda")
                 for r in range(w.P)]
-        for mode in ("fused", "stepwise"):
+        for mode in ("fused", "stepwise", "step2"):
             for op, want in (("sum", w.P * (w.P + 1) / 2), ("mean", (w.P + 1) / 2)):
                 for r, b in enumerate(bufs):
                     b.fill_(r + 1)
@@ -248,7 +253,7 @@ def test_workload_full_bitwise(name):
     g = host_inputs(w)
     ref = [x.copy() for x in g]
     oracle_full(w, ref)
-    for mode in ("fused", "fused1", "fused2", "stepwise"):
+    for mode in ("fused", "fused1", "fused2", "stepwise", "step1", "step2"):
         say(f"case workload {name} mode={mode}")
         bufs = to_device(g)
         run_ddl(bufs, w, mode, plan_api=False)
@@ -297,6 +302,17 @@ def test_workload_full_size_sampled(name):
     plan.execute(copy, events=events, stream=stream)
     torch.cuda.synchronize()
     iv = torch.int32
+    assert all(torch.equal(a.view(iv), b.view(iv)) for a, b in zip(bufs, copy))
+    # the other step form (persistent, or one launch per step), fresh inputs
+    other = 3 - plan.step_form()
+    plan.set_step_form(other)
+    say(f"case workload {name}: stepwise, form {other}")
+    for r, b in enumerate(copy):
+        synth.fill_device(b.data_ptr(), w.n, synth_dtype(w.dtype), w.dist, w.seed, r,
+                          sigma=w.sigma)
+    torch.cuda.synchronize()
+    plan.execute(copy, events=events, stream=stream)
+    torch.cuda.synchronize()
     assert all(torch.equal(a.view(iv), b.view(iv)) for a, b in zip(bufs, copy))
     plan.destroy()
     # the fused pass's other form, on fresh inputs: bit-identical as well
@@ -424,7 +440,8 @@ def test_profiling_counts_launches():
     bufs = [torch.ones(w.n, device="cuda") for _ in range(w.P)]
     for mode, launches in (("fused1", {"fused": 1}),
                            ("fused2", {"fused_reduce": 1, "broadcast": 1}),
-                           ("stepwise", {"reduce": 15, "gather": 15})):
+                           ("stepwise", {"reduce": 15, "gather": 15}),
+                           ("step2", {"walk": 1})):
         plan = make_plan(w, mode, "sum")
         plan.set_profiling(True)
         plan.execute(bufs)
@@ -533,13 +550,13 @@ def test_coalesce_threshold_merges_event_gated_buckets():
     oracle_full(w, ref)
     stream = torch.cuda.current_stream()
     counts = {}
-    for mode in ("fused", "stepwise"):
+    for mode in ("fused", "step1", "step2"):
         for thr in (0, 16 << 20):
             bufs = to_device(g)
             events = [torch.cuda.Event() for _ in w.bucket_list()]
             for e in events:
                 e.record(stream)
-            plan = ddl.Plan(w.P, w.n, w.dtype, w.op, ddl_topo(w), w.bucket_list(), mode)
+            plan = make_plan(w, mode)
             plan.set_coalesce_bytes(thr)
             plan.set_profiling(True)
             plan.execute(bufs, events=events, stream=stream)
@@ -547,7 +564,7 @@ def test_coalesce_threshold_merges_event_gated_buckets():
             # launches that start a group's work: the fused pass's first
             # kernel, or every step
             counts[(mode, thr)] = sum(kinds[k][1] for k in ("fused", "fused_reduce", "reduce",
-                                                              "gather"))
+                                                              "gather", "walk"))
             if mode == "fused":
                 # groups of at least 200 MB over the ranks take the two-kernel
                 # form (one broadcast each), smaller ones one kernel
@@ -558,9 +575,57 @@ def test_coalesce_threshold_merges_event_gated_buckets():
             plan.destroy()
             for r in (0, 7, 15):
                 assert bitwise_equal(out[r], ref[r]), (mode, thr, r)
-    assert counts[("fused", 0)] == 161 and counts[("stepwise", 0)] == 161 * 30
+    assert counts[("fused", 0)] == 161 and counts[("step1", 0)] == 161 * 30
+    assert counts[("step2", 0)] == 161
     assert counts[("fused", 16 << 20)] < 20
-    assert counts[("stepwise", 16 << 20)] == 30 * counts[("fused", 16 << 20)]
+    assert counts[("step1", 16 << 20)] == 30 * counts[("fused", 16 << 20)]
+    assert counts[("step2", 16 << 20)] == counts[("fused", 16 << 20)]
+
+
+@pytest.mark.parametrize("mode", ["fused1", "fused2", "step1", "step2"])
+def test_ordered_events_gate_each_group_on_its_last_event(mode):
+    """Back-propagation's pattern: on one stream, behind a long streaming
+    kernel, each bucket's gradient is written on every rank and then its
+    ready event recorded, output layer first.  With ordered events and a
+    grouping threshold, each group waits only for the event of its last
+    bucket, and every element still matches the oracle: a group that
+    started before its last gradient was written would read the zeros the
+    buffers held before."""
+    say(f"case ordered events {mode}")
+    rng = np.random.default_rng(31)
+    sizes = [int(x) for x in rng.choice([8, 64, 1000, 4096, 30_000, 120_000], 40)]
+    offs = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(int).tolist()
+    bl = list(zip(offs, sizes))[::-1]
+    w = Workload("ordered", 8, sum(sizes), "f32", "mean", "ring", dist="normal", sigma=1e-2,
+                 seed=31, buckets=bl)
+    g = host_inputs(w)
+    ref = [x.copy() for x in g]
+    oracle_full(w, ref)
+    src = to_device(g)
+    bufs = [torch.zeros_like(x) for x in src]
+    stream = torch.cuda.current_stream()
+    plan = make_plan(w, mode)
+    plan.set_ordered_events(True)
+    plan.set_coalesce_bytes(256 << 10)
+    plan.execute(bufs, stream=stream)   # binds the plan (its first call allocates)
+    torch.cuda.synchronize()
+    for b in bufs:
+        b.zero_()
+    hold = torch.zeros(1 << 27, device="cuda")
+    for _ in range(6):
+        synth.stream_compute(hold.data_ptr(), hold.numel(), 1.0, 0.0, stream.cuda_stream)
+    events = []
+    for off, cnt in bl:
+        for r in range(w.P):
+            bufs[r][off:off + cnt].copy_(src[r][off:off + cnt])
+        e = torch.cuda.Event()
+        e.record(stream)
+        events.append(e)
+    plan.execute(bufs, events=events, stream=stream)
+    out = to_host(bufs)
+    plan.destroy()
+    for r in range(w.P):
+        assert bitwise_equal(out[r], ref[r]), (mode, r)
 
 
 @pytest.mark.parametrize("mode", ["stepwise", "fused2"])
@@ -645,7 +710,7 @@ def test_max_ranks(dtype):
         g = host_inputs(w)
         ref = [x.copy() for x in g]
         oracle_full(w, ref)
-        for mode in ("fused1", "fused2", "stepwise"):
+        for mode in ("fused1", "fused2", "step1", "step2"):
             bufs = to_device(g)
             run_ddl(bufs, w, mode)
             out = to_host(bufs)
@@ -663,12 +728,14 @@ def test_custom_ring_orders():
         ref = [x.copy() for x in g]
         kind = "ring" if k == 1 else "multiring"
         orc.allreduce(ref, op=orc.MEAN, kind=KINDS[kind], k=k, ring_order=order)
-        for mode in ("fused1", "fused2", "stepwise"):
+        for mode in ("fused1", "fused2", "step1", "step2"):
             bufs = to_device(g)
             plan = ddl.Plan(P, n, dtype, "mean", ddl.topo(kind, k, ring_order=order), None,
-                            "fused" if mode in PASSES else mode)
+                            "fused" if mode in PASSES else "stepwise")
             if mode in PASSES:
                 plan.set_fused_passes(PASSES[mode])
+            else:
+                plan.set_step_form(STEP_FORMS[mode])
             plan.execute(bufs)
             out = to_host(bufs)
             plan.destroy()
@@ -676,7 +743,7 @@ def test_custom_ring_orders():
                 assert bitwise_equal(out[r], ref[r]), (P, k, mode, r)
 
 
-@pytest.mark.parametrize("mode", ["fused1", "fused2", "stepwise"])
+@pytest.mark.parametrize("mode", ["fused1", "fused2", "step1", "step2"])
 def test_hip_graph_capture_and_replay(mode):
     """An execution captured into a HIP graph (after one eager call has bound
     the plan) replays to the oracle's result, replay after replay, with the
@@ -758,7 +825,7 @@ def test_several_side_streams(nside):
         assert bitwise_equal(snap.cpu().numpy(), ref[2])
 
 
-@pytest.mark.parametrize("mode", ["stepwise", "fused2"])
+@pytest.mark.parametrize("mode", ["step1", "step2", "fused2"])
 def test_graph_capture_with_bucket_events_and_side_streams(mode):
     """Capture with a ready event per bucket (recorded inside the capture),
     so the work forks onto the plan's side streams (two, automatically, for

@@ -73,9 +73,11 @@ def draw(seed, wide=False):
     form = str(rng.choice(["fused1", "fused2", "stepwise"]))
     coalesce = int(rng.choice([0, 0, 4096, 1 << 20]))
     nside = int(rng.integers(0, 5))
+    # stepwise: one launch per step (1) or the persistent step kernel (2)
+    step_form = int(rng.integers(1, 3))
     return dict(P=P, dtype=dtype, op=op, kind=kind, k=k, rows=rows, cols=cols, order=order,
                 buckets=buckets, n=n, ev_of=ev_of if use_events else None, form=form,
-                coalesce=coalesce, nside=nside, seed=seed)
+                coalesce=coalesce, nside=nside, seed=seed, step_form=step_form)
 
 
 NWIDE_CASES = int(os.environ.get("DDL_RANDOM_WIDE_CASES", "4"))
@@ -88,7 +90,8 @@ def test_random_configuration(seed):
     c = draw(seed, wide=kind_ == "wide")
     say(f"case random {seed}: P={c['P']} {c['dtype']} {c['op']} {c['kind']} k={c['k']} "
         f"grid={c['rows']}x{c['cols']} n={c['n']} buckets={len(c['buckets'])} "
-        f"form={c['form']} events={c['ev_of'] is not None} coalesce={c['coalesce']} "
+        f"form={c['form']}/{c['step_form']} events={c['ev_of'] is not None} "
+        f"coalesce={c['coalesce']} "
         f"side={c['nside']}")
     P, n = c["P"], c["n"]
     sdt = synth.F32 if c["dtype"] == "f32" else synth.F16
@@ -105,6 +108,8 @@ def test_random_configuration(seed):
     plan = ddl.Plan(P, n, c["dtype"], c["op"], topo, c["buckets"], mode)
     if mode == "fused":
         plan.set_fused_passes(1 if c["form"] == "fused1" else 2)
+    else:
+        plan.set_step_form(c["step_form"])
     plan.set_coalesce_bytes(c["coalesce"])
     plan.set_side_streams(c["nside"])
     stream = torch.cuda.current_stream()
@@ -168,6 +173,8 @@ def test_random_sgd_and_lars(seed):
     plan = ddl.Plan(P, n, c["dtype"], c["op"], topo, c["buckets"], mode)
     if mode == "fused":
         plan.set_fused_passes(1 if c["form"] == "fused1" else 2)
+    else:
+        plan.set_step_form(c["step_form"])   # the LARS step follows either form
     plan.set_side_streams(c["nside"])
     stream = torch.cuda.current_stream()
     events = None

@@ -157,6 +157,42 @@ def interpret_fused(plan, bufs, nbuckets, dtype, mean, which=None):
                 bufs[r][off:off + cnt] = acc
 
 
+def interpret_walk(plan, bufs, nbuckets, dtype, mean, which=None):
+    """The persistent step kernel's rule, on host arrays: every fused span
+    (chain c in groups of C) goes through the row reduce-scatter of each
+    group, the reduce-scatter and all-gather over the groups' last entries,
+    and the row all-gather of each group, each step reading and writing the
+    ranks' arrays.  Returns the element accesses made (reads + writes)."""
+    P = len(bufs)
+    moved = 0
+    for b in (range(nbuckets) if which is None else which):
+        spans, C = plan.fused_spans(b)
+        G = P // C
+        for off, cnt, c in spans:
+            sl = slice(off, off + cnt)
+
+            def reduce(src, dst, last):
+                r = _add(bufs[c[dst]][sl], bufs[c[src]][sl], dtype)
+                bufs[c[dst]][sl] = _div(r, P, dtype) if last else r
+                return 3 * cnt
+
+            def copy(src, dst):
+                bufs[c[dst]][sl] = bufs[c[src]][sl]
+                return 2 * cnt
+
+            for g in range(G):
+                for t in range(C - 1):
+                    moved += reduce(g * C + t, g * C + t + 1, mean and G == 1 and t == C - 2)
+            for t in range(G - 1):
+                moved += reduce(t * C + C - 1, (t + 1) * C + C - 1, mean and t == G - 2)
+            for t in range(G - 1):
+                moved += copy(((t - 1) % G) * C + C - 1, t * C + C - 1)
+            for g in range(G):
+                for t in range(C - 1):
+                    moved += copy(g * C + (t - 1) % C, g * C + t)
+    return moved
+
+
 def _cases():
     rng = np.random.default_rng(21)
     cases = []
@@ -195,11 +231,15 @@ def test_tables_replay_to_the_oracle(case, op):
                              k=k, rows=rows, cols=cols, ring_order=order, buckets=buckets)
     t = ddl.topo(kind, k, rows, cols, order)
     dt = "f32" if dtype == np.float32 else "f16"
-    for mode in ("stepwise", "fused"):
-        plan = ddl.Plan(P, n, dt, op, t, buckets, mode)
+    for mode in ("stepwise", "fused", "walk"):
+        plan = ddl.Plan(P, n, dt, op, t, buckets, "stepwise" if mode == "walk" else mode)
         bufs = [x.copy() for x in g]
         if mode == "stepwise":
             interpret_steps(plan, bufs, len(buckets), dtype)
+        elif mode == "walk":
+            # the persistent step kernel's rule moves the stepwise bytes
+            moved = interpret_walk(plan, bufs, len(buckets), dtype, op == "mean")
+            assert moved == 5 * (P - 1) * n
         else:
             interpret_fused(plan, bufs, len(buckets), dtype, op == "mean")
         for r in range(P):
