@@ -658,10 +658,13 @@ def test_destroy_with_work_in_flight_is_busy():
     bufs = [torch.ones(n, device="cuda") for _ in range(P)]
     scratch = torch.zeros(1 << 28, device="cuda")
     stream = torch.cuda.current_stream()
+    plan = ddl.Plan(P, n, "f32", "sum", ddl.topo("ring"))
+    # the first call binds the plan, whose synchronous table upload would
+    # wait for the work below: bind it first
+    plan.execute([torch.zeros(n, device="cuda") for _ in range(P)], stream=stream)
     torch.cuda.synchronize()
     for _ in range(8):   # keep the stream busy for several milliseconds
         synth.stream_compute(scratch.data_ptr(), scratch.numel(), 1.0, 0.0, stream.cuda_stream)
-    plan = ddl.Plan(P, n, "f32", "sum", ddl.topo("ring"))
     plan.execute(bufs, stream=stream)
     rc = plan.try_destroy()
     # with launches serialised (AMD_SERIALIZE_KERNEL) nothing is ever in flight
