@@ -102,7 +102,11 @@ enum {
     DDL_E_HIP = -5,      /* a HIP runtime call failed */
     DDL_E_NOMEM = -6,    /* host or device allocation failed */
     DDL_E_BUSY = -7,     /* the plan still has work in flight */
-    DDL_E_DEVICE = -8    /* executed on a device other than the plan's */
+    DDL_E_DEVICE = -8,   /* executed on a device other than the plan's */
+    DDL_E_UNBOUND = -9,  /* allocation-free call on a plan that has not yet
+                            run on the device (ddl_plan_execute_lars_noalloc) */
+    DDL_E_SCRATCH = -10  /* the plan needs more than the allocation-free entry
+                            point's fixed scratch */
 };
 
 /* Build the schedule for P ranks of n elements each.  buckets[0..nbuckets)
@@ -223,6 +227,31 @@ int ddl_plan_execute_sgd(ddl_plan plan, void *const *bufs, void *const *weights,
 int ddl_plan_execute_lars(ddl_plan plan, void *const *bufs, void *const *weights, int nweights,
                           float lr, double coeff, double eps, float *rates_out,
                           void *const *ready_events, void *stream, void *done_event);
+
+/* The LARS step of ddl_plan_execute_lars for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same all-reduce and the same LARS arithmetic,
+ * bit for bit, but the per-tile partial sums and per-bucket rates live in
+ * a fixed scratch array the library holds on every device it runs on
+ * (8 MiB of partial sums, 16 bytes per tile of 1024 binary32 or 4096 binary16
+ * elements -- at most 536,870,912 binary32 elements in one bucket -- and
+ * 256 KiB of rates, at most 65,536 buckets), instead of the buffers
+ * ddl_plan_execute_lars allocates on its first call.  This call makes no
+ * device allocation and creates no HIP stream or event: the plan must
+ * already have run on the current device (any execute entry point binds it;
+ * otherwise DDL_E_UNBOUND), and profiling brackets are not recorded.
+ * DDL_E_SCRATCH, before anything else, for a plan whose tiles or buckets
+ * exceed the scratch; DDL_E_NOMEM if the plan has already run on eight
+ * other streams and this one is new (its completion tracking would need a
+ * new event).  The scratch keeps the last call's contents and every call on
+ * a device shares it: two such calls that may run at the same time on one
+ * device (any plans, different streams, no ordering between them) race.
+ * Other arguments, errors and the asynchrony are those of
+ * ddl_plan_execute_lars. */
+int ddl_plan_execute_lars_noalloc(ddl_plan plan, void *const *bufs, void *const *weights,
+                                  int nweights, float lr, double coeff, double eps,
+                                  float *rates_out, void *const *ready_events, void *stream,
+                                  void *done_event);
 
 /* One-shot form: looks up (or builds and caches) the plan for these
  * arguments -- the cache key is everything except the buffers and events --

@@ -81,6 +81,9 @@ def lib():
             "ddl_plan_execute_lars": ([vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32,
                                        ctypes.c_float, ctypes.c_double, ctypes.c_double,
                                        vp, ctypes.POINTER(vp), vp, vp], i32),
+            "ddl_plan_execute_lars_noalloc": ([vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32,
+                                               ctypes.c_float, ctypes.c_double, ctypes.c_double,
+                                               vp, ctypes.POINTER(vp), vp, vp], i32),
             "ddl_plan_traffic": ([vp, ctypes.POINTER(sz), ctypes.POINTER(sz)], i32),
             "ddl_plan_destroy": ([vp], i32),
             "ddl_cache_clear": ([], i32),
@@ -305,6 +308,22 @@ class Plan:
                                            len(weights), float(lr), float(coeff), float(eps),
                                            _ptr(rates_out), ev, _ptr(stream),
                                            _ptr(done_event)), "ddl_plan_execute_lars")
+
+    def execute_lars_noalloc(self, bufs, weights, lr, coeff=LARS_COEFF, eps=LARS_EPS,
+                             rates_out=None, events=None, stream=None, done_event=None):
+        """execute_lars without any device allocation: the partial sums and
+        rates live in the library's fixed per-device scratch (the plan must
+        have run on the device before; ddl_plan_execute_lars_noalloc)."""
+        if len(bufs) != self.P:
+            raise ValueError(f"expected {self.P} buffers, got {len(bufs)}")
+        ev = None
+        if events is not None:
+            ev = (ctypes.c_void_p * max(1, len(events)))(*[_ptr(e) for e in events])
+        _check(lib().ddl_plan_execute_lars_noalloc(self.handle, _bufs(bufs), _bufs(weights),
+                                                   len(weights), float(lr), float(coeff),
+                                                   float(eps), _ptr(rates_out), ev,
+                                                   _ptr(stream), _ptr(done_event)),
+               "ddl_plan_execute_lars_noalloc")
 
     def traffic(self):
         sent = (ctypes.c_size_t * self.P)()

@@ -199,6 +199,16 @@ struct LarsArgs {
     double coeff, eps;
 };
 
+// The allocation-free LARS entry point keeps its partial sums and rates in
+// a fixed per-device scratch of this size: up to 512Ki tiles of partial sums
+// (8 MiB, 536,870,912 binary32 elements in one bucket) after which the rates
+// start at a 256-byte boundary, up to 64Ki buckets (256 KiB).
+constexpr size_t kLarsScratchPartialBytes = 8u << 20;
+constexpr size_t kLarsScratchBytes = kLarsScratchPartialBytes + (256u << 10);
+// The device address and size of that scratch on `device` (looked up once
+// per device with the device current).  Returns a hipError_t.
+int lars_scratch(int device, void **ptr, size_t *bytes);
+
 // Current value of a ddl_tune_knob (its default unless ddl_set_tuning set it).
 int tuning(int knob);
 

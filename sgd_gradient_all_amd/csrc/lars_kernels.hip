@@ -37,7 +37,18 @@
 // boundary.
 #include "device_common.h"
 
+#include <map>
+#include <mutex>
+
 namespace ddl {
+
+// The fixed scratch of the allocation-free LARS entry point: per-tile
+// partial sums (16 bytes per tile) and per-bucket rates (4 bytes each) for
+// callers that cannot allocate.  Each device holds its own copy at its own
+// address; host code reaches it only through the address hipGetSymbolAddress
+// gives for that device (lars_scratch below), never through this name.
+static __device__ __align__(256) unsigned char scratch[kLarsScratchBytes];
+
 namespace {
 
 using namespace dev;
@@ -264,6 +275,32 @@ void launch_update(dim3 grid, hipStream_t s, const RankPtrs &w, const LarsArgs &
 }
 
 }  // namespace
+
+int lars_scratch(int device, void **ptr, size_t *bytes) {
+    static std::mutex mu;
+    static std::map<int, void *> &addr = *new std::map<int, void *>;
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = addr.find(device);
+    if (it == addr.end()) {
+        // once per device, with that device current
+        int cur = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess)
+            return (int)e;
+        if (cur != device && (e = hipSetDevice(device)) != hipSuccess)
+            return (int)e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != device)
+            (void)hipSetDevice(cur);
+        if (e != hipSuccess || !p)
+            return (int)(e != hipSuccess ? e : hipErrorInvalidSymbol);
+        it = addr.emplace(device, p).first;
+    }
+    *ptr = it->second;
+    *bytes = kLarsScratchBytes;
+    return (int)hipSuccess;
+}
 
 int launch_lars(int dtype, int kind, const RankPtrs &w, const LarsArgs &a, uint32_t blocks,
                 void *stream) {

@@ -716,8 +716,12 @@ hipEvent_t *last_event(ddl_plan p, hipStream_t ls, bool may_create = true) {
     return &p->last_ev.back().second;
 }
 
+// noalloc: the allocation-free entry point -- the plan must be bound, the
+// LARS buffers come in through lars, no event is created and no launch is
+// bracketed for profiling.
 int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stream_,
-                   void *done_event, const SgdArgs *sgd, const LarsCall *lars = nullptr) {
+                   void *done_event, const SgdArgs *sgd, const LarsCall *lars = nullptr,
+                   bool noalloc = false) {
     const int P = p->parts[0].s.P;
     bool any_elems = false;
     for (const Part &pt : p->parts)
@@ -744,6 +748,8 @@ int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stre
     if (hipGetDevice(&dev) != hipSuccess)
         return DDL_E_HIP;
     if (p->device < 0) {
+        if (noalloc)
+            return DDL_E_UNBOUND;
         int rc = bind_device(p, dev);
         if (rc) {
             release_device(p);
@@ -752,7 +758,7 @@ int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stre
     } else if (p->device != dev) {
         return DDL_E_DEVICE;
     }
-    if (lars) {
+    if (lars && !lars->partial) {
         int rc = ensure_lars(p);
         if (rc)
             return rc;
@@ -795,7 +801,7 @@ int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stre
     int b0 = 0, g = 0, used = 0;
     std::vector<std::pair<int, int>> range(p->parts.size());
     while (b0 < nb) {
-        L.prof = p->profiling && p->prof_group++ % (uint64_t)p->prof_stride == 0;
+        L.prof = !noalloc && p->profiling && p->prof_group++ % (uint64_t)p->prof_stride == 0;
         // the group: equal events, then (with a threshold) more buckets
         // until it holds coalesce_bytes per rank
         void *ev0 = ready ? ready[b0] : nullptr;
@@ -912,9 +918,9 @@ int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stre
     }
     if (done_event && hipEventRecord(static_cast<hipEvent_t>(done_event), ls) != hipSuccess)
         return DDL_E_HIP;
-    hipEvent_t *last = last_event(p, ls);
+    hipEvent_t *last = last_event(p, ls, !noalloc);
     if (!last)
-        return DDL_E_HIP;
+        return noalloc ? DDL_E_NOMEM : DDL_E_HIP;
     if (hipEventRecord(*last, ls) != hipSuccess)
         return DDL_E_HIP;
     p->in_flight = true;
@@ -1071,6 +1077,10 @@ const char *ddl_strerror(int code) {
     case DDL_E_NOMEM: return "allocation failed";
     case DDL_E_BUSY: return "the plan still has work in flight";
     case DDL_E_DEVICE: return "executed on a device other than the plan's";
+    case DDL_E_UNBOUND:
+        return "the plan has not run on this device yet (its tables are not in device memory)";
+    case DDL_E_SCRATCH:
+        return "the plan needs more than the allocation-free entry point's fixed scratch";
     default: return "unknown error";
     }
 }
@@ -1250,9 +1260,11 @@ int ddl_plan_execute_sgd(ddl_plan plan, void *const *bufs, void *const *weights,
 
 namespace {
 
+// scratch: the allocation-free form, whose partial sums and rates live in
+// the library's fixed per-device scratch instead of the plan's buffers.
 int execute_lars(ddl_plan plan, void *const *bufs, void *const *weights, int nweights, float lr,
                  double coeff, double eps, float *rates_out, void *const *ready_events,
-                 void *stream, void *done_event) {
+                 void *stream, void *done_event, bool scratch = false) {
     if (!plan || !bufs || !weights)
         return DDL_E_NULL;
     try {
@@ -1273,7 +1285,30 @@ int execute_lars(ddl_plan plan, void *const *bufs, void *const *weights, int nwe
         c.coeff = coeff;
         c.eps = eps;
         c.rates_out = rates_out;
-        return execute_locked(r.get(), bufs, ready_events, stream, done_event, nullptr, &c);
+        if (scratch) {
+            // sizes first (host-only), then the binding and the device
+            const Schedule &s = r->parts[0].s;
+            const size_t tiles = s.bk_prefix.empty() ? 0 : s.bk_prefix.back();
+            if (2 * tiles * sizeof(double) > kLarsScratchPartialBytes ||
+                s.buckets.size() * sizeof(float) > kLarsScratchBytes - kLarsScratchPartialBytes)
+                return DDL_E_SCRATCH;
+            if (r->device < 0)
+                return DDL_E_UNBOUND;
+            int dev = 0;
+            if (hipGetDevice(&dev) != hipSuccess)
+                return DDL_E_HIP;
+            if (dev != r->device)
+                return DDL_E_DEVICE;
+            void *base = nullptr;
+            size_t cap = 0;
+            if (lars_scratch(dev, &base, &cap) != hipSuccess || cap < kLarsScratchBytes)
+                return DDL_E_HIP;
+            c.partial = static_cast<double *>(base);
+            c.rate = reinterpret_cast<float *>(static_cast<char *>(base) +
+                                               kLarsScratchPartialBytes);
+        }
+        return execute_locked(r.get(), bufs, ready_events, stream, done_event, nullptr, &c,
+                              scratch);
     } catch (...) {
         return DDL_E_NOMEM;
     }
@@ -1286,6 +1321,14 @@ int ddl_plan_execute_lars(ddl_plan plan, void *const *bufs, void *const *weights
                           void *const *ready_events, void *stream, void *done_event) {
     return execute_lars(plan, bufs, weights, nweights, lr, coeff, eps, rates_out, ready_events,
                         stream, done_event);
+}
+
+int ddl_plan_execute_lars_noalloc(ddl_plan plan, void *const *bufs, void *const *weights,
+                                  int nweights, float lr, double coeff, double eps,
+                                  float *rates_out, void *const *ready_events, void *stream,
+                                  void *done_event) {
+    return execute_lars(plan, bufs, weights, nweights, lr, coeff, eps, rates_out, ready_events,
+                        stream, done_event, true);
 }
 
 int ddl_allreduce(void *const *bufs, int P, size_t n, ddl_dtype dtype, ddl_op op,

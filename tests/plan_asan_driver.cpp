@@ -56,7 +56,18 @@ static void stale_handles() {
     (void)hipStreamCreateWithFlags(&s, 0);
     ddl_plan plan = nullptr;
     check(ddl_plan_create(&plan, 4, n, DDL_F32, DDL_SUM, &ring, nullptr, 0, DDL_FUSED), "create");
+    std::vector<void *> w0(bufs);
+    expect(ddl_plan_execute_lars_noalloc(plan, bufs.data(), w0.data(), 1, 0.1f, 0.01, 1e-6,
+                                         nullptr, nullptr, s, nullptr),
+           DDL_E_UNBOUND, "allocation-free LARS before the plan has run");
     check(ddl_plan_execute(plan, bufs.data(), nullptr, s, nullptr), "execute");
+    // the allocation-free call makes no device allocation
+    const long allocs = g_live_allocs;
+    check(ddl_plan_execute_lars_noalloc(plan, bufs.data(), w0.data(), 1, 0.1f, 0.01, 1e-6,
+                                        nullptr, nullptr, s, nullptr),
+          "allocation-free LARS");
+    if (g_live_allocs != allocs)
+        fail("the allocation-free LARS call allocated device memory");
     check(ddl_plan_destroy(plan), "destroy");
     expect(ddl_plan_destroy(plan), DDL_E_ARG, "second destroy");
     expect(ddl_plan_execute(plan, bufs.data(), nullptr, s, nullptr), DDL_E_ARG,
@@ -211,6 +222,10 @@ int main(int argc, char **argv) {
                                         0.01, 1e-6, nullptr, uni(0, 1) ? evp.data() : nullptr,
                                         s, nullptr),
                   "execute_lars");
+            check(ddl_plan_execute_lars_noalloc(plan, bufs.data(), w.data(), uni(0, 1) ? 1 : P,
+                                                0.01f, 0.01, 1e-6, nullptr,
+                                                uni(0, 1) ? evp.data() : nullptr, s, nullptr),
+                  "execute_lars_noalloc");
         }
         double tot[DDL_K_COUNT], mx[DDL_K_COUNT];
         int cnt[DDL_K_COUNT];

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_strerror_covers_every_code():
-    for code in range(0, -9, -1):
+    for code in range(0, -11, -1):
         assert ddl.ddl_strerror(code) != "unknown error"
     assert ddl.ddl_strerror(-99) == "unknown error"
 
@@ -82,6 +82,33 @@ def test_stale_and_foreign_handles_are_argument_errors():
     assert L.ddl_plan_destroy(foreign) == -2
     assert L.ddl_plan_execute(foreign, bufs, None, None, None) == -2
     assert L.ddl_plan_destroy(None) == -1
+
+
+def test_noalloc_lars_rejections_need_no_device():
+    """The allocation-free LARS entry point rejects, before any device work,
+    a plan too large for its fixed scratch (DDL_E_SCRATCH) and a plan that
+    has not yet run on the device (DDL_E_UNBOUND); typed plans are
+    argument errors as for the allocating entry point."""
+    big = ddl.Plan(2, (1 << 29) + 4096, "f32", "mean", ddl.topo("ring"))
+    with pytest.raises(ddl.DDLError) as ei:
+        big.execute_lars_noalloc([0x1000, 0x2000], [0x3000], 0.1)
+    assert ei.value.code == -10
+    big.destroy()
+    many = ddl.Plan(2, 70_000, "f32", "mean", ddl.topo("ring"), [(i, 1) for i in range(70_000)])
+    with pytest.raises(ddl.DDLError) as ei:
+        many.execute_lars_noalloc([0x1000, 0x2000], [0x3000], 0.1)
+    assert ei.value.code == -10
+    many.destroy()
+    fits = ddl.Plan(4, (1 << 29) - 8192, "f32", "mean", ddl.topo("ring"))
+    with pytest.raises(ddl.DDLError) as ei:
+        fits.execute_lars_noalloc([0x1000 * (r + 1) for r in range(4)], [0x9000], 0.1)
+    assert ei.value.code == -9
+    fits.destroy()
+    typed = ddl.Plan.typed(2, 64, "mean", ddl.topo("ring"), [(0, 16, "f32")])
+    with pytest.raises(ddl.DDLError) as ei:
+        typed.execute_lars_noalloc([0x1000, 0x2000], [0x3000], 0.1)
+    assert ei.value.code == -2
+    typed.destroy()
 
 
 def test_argument_validation():
