@@ -189,6 +189,9 @@ def main():
     ap.add_argument("--passes", type=int, default=0, choices=[0, 1, 2],
                     help="fused pass form: 0 the plan's choice, 1 one kernel, "
                          "2 reduce + broadcast kernels")
+    ap.add_argument("--step-form", type=int, default=0, choices=[0, 1, 2],
+                    help="stepwise mode: 0 the plan's choice, 1 one launch per schedule "
+                         "step, 2 the persistent step kernel")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip every side measurement (--legs)")
     ap.add_argument("--legs", default=",".join(LEGS),
@@ -262,6 +265,8 @@ def main():
     plan_build_ms = (time.perf_counter() - t_plan) * 1e3
     if args.mode == "fused":
         plan.set_fused_passes(args.passes)
+    else:
+        plan.set_step_form(args.step_form)
     if args.coalesce_bytes:
         plan.set_coalesce_bytes(args.coalesce_bytes)
     passes = plan.fused_passes()
