@@ -230,6 +230,12 @@ def main():
     torch.cuda.set_device(0)
     dev_name = torch.cuda.get_device_name(0)
     log(f"bench: {w.name} ({w.description}) on {dev_name}, mode={args.mode}")
+    # the other workloads first, each on its own fresh buffers in a device
+    # that holds nothing else yet (the rate of a pass depends on the physical
+    # pages behind its buffers, and those of a later allocation land among
+    # the headline's 48 GB)
+    configs = (configs_leg(w, torch.cuda.current_stream(), torch, ddl, synth)
+               if "configs" in args.legs else None)
 
     # inputs, generated in HBM
     bufs = [torch.empty(w.n, dtype=tdt, device="cuda") for _ in range(w.P)]
@@ -336,6 +342,8 @@ def main():
         result["calib_copy_bytes"] = 2 * nel * 4
         del a, b
 
+    if configs is not None:
+        result["configs"] = configs
     if args.legs:
         result.update(extras(args, w, bufs, topo, buckets, main_stream, torch, ddl, synth,
                              hbm_bytes, ms))
@@ -348,10 +356,6 @@ def main():
 
 def extras(args, w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_bytes, fused_ms):
     out = {}
-    # the other workloads first: their buffers then take the pages the
-    # process gets first, before the large legs below have churned HBM
-    if "configs" in args.legs:
-        out["configs"] = configs_leg(w, main_stream, torch, ddl, synth)
     if "stepwise" in args.legs:
         out["stepwise"] = stepwise_leg(w, bufs, topo, buckets, main_stream, torch, ddl,
                                        fused_bytes)
@@ -519,18 +523,21 @@ def stepwise_leg(w, bufs, topo, buckets, main_stream, torch, ddl, fused_bytes):
 def latency_leg(main_stream, torch, ddl, synth, calls=4):
     """Small buckets (IBM's latency/bandwidth trade-off): the ResNet-50
     gradient over 16 ranks and 4 rings, binary32, each of its 161 tensors its
-    own bucket with its own ready event recorded as back-propagation would,
-    output layer first.  For the fused pass and both step forms, at grouping
-    thresholds 0 and 16 MB:
-      - gpu_ms: device time per all-reduce with the host ahead of the device
+    own bucket with its own ready event, recorded in list order on the
+    caller's stream as back-propagation would record them, output layer
+    first.  For the fused pass and both step forms, at grouping thresholds 0
+    and 16 MB (with and without the ordered-events promise):
+      - device_ms: device time of one call with the host ahead of the device
         (a streaming kernel on the caller's stream holds the device while the
-        calls are enqueued; timed from its end), i.e. what the schedule costs
-        the device;
-      - eager_ms: back-to-back calls, event recording included, i.e. the rate
-        when the host issues nothing else (host-bound when the host is
-        slower than the device);
-      - graph_ms: the same call (event records and all) captured once into a
-        HIP graph and replayed back to back;
+        call is enqueued): from the end of that kernel, through the caller's
+        161 event records, to the end of the all-reduce;
+      - after_events_ms: the same call from the moment the last ready event
+        has been recorded (every gradient ready) to the end of the
+        all-reduce -- what back-propagation would be left waiting for;
+      - graph_ms: the call, event records included, captured once into a HIP
+        graph and replayed back to back (the records become graph edges);
+      - eager_ms: back-to-back eager calls, event records included (host-
+        bound when the host is slower than the device);
       - host_ms: the host time of the library call itself.
     Against the same all-reduce with no events (one group)."""
     from synth.workloads import WORKLOADS
@@ -544,6 +551,7 @@ def latency_leg(main_stream, torch, ddl, synth, calls=4):
     gate = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
     cs = main_stream.cuda_stream
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    tm = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
 
     def hold(n):
@@ -556,10 +564,13 @@ def latency_leg(main_stream, torch, ddl, synth, calls=4):
     torch.cuda.synchronize()
     hold_ms = t0.elapsed_time(t1) / 4
 
+    def record_events(stream):
+        for e in events:
+            e.record(stream)
+
     def run(plan, gated):
         if gated:
-            for e in events:
-                e.record(main_stream)
+            record_events(main_stream)
         plan.execute(bufs, events=events if gated else None, stream=main_stream)
 
     def measure(plan, gated, graph_too):
@@ -569,8 +580,7 @@ def latency_leg(main_stream, torch, ddl, synth, calls=4):
         host = []
         for _ in range(calls):
             if gated:
-                for e in events:
-                    e.record(main_stream)
+                record_events(main_stream)
             h0 = time.perf_counter()
             plan.execute(bufs, events=events if gated else None, stream=main_stream)
             host.append(time.perf_counter() - h0)
@@ -583,20 +593,27 @@ def latency_leg(main_stream, torch, ddl, synth, calls=4):
         t1.record(main_stream)
         torch.cuda.synchronize()
         eager = t0.elapsed_time(t1) / calls
-        # host ahead: the calls are enqueued behind a streaming kernel long
-        # enough to cover their host time
-        need = (eager * calls * 1.5 + 2.0) / max(hold_ms, 1e-3)
-        hold(int(need) + 1)
-        t0.record(main_stream)
-        h0 = time.perf_counter()
+        # one call at a time behind a streaming kernel that covers its host
+        # time: device time from the kernel's end, and from the last record
+        nhold = int((eager * 1.5 + 1.0) / max(hold_ms, 1e-3)) + 1
+        dev, after, ahead = [], [], True
         for _ in range(calls):
-            run(plan, gated)
-        host_all = (time.perf_counter() - h0) * 1e3
-        t1.record(main_stream)
-        torch.cuda.synchronize()
-        row = {"gpu_ms": round(t0.elapsed_time(t1) / calls, 4), "eager_ms": round(eager, 4),
-               "host_ms": round(host_ms, 4),
-               "host_ahead": bool(host_all < (int(need) + 1) * hold_ms)}
+            hold(nhold)
+            h0 = time.perf_counter()
+            t0.record(main_stream)
+            if gated:
+                record_events(main_stream)
+            tm.record(main_stream)
+            plan.execute(bufs, events=events if gated else None, stream=main_stream)
+            t1.record(main_stream)
+            ahead = ahead and (time.perf_counter() - h0) * 1e3 < nhold * hold_ms
+            torch.cuda.synchronize()
+            dev.append(t0.elapsed_time(t1))
+            after.append(tm.elapsed_time(t1))
+        row = {"device_ms": round(sum(dev) / calls, 4),
+               "after_events_ms": round(sum(after) / calls, 4),
+               "eager_ms": round(eager, 4), "host_ms": round(host_ms, 4),
+               "host_ahead": bool(ahead)}
         if graph_too:
             graph = torch.cuda.CUDAGraph()
             cap = torch.cuda.Stream()
@@ -604,8 +621,7 @@ def latency_leg(main_stream, torch, ddl, synth, calls=4):
             with torch.cuda.stream(cap):
                 with torch.cuda.graph(graph, stream=cap):
                     if gated:
-                        for e in events:
-                            e.record(cap)
+                        record_events(cap)
                     plan.execute(bufs, events=events if gated else None, stream=cap)
             torch.cuda.synchronize()
             graph.replay()
@@ -623,7 +639,7 @@ def latency_leg(main_stream, torch, ddl, synth, calls=4):
     res = {"workload": w.name, "ranks": w.P, "tensors": len(buckets), "events": len(buckets),
            "hold_kernel_ms": round(hold_ms, 3)}
     plan = ddl.Plan(w.P, w.n, w.dtype, w.op, topo, buckets, "fused")
-    res["no_events_fused"] = measure(plan, False, False)
+    res["no_events_fused"] = measure(plan, False, True)
     plan.destroy()
     variants = [("fused", 0, 0, False), ("fused", 0, 16, False), ("fused", 0, 16, True),
                 ("stepwise", 2, 0, False), ("stepwise", 2, 16, True),
@@ -648,9 +664,9 @@ def latency_leg(main_stream, torch, ddl, synth, calls=4):
         res[key] = row
         # captured plans must outlive the graph, which is gone by now
         plan.destroy()
-    base = res["no_events_fused"]["gpu_ms"]
+    base = res["no_events_fused"]
     res["fused_per_tensor_events_over_no_events"] = {
-        k: round(res[k]["gpu_ms"] / base, 3)
+        k: {m: round(res[k][m] / base[m], 3) for m in ("device_ms", "graph_ms")}
         for k in ("fused_coalesce_0mb", "fused_coalesce_16mb", "fused_coalesce_16mb_ordered")}
     del bufs, gate
     torch.cuda.empty_cache()

@@ -358,9 +358,9 @@ int ddl_plan_get_fused_passes(ddl_plan plan, int *passes);
  * bytes, the same results); no barrier spans workgroups.  This is the
  * latency form for small buckets ("[论文解读] PowerAI DDL", ABSTRACT: the
  * latency/bandwidth trade-off): 2 (P-1) launches become one.
- * form = 0 (default): automatic, per group: persistent for groups of at most
- * 8 MB per rank, one launch per step above.  With the SGD step
- * (ddl_plan_execute_sgd) stepwise plans always launch per step.
+ * form = 0 (default): automatic, which is the persistent form (measured the
+ * faster on every workload).  With the SGD step (ddl_plan_execute_sgd)
+ * stepwise plans always launch per step.
  * DDL_E_ARG for other values; takes effect at the next execute.
  * ddl_plan_get_step_form reports the form of one group holding all the
  * plan's buckets, as in a call without ready events (0 for a fused plan). */

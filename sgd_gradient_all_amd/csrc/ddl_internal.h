@@ -124,6 +124,11 @@ struct FusedArgs {
     int anchor;      // tiles anchored at multiples of the tile size
     void *home;      // reduce kernel: where the result goes (rank 0's buffer,
                      // or a scratch buffer of n elements)
+    // reduce kernel of the LARS step (null otherwise): per tile t of this
+    // table, partial[2t] and partial[2t+1] receive the binary64 sums of
+    // w0^2 and y^2 over the tile (w0 replica 0's binary32 weights)
+    double *partial;
+    const float *w0;
 };
 
 // Spans of at most kTinySpanMax elements are "tiny": a group made only of
@@ -162,6 +167,13 @@ struct BcastArgs {
     int aligned;
     int tiles_per_group;  // consecutive tiles one workgroup copies
     int nxcd;             // > 1: all rank groups of a tile block on one die
+    // the LARS step's update, riding on the broadcast (table mode; null
+    // rate otherwise): with the reduced values in hand, the workgroup of
+    // rank group g also steps weight replicas -- those of its own ranks when
+    // nweights == P, plus replica 0 for g == 0; replica 0 alone for g == 0
+    // when nweights == 1 -- by w = w - rate[bucket] * y
+    const float *rate;
+    int nweights;
 };
 
 // The SGD step fused into the all-reduce's epilogue: binary32 weight
@@ -219,6 +231,9 @@ int launch_step(int dtype, int kind, int vpl, const RankPtrs &bufs, const StepAr
 int launch_fused(int dtype, const RankPtrs &bufs, const FusedArgs &a, const SgdArgs *sgd,
                  bool home, uint32_t tiles, void *stream);
 int launch_bcast(int dtype, const RankPtrs &bufs, const BcastArgs &a, void *stream);
+// The broadcast with the LARS step's update of the replicas w (a.rate set).
+int launch_bcast_update(int dtype, const RankPtrs &bufs, const RankPtrs &w, const BcastArgs &a,
+                        void *stream);
 int launch_tiny(int dtype, const RankPtrs &bufs, const TinyArgs &a, void *stream);
 // The persistent step kernel: tiles [a.tile_base, a.tile_base + tiles) of the
 // fused span table, every schedule step walked by the workgroup of a tile.

@@ -86,6 +86,33 @@ template <class V>
 __device__ __forceinline__ void stv(void *p, V v) {
     *reinterpret_cast<V *>(p) = v;
 }
+// Sum over the workgroup of one binary64 value per lane: a butterfly within
+// each wave64, then the waves' sums in wave order.  The result is in lane 0
+// of wave 0.  Every lane of the workgroup must call it (it holds a barrier).
+__device__ __forceinline__ double block_sum(double v, double *lds) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v += __shfl_xor(v, o, 64);
+    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    if (lane == 0)
+        lds[wave] = v;
+    __syncthreads();
+    double s = 0.0;
+    if (threadIdx.x == 0)
+        for (int i = 0; i < kBlock / 64; ++i)
+            s += lds[i];
+    return s;
+}
+
+// acc += the square of every binary32 component of x, in binary64 (each
+// square of a binary32 value is exact there), components in order.
+template <class W>
+__device__ __forceinline__ void add_squares(W x, double &acc) {
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(W) / sizeof(float)); ++i)
+        acc += (double)x[i] * (double)x[i];
+}
+
 // Largest i in [lo, hi) with prefix[i] <= tile (prefix is non-decreasing,
 // prefix[lo] <= tile < prefix[hi]).  Uniform across the workgroup.
 //

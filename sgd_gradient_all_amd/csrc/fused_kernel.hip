@@ -188,15 +188,22 @@ __device__ __forceinline__ void store_home(void *home, uint64_t e,
 }
 
 // kHome: write the result to the home buffer only (the first kernel of the
-// two-kernel form); otherwise to every rank.
-template <class E, bool kGrouped, bool kNt, bool kSgd, bool kHome, int kB>
+// two-kernel form); otherwise to every rank.  kLars (with kHome): also the
+// LARS step's norms -- per tile, the binary64 sums of the squares of the
+// result y and of replica 0's weights w0, each lane in element order, then
+// over the workgroup (block_sum), written to a.partial[2t] (w0) and
+// a.partial[2t + 1] (y).
+template <class E, bool kGrouped, bool kNt, bool kSgd, bool kHome, int kB, bool kLars = false>
 __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs &a,
                                            const SgdArgs *g) {
     using T = typename E::T;
     using V = typename E::V;
+    using Wv = typename E::W;
     constexpr int U = fused_vecs_per_lane(sizeof(T));
     constexpr uint64_t kTile = fused_tile_elems(sizeof(T));
+    constexpr uint64_t kStride = (uint64_t)kBlock * E::N;
     __shared__ uint64_t src[DDL_MAX_RANKS];  // rank stream addresses, chain order
+    __shared__ double lds_norm[2][kBlock / 64];
     const int P = a.P;
     const uint32_t tid = threadIdx.x;
     const uint32_t first = a.tile_base + blockIdx.x * (uint32_t)kFusedTilesPerGroup;
@@ -219,6 +226,7 @@ __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs
         const uint64_t base = tile_lo(sp.off, sh, kTile, j);
         const uint32_t cnt = (uint32_t)(tile_hi(sp.off, sp.len, sh, kTile, j) - base);
         uint32_t done = 0;
+        double sw = 0.0, sy = 0.0;  // kLars: this lane's sums of squares
         if (sp.flags & kItemAligned) {
             const uint32_t nvec = cnt / E::N;
             if (nvec == (uint32_t)(U * kBlock)) {
@@ -235,6 +243,17 @@ __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs
                     store_all<E, U>(bufs, P, e, acc);
                 if (kSgd)
                     sgd_all<E, kNt, U>(g, e, acc);
+                if (kLars) {
+                    Wv wv[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        wv[u] = ld_stream<Wv, true>(a.w0 + e + u * kStride);
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        add_squares<Wv>(E::widen(acc[u]), sy);
+                        add_squares<Wv>(wv[u], sw);
+                    }
+                }
             } else {
                 for (uint32_t v = tid; v < nvec; v += kBlock) {
                     const uint64_t e = base + (uint64_t)v * E::N;
@@ -248,6 +267,10 @@ __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs
                         store_all<E, 1>(bufs, P, e, acc);
                     if (kSgd)
                         sgd_all<E, kNt, 1>(g, e, acc);
+                    if (kLars) {
+                        add_squares<Wv>(E::widen(acc[0]), sy);
+                        add_squares<Wv>(ld_stream<Wv, true>(a.w0 + e), sw);
+                    }
                 }
             }
             done = nvec * E::N;
@@ -278,6 +301,20 @@ __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs
                     float *wp = static_cast<float *>(g->w.p[r]) + e;
                     *wp = sgd_step<float>(*wp, (float)acc, g->lr);
                 }
+            if (kLars) {
+                const double y = (double)(float)acc, x = (double)a.w0[e];
+                sy += y * y;
+                sw += x * x;
+            }
+        }
+        if (kLars) {
+            const double tw = block_sum(sw, lds_norm[0]);
+            const double ty = block_sum(sy, lds_norm[1]);
+            if (tid == 0) {
+                a.partial[2 * (uint64_t)tile] = tw;
+                a.partial[2 * (uint64_t)tile + 1] = ty;
+            }
+            __syncthreads();  // lds_norm is read before the next tile's sums
         }
     }
 }
@@ -305,6 +342,14 @@ void fused_reduce_kernel(RankPtrs bufs, FusedArgs a) {
     fused_body<E, kGrouped, kNt, false, true, kB>(bufs, a, nullptr);
 }
 
+// The reduce kernel of the LARS step's two-kernel form: also the per-tile
+// partial sums of the layer norms.
+template <class E, bool kGrouped, bool kNt, int kB>
+__global__ __launch_bounds__(kBlock) DDL_FUSED_OCCUPANCY
+void fused_reduce_lars_kernel(RankPtrs bufs, FusedArgs a) {
+    fused_body<E, kGrouped, kNt, false, true, kB, true>(bufs, a, nullptr);
+}
+
 // ---------------------------------------------------------------------------
 // broadcast: the second kernel of the two-kernel form.  Workgroup b copies
 // tiles_per_group anchored tiles from tile (b / ngroups) * tiles_per_group
@@ -314,28 +359,32 @@ void fused_reduce_kernel(RankPtrs bufs, FusedArgs a) {
 // a workgroup's first access is the load of the values it copies.
 // ---------------------------------------------------------------------------
 // One tile of the broadcast: tile q of the run (or table tile q past
-// tile_base) to ranks r0 .. r1.
-template <class E>
+// tile_base) to ranks r0 .. r1.  kUpd (table mode, the LARS step): with the
+// reduced values in hand, also step the weight replicas of rank group grp
+// (see BcastArgs) by the tile's bucket's rate.
+template <class E, bool kUpd>
 __device__ __forceinline__ void bcast_tile(const RankPtrs &bufs, const BcastArgs &a, uint64_t q,
-                                           int r0, int r1) {
+                                           int r0, int r1, const RankPtrs *w, uint32_t grp) {
     using T = typename E::T;
     using V = typename E::V;
+    using Wv = typename E::W;
     constexpr int U = fused_vecs_per_lane(sizeof(T));
     constexpr uint64_t kTile = fused_tile_elems(sizeof(T));
     constexpr uint64_t kStride = (uint64_t)kBlock * E::N;
     const uint32_t tid = threadIdx.x;
     uint64_t off = a.off, len = a.len, j = q;
     bool aligned = a.aligned != 0;
+    uint32_t bucket = 0;
     if (a.spans) {
         if (q >= (uint64_t)(a.tile_end - a.tile_base))
             return;
         const uint32_t tile = a.tile_base + (uint32_t)q;
-        const uint32_t i = a.tile_span[tile];
-        const DevSpan sp = a.spans[i];
+        bucket = a.tile_span[tile];
+        const DevSpan sp = a.spans[bucket];
         off = sp.off;
         len = sp.len;
         aligned = (sp.flags & kItemAligned) != 0;
-        j = tile - a.prefix[i];
+        j = tile - a.prefix[bucket];
     }
     const uint64_t sh = tile_shift(off, kTile, true);
     if (j >= tile_count(len, sh, kTile))
@@ -344,6 +393,12 @@ __device__ __forceinline__ void bcast_tile(const RankPtrs &bufs, const BcastArgs
     const uint32_t cnt = (uint32_t)(tile_hi(off, len, sh, kTile, j) - base);
     const T DDL_GLOBAL *home =
         reinterpret_cast<const T DDL_GLOBAL *>(reinterpret_cast<uint64_t>(bufs.p[0]));
+    // the replicas this workgroup steps: replica 0 for the first rank group
+    // (k = -1; no rank group writes rank 0), then replicas w0 .. w1 - 1 (its
+    // own ranks, with one replica per rank)
+    const bool rep0 = kUpd && grp == 0;
+    const int w0 = kUpd && a.nweights > 1 ? r0 : 0, w1 = kUpd && a.nweights > 1 ? r1 : 0;
+    const float rate = kUpd ? a.rate[bucket] : 0.0f;
     uint32_t done = 0;
     if (aligned) {
         const uint32_t nvec = cnt / E::N;
@@ -357,12 +412,27 @@ __device__ __forceinline__ void bcast_tile(const RankPtrs &bufs, const BcastArgs
 #pragma unroll
                 for (int u = 0; u < U; ++u)
                     st_stream<V>(static_cast<T *>(bufs.p[r]) + e + u * kStride, v[u]);
+            if (kUpd)
+                for (int k = rep0 ? -1 : 0; k < w1 - w0; ++k) {
+                    float *wr = static_cast<float *>(w->p[k < 0 ? 0 : w0 + k]) + e;
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        st_stream<Wv>(wr + u * kStride,
+                                      sgd_step<Wv>(ld_stream<Wv, true>(wr + u * kStride),
+                                                   E::widen(v[u]), rate));
+                }
         } else {
             for (uint32_t k = tid; k < nvec; k += kBlock) {
                 const uint64_t e = base + (uint64_t)k * E::N;
                 const V v = *reinterpret_cast<const V DDL_GLOBAL *>(home + e);
                 for (int r = r0; r < r1; ++r)
                     st_stream<V>(static_cast<T *>(bufs.p[r]) + e, v);
+                if (kUpd)
+                    for (int k = rep0 ? -1 : 0; k < w1 - w0; ++k) {
+                        float *wr = static_cast<float *>(w->p[k < 0 ? 0 : w0 + k]) + e;
+                        st_stream<Wv>(wr, sgd_step<Wv>(ld_stream<Wv, true>(wr), E::widen(v),
+                                                       rate));
+                    }
             }
         }
         done = nvec * E::N;
@@ -372,6 +442,11 @@ __device__ __forceinline__ void bcast_tile(const RankPtrs &bufs, const BcastArgs
         const T x = home[e];
         for (int r = r0; r < r1; ++r)
             static_cast<T *>(bufs.p[r])[e] = x;
+        if (kUpd)
+            for (int k = rep0 ? -1 : 0; k < w1 - w0; ++k) {
+                float *wr = static_cast<float *>(w->p[k < 0 ? 0 : w0 + k]) + e;
+                *wr = sgd_step<float>(*wr, (float)x, rate);
+            }
     }
 }
 
@@ -380,8 +455,9 @@ __device__ __forceinline__ void bcast_tile(const RankPtrs &bufs, const BcastArgs
 // dealt so that all rank groups of a tile block run on one accelerator die
 // (workgroup b runs on die b % nxcd), which then fetches the block's values
 // into its L2 once instead of once per die.
-template <class E>
-__global__ __launch_bounds__(kBlock) void bcast_kernel(RankPtrs bufs, BcastArgs a) {
+template <class E, bool kUpd>
+__device__ __forceinline__ void bcast_body(const RankPtrs &bufs, const BcastArgs &a,
+                                           const RankPtrs *w) {
     const uint32_t ng = (uint32_t)a.ngroups;
     uint32_t qb, grp;
     if (a.nxcd > 1) {
@@ -396,7 +472,20 @@ __global__ __launch_bounds__(kBlock) void bcast_kernel(RankPtrs bufs, BcastArgs 
     const int r1 = min(a.P, r0 + a.ranks_per_group);
     const uint64_t q0 = (uint64_t)qb * (uint64_t)a.tiles_per_group;
     for (int k = 0; k < a.tiles_per_group; ++k)
-        bcast_tile<E>(bufs, a, q0 + (uint64_t)k, r0, r1);
+        bcast_tile<E, kUpd>(bufs, a, q0 + (uint64_t)k, r0, r1, w, grp);
+}
+
+template <class E>
+__global__ __launch_bounds__(kBlock) void bcast_kernel(RankPtrs bufs, BcastArgs a) {
+    bcast_body<E, false>(bufs, a, nullptr);
+}
+
+// The broadcast of the LARS step's two-kernel form, with the update of the
+// weight replicas w.
+template <class E>
+__global__ __launch_bounds__(kBlock) void bcast_update_kernel(RankPtrs bufs, RankPtrs w,
+                                                              BcastArgs a) {
+    bcast_body<E, true>(bufs, a, &w);
 }
 
 // ---------------------------------------------------------------------------
@@ -459,7 +548,10 @@ template <class E, bool kGrouped, bool kNt, int kB>
 void launch_b(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a,
               const SgdArgs *sgd, bool home) {
     const dim3 block(kBlock);
-    if (home)
+    if (home && a.partial)
+        hipLaunchKernelGGL((fused_reduce_lars_kernel<E, kGrouped, kNt, kB>), grid, block, 0, s,
+                           bufs, a);
+    else if (home)
         hipLaunchKernelGGL((fused_reduce_kernel<E, kGrouped, kNt, kB>), grid, block, 0, s, bufs,
                            a);
     else if (sgd)
@@ -535,6 +627,44 @@ int launch_tiny(int dtype, const RankPtrs &bufs, const TinyArgs &a, void *stream
         hipLaunchKernelGGL((tiny_kernel<F32>), grid, block, 0, s, bufs, a);
     else
         hipLaunchKernelGGL((tiny_kernel<F16>), grid, block, 0, s, bufs, a);
+    return (int)hipGetLastError();
+}
+
+namespace {
+
+// Grid of a broadcast launch, or 0 with *bad set when it cannot be launched.
+uint64_t bcast_blocks(int dtype, const BcastArgs &a, bool *bad) {
+    const uint64_t tile = fused_tile_elems(dtype == DDL_F32 ? 4 : 2);
+    const uint64_t tiles = a.spans ? (uint64_t)(a.tile_end - a.tile_base)
+                                   : tile_count(a.len, tile_shift(a.off, tile, true), tile);
+    *bad = a.ngroups < 1 || a.ranks_per_group < 1 || a.tiles_per_group < 1;
+    if (*bad)
+        return 0;
+    const uint64_t qblocks = (tiles + (uint64_t)a.tiles_per_group - 1) / (uint64_t)a.tiles_per_group;
+    const uint64_t blocks =
+        a.nxcd > 1 ? (qblocks + (uint64_t)a.nxcd - 1) / (uint64_t)a.nxcd * (uint64_t)a.nxcd *
+                         (uint64_t)a.ngroups
+                   : qblocks * (uint64_t)a.ngroups;
+    *bad = blocks * kBlock > 0xffffffffull;
+    return *bad ? 0 : blocks;
+}
+
+}  // namespace
+
+int launch_bcast_update(int dtype, const RankPtrs &bufs, const RankPtrs &w, const BcastArgs &a,
+                        void *stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    bool bad = false;
+    const uint64_t blocks = bcast_blocks(dtype, a, &bad);
+    if (bad || !a.spans || !a.rate || a.nweights < 1)
+        return (int)hipErrorInvalidValue;
+    if (blocks == 0)
+        return (int)hipSuccess;
+    const dim3 grid((uint32_t)blocks), block(kBlock);
+    if (dtype == DDL_F32)
+        hipLaunchKernelGGL((bcast_update_kernel<F32>), grid, block, 0, s, bufs, w, a);
+    else
+        hipLaunchKernelGGL((bcast_update_kernel<F16>), grid, block, 0, s, bufs, w, a);
     return (int)hipGetLastError();
 }
 

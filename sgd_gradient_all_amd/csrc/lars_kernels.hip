@@ -87,30 +87,6 @@ __device__ __forceinline__ TileRange tile_range(const LarsArgs &a, uint32_t t) {
     return r;
 }
 
-// Sum over the workgroup of one binary64 value per lane: a butterfly within
-// each wave64, then the waves' sums in wave order.  The result is in lane 0
-// of wave 0.
-__device__ __forceinline__ double block_sum(double v, double *lds) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        v += __shfl_xor(v, o, 64);
-    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
-    if (lane == 0)
-        lds[wave] = v;
-    __syncthreads();
-    double s = 0.0;
-    if (threadIdx.x == 0)
-        for (int i = 0; i < kBlock / 64; ++i)
-            s += lds[i];
-    return s;
-}
-
-template <class W>
-__device__ __forceinline__ void add_squares(W x, double &acc) {
-#pragma unroll
-    for (int i = 0; i < (int)(sizeof(W) / sizeof(float)); ++i)
-        acc += (double)x[i] * (double)x[i];
-}
 
 // ---------------------------------------------------------------------------
 // norms: workgroup b sums the squares of tile tile_base + b

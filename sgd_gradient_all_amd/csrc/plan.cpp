@@ -76,7 +76,9 @@ struct Part {
     DevSpan *d_bk_spans = nullptr;
     uint32_t *d_bk_prefix = nullptr;
     uint32_t *d_bk_of_tile = nullptr;
-    double *d_lars_partial = nullptr;  // LARS: two sums per bucket-table tile
+    uint32_t *d_bk_span_tiles = nullptr;  // [b] first fused tile of bucket b, nb+1
+    double *d_lars_partial = nullptr;  // LARS: two sums per tile (bucket-table
+                                       // tiles, or fused tiles in the two-kernel form)
     float *d_lars_rate = nullptr;      // LARS: one rate per bucket
     void *d_sgd_home = nullptr;        // SGD without kept gradients, two-kernel
                                        // form: the reduced values (n elements)
@@ -167,6 +169,7 @@ void release_device(ddl_plan p) {
         (void)hipFree(pt.d_bk_spans);
         (void)hipFree(pt.d_bk_prefix);
         (void)hipFree(pt.d_bk_of_tile);
+        (void)hipFree(pt.d_bk_span_tiles);
         (void)hipFree(pt.d_lars_partial);
         (void)hipFree(pt.d_lars_rate);
         (void)hipFree(pt.d_sgd_home);
@@ -250,6 +253,11 @@ int bind_device(ddl_plan p, int dev) {
             (rc = upload(&pt.d_bk_prefix, s.bk_prefix.data(), s.bk_prefix.size())) ||
             (rc = upload(&pt.d_bk_of_tile, s.bk_of_tile.data(), s.bk_of_tile.size())))
             return rc;
+        std::vector<uint32_t> bst(s.buckets.size() + 1, 0);
+        for (size_t b = 0; b <= s.buckets.size(); ++b)
+            bst[b] = s.span_prefix[s.span_at[b]];
+        if ((rc = upload(&pt.d_bk_span_tiles, bst.data(), bst.size())))
+            return rc;
     }
     return DDL_OK;
 }
@@ -284,18 +292,20 @@ int fused_passes(ddl_plan p, const Schedule &s, uint64_t elems) {
     return s.P >= 16 && (uint64_t)s.P * elems * (uint64_t)s.esz >= min_bytes ? 2 : 1;
 }
 
-// Form of a stepwise group of `elems` elements per rank: one launch per
-// schedule step (1), or one persistent launch whose workgroups each walk
-// every step of one tile (2).  Automatic: persistent for groups of at most
-// kPersistentMaxBytes per rank, where the 2 (P - 1) launches' dispatch
-// dominates.  The SGD step rides on the per-step launches.
-constexpr uint64_t kPersistentMaxBytes = 8ull << 20;
-int step_form(ddl_plan p, const Schedule &s, uint64_t elems, bool sgd) {
+// Form of a stepwise group: one launch per schedule step (1), or one
+// persistent launch whose workgroups each walk every step of one tile (2).
+// Automatic: persistent, which measured faster on every workload on MI355X
+// (ms per all-reduce, per-step launches against persistent: 40 ranks x 300M
+// in 64 event-gated buckets 43.5 / 25.5; 8 ranks x 300M 6.93 / 3.97;
+// ResNet-50 over 16 ranks and 4 rings 1.47 / 0.74; the binary16 4x4 torus
+// 0.66 / 0.43; 4 ranks x 2^20 0.024 / 0.011): a tile's intermediate values
+// are re-read while they are still in the caches, and a group costs one
+// dispatch instead of 2 (P - 1).  The SGD step rides on the per-step
+// launches.
+int step_form(ddl_plan p, const Schedule &, uint64_t, bool sgd) {
     if (sgd)
         return 1;
-    if (p->step_form)
-        return p->step_form;
-    return elems * (uint64_t)s.esz <= kPersistentMaxBytes ? 2 : 1;
+    return p->step_form ? p->step_form : 2;
 }
 
 // Side streams event-gated groups alternate over.  Automatic: two for
@@ -355,6 +365,7 @@ struct Launcher {
     Part *pt = nullptr;  // the element type of the current group
     std::vector<Bucket> runs;
     bool prof = false;   // bracket the launches of the current group
+    bool lars_done = false;  // the group's LARS step rode on its fused pass
 
     int bracket_begin(int kind) {
         if (!prof)
@@ -490,6 +501,16 @@ struct Launcher {
         // plan's scratch buffer, and the gradient buffers stay as they were
         const bool scratch = two && sgd && !sgd->keep_grads;
         a.home = scratch ? pt->d_sgd_home : bufs.p[0];
+        // the LARS step in the two-kernel form: the reduce kernel also sums
+        // the squares of each tile, a rate kernel turns the sums into the
+        // buckets' rates, and the broadcast steps the replicas
+        const bool fused_lars = two && lars;
+        a.partial = nullptr;
+        a.w0 = nullptr;
+        if (fused_lars) {
+            a.partial = lars->partial ? lars->partial : pt->d_lars_partial;
+            a.w0 = static_cast<const float *>(lars->w.p[0]);
+        }
         for (uint32_t t = pre[lo]; t < pre[hi]; t += kMaxTilesPerLaunch) {
             const uint32_t tiles = std::min(kMaxTilesPerLaunch, pre[hi] - t);
             a.tile_base = t;
@@ -505,10 +526,59 @@ struct Launcher {
         }
         if (!two)
             return DDL_OK;
+        if (fused_lars)
+            return lars_pass_tail(b0, b1, a.partial);
         int rc = scratch ? DDL_OK : broadcast(b0, b1);
         if (rc || !sgd)
             return rc;
         return update(b0, b1, a.home, nullptr, sgd->lr, sgd->w, sgd->nweights);
+    }
+
+    // after the LARS reduce kernel of buckets [b0, b1): the rates from the
+    // fused tiles' partial sums, then the broadcast that steps the replicas
+    int lars_pass_tail(int b0, int b1, double *partial) {
+        const Schedule &s = pt->s;
+        LarsArgs la = update_args(b0, b1, bufs.p[0], lars->rate ? lars->rate : pt->d_lars_rate,
+                                  lars->lr, lars->nweights);
+        la.prefix = pt->d_bk_span_tiles;   // the buckets' fused-tile ranges
+        la.partial = partial;
+        la.rate_out = lars->rates_out;
+        la.coeff = lars->coeff;
+        la.eps = lars->eps;
+        int rc = bracket_begin(DDL_K_LARS_RATE);
+        if (rc)
+            return rc;
+        if (launch_lars(s.dtype, DDL_K_LARS_RATE, lars->w, la, (uint32_t)(b1 - b0), stream) !=
+            hipSuccess)
+            return DDL_E_HIP;
+        if ((rc = bracket_end()))
+            return rc;
+        BcastArgs bc;
+        std::memset(&bc, 0, sizeof(bc));
+        bc.P = s.P;
+        bc.ranks_per_group = bcast_ranks_per_group(s.P);
+        bc.ngroups = (s.P - 1 + bc.ranks_per_group - 1) / bc.ranks_per_group;
+        bc.tiles_per_group = 1;
+        bc.nxcd = 1;
+        bc.spans = pt->d_bk_spans;
+        bc.prefix = pt->d_bk_prefix;
+        bc.tile_span = pt->d_bk_of_tile;
+        bc.rate = la.rate;
+        bc.nweights = lars->nweights;
+        const uint32_t *bp = s.bk_prefix.data();
+        const uint32_t max_tiles = 0xffffffu / (uint32_t)bc.ngroups;
+        for (uint32_t t = bp[b0]; t < bp[b1]; t += max_tiles) {
+            bc.tile_base = t;
+            bc.tile_end = std::min(bp[b1], t + max_tiles);
+            if ((rc = bracket_begin(DDL_K_BROADCAST)))
+                return rc;
+            if (launch_bcast_update(s.dtype, bufs, lars->w, bc, stream) != hipSuccess)
+                return DDL_E_HIP;
+            if ((rc = bracket_end()))
+                return rc;
+        }
+        lars_done = true;
+        return DDL_OK;
     }
 
     // the broadcast of buckets [b0, b1) from rank 0 to ranks 1..P-1
@@ -652,6 +722,7 @@ struct Launcher {
     int group(int b0, int b1) {
         const Schedule &s = pt->s;
         int rc = DDL_OK;
+        lars_done = false;
         if (p->mode == DDL_FUSED || (sgd && s.P == 1)) {
             rc = fused(b0, b1);
         } else {
@@ -664,7 +735,7 @@ struct Launcher {
                 for (int st = 0; st < s.nsteps && !rc; ++st)
                     rc = step(st, s.item_at[st][b0], s.item_at[st][b1]);
         }
-        if (rc || !lars)
+        if (rc || !lars || lars_done)
             return rc;
         return lars_step(b0, b1);
     }
@@ -682,12 +753,20 @@ int ensure_sgd_home(ddl_plan p) {
     return DDL_OK;
 }
 
+// Tiles whose partial sums the LARS step keeps: the bucket table's (the norm
+// kernel's) or the fused tables' (the two-kernel form's reduce kernel).
+size_t lars_tiles(const Schedule &s) {
+    const size_t bk = s.bk_prefix.empty() ? 0 : s.bk_prefix.back();
+    const size_t sp = s.span_prefix.empty() ? 0 : s.span_prefix.back();
+    return std::max(bk, sp);
+}
+
 // Device memory of the LARS step, allocated by a plan's first LARS call.
 int ensure_lars(ddl_plan p) {
     for (Part &pt : p->parts) {
         if (pt.d_lars_partial)
             continue;
-        const size_t tiles = std::max<size_t>(1, pt.s.bk_prefix.empty() ? 0 : pt.s.bk_prefix.back());
+        const size_t tiles = std::max<size_t>(1, lars_tiles(pt.s));
         const size_t nb = std::max<size_t>(1, pt.s.buckets.size());
         if (hipMalloc((void **)&pt.d_lars_partial, 2 * tiles * sizeof(double)) != hipSuccess)
             return DDL_E_NOMEM;
@@ -1288,7 +1367,7 @@ int execute_lars(ddl_plan plan, void *const *bufs, void *const *weights, int nwe
         if (scratch) {
             // sizes first (host-only), then the binding and the device
             const Schedule &s = r->parts[0].s;
-            const size_t tiles = s.bk_prefix.empty() ? 0 : s.bk_prefix.back();
+            const size_t tiles = lars_tiles(s);
             if (2 * tiles * sizeof(double) > kLarsScratchPartialBytes ||
                 s.buckets.size() * sizeof(float) > kLarsScratchBytes - kLarsScratchPartialBytes)
                 return DDL_E_SCRATCH;

@@ -440,8 +440,8 @@ def test_profiling_counts_launches():
     bufs = [torch.ones(w.n, device="cuda") for _ in range(w.P)]
     for mode, launches in (("fused1", {"fused": 1}),
                            ("fused2", {"fused_reduce": 1, "broadcast": 1}),
-                           ("stepwise", {"reduce": 15, "gather": 15}),
-                           ("step2", {"walk": 1})):
+                           ("step1", {"reduce": 15, "gather": 15}),
+                           ("stepwise", {"walk": 1})):
         plan = make_plan(w, mode, "sum")
         plan.set_profiling(True)
         plan.execute(bufs)

@@ -76,6 +76,7 @@ def test_knob_setting_is_bitwise(knob, value, expected):
         g, ref = expected[w.name]
         bufs = [torch.from_numpy(x).cuda() for x in g]
         plan = ddl.Plan(w.P, w.n, w.dtype, w.op, ddl_topo(w), w.bucket_list(), "stepwise")
+        plan.set_step_form(1)   # the per-step kernels' tiles
         plan.execute(bufs)
         torch.cuda.synchronize()
         plan.destroy()

@@ -73,7 +73,7 @@ CASES = [
 
 
 @pytest.mark.parametrize("case", range(len(CASES)))
-@pytest.mark.parametrize("mode", ["fused1", "fused2", "stepwise"])
+@pytest.mark.parametrize("mode", ["fused1", "fused2", "step1", "step2"])
 @pytest.mark.parametrize("gated", [False, True])
 def test_typed_buckets_bitwise(case, mode, gated):
     P, tk, nb, mx = CASES[case]
@@ -87,8 +87,10 @@ def test_typed_buckets_bitwise(case, mode, gated):
     for d, h in zip(dev, host):
         d[:nbytes].copy_(torch.from_numpy(h))
     plan = ddl.Plan.typed(P, nbytes, "mean", ddl.topo(**tk), segs,
-                          "stepwise" if mode == "stepwise" else "fused")
-    if mode != "stepwise":
+                          "stepwise" if mode.startswith("step") else "fused")
+    if mode.startswith("step"):
+        plan.set_step_form(int(mode[-1]))
+    else:
         plan.set_fused_passes(1 if mode == "fused1" else 2)
     stream = torch.cuda.current_stream()
     events = None
@@ -137,7 +139,7 @@ def _paired_events(segs, stream):
     return [evs[b // 2] for b in range(len(segs))]
 
 
-@pytest.mark.parametrize("mode", ["fused1", "fused2", "stepwise"])
+@pytest.mark.parametrize("mode", ["fused1", "fused2", "step1", "step2"])
 def test_typed_mixed_groups_on_side_streams(mode):
     """Groups that hold both element types: the smaller type's pass runs on
     the plan's part stream beside the larger one's; every byte checked."""
@@ -150,8 +152,10 @@ def test_typed_mixed_groups_on_side_streams(mode):
     for d, h in zip(dev, host):
         d[:nbytes].copy_(torch.from_numpy(h))
     plan = ddl.Plan.typed(P, nbytes, "mean", ddl.topo(**tk), segs,
-                          "stepwise" if mode == "stepwise" else "fused")
-    if mode != "stepwise":
+                          "stepwise" if mode.startswith("step") else "fused")
+    if mode.startswith("step"):
+        plan.set_step_form(int(mode[-1]))
+    else:
         plan.set_fused_passes(1 if mode == "fused1" else 2)
     stream = torch.cuda.current_stream()
     plan.execute(dev, events=_paired_events(segs, stream), stream=stream)
@@ -161,7 +165,7 @@ def test_typed_mixed_groups_on_side_streams(mode):
         assert dev[r][:nbytes].cpu().numpy().tobytes() == want[r].tobytes(), (mode, r)
 
 
-@pytest.mark.parametrize("mode", ["fused2", "stepwise"])
+@pytest.mark.parametrize("mode", ["fused2", "step1", "step2"])
 @pytest.mark.parametrize("gated", [False, True])
 def test_typed_graph_capture_and_replay(mode, gated):
     """A typed plan's execution captured into a HIP graph (the element-type
@@ -178,8 +182,10 @@ def test_typed_graph_capture_and_replay(mode, gated):
         d[:nbytes].copy_(torch.from_numpy(h))
     dev = [t.clone() for t in src]
     plan = ddl.Plan.typed(P, nbytes, "mean", ddl.topo(**tk), segs,
-                          "stepwise" if mode == "stepwise" else "fused")
-    if mode != "stepwise":
+                          "stepwise" if mode.startswith("step") else "fused")
+    if mode.startswith("step"):
+        plan.set_step_form(int(mode[-1]))
+    else:
         plan.set_fused_passes(2)
     plan.execute(dev, stream=torch.cuda.current_stream())   # binds the plan
     torch.cuda.synchronize()
