@@ -72,7 +72,7 @@ def measured_traffic(workload, mode, passes):
 TRACE_FILES = {"fused2": ("fused_pass", ("fused_reduce_kernel", "bcast_kernel")),
                "fused1": ("fused_kernel", ("fused_kernel",)),
                "walk": ("walk_kernel", ("walk_kernel",)),
-               "steps": ("step_kernel", ("step_kernel",))}
+               "steps": ("step_kernel", ("reduce_step_kernel", "gather_step_kernel"))}
 
 
 def committed_trace(form, workload, bytes_per_unit):
@@ -89,7 +89,11 @@ def committed_trace(form, workload, bytes_per_unit):
     ks = rec.get("kernels", {})
     if not all(n in ks for n in names):
         return None
+    # a pass of the two-kernel form is one launch of each; a step-by-step
+    # unit is a launch of either kind, reduce and gather launches alternating
     avg_us = sum(ks[n]["avg_us"] for n in names)
+    if form == "steps":
+        avg_us /= len(names)
     achieved = bytes_per_unit / (avg_us * 1e-6) / 1e9
     return {"file": os.path.relpath(path.replace("_trace.json", ".md"), ROOT),
             "avg_unit_us": round(avg_us, 2),
@@ -192,6 +196,9 @@ def main():
     ap.add_argument("--step-form", type=int, default=0, choices=[0, 1, 2],
                     help="stepwise mode: 0 the plan's choice, 1 one launch per schedule "
                          "step, 2 the persistent step kernel")
+    ap.add_argument("--side-streams", type=int, default=0, choices=[0, 1, 2, 3, 4],
+                    help="side streams the headline plan's event-gated groups alternate over "
+                         "(0: the plan's choice)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip every side measurement (--legs)")
     ap.add_argument("--legs", default=",".join(LEGS),
@@ -202,6 +209,9 @@ def main():
     ap.add_argument("--prof-stride", type=int, default=8,
                     help="the roofline's HIP events bracket the launches of every m-th "
                          "bucket group of the timed steps (default 8)")
+    ap.add_argument("--tune", action="append", default=[], metavar="KNOB=VALUE",
+                    help="set a library tuning knob (ddl_set_tuning) before the run, "
+                         "e.g. bcast_xcd=8; repeatable")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run one plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -224,18 +234,15 @@ def main():
     import synth
     from synth.workloads import WORKLOADS
 
+    for kv in args.tune:
+        knob, _, val = kv.partition("=")
+        ddl.set_tuning(knob, int(val))
     w = WORKLOADS[args.workload]
     tdt = torch.float32 if w.dtype == "f32" else torch.float16
     sdt = synth.F32 if w.dtype == "f32" else synth.F16
     torch.cuda.set_device(0)
     dev_name = torch.cuda.get_device_name(0)
     log(f"bench: {w.name} ({w.description}) on {dev_name}, mode={args.mode}")
-    # the other workloads first, each on its own fresh buffers in a device
-    # that holds nothing else yet (the rate of a pass depends on the physical
-    # pages behind its buffers, and those of a later allocation land among
-    # the headline's 48 GB)
-    configs = (configs_leg(w, torch.cuda.current_stream(), torch, ddl, synth)
-               if "configs" in args.legs else None)
 
     # inputs, generated in HBM
     bufs = [torch.empty(w.n, dtype=tdt, device="cuda") for _ in range(w.P)]
@@ -275,6 +282,7 @@ def main():
         plan.set_step_form(args.step_form)
     if args.coalesce_bytes:
         plan.set_coalesce_bytes(args.coalesce_bytes)
+    plan.set_side_streams(args.side_streams)
     passes = plan.fused_passes()
     _, hbm_bytes = plan.traffic()
     evs = make_events()
@@ -342,8 +350,6 @@ def main():
         result["calib_copy_bytes"] = 2 * nel * 4
         del a, b
 
-    if configs is not None:
-        result["configs"] = configs
     if args.legs:
         result.update(extras(args, w, bufs, topo, buckets, main_stream, torch, ddl, synth,
                              hbm_bytes, ms))
@@ -356,6 +362,11 @@ def main():
 
 def extras(args, w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_bytes, fused_ms):
     out = {}
+    # the other workloads first, on fresh buffers, before the large legs
+    # below have churned HBM (the rate of a pass depends somewhat on the
+    # physical pages behind its buffers)
+    if "configs" in args.legs:
+        out["configs"] = configs_leg(w, main_stream, torch, ddl, synth)
     if "stepwise" in args.legs:
         out["stepwise"] = stepwise_leg(w, bufs, topo, buckets, main_stream, torch, ddl,
                                        fused_bytes)
@@ -383,7 +394,10 @@ def configs_leg(head, main_stream, torch, ddl, synth, allocations=3):
     4-rank 2^20 case fits the caches, so its figure is not an HBM one).  Each
     workload runs on `allocations` successive fresh allocations of its
     buffers (the rate depends somewhat on the physical pages behind them);
-    the reported figure is their median, every allocation's is listed."""
+    the reported figure is their median, every allocation's is listed.  On
+    the first allocation the stepwise mode is timed too, in both forms (the
+    persistent step kernel, and one launch per schedule step), over the
+    schedule's step bytes."""
     from synth.workloads import WORKLOADS
     out = {}
     for name, w in WORKLOADS.items():
@@ -421,6 +435,19 @@ def configs_leg(head, main_stream, torch, ddl, synth, allocations=3):
             runs.append(run(reps))
             passes = plan.fused_passes()
             plan.destroy()
+            if len(runs) == 1:
+                # the stepwise mode on the first allocation, in both forms
+                stepwise = {}
+                for form, label in ((2, "persistent"), (1, "per_step_launches")):
+                    plan = ddl.Plan(w.P, w.n, w.dtype, w.op,
+                                    ddl.topo(w.topo, w.k, w.rows, w.cols), buckets, "stepwise")
+                    plan.set_step_form(form)
+                    _, sbytes = plan.traffic()
+                    run(1)
+                    sms = run(max(3, reps // 5))
+                    stepwise[label] = {"ms": round(sms, 4),
+                                       "step_bytes_GBps": round(sbytes / (sms * 1e-3) / 1e9, 1)}
+                    plan.destroy()
             del bufs
             torch.cuda.empty_cache()
         ms = sorted(runs)[len(runs) // 2]
@@ -429,7 +456,7 @@ def configs_leg(head, main_stream, torch, ddl, synth, allocations=3):
                      "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
                      "ms_per_allocation": [round(x, 4) for x in runs],
                      "fused_passes": passes, "bytes": nbytes,
-                     "cache_resident": nbytes < (256 << 20)}
+                     "cache_resident": nbytes < (256 << 20), "stepwise": stepwise}
     log(f"bench: configs {out}")
     return out
 

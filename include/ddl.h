@@ -402,8 +402,10 @@ typedef enum {
      * form): weight replicas each workgroup steps (default 2); 0 = all of
      * them in one workgroup */
     DDL_TUNE_UPDATE_REPS = 8,
-    /* update kernel: replicas whose loads each lane issues before their
-     * stores (1, 2, 4 or 8; default 4) */
+    /* update kernel, and the broadcast that updates the replicas in the
+     * LARS step's two-kernel form: replicas whose loads each lane issues
+     * before their stores (1, 2, 4 or 8; default 4; the broadcast takes 8
+     * as 4) */
     DDL_TUNE_UPDATE_BATCH = 9,
     DDL_TUNE_COUNT = 10
 } ddl_tune_knob;

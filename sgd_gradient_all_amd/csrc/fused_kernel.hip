@@ -362,7 +362,7 @@ void fused_reduce_lars_kernel(RankPtrs bufs, FusedArgs a) {
 // tile_base) to ranks r0 .. r1.  kUpd (table mode, the LARS step): with the
 // reduced values in hand, also step the weight replicas of rank group grp
 // (see BcastArgs) by the tile's bucket's rate.
-template <class E, bool kUpd>
+template <class E, bool kUpd, int kRB = 1>
 __device__ __forceinline__ void bcast_tile(const RankPtrs &bufs, const BcastArgs &a, uint64_t q,
                                            int r0, int r1, const RankPtrs *w, uint32_t grp) {
     using T = typename E::T;
@@ -412,15 +412,35 @@ __device__ __forceinline__ void bcast_tile(const RankPtrs &bufs, const BcastArgs
 #pragma unroll
                 for (int u = 0; u < U; ++u)
                     st_stream<V>(static_cast<T *>(bufs.p[r]) + e + u * kStride, v[u]);
-            if (kUpd)
-                for (int k = rep0 ? -1 : 0; k < w1 - w0; ++k) {
-                    float *wr = static_cast<float *>(w->p[k < 0 ? 0 : w0 + k]) + e;
+            if (kUpd) {
+                // replicas in batches of kRB: every load of a batch is issued
+                // before its stores (a wave keeps kRB requests in flight)
+                const int nrep = (rep0 ? 1 : 0) + (w1 - w0);
+                for (int j0 = 0; j0 < nrep; j0 += kRB) {
+                    Wv x[kRB][U];
 #pragma unroll
-                    for (int u = 0; u < U; ++u)
-                        st_stream<Wv>(wr + u * kStride,
-                                      sgd_step<Wv>(ld_stream<Wv, true>(wr + u * kStride),
-                                                   E::widen(v[u]), rate));
+                    for (int k = 0; k < kRB; ++k)
+                        if (j0 + k < nrep) {
+                            const int j = j0 + k;
+                            const int r = rep0 ? (j == 0 ? 0 : w0 + j - 1) : w0 + j;
+                            const float *wr = static_cast<const float *>(w->p[r]) + e;
+#pragma unroll
+                            for (int u = 0; u < U; ++u)
+                                x[k][u] = ld_stream<Wv, true>(wr + u * kStride);
+                        }
+#pragma unroll
+                    for (int k = 0; k < kRB; ++k)
+                        if (j0 + k < nrep) {
+                            const int j = j0 + k;
+                            const int r = rep0 ? (j == 0 ? 0 : w0 + j - 1) : w0 + j;
+                            float *wr = static_cast<float *>(w->p[r]) + e;
+#pragma unroll
+                            for (int u = 0; u < U; ++u)
+                                st_stream<Wv>(wr + u * kStride,
+                                              sgd_step<Wv>(x[k][u], E::widen(v[u]), rate));
+                        }
                 }
+            }
         } else {
             for (uint32_t k = tid; k < nvec; k += kBlock) {
                 const uint64_t e = base + (uint64_t)k * E::N;
@@ -455,7 +475,7 @@ __device__ __forceinline__ void bcast_tile(const RankPtrs &bufs, const BcastArgs
 // dealt so that all rank groups of a tile block run on one accelerator die
 // (workgroup b runs on die b % nxcd), which then fetches the block's values
 // into its L2 once instead of once per die.
-template <class E, bool kUpd>
+template <class E, bool kUpd, int kRB = 1>
 __device__ __forceinline__ void bcast_body(const RankPtrs &bufs, const BcastArgs &a,
                                            const RankPtrs *w) {
     const uint32_t ng = (uint32_t)a.ngroups;
@@ -472,7 +492,7 @@ __device__ __forceinline__ void bcast_body(const RankPtrs &bufs, const BcastArgs
     const int r1 = min(a.P, r0 + a.ranks_per_group);
     const uint64_t q0 = (uint64_t)qb * (uint64_t)a.tiles_per_group;
     for (int k = 0; k < a.tiles_per_group; ++k)
-        bcast_tile<E, kUpd>(bufs, a, q0 + (uint64_t)k, r0, r1, w, grp);
+        bcast_tile<E, kUpd, kRB>(bufs, a, q0 + (uint64_t)k, r0, r1, w, grp);
 }
 
 template <class E>
@@ -481,11 +501,12 @@ __global__ __launch_bounds__(kBlock) void bcast_kernel(RankPtrs bufs, BcastArgs 
 }
 
 // The broadcast of the LARS step's two-kernel form, with the update of the
-// weight replicas w.
-template <class E>
+// weight replicas w, kRB replicas' loads ahead of their stores (knob
+// DDL_TUNE_UPDATE_BATCH, as the update kernel).
+template <class E, int kRB>
 __global__ __launch_bounds__(kBlock) void bcast_update_kernel(RankPtrs bufs, RankPtrs w,
                                                               BcastArgs a) {
-    bcast_body<E, true>(bufs, a, &w);
+    bcast_body<E, true, kRB>(bufs, a, &w);
 }
 
 // ---------------------------------------------------------------------------
@@ -661,10 +682,22 @@ int launch_bcast_update(int dtype, const RankPtrs &bufs, const RankPtrs &w, cons
     if (blocks == 0)
         return (int)hipSuccess;
     const dim3 grid((uint32_t)blocks), block(kBlock);
-    if (dtype == DDL_F32)
-        hipLaunchKernelGGL((bcast_update_kernel<F32>), grid, block, 0, s, bufs, w, a);
-    else
-        hipLaunchKernelGGL((bcast_update_kernel<F16>), grid, block, 0, s, bufs, w, a);
+    const int batch = tuning(DDL_TUNE_UPDATE_BATCH);
+    if (dtype == DDL_F32) {
+        if (batch <= 1)
+            hipLaunchKernelGGL((bcast_update_kernel<F32, 1>), grid, block, 0, s, bufs, w, a);
+        else if (batch == 2)
+            hipLaunchKernelGGL((bcast_update_kernel<F32, 2>), grid, block, 0, s, bufs, w, a);
+        else
+            hipLaunchKernelGGL((bcast_update_kernel<F32, 4>), grid, block, 0, s, bufs, w, a);
+    } else {
+        if (batch <= 1)
+            hipLaunchKernelGGL((bcast_update_kernel<F16, 1>), grid, block, 0, s, bufs, w, a);
+        else if (batch == 2)
+            hipLaunchKernelGGL((bcast_update_kernel<F16, 2>), grid, block, 0, s, bufs, w, a);
+        else
+            hipLaunchKernelGGL((bcast_update_kernel<F16, 4>), grid, block, 0, s, bufs, w, a);
+    }
     return (int)hipGetLastError();
 }
 

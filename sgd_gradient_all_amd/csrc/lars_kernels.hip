@@ -11,8 +11,12 @@
 // the SGD step w - rate * y.
 //
 // A layer's rate needs the whole layer reduced first, so the step cannot
-// ride in the all-reduce's epilogue as plain SGD does.  Per bucket group,
-// after its all-reduce, three launches over the buckets' anchored tiles:
+// ride in the all-reduce's epilogue as plain SGD does.  In the fused pass's
+// two-kernel form the norms ride in the reduce kernel (each workgroup sums
+// the squares of its tile of y and w_0) and the update in the broadcast
+// (fused_kernel.hip), with lars_rate_kernel between them over the fused
+// tiles' partial sums.  Otherwise, per bucket group, after its all-reduce,
+// three launches over the buckets' anchored tiles:
 //  - lars_norm_kernel: one workgroup per tile sums w_0[e]^2 and y[e]^2 in
 //    binary64 (each square of a binary32 value is exact there) and writes
 //    the two partial sums of the tile;
@@ -152,8 +156,26 @@ __global__ __launch_bounds__(kBlock) void lars_rate_kernel(LarsArgs a) {
     __shared__ double lds[2][kBlock / 64];
     const uint32_t i = a.bucket_lo + blockIdx.x;
     const uint32_t t0 = a.prefix[i], t1 = a.prefix[i + 1];
+    // each lane adds tiles t0 + lane, t0 + lane + kBlock, ... in that order;
+    // kU of them are loaded ahead of their adds (a bucket of the 300M-element
+    // workload has ~4600 tiles: one round of loads per kU instead of per tile)
+    constexpr uint32_t kU = 8;
     double sw = 0.0, sy = 0.0;
-    for (uint32_t t = t0 + threadIdx.x; t < t1; t += kBlock) {
+    uint32_t t = t0 + threadIdx.x;
+    for (; t + (kU - 1) * kBlock < t1; t += kU * kBlock) {
+        double pw[kU], py[kU];
+#pragma unroll
+        for (uint32_t u = 0; u < kU; ++u) {
+            pw[u] = a.partial[2 * (uint64_t)(t + u * kBlock)];
+            py[u] = a.partial[2 * (uint64_t)(t + u * kBlock) + 1];
+        }
+#pragma unroll
+        for (uint32_t u = 0; u < kU; ++u) {
+            sw += pw[u];
+            sy += py[u];
+        }
+    }
+    for (; t < t1; t += kBlock) {
         sw += a.partial[2 * (uint64_t)t];
         sy += a.partial[2 * (uint64_t)t + 1];
     }

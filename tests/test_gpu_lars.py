@@ -157,10 +157,13 @@ def restore_knobs():
                          [("update_batch", b) for b in (1, 2, 8)], ids=lambda v: str(v))
 def test_lars_knobs(knob, value, restore_knobs):
     # the update's replica split and load batch change launch shapes only
+    # (in the one-kernel form the update kernel reads them, in the two-kernel
+    # form the broadcast that steps the replicas reads the load batch)
     ddl.set_tuning(knob, value)
     for w in (CASES[2], CASES[5]):
-        say(f"case lars knob {knob}={value} {w.name}")
-        run_case(w, "fused", 0, False)
+        for passes in (1, 2):
+            say(f"case lars knob {knob}={value} {w.name} passes={passes}")
+            run_case(w, "fused", passes, False)
 
 
 def test_lars_page_constants_closed_form():
