@@ -28,7 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "achieved HBM GB/s and % of peak per all-reduce (300M fp32, P=40 ring)"
-LEGS = ("configs", "stepwise", "latency", "overlap", "sgd", "lars", "typed", "per_gpu_step")
+LEGS = ("configs", "ceilings", "stepwise", "latency", "overlap", "sgd", "lars", "typed", "per_gpu_step")
 PEAK_HBM_GBPS = 8000.0
 # committed counter summaries: one file per form of the fused pass
 TRAFFIC_FILES = {1: ("fused_kernel", "hbm_bytes_per_launch"),
@@ -348,6 +348,16 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         result["calib_copy_bytes"] = 2 * nel * 4
+        # the in-tree streams of known bytes: nel floats read, then written,
+        # then copied (read and written)
+        sink = torch.zeros(256, dtype=torch.float32, device="cuda")
+        cs = main_stream.cuda_stream
+        synth.stream_read(a.data_ptr(), nel, sink.data_ptr(), cs)
+        synth.stream_write(b.data_ptr(), nel, 2.0, cs)
+        synth.stream_copy(a.data_ptr(), b.data_ptr(), nel, cs)
+        torch.cuda.synchronize()
+        result["calib_stream_bytes"] = nel * 4
+        del sink
         del a, b
 
     if args.legs:
@@ -367,6 +377,15 @@ def extras(args, w, bufs, topo, buckets, main_stream, torch, ddl, synth, fused_b
     # physical pages behind its buffers)
     if "configs" in args.legs:
         out["configs"] = configs_leg(w, main_stream, torch, ddl, synth)
+    if "ceilings" in args.legs:
+        out["hbm_ceilings"] = ceilings_leg(main_stream, torch, synth)
+        copy = out["hbm_ceilings"]["copy"]["GBps"]
+        # each pass moves as many bytes in as out, as a copy does
+        rel = {w.name: round(fused_bytes / (fused_ms * 1e-3) / 1e9 / copy, 3)}
+        for name, row in out.get("configs", {}).items():
+            if not row["cache_resident"]:
+                rel[name] = round(row["hbm_GBps"] / copy, 3)
+        out["hbm_ceilings"]["fused_pass_over_copy"] = rel
     if "stepwise" in args.legs:
         out["stepwise"] = stepwise_leg(w, bufs, topo, buckets, main_stream, torch, ddl,
                                        fused_bytes)
@@ -458,6 +477,44 @@ def configs_leg(head, main_stream, torch, ddl, synth, allocations=3):
                      "fused_passes": passes, "bytes": nbytes,
                      "cache_resident": nbytes < (256 << 20), "stepwise": stepwise}
     log(f"bench: configs {out}")
+    return out
+
+
+def ceilings_leg(main_stream, torch, synth, nbytes=1_200_000_000, reps=7):
+    """The rates plain streams reach on this device (in-tree kernels of
+    known bytes, non-temporal 16-byte accesses, one 8 KB tile per
+    workgroup): a copy of nbytes (nbytes read and nbytes written), a read
+    and a write.  The fused pass reads and writes the same number of bytes,
+    as a copy does, so the copy's rate is the one to hold it against."""
+    n = nbytes // 4
+    a = torch.empty(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    sink = torch.zeros(256, dtype=torch.float32, device="cuda")
+    cs = main_stream.cuda_stream
+    synth.stream_write(a.data_ptr(), n, 1.0, cs)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, moved):
+        fn()
+        times = []
+        for _ in range(reps):
+            t0.record(main_stream)
+            fn()
+            t1.record(main_stream)
+            torch.cuda.synchronize()
+            times.append(t0.elapsed_time(t1))
+        ms = sorted(times)[reps // 2]
+        gbps = moved / (ms * 1e-3) / 1e9
+        return {"ms": round(ms, 4), "GBps": round(gbps, 1),
+                "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+
+    out = {"bytes_per_stream": n * 4,
+           "copy": timed(lambda: synth.stream_copy(a.data_ptr(), b.data_ptr(), n, cs), 8 * n),
+           "read": timed(lambda: synth.stream_read(a.data_ptr(), n, sink.data_ptr(), cs), 4 * n),
+           "write": timed(lambda: synth.stream_write(b.data_ptr(), n, 2.0, cs), 4 * n)}
+    del a, b, sink
+    torch.cuda.empty_cache()
+    log(f"bench: ceilings {out}")
     return out
 
 

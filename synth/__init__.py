@@ -3,8 +3,9 @@
 Definitions of the values are in synth.h.  Host generation is synth.c
 (libsynth_host.so, gcc); device generation is synth_fill.hip
 (libsynth_dev.so, hipcc), which also holds the streaming compute kernel the
-overlap measurement runs beside the all-reduce.  Neither holds any of the
-all-reduce's arithmetic.
+overlap measurement runs beside the all-reduce and plain streams of known
+bytes (copy, read, write) for counter calibration and the rate a plain
+stream reaches.  Neither holds any of the all-reduce's arithmetic.
 """
 import ctypes
 import os
@@ -83,6 +84,12 @@ def dev_lib():
         L.synth_fill_device.restype = i32
         L.synth_stream_compute.argtypes = [vp, u64, f32, f32, vp]
         L.synth_stream_compute.restype = i32
+        L.synth_stream_copy.argtypes = [vp, vp, u64, vp]
+        L.synth_stream_copy.restype = i32
+        L.synth_stream_read.argtypes = [vp, u64, vp, vp]
+        L.synth_stream_read.restype = i32
+        L.synth_stream_write.argtypes = [vp, u64, f32, vp]
+        L.synth_stream_write.restype = i32
         _dev = L
     return _dev
 
@@ -121,3 +128,25 @@ def stream_compute(ptr, n, alpha, beta, stream=0):
     rc = dev_lib().synth_stream_compute(ptr, n, alpha, beta, stream)
     if rc != 0:
         raise RuntimeError(f"synth_stream_compute failed ({rc})")
+
+
+def stream_copy(src, dst, n, stream=0):
+    """dst = src over n fp32 elements, non-temporal (a stream of known bytes)."""
+    rc = dev_lib().synth_stream_copy(src, dst, n, stream)
+    if rc != 0:
+        raise RuntimeError(f"synth_stream_copy failed ({rc})")
+
+
+def stream_read(src, n, sink, stream=0):
+    """Reads n fp32 elements (sink: 256 floats, written only in a case that
+    does not arise)."""
+    rc = dev_lib().synth_stream_read(src, n, sink, stream)
+    if rc != 0:
+        raise RuntimeError(f"synth_stream_read failed ({rc})")
+
+
+def stream_write(dst, n, value, stream=0):
+    """dst = value over n fp32 elements, non-temporal."""
+    rc = dev_lib().synth_stream_write(dst, n, value, stream)
+    if rc != 0:
+        raise RuntimeError(f"synth_stream_write failed ({rc})")

@@ -1,7 +1,10 @@
 // synth_fill.hip -- device side of the seeded synthetic gradients (the
 // definitions are in synth.h; synth.c is the host side and must produce the
-// same bits), and the streaming compute kernel the overlap measurement runs
-// beside the all-reduce.  None of the all-reduce's arithmetic is here.
+// same bits), the streaming compute kernel the overlap measurement runs
+// beside the all-reduce, and plain streaming kernels of known bytes (a copy,
+// a read, a write) that calibrate the memory counters and give the rate the
+// hardware reaches on a plain stream.  None of the all-reduce's arithmetic
+// is here.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -69,6 +72,68 @@ __global__ void stream_compute(float *a, uint64_t n, float alpha, float beta) {
         a[i] = a[i] * alpha + beta;
 }
 
+// Plain streams of known bytes: every workgroup moves tiles of 2 x 256
+// 16-byte vectors with non-temporal accesses (each byte touched once); the
+// elements past the last whole tile go one per lane.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr uint64_t kStreamTile = 2 * 256;  // vectors per tile
+
+__global__ __launch_bounds__(256) void stream_copy(const float *src, float *dst, uint64_t n) {
+    const f32x4 *s = reinterpret_cast<const f32x4 *>(src);
+    f32x4 *d = reinterpret_cast<f32x4 *>(dst);
+    const uint64_t tiles = n / 4 / kStreamTile;
+    for (uint64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+        const uint64_t i = t * kStreamTile + threadIdx.x;
+        const f32x4 a = __builtin_nontemporal_load(s + i);
+        const f32x4 b = __builtin_nontemporal_load(s + i + 256);
+        __builtin_nontemporal_store(a, d + i);
+        __builtin_nontemporal_store(b, d + i + 256);
+    }
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t i = tiles * kStreamTile * 4 + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+         i < n; i += stride)
+        dst[i] = src[i];
+}
+
+// Reads n floats; a lane writes its sum to sink[lane] only if it equals a
+// value no input here produces (so the loads cannot be dropped).
+__global__ __launch_bounds__(256) void stream_read(const float *src, uint64_t n, float *sink) {
+    const f32x4 *s = reinterpret_cast<const f32x4 *>(src);
+    const uint64_t tiles = n / 4 / kStreamTile;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (uint64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+        const uint64_t i = t * kStreamTile + threadIdx.x;
+        acc += __builtin_nontemporal_load(s + i);
+        acc += __builtin_nontemporal_load(s + i + 256);
+    }
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t i = tiles * kStreamTile * 4 + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+         i < n; i += stride)
+        acc.x += src[i];
+    if (acc.x + acc.y + acc.z + acc.w == -0x1.fffffep127f)
+        sink[threadIdx.x] = acc.x;
+}
+
+__global__ __launch_bounds__(256) void stream_write(float *dst, uint64_t n, float value) {
+    f32x4 *d = reinterpret_cast<f32x4 *>(dst);
+    const f32x4 v = {value, value, value, value};
+    const uint64_t tiles = n / 4 / kStreamTile;
+    for (uint64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+        const uint64_t i = t * kStreamTile + threadIdx.x;
+        __builtin_nontemporal_store(v, d + i);
+        __builtin_nontemporal_store(v, d + i + 256);
+    }
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t i = tiles * kStreamTile * 4 + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+         i < n; i += stride)
+        dst[i] = value;
+}
+
+unsigned stream_grid(uint64_t n) {
+    const uint64_t tiles = n / 4 / kStreamTile;
+    return (unsigned)(tiles < 1 ? 1 : tiles < (1u << 20) ? tiles : (1u << 20));
+}
+
 }  // namespace
 
 extern "C" {
@@ -106,6 +171,41 @@ int synth_stream_compute(void *a, uint64_t n, float alpha, float beta, void *str
     hipLaunchKernelGGL(stream_compute, dim3(blocks), dim3(256), 0,
                        static_cast<hipStream_t>(stream), static_cast<float *>(a), n, alpha,
                        beta);
+    return (int)hipGetLastError();
+}
+
+// The plain streams (n floats, pointers 16-byte aligned): dst = src, a read
+// of src (sink: 256 floats the kernel writes only in a case that does not
+// arise), and dst = value.  Return a hipError_t.
+int synth_stream_copy(const void *src, void *dst, uint64_t n, void *stream) {
+    if (n == 0)
+        return 0;
+    if (!src || !dst || (((uintptr_t)src | (uintptr_t)dst) & 15))
+        return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(stream_copy, dim3(stream_grid(n)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const float *>(src),
+                       static_cast<float *>(dst), n);
+    return (int)hipGetLastError();
+}
+
+int synth_stream_read(const void *src, uint64_t n, void *sink, void *stream) {
+    if (n == 0)
+        return 0;
+    if (!src || !sink || ((uintptr_t)src & 15))
+        return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(stream_read, dim3(stream_grid(n)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const float *>(src), n,
+                       static_cast<float *>(sink));
+    return (int)hipGetLastError();
+}
+
+int synth_stream_write(void *dst, uint64_t n, float value, void *stream) {
+    if (n == 0)
+        return 0;
+    if (!dst || ((uintptr_t)dst & 15))
+        return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(stream_write, dim3(stream_grid(n)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<float *>(dst), n, value);
     return (int)hipGetLastError();
 }
 
