@@ -623,7 +623,11 @@ def latency_leg(main_stream, torch, ddl, synth, calls=4):
       - eager_ms: back-to-back eager calls, event records included (host-
         bound when the host is slower than the device);
       - host_ms: the host time of the library call itself.
-    Against the same all-reduce with no events (one group)."""
+    Against the same all-reduce with no events (one group).  The
+    `..._group_events` variants record one event per group that
+    ddl_plan_event_groups reports (after the group's last tensor) and pass it
+    for each of the group's tensors: the same groups and launches, with one
+    record per group instead of one per tensor."""
     from synth.workloads import WORKLOADS
     w = WORKLOADS["multiring_k4_p16_resnet50"]
     bufs = [torch.empty(w.n, dtype=torch.float32, device="cuda") for _ in range(w.P)]
@@ -648,14 +652,17 @@ def latency_leg(main_stream, torch, ddl, synth, calls=4):
     torch.cuda.synchronize()
     hold_ms = t0.elapsed_time(t1) / 4
 
+    # the events recorded (in list order) and those passed, one per bucket
+    rec, passed = events, events
+
     def record_events(stream):
-        for e in events:
+        for e in rec:
             e.record(stream)
 
     def run(plan, gated):
         if gated:
             record_events(main_stream)
-        plan.execute(bufs, events=events if gated else None, stream=main_stream)
+        plan.execute(bufs, events=passed if gated else None, stream=main_stream)
 
     def measure(plan, gated, graph_too):
         run(plan, gated)
@@ -666,7 +673,7 @@ def latency_leg(main_stream, torch, ddl, synth, calls=4):
             if gated:
                 record_events(main_stream)
             h0 = time.perf_counter()
-            plan.execute(bufs, events=events if gated else None, stream=main_stream)
+            plan.execute(bufs, events=passed if gated else None, stream=main_stream)
             host.append(time.perf_counter() - h0)
         torch.cuda.synchronize()
         host_ms = sorted(host)[len(host) // 2] * 1e3
@@ -688,7 +695,7 @@ def latency_leg(main_stream, torch, ddl, synth, calls=4):
             if gated:
                 record_events(main_stream)
             tm.record(main_stream)
-            plan.execute(bufs, events=events if gated else None, stream=main_stream)
+            plan.execute(bufs, events=passed if gated else None, stream=main_stream)
             t1.record(main_stream)
             ahead = ahead and (time.perf_counter() - h0) * 1e3 < nhold * hold_ms
             torch.cuda.synchronize()
@@ -706,7 +713,7 @@ def latency_leg(main_stream, torch, ddl, synth, calls=4):
                 with torch.cuda.graph(graph, stream=cap):
                     if gated:
                         record_events(cap)
-                    plan.execute(bufs, events=events if gated else None, stream=cap)
+                    plan.execute(bufs, events=passed if gated else None, stream=cap)
             torch.cuda.synchronize()
             graph.replay()
             torch.cuda.synchronize()
@@ -725,10 +732,12 @@ def latency_leg(main_stream, torch, ddl, synth, calls=4):
     plan = ddl.Plan(w.P, w.n, w.dtype, w.op, topo, buckets, "fused")
     res["no_events_fused"] = measure(plan, False, True)
     plan.destroy()
-    variants = [("fused", 0, 0, False), ("fused", 0, 16, False), ("fused", 0, 16, True),
-                ("stepwise", 2, 0, False), ("stepwise", 2, 16, True),
-                ("stepwise", 1, 0, False), ("stepwise", 1, 16, True)]
-    for mode, form, thr_mb, ordered in variants:
+    variants = [("fused", 0, 0, False, False), ("fused", 0, 16, False, False),
+                ("fused", 0, 16, True, False), ("fused", 0, 16, True, True),
+                ("stepwise", 2, 0, False, False), ("stepwise", 2, 16, True, False),
+                ("stepwise", 2, 16, True, True),
+                ("stepwise", 1, 0, False, False), ("stepwise", 1, 16, True, False)]
+    for mode, form, thr_mb, ordered, grouped in variants:
         plan = ddl.Plan(w.P, w.n, w.dtype, w.op, topo, buckets, mode)
         if mode == "stepwise":
             plan.set_step_form(form)
@@ -736,22 +745,30 @@ def latency_leg(main_stream, torch, ddl, synth, calls=4):
         # the events are recorded in list order on one stream, as
         # back-propagation records them: the promise may be made
         plan.set_ordered_events(ordered)
+        if grouped:
+            last = plan.event_groups()
+            rec = [torch.cuda.Event() for _ in last]
+            passed = [rec[sum(1 for x in last if x < b)] for b in range(len(buckets))]
+        else:
+            rec, passed = events, events
         plan.set_profiling(1)
         run(plan, True)
         torch.cuda.synchronize()
         launches = sum(v[1] for v in plan.profile_read_kinds().values())
         plan.set_profiling(0)
         key = (f"{mode}{'' if mode == 'fused' else '_form%d' % form}_coalesce_{thr_mb}mb"
-               f"{'_ordered' if ordered else ''}")
+               f"{'_ordered' if ordered else ''}{'_group_events' if grouped else ''}")
         row = measure(plan, True, True)
         row["launches"] = launches
+        row["events_recorded"] = len(rec)
         res[key] = row
         # captured plans must outlive the graph, which is gone by now
         plan.destroy()
     base = res["no_events_fused"]
-    res["fused_per_tensor_events_over_no_events"] = {
+    res["fused_event_gated_over_no_events"] = {
         k: {m: round(res[k][m] / base[m], 3) for m in ("device_ms", "graph_ms")}
-        for k in ("fused_coalesce_0mb", "fused_coalesce_16mb", "fused_coalesce_16mb_ordered")}
+        for k in ("fused_coalesce_0mb", "fused_coalesce_16mb", "fused_coalesce_16mb_ordered",
+                  "fused_coalesce_16mb_ordered_group_events")}
     del bufs, gate
     torch.cuda.empty_cache()
     log(f"bench: latency {res}")

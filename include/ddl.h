@@ -308,6 +308,19 @@ const char *ddl_strerror(int code);
  * for all their events before it starts.  Default 0. */
 int ddl_plan_set_coalesce_bytes(ddl_plan plan, size_t bytes);
 
+/* The groups a call forms, at the current threshold, when every bucket has a
+ * ready event of its own: returns their number G (>= 1 for a plan with
+ * buckets; a negative DDL_E_* code on error) and writes to last[g], for
+ * g < min(G, cap), the list index of group g's last bucket (increasing; the
+ * last is nbuckets - 1).  A caller that records one ready event per group
+ * -- once the gradients of buckets last[g-1]+1 .. last[g] are complete --
+ * and passes it for each of those buckets gets the same groups and the same
+ * results, with one event record and one wait per group instead of one per
+ * bucket: each record costs the device a few microseconds, more than a
+ * small bucket's share of the pass.  last may be NULL with cap = 0 to count
+ * only; DDL_E_ARG for cap < 0 or a NULL last with cap > 0. */
+int ddl_plan_event_groups(ddl_plan plan, int *last, int cap);
+
 /* The caller's promise that it records the buckets' ready events in list
  * order on one stream -- as back-propagation produces the gradients, output
  * layer first (Baidu article, opening paragraphs) -- so that the completion

@@ -92,6 +92,7 @@ def lib():
             "ddl_plan_set_coalesce_bytes": ([vp, sz], i32),
             "ddl_plan_set_side_streams": ([vp, i32], i32),
             "ddl_plan_set_ordered_events": ([vp, i32], i32),
+            "ddl_plan_event_groups": ([vp, ctypes.POINTER(i32), i32], i32),
             "ddl_plan_set_fused_passes": ([vp, i32], i32),
             "ddl_set_tuning": ([i32, i32], i32),
             "ddl_get_tuning": ([i32, ctypes.POINTER(i32)], i32),
@@ -333,6 +334,18 @@ class Plan:
 
     def set_coalesce_bytes(self, nbytes):
         _check(lib().ddl_plan_set_coalesce_bytes(self.handle, nbytes), "set_coalesce_bytes")
+
+    def event_groups(self):
+        """List index of the last bucket of each group a call forms at the
+        current threshold when every bucket has its own ready event; one
+        event per group, shared by the group's buckets, gives the same
+        groups with one record and one wait per group."""
+        n = lib().ddl_plan_event_groups(self.handle, None, 0)
+        if n < 0:
+            _check(n, "ddl_plan_event_groups")
+        last = (ctypes.c_int * max(1, n))()
+        _check(min(0, lib().ddl_plan_event_groups(self.handle, last, n)), "ddl_plan_event_groups")
+        return list(last[:n])
 
     def set_ordered_events(self, ordered=True):
         """Promise that the ready events are recorded in bucket list order on

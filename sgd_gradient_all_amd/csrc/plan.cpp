@@ -795,6 +795,31 @@ hipEvent_t *last_event(ddl_plan p, hipStream_t ls, bool may_create = true) {
     return &p->last_ev.back().second;
 }
 
+// The end (one past the last bucket, in list order) of the group that
+// starts at bucket b0: consecutive buckets with equal ready events, then,
+// with a threshold, following buckets until the group holds coalesce_bytes
+// per rank.  ready == nullptr: every event is NULL (equal); distinct: every
+// bucket's event differs from the others' (the grouping a caller gets with
+// one event per bucket).
+int group_end(const ddl_plan_s *p, void *const *ready, int b0, bool distinct = false) {
+    const int nb = (int)p->order.size();
+    auto bucket_bytes = [&](int i) {
+        const Part &pt = p->parts[p->order[i].first];
+        return (size_t)pt.s.buckets[p->order[i].second].len * (size_t)pt.s.esz;
+    };
+    void *ev0 = ready ? ready[b0] : nullptr;
+    int b1 = b0 + 1;
+    size_t bytes = bucket_bytes(b0);
+    while (b1 < nb) {
+        const bool same = !distinct && (ready ? ready[b1] : nullptr) == ev0;
+        if (!same && !(p->coalesce_bytes && bytes < p->coalesce_bytes))
+            break;
+        bytes += bucket_bytes(b1);
+        ++b1;
+    }
+    return b1;
+}
+
 // noalloc: the allocation-free entry point -- the plan must be bound, the
 // LARS buffers come in through lars, no event is created and no launch is
 // bracketed for profiling.
@@ -873,28 +898,11 @@ int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stre
         return DDL_E_HIP;
 
     Launcher L{p, rp, ls, sgd, lars};
-    auto bucket_bytes = [&](int i) {
-        const Part &pt = p->parts[p->order[i].first];
-        return (size_t)pt.s.buckets[p->order[i].second].len * (size_t)pt.s.esz;
-    };
     int b0 = 0, g = 0, used = 0;
     std::vector<std::pair<int, int>> range(p->parts.size());
     while (b0 < nb) {
         L.prof = !noalloc && p->profiling && p->prof_group++ % (uint64_t)p->prof_stride == 0;
-        // the group: equal events, then (with a threshold) more buckets
-        // until it holds coalesce_bytes per rank
-        void *ev0 = ready ? ready[b0] : nullptr;
-        int b1 = b0 + 1;
-        size_t bytes = bucket_bytes(b0);
-        while (b1 < nb) {
-            void *ev = ready ? ready[b1] : nullptr;
-            if (ev == ev0 || (p->coalesce_bytes && bytes < p->coalesce_bytes)) {
-                bytes += bucket_bytes(b1);
-                ++b1;
-            } else {
-                break;
-            }
-        }
+        const int b1 = group_end(p, ready, b0);
         if (any_event) {
             // groups alternate over the side streams: independent buckets,
             // so one group's tail overlaps the next one's start
@@ -1517,6 +1525,25 @@ int ddl_plan_set_coalesce_bytes(ddl_plan plan, size_t bytes) {
         return r.rc;
     r->coalesce_bytes = bytes;
     return DDL_OK;
+}
+
+int ddl_plan_event_groups(ddl_plan plan, int *last, int cap) {
+    if (!plan)
+        return DDL_E_NULL;
+    if (cap < 0 || (cap > 0 && !last))
+        return DDL_E_ARG;
+    PlanRef r = acquire(plan);
+    if (r.rc)
+        return r.rc;
+    const int nb = (int)r->order.size();
+    int g = 0;
+    for (int b0 = 0; b0 < nb; ++g) {
+        const int b1 = group_end(r.sp.get(), nullptr, b0, true);
+        if (g < cap)
+            last[g] = b1 - 1;
+        b0 = b1;
+    }
+    return g;
 }
 
 int ddl_plan_set_ordered_events(ddl_plan plan, int ordered) {

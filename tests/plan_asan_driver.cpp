@@ -99,6 +99,92 @@ static void stale_handles() {
 // The one-shot cache makes room by destroying idle plans, but never one
 // whose execution was captured into a HIP graph: the graph's replays read
 // its tables.  ddl_cache_clear keeps those too.
+// ddl_plan_event_groups reports the groups that a call with one ready event
+// per bucket forms: one event per reported group, passed for each of its
+// buckets, gives the same launches with one wait per group.
+static void event_groups_match() {
+    std::mt19937_64 rng(777);
+    auto uni = [&](int lo, int hi) { return lo + (int)(rng() % (uint64_t)(hi - lo + 1)); };
+    const size_t thresholds[] = {0, 1, 4096, 65536, 1 << 20, (size_t)1 << 30};
+    for (int c = 0; c < 48; ++c) {
+        const int P = uni(2, 9), nb = uni(1, 24);
+        std::vector<ddl_bucket> bk(nb);
+        size_t n = 0;
+        for (int b = 0; b < nb; ++b) {
+            const size_t cnt = uni(0, 4) == 0 ? (size_t)uni(1, 40) : (size_t)uni(40, 50000);
+            bk[b] = {n, cnt, nullptr};
+            n += cnt;
+        }
+        std::shuffle(bk.begin(), bk.end(), rng);
+        ddl_topo topo = {DDL_RING, 1, 0, 0, nullptr};
+        const ddl_mode mode = c % 2 ? DDL_STEPWISE : DDL_FUSED;
+        ddl_plan plan = nullptr;
+        check(ddl_plan_create(&plan, P, n, DDL_F32, DDL_SUM, &topo, bk.data(), nb, mode),
+              "create");
+        const bool ordered = uni(0, 1);
+        check(ddl_plan_set_coalesce_bytes(plan, thresholds[c % 6]), "coalesce");
+        check(ddl_plan_set_ordered_events(plan, ordered), "ordered");
+        const int G = ddl_plan_event_groups(plan, nullptr, 0);
+        if (G < 1 || G > nb)
+            fail("event_groups count");
+        std::vector<int> last(G + 1, -5);
+        if (ddl_plan_event_groups(plan, last.data(), G) != G || last[G] != -5 ||
+            last[G - 1] != nb - 1)
+            fail("event_groups list");
+        for (int g = 1; g < G; ++g)
+            if (last[g] <= last[g - 1])
+                fail("event_groups not increasing");
+        if (thresholds[c % 6] == 0 && G != nb)
+            fail("event_groups without a threshold");
+        int first = -5;
+        if (ddl_plan_event_groups(plan, &first, 1) != G || first != last[0])
+            fail("event_groups with a short array");
+        if (ddl_plan_event_groups(plan, nullptr, 1) != DDL_E_ARG ||
+            ddl_plan_event_groups(plan, last.data(), -1) != DDL_E_ARG ||
+            ddl_plan_event_groups(nullptr, nullptr, 0) != DDL_E_NULL)
+            fail("event_groups argument checks");
+        std::vector<void *> bufs(P);
+        for (int r = 0; r < P; ++r)
+            bufs[r] = std::aligned_alloc(16, ((n * 4 + 15) / 16 + 1) * 16);
+        std::vector<hipEvent_t> ev(nb), gev(G);
+        std::vector<void *> own(nb), shared(nb);
+        for (int b = 0; b < nb; ++b) {
+            (void)hipEventCreate(&ev[b]);
+            own[b] = ev[b];
+            g_caller_events.insert(ev[b]);
+        }
+        for (int g = 0, b = 0; g < G; ++g) {
+            (void)hipEventCreate(&gev[g]);
+            g_caller_events.insert(gev[g]);
+            for (; b <= last[g]; ++b)
+                shared[b] = gev[g];
+        }
+        hipStream_t s;
+        (void)hipStreamCreateWithFlags(&s, 0);
+        g_caller_waits = 0;
+        long l0 = g_launches;
+        check(ddl_plan_execute(plan, bufs.data(), own.data(), s, nullptr), "execute own");
+        const long w_own = g_caller_waits, l_own = g_launches - l0;
+        g_caller_waits = 0;
+        l0 = g_launches;
+        check(ddl_plan_execute(plan, bufs.data(), shared.data(), s, nullptr), "execute shared");
+        const long w_shared = g_caller_waits, l_shared = g_launches - l0;
+        if (l_own != l_shared)
+            fail("group events change the launches");
+        if (w_shared != G || w_own != (ordered ? G : nb))
+            fail("waits on the caller's events");
+        check(ddl_plan_destroy(plan), "destroy");
+        for (int b = 0; b < nb; ++b)
+            (void)hipEventDestroy(ev[b]);
+        for (int g = 0; g < G; ++g)
+            (void)hipEventDestroy(gev[g]);
+        g_caller_events.clear();
+        (void)hipStreamDestroy(s);
+        for (int r = 0; r < P; ++r)
+            std::free(bufs[r]);
+    }
+}
+
 static void captured_plans_stay_cached() {
     ddl_topo ring = {DDL_RING, 1, 0, 0, nullptr};
     const size_t n = 10000;
@@ -291,6 +377,7 @@ int main(int argc, char **argv) {
     }
     check(ddl_cache_clear(), "cache clear");
     stale_handles();
+    event_groups_match();
     if (g_live_allocs || g_live_streams || g_live_events)
         std::printf("FAILED: leaked %ld allocations, %ld streams, %ld events\n", g_live_allocs,
                     g_live_streams, g_live_events),

@@ -628,6 +628,70 @@ def test_ordered_events_gate_each_group_on_its_last_event(mode):
         assert bitwise_equal(out[r], ref[r]), (mode, r)
 
 
+@pytest.mark.parametrize("mode", ["fused1", "fused2", "step1", "step2"])
+@pytest.mark.parametrize("ordered", [False, True])
+def test_one_event_per_reported_group(mode, ordered):
+    """The caller records one ready event per group that event_groups
+    reports -- after the last gradient of the group is written, as
+    back-propagation would -- and passes it for each of the group's buckets:
+    every element matches the oracle, and the plan makes the same launches
+    as with one event per bucket (a group that started before its last
+    gradient was written would read the zeros the buffers held before)."""
+    say(f"case group events {mode} ordered={ordered}")
+    rng = np.random.default_rng(37)
+    sizes = [int(x) for x in rng.choice([8, 64, 1000, 4096, 30_000, 120_000], 40)]
+    offs = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(int).tolist()
+    bl = list(zip(offs, sizes))[::-1]
+    w = Workload("groups", 8, sum(sizes), "f32", "mean", "ring", dist="normal", sigma=1e-2,
+                 seed=37, buckets=bl)
+    g = host_inputs(w)
+    ref = [x.copy() for x in g]
+    oracle_full(w, ref)
+    src = to_device(g)
+    bufs = [torch.zeros_like(x) for x in src]
+    stream = torch.cuda.current_stream()
+    plan = make_plan(w, mode)
+    plan.set_ordered_events(ordered)
+    plan.set_coalesce_bytes(256 << 10)
+    last = plan.event_groups()
+    assert last[-1] == len(bl) - 1 and all(a < b for a, b in zip(last, last[1:]))
+    assert 1 < len(last) < len(bl)
+    plan.execute(bufs, stream=stream)   # binds the plan (its first call allocates)
+    torch.cuda.synchronize()
+    launches = {}
+    for kind in ("own", "group"):
+        for b in bufs:
+            b.zero_()
+        hold = torch.zeros(1 << 27, device="cuda")
+        for _ in range(6):
+            synth.stream_compute(hold.data_ptr(), hold.numel(), 1.0, 0.0, stream.cuda_stream)
+        events, gi = [], 0
+        for i, (off, cnt) in enumerate(bl):
+            for r in range(w.P):
+                bufs[r][off:off + cnt].copy_(src[r][off:off + cnt])
+            if kind == "own" or i == last[gi]:
+                e = torch.cuda.Event()
+                e.record(stream)
+                events.append(e)
+                gi += i == last[gi]
+        if kind == "group":
+            # each bucket gets its group's event
+            per, gi = [], 0
+            for i in range(len(bl)):
+                per.append(events[gi])
+                gi += i == last[gi]
+            events = per
+        plan.set_profiling(1)
+        plan.execute(bufs, events=events, stream=stream)
+        out = to_host(bufs)
+        launches[kind] = sum(v[1] for v in plan.profile_read_kinds().values())
+        plan.set_profiling(0)
+        for r in range(w.P):
+            assert bitwise_equal(out[r], ref[r]), (mode, kind, r)
+    plan.destroy()
+    assert launches["own"] == launches["group"], launches
+
+
 @pytest.mark.parametrize("mode", ["stepwise", "fused2"])
 def test_caller_stream_waits_for_side_stream_work(mode):
     """Work enqueued on the caller's stream right after an event-gated
