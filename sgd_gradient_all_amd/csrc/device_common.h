@@ -11,7 +11,8 @@
 //  - mean: one correctly rounded binary32 division by P (binary16: of the
 //    value widened to binary32, then rounded to binary16), fused into the
 //    store of the add that completes the sum (Baidu Ring-Allreduce article,
-//    "总结": gradients are averaged).
+//    "总结": gradients are averaged).  Binary16 takes the cheaper
+//    quotient_by_rank below, which rounds to the same binary16 value.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -35,6 +36,25 @@ __device__ __forceinline__ f32x8 opaque(f32x8 v) {
 __device__ __forceinline__ float opaque1(float v) {
     asm volatile("" : "+v"(v));
     return v;
+}
+
+// x / d rounded to binary16 as RN16(RN32(x / d)) does, for x a binary16
+// value widened to binary32 and d a rank count in [1, 128], with r =
+// RN32(1 / d): q = RN32(x r) is within 2^-23 of x / d (relative), and
+// e = x - q d is exact (x and q d are multiples of ulp(q), |e| <= 1.5 d
+// ulps), so c = RN32(q + e r) is x / d up to 2^-47 (relative).  x / d is
+// either a binary16 midpoint -- then c equals it exactly and both round the
+// tie the same way -- or at least 2^-18 (relative; 2^-32 absolute among the
+// subnormals) away from every midpoint, so that c, q's error far smaller,
+// rounds to the same binary16 value as x / d, and x / d as RN32(x / d).
+// e = 0 (x exact in q, +-0 included: c would lose the sign of -0) and
+// non-finite x (e is NaN) keep q.  Every binary16 x at every d is checked
+// against numpy's binary32 division on the device.
+__device__ __forceinline__ float quotient_by_rank(float x, float d, float r) {
+    const float q = x * r;
+    const float e = __builtin_fmaf(-q, d, x);
+    const float c = __builtin_fmaf(e, r, q);
+    return (e != 0.0f && e == e) ? c : q;
 }
 
 // E::W is the binary32 vector of the N elements of one E::V (the weights
@@ -62,11 +82,17 @@ struct F16 {
         return __builtin_convertvector(s, f16x8);
     }
     __device__ static V div(V a, float d) {
-        f32x8 q = opaque(__builtin_convertvector(a, f32x8) / d);
-        return __builtin_convertvector(q, f16x8);
+        const float r = 1.0f / d;
+        f32x8 x = __builtin_convertvector(a, f32x8), q;
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            q[i] = quotient_by_rank(x[i], d, r);
+        return __builtin_convertvector(opaque(q), f16x8);
     }
     __device__ static T add1(T a, T b) { return (T)((float)a + (float)b); }
-    __device__ static T div1(T a, float d) { return (T)opaque1((float)a / d); }
+    __device__ static T div1(T a, float d) {
+        return (T)opaque1(quotient_by_rank((float)a, d, 1.0f / d));
+    }
 };
 
 // The SGD step w - lr * y in binary32: the product is rounded before the

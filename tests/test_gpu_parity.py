@@ -933,3 +933,38 @@ def test_graph_capture_with_bucket_events_and_side_streams(mode):
     del graph
     torch.cuda.synchronize()
     plan.destroy()
+
+
+F16_MEAN_P = [2, 3, 5, 6, 7, 9, 11, 13, 16, 24, 40, 63, 100, 127, 128]
+
+
+@pytest.mark.parametrize("mode", ["fused1", "fused2", "step1", "step2"])
+def test_f16_mean_of_every_value(mode):
+    """The binary16 mean (Sony article, "训练设置": binary16 gradients;
+    Baidu article, "总结": averaged) of every binary16 value.  Rank 0 holds
+    all 65536 bit patterns and the other ranks zeros, so each element's sum
+    is the value itself (+0 for -0, which meets a +0), and its mean must be
+    the binary32 quotient by P correctly rounded, then rounded to binary16:
+    numpy's division in binary32 gives it.  The one-kernel form runs every P
+    from 1 to 128, the other forms a spread of P."""
+    x = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    ps = range(1, 129) if mode == "fused1" else F16_MEAN_P
+    say(f"case binary16 mean of every value {mode}")
+    for P in ps:
+        w = Workload("f16mean", P, x.size, "f16", "mean", "ring", dist="normal", sigma=1.0,
+                     seed=1)
+        bufs = [torch.from_numpy(x.copy()).cuda()] + [
+            torch.zeros(x.size, dtype=torch.float16, device="cuda") for _ in range(P - 1)]
+        plan = make_plan(w, mode)
+        plan.execute(bufs)
+        out = to_host(bufs)
+        plan.destroy()
+        s = x.copy()
+        if P > 1:
+            s[s.view(np.uint16) == 0x8000] = 0
+        want = (s.astype(np.float32) / np.float32(P)).astype(np.float16)
+        for r in (0, P - 1):
+            if not bitwise_equal(out[r], want):
+                bad = np.flatnonzero(out[r].view(np.uint16) != want.view(np.uint16))
+                raise AssertionError(f"{mode} P={P} rank {r}: {bad.size} values differ, "
+                                     f"first x bits {int(x.view(np.uint16)[bad[0]]):#06x}")
