@@ -218,7 +218,7 @@ int ddl_plan_execute_sgd(ddl_plan plan, void *const *bufs, void *const *weights,
  * order, so a rate can differ from an index-order evaluation when lr * trust
  * lies within about 1e-13 (relative) of a binary32 rounding boundary.  The
  * first call allocates 16 bytes per tile of the plan's buckets (a tile is
- * 1024 binary32 or 4096 binary16 elements) plus 4 per bucket, once.
+ * 4 KB: 1024 binary32 or 2048 binary16 elements) plus 4 per bucket, once.
  * The partial sums and rates are the plan's: two LARS calls on one plan that
  * may run at the same time on the device (different streams, no ordering
  * event) race; order them.
@@ -233,9 +233,9 @@ int ddl_plan_execute_lars(ddl_plan plan, void *const *bufs, void *const *weights
  * that forbid hipMalloc): the same all-reduce and the same LARS arithmetic,
  * bit for bit, but the per-tile partial sums and per-bucket rates live in
  * a fixed scratch array the library holds on every device it runs on
- * (8 MiB of partial sums, 16 bytes per tile of 1024 binary32 or 4096 binary16
- * elements -- at most 536,870,912 binary32 elements in one bucket -- and
- * 256 KiB of rates, at most 65,536 buckets), instead of the buffers
+ * (8 MiB of partial sums, 16 bytes per 4 KB tile -- at most 524,288 tiles
+ * over the plan's buckets, 536,870,912 binary32 elements in whole tiles --
+ * and 256 KiB of rates, at most 65,536 buckets), instead of the buffers
  * ddl_plan_execute_lars allocates on its first call.  This call makes no
  * device allocation and creates no HIP stream or event: the plan must
  * already have run on the current device (any execute entry point binds it;
@@ -392,8 +392,9 @@ typedef enum {
     /* two-kernel form: 1 = the reduce kernel's loads are non-temporal
      * (default), 0 = cached */
     DDL_TUNE_REDUCE_NT_LOAD = 1,
-    /* one-kernel form: loads are non-temporal while P x vectors per lane is
-     * at most this (default 24) */
+    /* one-kernel form: loads are non-temporal while P x the elements a lane
+     * loads per rank is at most 4 x this (default 24: up to 24 binary32
+     * ranks, 12 binary16 ranks) */
     DDL_TUNE_FUSED_NT_LOAD_MAX_P = 2,
     /* tile anchoring of the plans created afterwards: 0 = automatic (tables
      * whose ranges average at least 2 tiles), 1 = never, 2 = always */

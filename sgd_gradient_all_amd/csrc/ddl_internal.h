@@ -21,13 +21,16 @@ constexpr int kVecBytes = 16;
 #define DDL_FUSED_VPL_F32 1
 #endif
 #ifndef DDL_FUSED_VPL_F16
-#define DDL_FUSED_VPL_F16 2
+#define DDL_FUSED_VPL_F16 1
 #endif
 #ifndef DDL_FUSED_TPW
 #define DDL_FUSED_TPW 1
 #endif
-// Fused pass, vectors per lane per tile: one dwordx4 of binary32, two of
-// binary16 (measured best for the 40-rank fp32 and 16-rank fp16 passes).
+// Fused pass, vectors per lane per tile: one dwordx4 of either type.
+// Measured on MI355X (paired, three rounds), binary16 with one against two:
+// 16-rank torus fused -2%, persistent stepwise -6%; 8-rank ring one kernel
+// -4.5%; mixed-precision ResNet-50 stepwise -8.6%.  Binary32 with two or
+// four: -3%, -8% at 40 ranks.
 constexpr int fused_vecs_per_lane(int esz) {
     return esz == 4 ? DDL_FUSED_VPL_F32 : DDL_FUSED_VPL_F16;
 }
@@ -213,7 +216,8 @@ struct LarsArgs {
 
 // The allocation-free LARS entry point keeps its partial sums and rates in
 // a fixed per-device scratch of this size: up to 512Ki tiles of partial sums
-// (8 MiB, 536,870,912 binary32 elements in one bucket) after which the rates
+// over the plan's buckets (8 MiB; 536,870,912 binary32 elements in whole
+// tiles) after which the rates
 // start at a 256-byte boundary, up to 64Ki buckets (256 KiB).
 constexpr size_t kLarsScratchPartialBytes = 8u << 20;
 constexpr size_t kLarsScratchBytes = kLarsScratchPartialBytes + (256u << 10);

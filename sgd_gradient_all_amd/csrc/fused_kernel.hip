@@ -28,10 +28,11 @@ using namespace dev;
 
 // Streaming accesses.  Every element is touched once per pass, so the
 // results are written with non-temporal stores.  In the one-kernel form,
-// loads are non-temporal when P times the vectors per lane is at most 24
-// (knob DDL_TUNE_FUSED_NT_LOAD_MAX_P).  Measured on MI355X: +7..+15% for
-// binary32 at 8 and 16 ranks and binary16 at 8, -4% for binary32 at 40
-// ranks, -9..-14% for binary16 at 16.
+// loads are non-temporal when P times the elements a lane loads per rank is
+// at most 4 x 24 (knob DDL_TUNE_FUSED_NT_LOAD_MAX_P): up to 24 binary32
+// ranks, 12 binary16 ranks.  Measured on MI355X: +7..+15% for binary32 at 8
+// and 16 ranks and binary16 at 8, -4% for binary32 at 40 ranks; binary16 at
+// 12-16 ranks either way by size (-7..+10%).
 #ifndef DDL_NT_STORE
 #define DDL_NT_STORE 1
 #endif
@@ -608,8 +609,8 @@ void launch_e(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a
             launch_nt<E, kGrouped, false>(grid, s, bufs, a, nullptr, true, batch);
         return;
     }
-    const bool nt = a.P * fused_vecs_per_lane(sizeof(typename E::T)) <=
-                    tuning(DDL_TUNE_FUSED_NT_LOAD_MAX_P);
+    constexpr int kLaneElems = fused_vecs_per_lane(sizeof(typename E::T)) * E::N;
+    const bool nt = a.P * kLaneElems <= 4 * tuning(DDL_TUNE_FUSED_NT_LOAD_MAX_P);
     const int batch = tuning(DDL_TUNE_FUSED_BATCH);
     if (nt)
         launch_nt<E, kGrouped, true>(grid, s, bufs, a, sgd, false, batch);
