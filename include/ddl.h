@@ -186,8 +186,8 @@ int ddl_plan_execute(ddl_plan plan, void *const *bufs, void *const *ready_events
  *              never written, saving P writes per element.
  * In DDL_FUSED plans the update rides in the one-kernel pass's epilogue, or
  * follows the two-kernel pass (ddl_plan_set_fused_passes).  In DDL_STEPWISE
- * plans the owner of each chunk updates at the add that completes the sum and
- * every other rank when the all-gather delivers it.
+ * plans, in either step form, the owner of each chunk updates at the add that
+ * completes the sum and every other rank when the all-gather delivers it.
  * Other arguments and the asynchrony are those of ddl_plan_execute.  Calls
  * with keep_grads == 0 in the two-kernel form share the plan's scratch
  * buffer: two such calls on one plan that may run at the same time on the
@@ -372,8 +372,8 @@ int ddl_plan_get_fused_passes(ddl_plan plan, int *passes);
  * latency form for small buckets ("[论文解读] PowerAI DDL", ABSTRACT: the
  * latency/bandwidth trade-off): 2 (P-1) launches become one.
  * form = 0 (default): automatic, which is the persistent form (measured the
- * faster on every workload).  With the SGD step (ddl_plan_execute_sgd)
- * stepwise plans always launch per step.
+ * faster on every workload).  The SGD step (ddl_plan_execute_sgd) rides on
+ * either form.
  * DDL_E_ARG for other values; takes effect at the next execute.
  * ddl_plan_get_step_form reports the form of one group holding all the
  * plan's buckets, as in a call without ready events (0 for a fused plan). */

@@ -240,9 +240,10 @@ int launch_bcast_update(int dtype, const RankPtrs &bufs, const RankPtrs &w, cons
                         void *stream);
 int launch_tiny(int dtype, const RankPtrs &bufs, const TinyArgs &a, void *stream);
 // The persistent step kernel: tiles [a.tile_base, a.tile_base + tiles) of the
-// fused span table, every schedule step walked by the workgroup of a tile.
-int launch_walk(int dtype, const RankPtrs &bufs, const FusedArgs &a, uint32_t tiles,
-                void *stream);
+// fused span table, every schedule step walked by the workgroup of a tile
+// (with sgd, the SGD step of each rank where the reduced value reaches it).
+int launch_walk(int dtype, const RankPtrs &bufs, const FusedArgs &a, const SgdArgs *sgd,
+                uint32_t tiles, void *stream);
 // kind: DDL_K_LARS_NORM or DDL_K_UPDATE (blocks = tiles from
 // a.tile_base), DDL_K_LARS_RATE (blocks = buckets from a.bucket_lo).
 int launch_lars(int dtype, int kind, const RankPtrs &w, const LarsArgs &a, uint32_t blocks,

@@ -300,11 +300,8 @@ int fused_passes(ddl_plan p, const Schedule &s, uint64_t elems) {
 // ResNet-50 over 16 ranks and 4 rings 1.47 / 0.74; the binary16 4x4 torus
 // 0.66 / 0.43; 4 ranks x 2^20 0.024 / 0.011): a tile's intermediate values
 // are re-read while they are still in the caches, and a group costs one
-// dispatch instead of 2 (P - 1).  The SGD step rides on the per-step
-// launches.
-int step_form(ddl_plan p, const Schedule &, uint64_t, bool sgd) {
-    if (sgd)
-        return 1;
+// dispatch instead of 2 (P - 1).  The SGD step rides on either form.
+int step_form(ddl_plan p, const Schedule &, uint64_t) {
     return p->step_form ? p->step_form : 2;
 }
 
@@ -445,7 +442,7 @@ struct Launcher {
             int rc = bracket_begin(DDL_K_WALK);
             if (rc)
                 return rc;
-            if (launch_walk(s.dtype, bufs, a, tiles, stream) != hipSuccess)
+            if (launch_walk(s.dtype, bufs, a, sgd, tiles, stream) != hipSuccess)
                 return DDL_E_HIP;
             if ((rc = bracket_end()))
                 return rc;
@@ -729,7 +726,7 @@ struct Launcher {
             uint64_t elems = 0;
             for (int b = b0; b < b1; ++b)
                 elems += s.buckets[b].len;
-            if (s.nsteps > 0 && step_form(p, s, elems, sgd != nullptr) == 2)
+            if (s.nsteps > 0 && step_form(p, s, elems) == 2)
                 rc = walk(b0, b1);
             else
                 for (int st = 0; st < s.nsteps && !rc; ++st)
@@ -1702,7 +1699,7 @@ int ddl_plan_get_step_form(ddl_plan plan, int *form) {
     uint64_t all = 0;
     for (const Bucket &b : s.buckets)
         all += b.len;
-    *form = r->mode == DDL_STEPWISE ? step_form(r.get(), s, all, false) : 0;
+    *form = r->mode == DDL_STEPWISE ? step_form(r.get(), s, all) : 0;
     return DDL_OK;
 }
 

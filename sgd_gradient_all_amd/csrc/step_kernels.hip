@@ -4,6 +4,8 @@
 // schedule is race-free within a step, so all pairs run at once.  Each lane
 // moves dwordx4 vectors of one source and one destination chunk.  The
 // stores stay cached: the next step reads what this one wrote.
+#include <type_traits>
+
 #include "device_common.h"
 
 // global (address space 1) accesses from addresses kept in LDS
@@ -152,13 +154,49 @@ __device__ __forceinline__ void st_at(uint64_t addr, V v) {
     *reinterpret_cast<V DDL_STEP_GLOBAL *>(addr) = v;
 }
 
+// The SGD step riding on the walk (null for the plain all-reduce): weight
+// replica addresses in chain order (every entry replica 0 when one replica
+// is shared), the rate, and whether the replica is shared.
+struct WalkSgd {
+    const uint64_t *w;
+    float lr;
+    bool shared;
+};
+
 // The walk of U values of type X (vectors, or single elements with U = 1)
 // at byte offsets off + u * stride of every rank, rank addresses in chain
-// order in c[].
-template <class E, class X, int U>
+// order in c[].  With kSgd, each rank's weights (binary32, at element
+// offsets off / sizeof(T)) take their step where the reduced value reaches
+// the rank: chain entry P - 1 at the add that completes the sum, every other
+// entry when an all-gather copy delivers it (with one shared replica, entry
+// P - 1 alone) -- the ranks and values of the per-step launches.
+template <class E, class X, int U, bool kSgd = false>
 __device__ __forceinline__ void walk_body(const uint64_t *c, int P, int C, bool mean,
-                                          float divisor, uint64_t off, uint64_t stride) {
+                                          float divisor, uint64_t off, uint64_t stride,
+                                          const WalkSgd *sgd = nullptr) {
+    using T = typename E::T;
+    constexpr bool kVec = sizeof(X) == sizeof(typename E::V);
+    using Wx = typename std::conditional<kVec, typename E::W, float>::type;
     const int G = P / C;
+    // the weights of chain entry dst take their step with the values r
+    auto update = [&](int dst, const X (&r)[U]) {
+        if constexpr (kSgd) {
+            if (sgd->shared && dst != P - 1)
+                return;
+            const uint64_t wo = off / sizeof(T) * sizeof(float);
+            const uint64_t ws = stride / sizeof(T) * sizeof(float);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint64_t wa = sgd->w[dst] + wo + u * ws;
+                Wx y;
+                if constexpr (kVec)
+                    y = E::widen(r[u]);
+                else
+                    y = (float)r[u];
+                st_at<Wx>(wa, sgd_step<Wx>(ld_at<Wx>(wa), y, sgd->lr));
+            }
+        }
+    };
     auto add = [](X a, X b) {
         if constexpr (sizeof(X) == sizeof(typename E::V))
             return E::add(a, b);
@@ -171,8 +209,9 @@ __device__ __forceinline__ void walk_body(const uint64_t *c, int P, int C, bool 
         else
             return E::div1(a, d);
     };
-    // reduce: dst (+)= src, then / P when last
-    auto reduce = [&](int src, int dst, bool last) {
+    // reduce: dst (+)= src; the add that completes the sum (fin) also
+    // divides by P for the mean and takes the owner's SGD step
+    auto reduce = [&](int src, int dst, bool fin) {
         X s[U], d[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -181,11 +220,13 @@ __device__ __forceinline__ void walk_body(const uint64_t *c, int P, int C, bool 
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            X r = add(d[u], s[u]);
-            if (last)
-                r = div(r, divisor);
-            st_at<X>(c[dst] + off + u * stride, r);
+            d[u] = add(d[u], s[u]);
+            if (fin && mean)
+                d[u] = div(d[u], divisor);
+            st_at<X>(c[dst] + off + u * stride, d[u]);
         }
+        if (fin)
+            update(dst, d);
     };
     auto copy = [&](int src, int dst) {
         X s[U];
@@ -195,12 +236,13 @@ __device__ __forceinline__ void walk_body(const uint64_t *c, int P, int C, bool 
 #pragma unroll
         for (int u = 0; u < U; ++u)
             st_at<X>(c[dst] + off + u * stride, s[u]);
+        update(dst, s);
     };
     for (int g = 0; g < G; ++g)
         for (int t = 0; t + 1 < C; ++t)
-            reduce(g * C + t, g * C + t + 1, mean && G == 1 && t == C - 2);
+            reduce(g * C + t, g * C + t + 1, G == 1 && t == C - 2);
     for (int t = 0; t + 1 < G; ++t)
-        reduce(t * C + C - 1, (t + 1) * C + C - 1, mean && t == G - 2);
+        reduce(t * C + C - 1, (t + 1) * C + C - 1, t == G - 2);
     for (int t = 0; t + 1 < G; ++t)
         copy(((t + G - 1) % G) * C + C - 1, t * C + C - 1);
     for (int g = 0; g < G; ++g)
@@ -208,23 +250,32 @@ __device__ __forceinline__ void walk_body(const uint64_t *c, int P, int C, bool 
             copy(g * C + (t + C - 1) % C, g * C + t);
 }
 
-// Workgroup b walks tile tile_base + b of the fused span table.
-template <class E>
-__global__ __launch_bounds__(kBlock) void walk_kernel(RankPtrs bufs, FusedArgs a) {
+// Workgroup b walks tile tile_base + b of the fused span table (with kSgd,
+// taking the SGD step of g on the way).
+template <class E, bool kSgd>
+__device__ __forceinline__ void walk_tile(const RankPtrs &bufs, const FusedArgs &a,
+                                          const SgdArgs *g) {
     using T = typename E::T;
     using V = typename E::V;
     constexpr int U = fused_vecs_per_lane(sizeof(T));
     constexpr uint64_t kTile = fused_tile_elems(sizeof(T));
     constexpr uint64_t kStride = (uint64_t)kBlock * E::N * sizeof(T);
-    __shared__ uint64_t c[DDL_MAX_RANKS];  // rank addresses, chain order
+    __shared__ uint64_t c[DDL_MAX_RANKS];   // rank addresses, chain order
+    __shared__ uint64_t wc[kSgd ? DDL_MAX_RANKS : 1];  // their weight replicas
     const int P = a.P;
     const uint32_t tid = threadIdx.x;
     const uint32_t tile = a.tile_base + blockIdx.x;
     const uint32_t i = a.tile_span[tile];
     const DevSpan sp = a.spans[i];
-    for (int j = (int)tid; j < P; j += kBlock)
-        c[j] = reinterpret_cast<uint64_t>(bufs.p[a.chains[sp.chain_off + j]]);
+    for (int j = (int)tid; j < P; j += kBlock) {
+        const int r = a.chains[sp.chain_off + j];
+        c[j] = reinterpret_cast<uint64_t>(bufs.p[r]);
+        if (kSgd)
+            wc[j] = reinterpret_cast<uint64_t>(g->w.p[g->nweights == 1 ? 0 : r]);
+    }
     __syncthreads();
+    WalkSgd ws{wc, kSgd ? g->lr : 0.0f, kSgd && g->nweights == 1};
+    const WalkSgd *wsp = kSgd ? &ws : nullptr;
     const uint64_t j = tile - a.prefix[i];
     const uint64_t sh = tile_shift(sp.off, kTile, a.anchor);
     const uint64_t base = tile_lo(sp.off, sh, kTile, j);
@@ -234,17 +285,29 @@ __global__ __launch_bounds__(kBlock) void walk_kernel(RankPtrs bufs, FusedArgs a
     if (sp.flags & kItemAligned) {
         const uint32_t nvec = cnt / E::N;
         if (nvec == (uint32_t)(U * kBlock)) {
-            walk_body<E, V, U>(c, P, a.group, mean, a.divisor,
-                               (base + (uint64_t)tid * E::N) * sizeof(T), kStride);
+            walk_body<E, V, U, kSgd>(c, P, a.group, mean, a.divisor,
+                                     (base + (uint64_t)tid * E::N) * sizeof(T), kStride, wsp);
         } else {
             for (uint32_t v = tid; v < nvec; v += kBlock)
-                walk_body<E, V, 1>(c, P, a.group, mean, a.divisor,
-                                   (base + (uint64_t)v * E::N) * sizeof(T), 0);
+                walk_body<E, V, 1, kSgd>(c, P, a.group, mean, a.divisor,
+                                         (base + (uint64_t)v * E::N) * sizeof(T), 0, wsp);
         }
         done = nvec * E::N;
     }
     for (uint32_t k = done + tid; k < cnt; k += kBlock)
-        walk_body<E, T, 1>(c, P, a.group, mean, a.divisor, (base + k) * sizeof(T), 0);
+        walk_body<E, T, 1, kSgd>(c, P, a.group, mean, a.divisor, (base + k) * sizeof(T), 0,
+                                 wsp);
+}
+
+template <class E>
+__global__ __launch_bounds__(kBlock) void walk_kernel(RankPtrs bufs, FusedArgs a) {
+    walk_tile<E, false>(bufs, a, nullptr);
+}
+
+template <class E>
+__global__ __launch_bounds__(kBlock) void walk_sgd_kernel(RankPtrs bufs, FusedArgs a,
+                                                          SgdArgs g) {
+    walk_tile<E, true>(bufs, a, &g);
 }
 
 }  // namespace
@@ -283,15 +346,22 @@ void launch_e(int kind, int vpl, dim3 grid, hipStream_t s, const RankPtrs &bufs,
 
 }  // namespace
 
-int launch_walk(int dtype, const RankPtrs &bufs, const FusedArgs &a, uint32_t tiles,
-                void *stream) {
+int launch_walk(int dtype, const RankPtrs &bufs, const FusedArgs &a, const SgdArgs *sgd,
+                uint32_t tiles, void *stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (tiles == 0)
         return (int)hipSuccess;
-    if (dtype == DDL_F32)
-        hipLaunchKernelGGL((walk_kernel<F32>), dim3(tiles), dim3(kBlock), 0, s, bufs, a);
-    else
-        hipLaunchKernelGGL((walk_kernel<F16>), dim3(tiles), dim3(kBlock), 0, s, bufs, a);
+    const dim3 grid(tiles), block(kBlock);
+    if (sgd) {
+        if (dtype == DDL_F32)
+            hipLaunchKernelGGL((walk_sgd_kernel<F32>), grid, block, 0, s, bufs, a, *sgd);
+        else
+            hipLaunchKernelGGL((walk_sgd_kernel<F16>), grid, block, 0, s, bufs, a, *sgd);
+    } else if (dtype == DDL_F32) {
+        hipLaunchKernelGGL((walk_kernel<F32>), grid, block, 0, s, bufs, a);
+    } else {
+        hipLaunchKernelGGL((walk_kernel<F16>), grid, block, 0, s, bufs, a);
+    }
     return (int)hipGetLastError();
 }
 

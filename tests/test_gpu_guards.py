@@ -100,7 +100,7 @@ def test_guards_untouched_by_the_allreduce(w, mode):
 
 
 @pytest.mark.parametrize("mode,keep", [("fused1", True), ("fused1", False), ("fused2", True),
-                                       ("fused2", False), ("stepwise", True)])
+                                       ("fused2", False), ("step1", True), ("step2", True)])
 def test_guards_untouched_by_the_sgd_step(mode, keep):
     """The SGD step's weight replicas between guards as well."""
     w = CASES[0]
@@ -116,8 +116,10 @@ def test_guards_untouched_by_the_sgd_step(mode, keep):
     wallocs, wviews = guarded(Workload("wts", w.P, w.n, "f32", "sum", "ring"), [w0] * w.P)
     torch.cuda.synchronize()
     plan = ddl.Plan(w.P, w.n, w.dtype, w.op, ddl_topo(w), w.bucket_list(),
-                    "stepwise" if mode == "stepwise" else "fused")
-    if mode != "stepwise":
+                    "stepwise" if mode.startswith("step") else "fused")
+    if mode.startswith("step"):
+        plan.set_step_form(int(mode[-1]))
+    else:
         plan.set_fused_passes(1 if mode == "fused1" else 2)
     plan.execute_sgd([v.data_ptr() for v in views], [v.data_ptr() for v in wviews], lr,
                      keep_grads=keep)

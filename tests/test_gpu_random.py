@@ -174,7 +174,7 @@ def test_random_sgd_and_lars(seed):
     if mode == "fused":
         plan.set_fused_passes(1 if c["form"] == "fused1" else 2)
     else:
-        plan.set_step_form(c["step_form"])   # the LARS step follows either form
+        plan.set_step_form(c["step_form"])   # the SGD and LARS steps ride on either form
     plan.set_side_streams(c["nside"])
     stream = torch.cuda.current_stream()
     events = None

@@ -46,7 +46,8 @@ def expected(w, weights0, lr):
 @pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
 @pytest.mark.parametrize("mode,keep,passes", [("fused", True, 1), ("fused", False, 1),
                                               ("fused", True, 2), ("fused", False, 2),
-                                              ("stepwise", True, 0)], ids=lambda v: str(v))
+                                              ("step1", True, 0), ("step2", True, 0)],
+                         ids=lambda v: str(v))
 @pytest.mark.parametrize("shared", [False, True])
 def test_sgd_bitwise(w, mode, keep, passes, shared):
     # passes 1: the update in the one-kernel pass's epilogue; 2: reduce
@@ -60,9 +61,13 @@ def test_sgd_bitwise(w, mode, keep, passes, shared):
     g, y, want_w = expected(w, w0, lr)
     bufs = [torch.from_numpy(x).cuda() for x in g]
     weights = [torch.from_numpy(x).cuda() for x in w0]
-    plan = ddl.Plan(w.P, w.n, w.dtype, w.op, ddl_topo(w), w.bucket_list(), mode)
+    plan = ddl.Plan(w.P, w.n, w.dtype, w.op, ddl_topo(w), w.bucket_list(),
+                    "fused" if mode == "fused" else "stepwise")
     if mode == "fused":
         plan.set_fused_passes(passes)
+    else:
+        # one launch per step, or the persistent step kernel
+        plan.set_step_form(int(mode[-1]))
     plan.execute_sgd(bufs, weights, lr, keep_grads=keep)
     torch.cuda.synchronize()
     plan.destroy()
