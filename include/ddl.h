@@ -345,10 +345,10 @@ int ddl_plan_set_side_streams(ddl_plan plan, int n);
  * the weights).  passes = 2: a reduce kernel reads every rank and writes the
  * result to rank 0, then a broadcast kernel copies it from rank 0 to ranks
  * 1..P-1 while it is still in the device caches, so HBM serves a read phase
- * and then a write phase; with the SGD step an update kernel then steps the
- * weights from rank 0's result (without kept gradients the reduce kernel
- * writes to a scratch buffer of n elements instead, allocated by the first
- * such call, and nothing is broadcast).  passes = 0 (default): automatic,
+ * and then a write phase; with the SGD step the broadcast also steps the
+ * weights as it copies (without kept gradients the reduce kernel writes to a
+ * scratch buffer of n elements instead, allocated by the first such call,
+ * nothing is broadcast, and an update kernel steps the weights from it).  passes = 0 (default): automatic,
  * per group: two kernels from 16 ranks on for groups of at least 200 MB
  * summed over the ranks (400 MB for binary16), one kernel otherwise (short
  * passes are launch-bound, and the second launch costs more than it saves).

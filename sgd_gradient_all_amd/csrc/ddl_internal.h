@@ -170,12 +170,14 @@ struct BcastArgs {
     int aligned;
     int tiles_per_group;  // consecutive tiles one workgroup copies
     int nxcd;             // > 1: all rank groups of a tile block on one die
-    // the LARS step's update, riding on the broadcast (table mode; null
-    // rate otherwise): with the reduced values in hand, the workgroup of
-    // rank group g also steps weight replicas -- those of its own ranks when
-    // nweights == P, plus replica 0 for g == 0; replica 0 alone for g == 0
-    // when nweights == 1 -- by w = w - rate[bucket] * y
+    // the weight update riding on the broadcast (launch_bcast_update, table
+    // mode): with the reduced values in hand, the workgroup of rank group g
+    // also steps weight replicas -- those of its own ranks when nweights ==
+    // P, plus replica 0 for g == 0; replica 0 alone for g == 0 when nweights
+    // == 1 -- by w = w - rate[bucket] * y (the LARS step), or w = w - lr * y
+    // when rate is null (the SGD step)
     const float *rate;
+    float lr;
     int nweights;
 };
 
@@ -235,7 +237,8 @@ int launch_step(int dtype, int kind, int vpl, const RankPtrs &bufs, const StepAr
 int launch_fused(int dtype, const RankPtrs &bufs, const FusedArgs &a, const SgdArgs *sgd,
                  bool home, uint32_t tiles, void *stream);
 int launch_bcast(int dtype, const RankPtrs &bufs, const BcastArgs &a, void *stream);
-// The broadcast with the LARS step's update of the replicas w (a.rate set).
+// The broadcast with the update of the replicas w riding on it (the LARS
+// step's rates, or the SGD step's constant lr when a.rate is null).
 int launch_bcast_update(int dtype, const RankPtrs &bufs, const RankPtrs &w, const BcastArgs &a,
                         void *stream);
 int launch_tiny(int dtype, const RankPtrs &bufs, const TinyArgs &a, void *stream);

@@ -399,7 +399,7 @@ __device__ __forceinline__ void bcast_tile(const RankPtrs &bufs, const BcastArgs
     // own ranks, with one replica per rank)
     const bool rep0 = kUpd && grp == 0;
     const int w0 = kUpd && a.nweights > 1 ? r0 : 0, w1 = kUpd && a.nweights > 1 ? r1 : 0;
-    const float rate = kUpd ? a.rate[bucket] : 0.0f;
+    const float rate = kUpd ? (a.rate ? a.rate[bucket] : a.lr) : 0.0f;
     uint32_t done = 0;
     if (aligned) {
         const uint32_t nvec = cnt / E::N;
@@ -501,9 +501,10 @@ __global__ __launch_bounds__(kBlock) void bcast_kernel(RankPtrs bufs, BcastArgs 
     bcast_body<E, false>(bufs, a, nullptr);
 }
 
-// The broadcast of the LARS step's two-kernel form, with the update of the
-// weight replicas w, kRB replicas' loads ahead of their stores (knob
-// DDL_TUNE_UPDATE_BATCH, as the update kernel).
+// The broadcast of the two-kernel form with the update of the weight
+// replicas w riding on it: the LARS step (each bucket's rate) or the SGD
+// step with kept gradients (the constant rate lr), kRB replicas' loads ahead
+// of their stores (knob DDL_TUNE_UPDATE_BATCH, as the update kernel).
 template <class E, int kRB>
 __global__ __launch_bounds__(kBlock) void bcast_update_kernel(RankPtrs bufs, RankPtrs w,
                                                               BcastArgs a) {
@@ -678,7 +679,7 @@ int launch_bcast_update(int dtype, const RankPtrs &bufs, const RankPtrs &w, cons
     hipStream_t s = static_cast<hipStream_t>(stream);
     bool bad = false;
     const uint64_t blocks = bcast_blocks(dtype, a, &bad);
-    if (bad || !a.spans || !a.rate || a.nweights < 1)
+    if (bad || !a.spans || a.nweights < 1)
         return (int)hipErrorInvalidValue;
     if (blocks == 0)
         return (int)hipSuccess;

@@ -279,9 +279,9 @@ constexpr uint32_t kMaxTilesPerLaunch = 1u << 23;
 // 16 ranks fp32 win from 16 MB (-3%), lose at 8 MB (+4%) and below (+16..19%,
 // launch-bound); 16 ranks fp16 still lose at 16 MB (+8%).  With the SGD
 // step, the one-kernel form updates the weights in its epilogue; the
-// two-kernel form reduces (to rank 0, or to a scratch buffer when the
-// gradients are not kept), broadcasts (when they are), then runs the update
-// kernel with the constant rate lr.
+// two-kernel form reduces to rank 0 and its broadcast steps the replicas as
+// it copies, or, when the gradients are not kept, reduces to a scratch
+// buffer and runs the update kernel from it.
 constexpr uint64_t kTwoKernelMinBytes = 200ull << 20;
 int fused_passes(ddl_plan p, const Schedule &s, uint64_t elems) {
     if (s.P < 2)
@@ -525,10 +525,46 @@ struct Launcher {
             return DDL_OK;
         if (fused_lars)
             return lars_pass_tail(b0, b1, a.partial);
-        int rc = scratch ? DDL_OK : broadcast(b0, b1);
-        if (rc || !sgd)
-            return rc;
-        return update(b0, b1, a.home, nullptr, sgd->lr, sgd->w, sgd->nweights);
+        if (scratch)
+            return update(b0, b1, a.home, nullptr, sgd->lr, sgd->w, sgd->nweights);
+        // with the SGD step, the broadcast steps the replicas as it copies
+        return sgd ? bcast_update(b0, b1, nullptr, sgd->lr, sgd->w, sgd->nweights)
+                   : broadcast(b0, b1);
+    }
+
+    // the broadcast of buckets [b0, b1) over the bucket table, whose
+    // workgroups also step the weight replicas w with each bucket's rate
+    // (rate null: the constant lr)
+    int bcast_update(int b0, int b1, const float *rate, float lr, const RankPtrs &w,
+                     int nweights) {
+        const Schedule &s = pt->s;
+        BcastArgs bc;
+        std::memset(&bc, 0, sizeof(bc));
+        bc.P = s.P;
+        bc.ranks_per_group = bcast_ranks_per_group(s.P);
+        bc.ngroups = (s.P - 1 + bc.ranks_per_group - 1) / bc.ranks_per_group;
+        bc.tiles_per_group = 1;
+        bc.nxcd = 1;
+        bc.spans = pt->d_bk_spans;
+        bc.prefix = pt->d_bk_prefix;
+        bc.tile_span = pt->d_bk_of_tile;
+        bc.rate = rate;
+        bc.lr = lr;
+        bc.nweights = nweights;
+        const uint32_t *bp = s.bk_prefix.data();
+        const uint32_t max_tiles = 0xffffffu / (uint32_t)bc.ngroups;
+        for (uint32_t t = bp[b0]; t < bp[b1]; t += max_tiles) {
+            bc.tile_base = t;
+            bc.tile_end = std::min(bp[b1], t + max_tiles);
+            int rc = bracket_begin(DDL_K_BROADCAST);
+            if (rc)
+                return rc;
+            if (launch_bcast_update(s.dtype, bufs, w, bc, stream) != hipSuccess)
+                return DDL_E_HIP;
+            if ((rc = bracket_end()))
+                return rc;
+        }
+        return DDL_OK;
     }
 
     // after the LARS reduce kernel of buckets [b0, b1): the rates from the
@@ -550,30 +586,8 @@ struct Launcher {
             return DDL_E_HIP;
         if ((rc = bracket_end()))
             return rc;
-        BcastArgs bc;
-        std::memset(&bc, 0, sizeof(bc));
-        bc.P = s.P;
-        bc.ranks_per_group = bcast_ranks_per_group(s.P);
-        bc.ngroups = (s.P - 1 + bc.ranks_per_group - 1) / bc.ranks_per_group;
-        bc.tiles_per_group = 1;
-        bc.nxcd = 1;
-        bc.spans = pt->d_bk_spans;
-        bc.prefix = pt->d_bk_prefix;
-        bc.tile_span = pt->d_bk_of_tile;
-        bc.rate = la.rate;
-        bc.nweights = lars->nweights;
-        const uint32_t *bp = s.bk_prefix.data();
-        const uint32_t max_tiles = 0xffffffu / (uint32_t)bc.ngroups;
-        for (uint32_t t = bp[b0]; t < bp[b1]; t += max_tiles) {
-            bc.tile_base = t;
-            bc.tile_end = std::min(bp[b1], t + max_tiles);
-            if ((rc = bracket_begin(DDL_K_BROADCAST)))
-                return rc;
-            if (launch_bcast_update(s.dtype, bufs, lars->w, bc, stream) != hipSuccess)
-                return DDL_E_HIP;
-            if ((rc = bracket_end()))
-                return rc;
-        }
+        if ((rc = bcast_update(b0, b1, la.rate, 0.0f, lars->w, lars->nweights)))
+            return rc;
         lars_done = true;
         return DDL_OK;
     }
