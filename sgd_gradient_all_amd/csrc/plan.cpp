@@ -32,6 +32,14 @@ constexpr int kMaxSideStreams = 4;
 // Events a plan makes when it binds, for the completion tracking of the
 // first caller streams it is executed on.
 constexpr int kSpareEvents = 8;
+// Flags of the completion-tracking events.  The host only asks them whether
+// the plan's launches have finished (before its tables are freed); no
+// stream waits for them and the host reads nothing the launches wrote, so
+// they skip the system-scope fence (a cache writeback and invalidate) that
+// an event record performs by default.  Measured on MI355X (paired, three
+// rounds): back-to-back calls of the binary16 torus 305.6-306.6 -> 304.2-
+// 304.4 us; a build with no record at all gained 2.8 us per call.
+constexpr unsigned kTrackEventFlags = hipEventDisableTiming | hipEventDisableSystemFence;
 
 // process-wide tuning knobs (ddl_set_tuning), stored as value + 1 so that
 // the zero-initialised array means "every knob at its default"
@@ -216,7 +224,7 @@ int bind_device(ddl_plan p, int dev) {
         return DDL_E_HIP;
     for (int i = 0; i < kSpareEvents; ++i) {
         hipEvent_t e;
-        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
+        if (hipEventCreateWithFlags(&e, kTrackEventFlags) != hipSuccess)
             return DDL_E_HIP;
         p->spare_ev.push_back(e);
     }
@@ -798,8 +806,7 @@ hipEvent_t *last_event(ddl_plan p, hipStream_t ls, bool may_create = true) {
     if (!p->spare_ev.empty()) {
         e = p->spare_ev.back();
         p->spare_ev.pop_back();
-    } else if (!may_create ||
-               hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+    } else if (!may_create || hipEventCreateWithFlags(&e, kTrackEventFlags) != hipSuccess) {
         return nullptr;
     }
     p->last_ev.emplace_back(ls, e);
