@@ -654,7 +654,9 @@ def latency_leg(main_stream, torch, ddl, synth, calls=4):
     `..._group_events` variants record one event per group that
     ddl_plan_event_groups reports (after the group's last tensor) and pass it
     for each of the group's tensors: the same groups and launches, with one
-    record per group instead of one per tensor."""
+    record per group instead of one per tensor.  The `..._nofence`
+    variants record the per-tensor events as the binding's ReadyEvent makes
+    them, without the system-scope fence of a default record."""
     from synth.workloads import WORKLOADS
     w = WORKLOADS["multiring_k4_p16_resnet50"]
     bufs = [torch.empty(w.n, dtype=torch.float32, device="cuda") for _ in range(w.P)]
@@ -663,6 +665,7 @@ def latency_leg(main_stream, torch, ddl, synth, calls=4):
     buckets = w.bucket_list()
     topo = ddl.topo(w.topo, w.k, w.rows, w.cols)
     events = [torch.cuda.Event() for _ in buckets]
+    nofence_events = [ddl.ReadyEvent() for _ in buckets]
     gate = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
     cs = main_stream.cuda_stream
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -759,12 +762,13 @@ def latency_leg(main_stream, torch, ddl, synth, calls=4):
     plan = ddl.Plan(w.P, w.n, w.dtype, w.op, topo, buckets, "fused")
     res["no_events_fused"] = measure(plan, False, True)
     plan.destroy()
-    variants = [("fused", 0, 0, False, False), ("fused", 0, 16, False, False),
-                ("fused", 0, 16, True, False), ("fused", 0, 16, True, True),
-                ("stepwise", 2, 0, False, False), ("stepwise", 2, 16, True, False),
-                ("stepwise", 2, 16, True, True),
-                ("stepwise", 1, 0, False, False), ("stepwise", 1, 16, True, False)]
-    for mode, form, thr_mb, ordered, grouped in variants:
+    variants = [("fused", 0, 0, False, False, False), ("fused", 0, 16, False, False, False),
+                ("fused", 0, 16, True, False, False), ("fused", 0, 16, True, True, False),
+                ("fused", 0, 16, True, False, True),
+                ("stepwise", 2, 0, False, False, False), ("stepwise", 2, 16, True, False, False),
+                ("stepwise", 2, 16, True, True, False), ("stepwise", 2, 16, True, False, True),
+                ("stepwise", 1, 0, False, False, False), ("stepwise", 1, 16, True, False, False)]
+    for mode, form, thr_mb, ordered, grouped, nofence in variants:
         plan = ddl.Plan(w.P, w.n, w.dtype, w.op, topo, buckets, mode)
         if mode == "stepwise":
             plan.set_step_form(form)
@@ -776,6 +780,8 @@ def latency_leg(main_stream, torch, ddl, synth, calls=4):
             last = plan.event_groups()
             rec = [torch.cuda.Event() for _ in last]
             passed = [rec[sum(1 for x in last if x < b)] for b in range(len(buckets))]
+        elif nofence:
+            rec, passed = nofence_events, nofence_events
         else:
             rec, passed = events, events
         plan.set_profiling(1)
@@ -784,7 +790,8 @@ def latency_leg(main_stream, torch, ddl, synth, calls=4):
         launches = sum(v[1] for v in plan.profile_read_kinds().values())
         plan.set_profiling(0)
         key = (f"{mode}{'' if mode == 'fused' else '_form%d' % form}_coalesce_{thr_mb}mb"
-               f"{'_ordered' if ordered else ''}{'_group_events' if grouped else ''}")
+               f"{'_ordered' if ordered else ''}{'_group_events' if grouped else ''}"
+               f"{'_nofence' if nofence else ''}")
         row = measure(plan, True, True)
         row["launches"] = launches
         row["events_recorded"] = len(rec)
@@ -795,8 +802,9 @@ def latency_leg(main_stream, torch, ddl, synth, calls=4):
     res["fused_event_gated_over_no_events"] = {
         k: {m: round(res[k][m] / base[m], 3) for m in ("device_ms", "graph_ms")}
         for k in ("fused_coalesce_0mb", "fused_coalesce_16mb", "fused_coalesce_16mb_ordered",
+                  "fused_coalesce_16mb_ordered_nofence",
                   "fused_coalesce_16mb_ordered_group_events")}
-    del bufs, gate
+    del bufs, gate, nofence_events
     torch.cuda.empty_cache()
     log(f"bench: latency {res}")
     return res

@@ -146,6 +146,56 @@ def _ptr(x):
     return int(x)
 
 
+_hip = None
+
+
+def _hip_lib():
+    global _hip
+    if _hip is None:
+        h = ctypes.CDLL("libamdhip64.so")
+        h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        h.hipEventCreateWithFlags.restype = ctypes.c_int
+        h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        h.hipEventRecord.restype = ctypes.c_int
+        h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        h.hipEventDestroy.restype = ctypes.c_int
+        _hip = h
+    return _hip
+
+
+class ReadyEvent:
+    """A HIP event for a bucket's readiness, made through the HIP runtime
+    (hipEventCreateWithFlags), with timing disabled and, by default, without
+    the system-scope fence an event record otherwise performs: the library
+    only makes its streams wait for ready events, which orders the device
+    work on either side, and never inspects them from the host.  A record
+    then costs the device less, and does not write back and invalidate the
+    caches under the kernels running beside it.  Pass it wherever an event
+    goes (it has cuda_event); record(stream) records it on a stream (a torch
+    stream or a raw handle; None = the null stream)."""
+
+    DISABLE_TIMING = 0x2
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, system_fence=False):
+        flags = self.DISABLE_TIMING | (0 if system_fence else self.DISABLE_SYSTEM_FENCE)
+        h = ctypes.c_void_p()
+        rc = _hip_lib().hipEventCreateWithFlags(ctypes.byref(h), flags)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.cuda_event = h.value
+
+    def record(self, stream=None):
+        rc = _hip_lib().hipEventRecord(self.cuda_event, _ptr(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def __del__(self):
+        if getattr(self, "cuda_event", None) and _hip is not None:
+            _hip.hipEventDestroy(self.cuda_event)
+            self.cuda_event = None
+
+
 def topo(kind="ring", k=1, rows=0, cols=0, ring_order=None):
     """A ddl_topo (the ring order array is kept alive on the object)."""
     t = ddl_topo()

@@ -387,12 +387,22 @@ def test_element_indices_beyond_32_bits(dtype, P, n):
 # ---------------------------------------------------------------------------
 # dispatcher: ready events gate buckets
 # ---------------------------------------------------------------------------
-def test_ready_events_gate_buckets():
+def ready_event(kind):
+    """A caller's ready event: torch's, or the binding's ReadyEvent, which
+    skips the system-scope fence of the record."""
+    return torch.cuda.Event() if kind == "torch" else ddl.ReadyEvent()
+
+
+@pytest.mark.parametrize("ev", ["torch", "nofence"])
+@pytest.mark.parametrize("mode", ["fused", "fused1", "step2"])
+def test_ready_events_gate_buckets(mode, ev):
     """Inputs are written by kernels queued behind a long kernel on the main
     stream, bucket by bucket, each followed by its event.  The all-reduce is
     enqueued right after: correct results need every bucket to have waited
-    for its own event."""
-    say("case ready events")
+    for its own event, and the writes before each record to be visible to
+    the library's kernels (also with records that skip the system-scope
+    fence)."""
+    say(f"case ready events {mode} {ev}")
     w = Workload("events", 8, 64 * 65_536, "f32", "mean", "ring", dist="normal", sigma=1e-3,
                  seed=11, buckets=[(i * 65_536, 65_536) for i in reversed(range(64))])
     bufs = [torch.full((w.n,), float("nan"), device="cuda") for _ in range(w.P)]
@@ -405,10 +415,10 @@ def test_ready_events_gate_buckets():
         for r, b in enumerate(bufs):
             synth.fill_device(b.data_ptr() + 4 * off, cnt, synth.F32, w.dist, w.seed, r,
                               first=off, sigma=w.sigma, stream=main.cuda_stream)
-        e = torch.cuda.Event()
+        e = ready_event(ev)
         e.record(main)
         events.append(e)
-    plan = ddl.Plan(w.P, w.n, w.dtype, w.op, ddl_topo(w), w.bucket_list(), "fused")
+    plan = make_plan(w, mode)
     plan.execute(bufs, events=events, stream=main)
     torch.cuda.synchronize()
     g = host_inputs(w)
@@ -582,8 +592,9 @@ def test_coalesce_threshold_merges_event_gated_buckets():
     assert counts[("step2", 16 << 20)] == counts[("fused", 16 << 20)]
 
 
+@pytest.mark.parametrize("ev", ["torch", "nofence"])
 @pytest.mark.parametrize("mode", ["fused1", "fused2", "step1", "step2"])
-def test_ordered_events_gate_each_group_on_its_last_event(mode):
+def test_ordered_events_gate_each_group_on_its_last_event(mode, ev):
     """Back-propagation's pattern: on one stream, behind a long streaming
     kernel, each bucket's gradient is written on every rank and then its
     ready event recorded, output layer first.  With ordered events and a
@@ -591,7 +602,7 @@ def test_ordered_events_gate_each_group_on_its_last_event(mode):
     bucket, and every element still matches the oracle: a group that
     started before its last gradient was written would read the zeros the
     buffers held before."""
-    say(f"case ordered events {mode}")
+    say(f"case ordered events {mode} {ev}")
     rng = np.random.default_rng(31)
     sizes = [int(x) for x in rng.choice([8, 64, 1000, 4096, 30_000, 120_000], 40)]
     offs = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(int).tolist()
@@ -618,7 +629,7 @@ def test_ordered_events_gate_each_group_on_its_last_event(mode):
     for off, cnt in bl:
         for r in range(w.P):
             bufs[r][off:off + cnt].copy_(src[r][off:off + cnt])
-        e = torch.cuda.Event()
+        e = ready_event(ev)
         e.record(stream)
         events.append(e)
     plan.execute(bufs, events=events, stream=stream)
