@@ -151,7 +151,11 @@ int ddl_plan_create_typed(ddl_plan *out, int P, size_t nbytes, ddl_op op,
 /* Enqueue the all-reduce of bufs[0..P) (device pointers, each 16-byte
  * aligned, n elements) on the current HIP device.
  *  ready_events  NULL, or nbuckets hipEvent_t (entries may be NULL) in bucket
- *                list order: bucket b's work waits for ready_events[b].
+ *                list order: bucket b's work waits for ready_events[b].  The
+ *                library only makes its streams wait for them and never
+ *                inspects them from the host, so events created with
+ *                hipEventDisableSystemFence serve: their records skip the
+ *                cache writeback and invalidate of the default fence.
  *  stream        the caller's hipStream_t (NULL = default stream).  Buckets
  *                without an event wait for the work already enqueued on it.
  *  done_event    NULL or a hipEvent_t recorded when every bucket is done.
