@@ -497,7 +497,7 @@ def configs_leg(head, main_stream, torch, ddl, synth, allocations=3):
 
 def ceilings_leg(main_stream, torch, synth, nbytes=1_200_000_000, reps=7):
     """The rates plain streams reach on this device (in-tree kernels of
-    known bytes, non-temporal 16-byte accesses, one 8 KB tile per
+    known bytes, non-temporal 16-byte accesses, one 4 KB tile per
     workgroup): a copy of nbytes (nbytes read and nbytes written), a read
     and a write.  The fused pass reads and writes the same number of bytes,
     as a copy does, so the copy's rate is the one to hold it against."""

@@ -72,11 +72,14 @@ __global__ void stream_compute(float *a, uint64_t n, float alpha, float beta) {
         a[i] = a[i] * alpha + beta;
 }
 
-// Plain streams of known bytes: every workgroup moves tiles of 2 x 256
-// 16-byte vectors with non-temporal accesses (each byte touched once); the
-// elements past the last whole tile go one per lane.
+// Plain streams of known bytes: every workgroup moves tiles of 256 16-byte
+// vectors, one per lane (4 KB), with non-temporal accesses (each byte
+// touched once); the elements past the last whole tile go one per lane.
+// Measured on MI355X over 1.2 GB, one tile per workgroup: a copy 6.43-6.58
+// TB/s with one vector per lane against 5.80-5.90 with two (and 5.56 with
+// eight), a read 6.95-7.01, a write 6.42-6.79.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-constexpr uint64_t kStreamTile = 2 * 256;  // vectors per tile
+constexpr uint64_t kStreamTile = 256;  // vectors per tile
 
 __global__ __launch_bounds__(256) void stream_copy(const float *src, float *dst, uint64_t n) {
     const f32x4 *s = reinterpret_cast<const f32x4 *>(src);
@@ -84,10 +87,7 @@ __global__ __launch_bounds__(256) void stream_copy(const float *src, float *dst,
     const uint64_t tiles = n / 4 / kStreamTile;
     for (uint64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
         const uint64_t i = t * kStreamTile + threadIdx.x;
-        const f32x4 a = __builtin_nontemporal_load(s + i);
-        const f32x4 b = __builtin_nontemporal_load(s + i + 256);
-        __builtin_nontemporal_store(a, d + i);
-        __builtin_nontemporal_store(b, d + i + 256);
+        __builtin_nontemporal_store(__builtin_nontemporal_load(s + i), d + i);
     }
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
     for (uint64_t i = tiles * kStreamTile * 4 + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -104,7 +104,6 @@ __global__ __launch_bounds__(256) void stream_read(const float *src, uint64_t n,
     for (uint64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
         const uint64_t i = t * kStreamTile + threadIdx.x;
         acc += __builtin_nontemporal_load(s + i);
-        acc += __builtin_nontemporal_load(s + i + 256);
     }
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
     for (uint64_t i = tiles * kStreamTile * 4 + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -121,7 +120,6 @@ __global__ __launch_bounds__(256) void stream_write(float *dst, uint64_t n, floa
     for (uint64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
         const uint64_t i = t * kStreamTile + threadIdx.x;
         __builtin_nontemporal_store(v, d + i);
-        __builtin_nontemporal_store(v, d + i + 256);
     }
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
     for (uint64_t i = tiles * kStreamTile * 4 + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
