@@ -404,8 +404,9 @@ typedef enum {
      * whose ranges average at least 2 tiles), 1 = never, 2 = always */
     DDL_TUNE_ANCHOR = 3,
     /* loads each lane issues ahead of their adds (1, 2, 4 or 8; other values
-     * act as 1) in the one-kernel pass (default 1) and in the reduce kernel
-     * (default 4); the adds keep the schedule's order */
+     * act as 1) in the one-kernel pass (default 1) and in the reduce
+     * kernel's tile-by-tile form (default 4); the adds keep the schedule's
+     * order */
     DDL_TUNE_FUSED_BATCH = 4,
     DDL_TUNE_REDUCE_BATCH = 5,
     /* two-kernel form: consecutive tiles each broadcast workgroup copies
@@ -425,7 +426,12 @@ typedef enum {
      * before their stores (1, 2, 4 or 8; default 4; the broadcast takes 8
      * as 4) */
     DDL_TUNE_UPDATE_BATCH = 9,
-    DDL_TUNE_COUNT = 10
+    /* two-kernel form: the reduce kernel walks the tiles of each workgroup
+     * rank by rank (eight tiles per workgroup, the loads of one rank two at
+     * a time) from this many ranks on, and tile by tile (one tile per
+     * workgroup, DDL_TUNE_REDUCE_BATCH loads at a time) below; default 32 */
+    DDL_TUNE_REDUCE_RANKS_MIN_P = 10,
+    DDL_TUNE_COUNT = 11
 } ddl_tune_knob;
 int ddl_set_tuning(int knob, int value);
 int ddl_get_tuning(int knob, int *value);

@@ -37,6 +37,17 @@ constexpr int fused_vecs_per_lane(int esz) {
 // Consecutive tiles one fused workgroup walks (address translations of the
 // P rank streams are reused from tile to tile).
 constexpr int kFusedTilesPerGroup = DDL_FUSED_TPW;
+// Consecutive tiles one workgroup of the two-kernel form's reduce kernel
+// takes, rank by rank, and the loads it issues at a time ahead of their
+// adds (fused_kernel.hip, reduce_tiles).
+#ifndef DDL_REDUCE_TILES
+#define DDL_REDUCE_TILES 8
+#endif
+#ifndef DDL_REDUCE_ISSUE
+#define DDL_REDUCE_ISSUE 2
+#endif
+constexpr int kReduceTiles = DDL_REDUCE_TILES;
+constexpr int kReduceIssue = DDL_REDUCE_ISSUE;
 
 // Elements of one tile, by element size.
 // Step kernels take 1, 2 or 4 vectors per lane per tile; each plan picks

@@ -337,6 +337,9 @@ void fused_sgd_kernel(RankPtrs bufs, FusedArgs a, SgdArgs g) {
     fused_body<E, kGrouped, kNt, true, false, kB>(bufs, a, &g);
 }
 
+// The reduce kernel of the two-kernel form, tile by tile: each workgroup
+// reads its tile from all P ranks (loads in batches of kB ranks) and
+// writes the result to the home buffer.
 template <class E, bool kGrouped, bool kNt, int kB>
 __global__ __launch_bounds__(kBlock) DDL_FUSED_OCCUPANCY
 void fused_reduce_kernel(RankPtrs bufs, FusedArgs a) {
@@ -349,6 +352,206 @@ template <class E, bool kGrouped, bool kNt, int kB>
 __global__ __launch_bounds__(kBlock) DDL_FUSED_OCCUPANCY
 void fused_reduce_lars_kernel(RankPtrs bufs, FusedArgs a) {
     fused_body<E, kGrouped, kNt, false, true, kB, true>(bufs, a, nullptr);
+}
+
+// ---------------------------------------------------------------------------
+// The reduce kernel of the two-kernel form, rank by rank.  Workgroup b takes
+// the kReduceTiles consecutive tiles from tile_base + b kReduceTiles on
+// (each of any span: a tile's chain and bounds are its own) and walks the
+// chain positions j = 0 .. P-1: at each, it loads the tiles' elements of
+// their chain entry j, one vector per lane per tile, and adds them to the
+// tiles' sums, kReduceIssue loads at a time ahead of their adds.  Every
+// element still takes its adds in chain order (groups of `group` entries,
+// then the group sums), so the results are the bits of the tile-by-tile
+// walk.  Lanes past a tile's whole vectors re-load its last one; a tile's
+// last elements (fewer than a vector, or all of a span whose offset is not
+// vector-aligned) are summed one by one after the walk.
+// Measured on MI355X as plain kernels over the pass's own geometry (40
+// ranks, 18.75 MB slices of 1.2 GB buffers, the ring's chunks with anchored
+// tiles, 8 tiles per workgroup): loads two at a time 123 us per bucket,
+// four at a time 128, all eight 131, one 169; tile by tile with batches of
+// 4 ranks (the form this replaces) 134.
+// ---------------------------------------------------------------------------
+
+// A 16-byte vector of zeros: the load of a tile with no whole vectors.
+__device__ __align__(16) const uint32_t kZeroVec[4] = {0, 0, 0, 0};
+
+template <class E, bool kGrouped, bool kNt, bool kLars>
+__device__ __forceinline__ void reduce_tiles(const RankPtrs &bufs, const FusedArgs &a) {
+    using T = typename E::T;
+    using V = typename E::V;
+    using Wv = typename E::W;
+    static_assert(fused_vecs_per_lane(sizeof(T)) == 1, "one vector per lane per tile");
+    constexpr uint64_t kTile = fused_tile_elems(sizeof(T));
+    constexpr int K = kReduceTiles;
+    constexpr int kIssue = kReduceIssue;
+    static_assert(K % kIssue == 0, "loads in whole groups");
+    constexpr int kZeroSlot = K;
+    // rank addresses in chain order: one slot per distinct span of the
+    // workgroup's tiles, and a slot whose every entry is the zero vector
+    __shared__ uint64_t src[K + 1][DDL_MAX_RANKS];
+    __shared__ double lds_norm[2][kBlock / 64];
+    const int P = a.P;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t first = a.tile_base + blockIdx.x * (uint32_t)K;
+    const uint32_t nt = min((uint32_t)K, a.tile_end - first);
+    uint64_t base[K];     // first element of each tile
+    uint32_t cnt[K];      // its elements
+    uint32_t nvec[K];     // its whole vectors (none when its span is not aligned)
+    int slot[K];          // the slot of its span's chain
+    uint32_t coff[K];     // chain offset of each slot
+    int nslots = 0;
+    uint32_t prev = UINT32_MAX;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        base[k] = 0;
+        cnt[k] = nvec[k] = 0;
+        slot[k] = kZeroSlot;
+        coff[k] = 0;
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        if ((uint32_t)k < nt) {
+            const uint32_t tile = first + (uint32_t)k;
+            const uint32_t i = a.tile_span[tile];
+            const DevSpan sp = a.spans[i];
+            const uint64_t j = tile - a.prefix[i];
+            const uint64_t sh = tile_shift(sp.off, kTile, a.anchor);
+            base[k] = tile_lo(sp.off, sh, kTile, j);
+            cnt[k] = (uint32_t)(tile_hi(sp.off, sp.len, sh, kTile, j) - base[k]);
+            nvec[k] = (sp.flags & kItemAligned) ? cnt[k] / E::N : 0;
+            // consecutive tiles of one span are adjacent
+            if (i != prev) {
+#pragma unroll
+                for (int q = 0; q < K; ++q)
+                    if (q == nslots)
+                        coff[q] = sp.chain_off;
+                ++nslots;
+                prev = i;
+            }
+            slot[k] = nslots - 1;
+        }
+    }
+    // every slot's entries at once: one dependent pair of loads per lane
+    for (int m = (int)tid; m < (nslots + 1) * P; m += kBlock) {
+        const int q = m / P, r = m - q * P;
+        uint64_t addr = reinterpret_cast<uint64_t>(&kZeroVec);
+        if (q < nslots) {
+            uint32_t co = coff[0];
+#pragma unroll
+            for (int q2 = 1; q2 < K; ++q2)
+                if (q == q2)
+                    co = coff[q2];
+            addr = reinterpret_cast<uint64_t>(bufs.p[a.chains[co + r]]);
+        }
+        src[q < nslots ? q : kZeroSlot][r] = addr;
+    }
+    // Every load of the walk is unconditional (branches around them would
+    // keep K values live per path): lanes past a tile's whole vectors
+    // re-load its last one (a line already in flight), and a tile without
+    // whole vectors (or past the launch's last tile) reads the zero vector
+    // at every chain position.
+    int vslot[K];
+    uint64_t lane_off[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        vslot[k] = nvec[k] ? slot[k] : kZeroSlot;
+        lane_off[k] = nvec[k] ? (base[k] + (uint64_t)min(tid, nvec[k] - 1) * E::N) * sizeof(T)
+                              : 0;
+    }
+    __syncthreads();
+    Chain<E> c[K];
+    V acc[K];
+    for (int r = 0; r < P; ++r) {
+#pragma unroll
+        for (int k0 = 0; k0 < K; k0 += kIssue) {
+            V x[kIssue];
+#pragma unroll
+            for (int q = 0; q < kIssue; ++q)
+                x[q] = ld_global<V, kNt>(src[vslot[k0 + q]][r] + lane_off[k0 + q]);
+            // the group's loads issue before its adds: left alone, the
+            // scheduler may keep a single load in flight
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int q = 0; q < kIssue; ++q) {
+                const int k = k0 + q;
+                if (kGrouped)
+                    c[k].push(x[q], a.group);
+                else
+                    acc[k] = r == 0 ? x[q] : E::add(acc[k], x[q]);
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        V y = kGrouped ? c[k].acc : acc[k];
+        if (a.mean)
+            y = E::div(y, a.divisor);
+        acc[k] = y;
+        if (tid < nvec[k]) {
+            const V one[1] = {y};
+            store_home<E, 1>(a.home, base[k] + (uint64_t)tid * E::N, one);
+        }
+    }
+    // each tile's last elements one by one, then (kLars) its norm partial
+    // sums: each lane its vector, then its elements, then the workgroup
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        if ((uint32_t)k >= nt)
+            continue;
+        double sw = 0.0, sy = 0.0;
+        if (kLars && tid < nvec[k]) {
+            const uint64_t e = base[k] + (uint64_t)tid * E::N;
+            add_squares<Wv>(E::widen(acc[k]), sy);
+            add_squares<Wv>(ld_stream<Wv, true>(a.w0 + e), sw);
+        }
+        for (uint32_t m = nvec[k] * E::N + tid; m < cnt[k]; m += kBlock) {
+            const uint64_t e = base[k] + m;
+            T s = 0, gs = 0;
+            int pos = 0;
+            bool first_group = true;
+            for (int j = 0; j < P; ++j) {
+                const T v =
+                    *reinterpret_cast<const T DDL_GLOBAL *>(src[slot[k]][j] + e * sizeof(T));
+                gs = pos == 0 ? v : E::add1(gs, v);
+                if (++pos == a.group) {
+                    s = first_group ? gs : E::add1(s, gs);
+                    first_group = false;
+                    pos = 0;
+                }
+            }
+            if (a.mean)
+                s = E::div1(s, a.divisor);
+            static_cast<T *>(a.home)[e] = s;
+            if (kLars) {
+                const double y = (double)(float)s, w = (double)a.w0[e];
+                sy += y * y;
+                sw += w * w;
+            }
+        }
+        if (kLars) {
+            const double tw = block_sum(sw, lds_norm[0]);
+            const double ty = block_sum(sy, lds_norm[1]);
+            if (tid == 0) {
+                a.partial[2 * (uint64_t)(first + k)] = tw;
+                a.partial[2 * (uint64_t)(first + k) + 1] = ty;
+            }
+            __syncthreads();  // lds_norm is read before the next tile's sums
+        }
+    }
+}
+
+template <class E, bool kGrouped, bool kNt>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4)))
+void reduce_ranks_kernel(RankPtrs bufs, FusedArgs a) {
+    reduce_tiles<E, kGrouped, kNt, false>(bufs, a);
+}
+
+// The same with the LARS step's per-tile partial sums of the layer norms.
+template <class E, bool kGrouped, bool kNt>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4)))
+void reduce_ranks_lars_kernel(RankPtrs bufs, FusedArgs a) {
+    reduce_tiles<E, kGrouped, kNt, true>(bufs, a);
 }
 
 // ---------------------------------------------------------------------------
@@ -595,16 +798,36 @@ void launch_nt(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &
     }
 }
 
+// The rank-by-rank reduce kernel (with the LARS partial sums when
+// a.partial is set).
+template <class E, bool kGrouped, bool kNt>
+void launch_ranks(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a) {
+    const dim3 block(kBlock);
+    if (a.partial)
+        hipLaunchKernelGGL((reduce_ranks_lars_kernel<E, kGrouped, kNt>), grid, block, 0, s, bufs,
+                           a);
+    else
+        hipLaunchKernelGGL((reduce_ranks_kernel<E, kGrouped, kNt>), grid, block, 0, s, bufs, a);
+}
+
 template <class E, bool kGrouped>
 void launch_e(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a,
-              const SgdArgs *sgd, bool home) {
+              const SgdArgs *sgd, bool home, bool ranks) {
     if (home) {
         // the reduce kernel reads the ranks with non-temporal loads whatever
         // P: the P input streams must not evict the results the broadcast
         // kernel re-reads (measured on MI355X, 40 ranks: 6031 GB/s against
         // 5242 with cached loads)
+        const bool nt = tuning(DDL_TUNE_REDUCE_NT_LOAD) != 0;
+        if (ranks) {
+            if (nt)
+                launch_ranks<E, kGrouped, true>(grid, s, bufs, a);
+            else
+                launch_ranks<E, kGrouped, false>(grid, s, bufs, a);
+            return;
+        }
         const int batch = tuning(DDL_TUNE_REDUCE_BATCH);
-        if (tuning(DDL_TUNE_REDUCE_NT_LOAD) != 0)
+        if (nt)
             launch_nt<E, kGrouped, true>(grid, s, bufs, a, nullptr, true, batch);
         else
             launch_nt<E, kGrouped, false>(grid, s, bufs, a, nullptr, true, batch);
@@ -624,18 +847,25 @@ void launch_e(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a
 int launch_fused(int dtype, const RankPtrs &bufs, const FusedArgs &a, const SgdArgs *sgd,
                  bool home, uint32_t tiles, void *stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    dim3 grid((tiles + kFusedTilesPerGroup - 1) / kFusedTilesPerGroup);
+    // the reduce kernel walks its workgroups' tiles rank by rank from
+    // DDL_TUNE_REDUCE_RANKS_MIN_P ranks on, tile by tile below (measured on
+    // MI355X, reduce kernel per launch: 40 ranks 122.9 against 134.4 us; 16
+    // ranks, the multi-ring ResNet-50 317.0 against 300.4 us and the
+    // binary16 torus 162.8 against 151.2 us)
+    const bool ranks = home && a.P >= tuning(DDL_TUNE_REDUCE_RANKS_MIN_P);
+    const uint32_t per = ranks ? (uint32_t)kReduceTiles : (uint32_t)kFusedTilesPerGroup;
+    dim3 grid((tiles + per - 1) / per);
     const bool grouped = a.group != a.P;
     if (dtype == DDL_F32) {
         if (grouped)
-            launch_e<F32, true>(grid, s, bufs, a, sgd, home);
+            launch_e<F32, true>(grid, s, bufs, a, sgd, home, ranks);
         else
-            launch_e<F32, false>(grid, s, bufs, a, sgd, home);
+            launch_e<F32, false>(grid, s, bufs, a, sgd, home, ranks);
     } else {
         if (grouped)
-            launch_e<F16, true>(grid, s, bufs, a, sgd, home);
+            launch_e<F16, true>(grid, s, bufs, a, sgd, home, ranks);
         else
-            launch_e<F16, false>(grid, s, bufs, a, sgd, home);
+            launch_e<F16, false>(grid, s, bufs, a, sgd, home, ranks);
     }
     return (int)hipGetLastError();
 }

@@ -149,16 +149,20 @@ def test_lars_events_two_calls_and_zero_layers(mode, passes):
 @pytest.fixture
 def restore_knobs():
     yield
-    for k in ("update_reps", "update_batch"):
+    for k in ("update_reps", "update_batch", "reduce_ranks_min_p"):
         ddl.set_tuning(k, -1)
 
 
 @pytest.mark.parametrize("knob,value", [("update_reps", g) for g in (0, 1, 3, 7, 100)] +
-                         [("update_batch", b) for b in (1, 2, 8)], ids=lambda v: str(v))
+                         [("update_batch", b) for b in (1, 2, 8)] +
+                         [("reduce_ranks_min_p", 0), ("reduce_ranks_min_p", 1000)],
+                         ids=lambda v: str(v))
 def test_lars_knobs(knob, value, restore_knobs):
     # the update's replica split and load batch change launch shapes only
     # (in the one-kernel form the update kernel reads them, in the two-kernel
-    # form the broadcast that steps the replicas reads the load batch)
+    # form the broadcast that steps the replicas reads the load batch); the
+    # reduce kernel's loop order changes the order of nothing that is summed
+    # (each tile's norm partial sums are formed as before)
     ddl.set_tuning(knob, value)
     for w in (CASES[2], CASES[5]):
         for passes in (1, 2):

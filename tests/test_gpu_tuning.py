@@ -2,7 +2,7 @@
 
 The knobs (ddl_set_tuning) change launch shapes and instruction order only:
 load batch, broadcast ranks per workgroup, non-temporal loads, tile
-anchoring.  Each setting is run on small cases with ragged chunks (ring,
+anchoring, the reduce kernel's loop order.  Each setting is run on small cases with ragged chunks (ring,
 multi-ring, torus; binary32 and binary16) and compared bit for bit with the
 oracle's walk.
 """
@@ -33,7 +33,10 @@ SETTINGS = ([("fused_batch", b) for b in (2, 4, 8)] +
             [("bcast_tiles", t) for t in (2, 5)] +
             [("bcast_xcd", 8), ("bcast_xcd", 3)] +
             [("reduce_nt_load", 0), ("fused_nt_load_max_p", 1000), ("anchor", 1),
-             ("anchor", 2)])
+             ("anchor", 2)] +
+            # the reduce kernel rank by rank at every rank count, and tile
+            # by tile at every rank count
+            [("reduce_ranks_min_p", 0), ("reduce_ranks_min_p", 1000)])
 
 
 @pytest.fixture(autouse=True)
