@@ -90,6 +90,12 @@ TRACE_FILES = {"fused2": ("fused_pass", ("fused_reduce_kernel", "bcast_kernel"))
                "steps": ("step_kernel", ("reduce_step_kernel", "gather_step_kernel"))}
 
 
+def lib_tuning(knob):
+    """A kernel knob's current value (ddl_get_tuning)."""
+    import sgd_gradient_all_amd as ddl
+    return ddl.get_tuning(knob)
+
+
 def committed_trace(form, workload, bytes_per_unit):
     """The rocprofv3 average kernel durations of this form and workload from
     the committed summary (profiles/<stem>_<workload>_trace.json), the
@@ -146,7 +152,12 @@ def roofline_of(args, w, passes, hbm_bytes, ms, ms_prof, kinds, per_step):
                              "max_launch_us": round(mx * 1e3, 2),
                              "algorithmic_bytes_per_launch": int(nb),
                              "GBps": round(nb / (tot / cnt * 1e-3) / 1e9, 1)}
-        kernel_name = "fused pass: fused_reduce_kernel + bcast_kernel"
+        # the reduce kernel walks its tiles rank by rank from 32 ranks on
+        # (fused_reduce_ranks_kernel), tile by tile below; both fill the
+        # fused_reduce_kernel entries here and in the committed summaries
+        red_name = ("fused_reduce_ranks_kernel" if w.P >= lib_tuning("reduce_ranks_min_p")
+                    else "fused_reduce_kernel")
+        kernel_name = f"fused pass: {red_name} + bcast_kernel"
     else:
         if args.mode == "fused":
             form, keys, kernel_name = "fused1", ("fused",), "fused_kernel"

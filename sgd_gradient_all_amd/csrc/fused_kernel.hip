@@ -543,14 +543,14 @@ __device__ __forceinline__ void reduce_tiles(const RankPtrs &bufs, const FusedAr
 
 template <class E, bool kGrouped, bool kNt>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4)))
-void reduce_ranks_kernel(RankPtrs bufs, FusedArgs a) {
+void fused_reduce_ranks_kernel(RankPtrs bufs, FusedArgs a) {
     reduce_tiles<E, kGrouped, kNt, false>(bufs, a);
 }
 
 // The same with the LARS step's per-tile partial sums of the layer norms.
 template <class E, bool kGrouped, bool kNt>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4)))
-void reduce_ranks_lars_kernel(RankPtrs bufs, FusedArgs a) {
+void fused_reduce_ranks_lars_kernel(RankPtrs bufs, FusedArgs a) {
     reduce_tiles<E, kGrouped, kNt, true>(bufs, a);
 }
 
@@ -804,10 +804,11 @@ template <class E, bool kGrouped, bool kNt>
 void launch_ranks(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a) {
     const dim3 block(kBlock);
     if (a.partial)
-        hipLaunchKernelGGL((reduce_ranks_lars_kernel<E, kGrouped, kNt>), grid, block, 0, s, bufs,
-                           a);
+        hipLaunchKernelGGL((fused_reduce_ranks_lars_kernel<E, kGrouped, kNt>), grid, block, 0, s,
+                           bufs, a);
     else
-        hipLaunchKernelGGL((reduce_ranks_kernel<E, kGrouped, kNt>), grid, block, 0, s, bufs, a);
+        hipLaunchKernelGGL((fused_reduce_ranks_kernel<E, kGrouped, kNt>), grid, block, 0, s, bufs,
+                           a);
 }
 
 template <class E, bool kGrouped>
