@@ -373,8 +373,36 @@ void fused_reduce_lars_kernel(RankPtrs bufs, FusedArgs a) {
 // 4 ranks (the form this replaces) 134.
 // ---------------------------------------------------------------------------
 
-// A 16-byte vector of zeros: the load of a tile with no whole vectors.
-__device__ __align__(16) const uint32_t kZeroVec[4] = {0, 0, 0, 0};
+// Zeros to load for a tile with no whole vectors (room for the widest
+// vector loaded, eight binary32 weights).
+__device__ __align__(32) const uint32_t kZeroVec[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+
+// M binary64 sums over the workgroup at once, each exactly as block_sum
+// forms it (the same butterfly within each wave, then the waves' sums in
+// wave order from zero), with one barrier.  The results are in v[] of
+// lane 0 of wave 0; every lane of the workgroup must call it.
+template <int M>
+__device__ __forceinline__ void block_sums(double (&v)[M], double (*lds)[M]) {
+#pragma unroll
+    for (int j = 0; j < M; ++j)
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1)
+            v[j] += __shfl_xor(v[j], o, 64);
+    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    if (lane == 0)
+#pragma unroll
+        for (int j = 0; j < M; ++j)
+            lds[wave][j] = v[j];
+    __syncthreads();
+    if (threadIdx.x == 0)
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+            double s = 0.0;
+            for (int i = 0; i < kBlock / 64; ++i)
+                s += lds[i][j];
+            v[j] = s;
+        }
+}
 
 template <class E, bool kGrouped, bool kNt, bool kLars>
 __device__ __forceinline__ void reduce_tiles(const RankPtrs &bufs, const FusedArgs &a) {
@@ -390,7 +418,7 @@ __device__ __forceinline__ void reduce_tiles(const RankPtrs &bufs, const FusedAr
     // rank addresses in chain order: one slot per distinct span of the
     // workgroup's tiles, and a slot whose every entry is the zero vector
     __shared__ uint64_t src[K + 1][DDL_MAX_RANKS];
-    __shared__ double lds_norm[2][kBlock / 64];
+    __shared__ double lds_norm[kLars ? kBlock / 64 : 1][2 * K];
     const int P = a.P;
     const uint32_t tid = threadIdx.x;
     const uint32_t first = a.tile_base + blockIdx.x * (uint32_t)K;
@@ -482,6 +510,16 @@ __device__ __forceinline__ void reduce_tiles(const RankPtrs &bufs, const FusedAr
             }
         }
     }
+    // kLars: replica 0's weights of the tiles' vectors, loaded before the
+    // results are stored (replicas never overlap the gradient buffers)
+    Wv wv[kLars ? K : 1];
+    if constexpr (kLars)
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            wv[k] = ld_stream<Wv, true>(
+                nvec[k] ? static_cast<const void *>(a.w0 + base[k] +
+                                                    (uint64_t)min(tid, nvec[k] - 1) * E::N)
+                        : static_cast<const void *>(kZeroVec));
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         V y = kGrouped ? c[k].acc : acc[k];
@@ -493,17 +531,22 @@ __device__ __forceinline__ void reduce_tiles(const RankPtrs &bufs, const FusedAr
             store_home<E, 1>(a.home, base[k] + (uint64_t)tid * E::N, one);
         }
     }
-    // each tile's last elements one by one, then (kLars) its norm partial
+    // each tile's last elements one by one, and (kLars) its norm partial
     // sums: each lane its vector, then its elements, then the workgroup
+    double sums[kLars ? 2 * K : 1];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        if ((uint32_t)k >= nt)
-            continue;
         double sw = 0.0, sy = 0.0;
-        if (kLars && tid < nvec[k]) {
-            const uint64_t e = base[k] + (uint64_t)tid * E::N;
-            add_squares<Wv>(E::widen(acc[k]), sy);
-            add_squares<Wv>(ld_stream<Wv, true>(a.w0 + e), sw);
+        if ((uint32_t)k >= nt) {
+            if constexpr (kLars)
+                sums[2 * k] = sums[2 * k + 1] = 0.0;
+            continue;
+        }
+        if constexpr (kLars) {
+            if (tid < nvec[k]) {
+                add_squares<Wv>(E::widen(acc[k]), sy);
+                add_squares<Wv>(wv[k], sw);
+            }
         }
         for (uint32_t m = nvec[k] * E::N + tid; m < cnt[k]; m += kBlock) {
             const uint64_t e = base[k] + m;
@@ -529,15 +572,20 @@ __device__ __forceinline__ void reduce_tiles(const RankPtrs &bufs, const FusedAr
                 sw += w * w;
             }
         }
-        if (kLars) {
-            const double tw = block_sum(sw, lds_norm[0]);
-            const double ty = block_sum(sy, lds_norm[1]);
-            if (tid == 0) {
-                a.partial[2 * (uint64_t)(first + k)] = tw;
-                a.partial[2 * (uint64_t)(first + k) + 1] = ty;
-            }
-            __syncthreads();  // lds_norm is read before the next tile's sums
+        if constexpr (kLars) {
+            sums[2 * k] = sw;
+            sums[2 * k + 1] = sy;
         }
+    }
+    if constexpr (kLars) {
+        block_sums<2 * K>(sums, lds_norm);
+        if (tid == 0)
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                if ((uint32_t)k < nt) {
+                    a.partial[2 * (uint64_t)(first + k)] = sums[2 * k];
+                    a.partial[2 * (uint64_t)(first + k) + 1] = sums[2 * k + 1];
+                }
     }
 }
 
