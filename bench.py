@@ -152,7 +152,7 @@ def roofline_of(args, w, passes, hbm_bytes, ms, ms_prof, kinds, per_step):
                              "max_launch_us": round(mx * 1e3, 2),
                              "algorithmic_bytes_per_launch": int(nb),
                              "GBps": round(nb / (tot / cnt * 1e-3) / 1e9, 1)}
-        # the reduce kernel walks its tiles rank by rank from 32 ranks on
+        # the reduce kernel walks its tiles rank by rank from 16 ranks on
         # (fused_reduce_ranks_kernel), tile by tile below; both fill the
         # fused_reduce_kernel entries here and in the committed summaries
         red_name = ("fused_reduce_ranks_kernel" if w.P >= lib_tuning("reduce_ranks_min_p")

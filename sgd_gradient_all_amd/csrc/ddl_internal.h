@@ -37,17 +37,28 @@ constexpr int fused_vecs_per_lane(int esz) {
 // Consecutive tiles one fused workgroup walks (address translations of the
 // P rank streams are reused from tile to tile).
 constexpr int kFusedTilesPerGroup = DDL_FUSED_TPW;
-// Consecutive tiles one workgroup of the two-kernel form's reduce kernel
-// takes, rank by rank, and the loads it issues at a time ahead of their
-// adds (fused_kernel.hip, reduce_tiles).
-#ifndef DDL_REDUCE_TILES
-#define DDL_REDUCE_TILES 8
+// The two-kernel form's reduce kernel rank by rank (fused_kernel.hip,
+// reduce_tiles): consecutive tiles one workgroup takes -- 8 from 32 ranks
+// on, 4 below -- and the loads it issues at a time ahead of their adds.
+// Measured on MI355X, paired against the reduce tile by tile: 40 ranks 8
+// tiles -3.3% per pass (4: -1.5%); 16 ranks 4 tiles, the binary16 torus
+// -1.6..-2.2% and the multi-ring ResNet-50 -0.7% (8 tiles: +1.5..+1.7% and
+// -0.4%); loads one or four at a time lose at both sizes.
+#ifndef DDL_REDUCE_TILES_WIDE
+#define DDL_REDUCE_TILES_WIDE 8
+#endif
+#ifndef DDL_REDUCE_TILES_NARROW
+#define DDL_REDUCE_TILES_NARROW 4
 #endif
 #ifndef DDL_REDUCE_ISSUE
 #define DDL_REDUCE_ISSUE 2
 #endif
-constexpr int kReduceTiles = DDL_REDUCE_TILES;
+constexpr int kReduceTilesWide = DDL_REDUCE_TILES_WIDE;
+constexpr int kReduceTilesNarrow = DDL_REDUCE_TILES_NARROW;
 constexpr int kReduceIssue = DDL_REDUCE_ISSUE;
+constexpr int reduce_tiles_per_group(int P) {
+    return P >= 32 ? kReduceTilesWide : kReduceTilesNarrow;
+}
 
 // Elements of one tile, by element size.
 // Step kernels take 1, 2 or 4 vectors per lane per tile; each plan picks

@@ -356,21 +356,21 @@ void fused_reduce_lars_kernel(RankPtrs bufs, FusedArgs a) {
 
 // ---------------------------------------------------------------------------
 // The reduce kernel of the two-kernel form, rank by rank.  Workgroup b takes
-// the kReduceTiles consecutive tiles from tile_base + b kReduceTiles on
-// (each of any span: a tile's chain and bounds are its own) and walks the
-// chain positions j = 0 .. P-1: at each, it loads the tiles' elements of
-// their chain entry j, one vector per lane per tile, and adds them to the
-// tiles' sums, kReduceIssue loads at a time ahead of their adds.  Every
-// element still takes its adds in chain order (groups of `group` entries,
-// then the group sums), so the results are the bits of the tile-by-tile
-// walk.  Lanes past a tile's whole vectors re-load its last one; a tile's
-// last elements (fewer than a vector, or all of a span whose offset is not
-// vector-aligned) are summed one by one after the walk.
-// Measured on MI355X as plain kernels over the pass's own geometry (40
-// ranks, 18.75 MB slices of 1.2 GB buffers, the ring's chunks with anchored
-// tiles, 8 tiles per workgroup): loads two at a time 123 us per bucket,
-// four at a time 128, all eight 131, one 169; tile by tile with batches of
-// 4 ranks (the form this replaces) 134.
+// the K consecutive tiles from tile_base + b K on (K = 8 from 32 ranks on,
+// 4 below; each tile of any span: a tile's chain and bounds are its own)
+// and walks the chain positions j = 0 .. P-1: at each, it loads the tiles'
+// elements of their chain entry j, one vector per lane per tile, and adds
+// them to the tiles' sums, kReduceIssue loads at a time ahead of their
+// adds.  Every element still takes its adds in chain order (groups of
+// `group` entries, then the group sums), so the results are the bits of
+// the tile-by-tile walk.  Lanes past a tile's whole vectors re-load its
+// last one; a tile's last elements (fewer than a vector, or all of a span
+// whose offset is not vector-aligned) are summed one by one after the
+// walk.  Measured on MI355X as plain kernels over the pass's own geometry
+// (40 ranks, 18.75 MB slices of 1.2 GB buffers, the ring's chunks with
+// anchored tiles, 8 tiles per workgroup): loads two at a time 123 us per
+// bucket, four at a time 128, all eight 131, one 169; tile by tile with
+// batches of 4 ranks 134.
 // ---------------------------------------------------------------------------
 
 // Zeros to load for a tile with no whole vectors (room for the widest
@@ -404,14 +404,13 @@ __device__ __forceinline__ void block_sums(double (&v)[M], double (*lds)[M]) {
         }
 }
 
-template <class E, bool kGrouped, bool kNt, bool kLars>
+template <class E, bool kGrouped, bool kNt, bool kLars, int K>
 __device__ __forceinline__ void reduce_tiles(const RankPtrs &bufs, const FusedArgs &a) {
     using T = typename E::T;
     using V = typename E::V;
     using Wv = typename E::W;
     static_assert(fused_vecs_per_lane(sizeof(T)) == 1, "one vector per lane per tile");
     constexpr uint64_t kTile = fused_tile_elems(sizeof(T));
-    constexpr int K = kReduceTiles;
     constexpr int kIssue = kReduceIssue;
     static_assert(K % kIssue == 0, "loads in whole groups");
     constexpr int kZeroSlot = K;
@@ -589,17 +588,17 @@ __device__ __forceinline__ void reduce_tiles(const RankPtrs &bufs, const FusedAr
     }
 }
 
-template <class E, bool kGrouped, bool kNt>
+template <class E, bool kGrouped, bool kNt, int K>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4)))
 void fused_reduce_ranks_kernel(RankPtrs bufs, FusedArgs a) {
-    reduce_tiles<E, kGrouped, kNt, false>(bufs, a);
+    reduce_tiles<E, kGrouped, kNt, false, K>(bufs, a);
 }
 
 // The same with the LARS step's per-tile partial sums of the layer norms.
-template <class E, bool kGrouped, bool kNt>
+template <class E, bool kGrouped, bool kNt, int K>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4)))
 void fused_reduce_ranks_lars_kernel(RankPtrs bufs, FusedArgs a) {
-    reduce_tiles<E, kGrouped, kNt, true>(bufs, a);
+    reduce_tiles<E, kGrouped, kNt, true, K>(bufs, a);
 }
 
 // ---------------------------------------------------------------------------
@@ -848,15 +847,23 @@ void launch_nt(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &
 
 // The rank-by-rank reduce kernel (with the LARS partial sums when
 // a.partial is set).
-template <class E, bool kGrouped, bool kNt>
-void launch_ranks(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a) {
+template <class E, bool kGrouped, bool kNt, int K>
+void launch_ranks_k(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a) {
     const dim3 block(kBlock);
     if (a.partial)
-        hipLaunchKernelGGL((fused_reduce_ranks_lars_kernel<E, kGrouped, kNt>), grid, block, 0, s,
-                           bufs, a);
+        hipLaunchKernelGGL((fused_reduce_ranks_lars_kernel<E, kGrouped, kNt, K>), grid, block, 0,
+                           s, bufs, a);
     else
-        hipLaunchKernelGGL((fused_reduce_ranks_kernel<E, kGrouped, kNt>), grid, block, 0, s, bufs,
-                           a);
+        hipLaunchKernelGGL((fused_reduce_ranks_kernel<E, kGrouped, kNt, K>), grid, block, 0, s,
+                           bufs, a);
+}
+
+template <class E, bool kGrouped, bool kNt>
+void launch_ranks(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a) {
+    if (reduce_tiles_per_group(a.P) == kReduceTilesWide)
+        launch_ranks_k<E, kGrouped, kNt, kReduceTilesWide>(grid, s, bufs, a);
+    else
+        launch_ranks_k<E, kGrouped, kNt, kReduceTilesNarrow>(grid, s, bufs, a);
 }
 
 template <class E, bool kGrouped>
@@ -897,12 +904,10 @@ int launch_fused(int dtype, const RankPtrs &bufs, const FusedArgs &a, const SgdA
                  bool home, uint32_t tiles, void *stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     // the reduce kernel walks its workgroups' tiles rank by rank from
-    // DDL_TUNE_REDUCE_RANKS_MIN_P ranks on, tile by tile below (measured on
-    // MI355X, reduce kernel per launch: 40 ranks 122.9 against 134.4 us; 16
-    // ranks, the multi-ring ResNet-50 317.0 against 300.4 us and the
-    // binary16 torus 162.8 against 151.2 us)
+    // DDL_TUNE_REDUCE_RANKS_MIN_P ranks on, tile by tile below
     const bool ranks = home && a.P >= tuning(DDL_TUNE_REDUCE_RANKS_MIN_P);
-    const uint32_t per = ranks ? (uint32_t)kReduceTiles : (uint32_t)kFusedTilesPerGroup;
+    const uint32_t per =
+        ranks ? (uint32_t)reduce_tiles_per_group(a.P) : (uint32_t)kFusedTilesPerGroup;
     dim3 grid((tiles + per - 1) / per);
     const bool grouped = a.group != a.P;
     if (dtype == DDL_F32) {

@@ -54,7 +54,7 @@ constexpr int kTuneDefault[] = {
     0,   // DDL_TUNE_BCAST_XCD: off
     2,   // DDL_TUNE_UPDATE_REPS
     4,   // DDL_TUNE_UPDATE_BATCH
-    32,  // DDL_TUNE_REDUCE_RANKS_MIN_P
+    16,  // DDL_TUNE_REDUCE_RANKS_MIN_P
 };
 static_assert(sizeof(kTuneDefault) / sizeof(kTuneDefault[0]) == DDL_TUNE_COUNT,
               "one default per knob");
