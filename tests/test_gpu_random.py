@@ -87,8 +87,32 @@ NWIDE_CASES = int(os.environ.get("DDL_RANDOM_WIDE_CASES", "4"))
                          [("wide", s) for s in range(NWIDE_CASES)], ids=str)
 def test_random_configuration(seed):
     kind_, seed = seed
-    c = draw(seed, wide=kind_ == "wide")
-    say(f"case random {seed}: P={c['P']} {c['dtype']} {c['op']} {c['kind']} k={c['k']} "
+    run_drawn(draw(seed, wide=kind_ == "wide"), f"random {seed}")
+
+
+NRANKS_CASES = int(os.environ.get("DDL_RANDOM_RANKS_CASES", "16"))
+
+
+@pytest.mark.parametrize("seed", range(NRANKS_CASES))
+def test_random_rank_by_rank_reduce(seed):
+    """The two-kernel pass with its reduce kernel rank by rank at every rank
+    count (reduce_ranks_min_p = 0: four tiles per workgroup under 32 ranks,
+    eight from 32 on), on drawn configurations -- ragged, empty and
+    misaligned buckets, rings, multi-rings and tori, both element types --
+    every rank bit for bit against the oracle."""
+    c = draw(300 + seed, wide=seed % 4 == 3)
+    c["form"] = "fused2"
+    ddl.set_tuning("reduce_ranks_min_p", 0)
+    try:
+        run_drawn(c, f"random rank-by-rank {seed}")
+    finally:
+        ddl.set_tuning("reduce_ranks_min_p", -1)
+
+
+def run_drawn(c, tag):
+    """One all-reduce of a drawn configuration against the oracle."""
+    seed = c["seed"]
+    say(f"case {tag}: P={c['P']} {c['dtype']} {c['op']} {c['kind']} k={c['k']} "
         f"grid={c['rows']}x{c['cols']} n={c['n']} buckets={len(c['buckets'])} "
         f"form={c['form']}/{c['step_form']} events={c['ev_of'] is not None} "
         f"coalesce={c['coalesce']} "
