@@ -432,7 +432,12 @@ typedef enum {
      * tile by tile (one tile per workgroup, DDL_TUNE_REDUCE_BATCH loads at a
      * time) below; default 16 */
     DDL_TUNE_REDUCE_RANKS_MIN_P = 10,
-    DDL_TUNE_COUNT = 11
+    /* two-kernel form: the broadcast waits for each rank's stores to
+     * complete before storing to the next rank (and, in the broadcast that
+     * steps weight replicas, for each batch of replicas): 0 never, 1
+     * always, 2 (default) for binary32 */
+    DDL_TUNE_BCAST_STORE_WAIT = 11,
+    DDL_TUNE_COUNT = 12
 } ddl_tune_knob;
 int ddl_set_tuning(int knob, int value);
 int ddl_get_tuning(int knob, int *value);

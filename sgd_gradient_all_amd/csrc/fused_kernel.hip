@@ -613,7 +613,11 @@ void fused_reduce_ranks_lars_kernel(RankPtrs bufs, FusedArgs a) {
 // tile_base) to ranks r0 .. r1.  kUpd (table mode, the LARS step): with the
 // reduced values in hand, also step the weight replicas of rank group grp
 // (see BcastArgs) by the tile's bucket's rate.
-template <class E, bool kUpd, int kRB = 1>
+// Wait until this wave's memory operations in flight, its stores included,
+// have completed.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <class E, bool kUpd, int kRB = 1, bool kWait = false>
 __device__ __forceinline__ void bcast_tile(const RankPtrs &bufs, const BcastArgs &a, uint64_t q,
                                            int r0, int r1, const RankPtrs *w, uint32_t grp) {
     using T = typename E::T;
@@ -659,10 +663,13 @@ __device__ __forceinline__ void bcast_tile(const RankPtrs &bufs, const BcastArgs
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 v[u] = *reinterpret_cast<const V DDL_GLOBAL *>(home + e + u * kStride);
-            for (int r = r0; r < r1; ++r)
+            for (int r = r0; r < r1; ++r) {
 #pragma unroll
                 for (int u = 0; u < U; ++u)
                     st_stream<V>(static_cast<T *>(bufs.p[r]) + e + u * kStride, v[u]);
+                if (kWait)
+                    wait_stores();
+            }
             if (kUpd) {
                 // replicas in batches of kRB: every load of a batch is issued
                 // before its stores (a wave keeps kRB requests in flight)
@@ -690,6 +697,8 @@ __device__ __forceinline__ void bcast_tile(const RankPtrs &bufs, const BcastArgs
                                 st_stream<Wv>(wr + u * kStride,
                                               sgd_step<Wv>(x[k][u], E::widen(v[u]), rate));
                         }
+                    if (kWait)
+                        wait_stores();
                 }
             }
         } else {
@@ -726,7 +735,7 @@ __device__ __forceinline__ void bcast_tile(const RankPtrs &bufs, const BcastArgs
 // dealt so that all rank groups of a tile block run on one accelerator die
 // (workgroup b runs on die b % nxcd), which then fetches the block's values
 // into its L2 once instead of once per die.
-template <class E, bool kUpd, int kRB = 1>
+template <class E, bool kUpd, int kRB = 1, bool kWait = false>
 __device__ __forceinline__ void bcast_body(const RankPtrs &bufs, const BcastArgs &a,
                                            const RankPtrs *w) {
     const uint32_t ng = (uint32_t)a.ngroups;
@@ -743,22 +752,22 @@ __device__ __forceinline__ void bcast_body(const RankPtrs &bufs, const BcastArgs
     const int r1 = min(a.P, r0 + a.ranks_per_group);
     const uint64_t q0 = (uint64_t)qb * (uint64_t)a.tiles_per_group;
     for (int k = 0; k < a.tiles_per_group; ++k)
-        bcast_tile<E, kUpd, kRB>(bufs, a, q0 + (uint64_t)k, r0, r1, w, grp);
+        bcast_tile<E, kUpd, kRB, kWait>(bufs, a, q0 + (uint64_t)k, r0, r1, w, grp);
 }
 
-template <class E>
+template <class E, bool kWait>
 __global__ __launch_bounds__(kBlock) void bcast_kernel(RankPtrs bufs, BcastArgs a) {
-    bcast_body<E, false>(bufs, a, nullptr);
+    bcast_body<E, false, 1, kWait>(bufs, a, nullptr);
 }
 
 // The broadcast of the two-kernel form with the update of the weight
 // replicas w riding on it: the LARS step (each bucket's rate) or the SGD
 // step with kept gradients (the constant rate lr), kRB replicas' loads ahead
 // of their stores (knob DDL_TUNE_UPDATE_BATCH, as the update kernel).
-template <class E, int kRB>
+template <class E, int kRB, bool kWait>
 __global__ __launch_bounds__(kBlock) void bcast_update_kernel(RankPtrs bufs, RankPtrs w,
                                                               BcastArgs a) {
-    bcast_body<E, true, kRB>(bufs, a, &w);
+    bcast_body<E, true, kRB, kWait>(bufs, a, &w);
 }
 
 // ---------------------------------------------------------------------------
@@ -956,6 +965,42 @@ uint64_t bcast_blocks(int dtype, const BcastArgs &a, bool *bad) {
     return *bad ? 0 : blocks;
 }
 
+template <class E, bool kWait>
+void launch_bcast_update_t(int batch, dim3 grid, hipStream_t s, const RankPtrs &bufs,
+                           const RankPtrs &w, const BcastArgs &a) {
+    const dim3 block(kBlock);
+    if (batch <= 1)
+        hipLaunchKernelGGL((bcast_update_kernel<E, 1, kWait>), grid, block, 0, s, bufs, w, a);
+    else if (batch == 2)
+        hipLaunchKernelGGL((bcast_update_kernel<E, 2, kWait>), grid, block, 0, s, bufs, w, a);
+    else
+        hipLaunchKernelGGL((bcast_update_kernel<E, 4, kWait>), grid, block, 0, s, bufs, w, a);
+}
+
+template <bool kWait>
+void launch_bcast_update_e(int dtype, int batch, dim3 grid, hipStream_t s, const RankPtrs &bufs,
+                           const RankPtrs &w, const BcastArgs &a) {
+    if (dtype == DDL_F32)
+        launch_bcast_update_t<F32, kWait>(batch, grid, s, bufs, w, a);
+    else
+        launch_bcast_update_t<F16, kWait>(batch, grid, s, bufs, w, a);
+}
+
+// Whether the broadcast waits for each rank's stores to complete before
+// storing to the next (DDL_TUNE_BCAST_STORE_WAIT: 0 never, 1 always,
+// otherwise for binary32).  A wave that leaves right after issuing its
+// stores lets the next workgroup's pile up behind them.  Measured on
+// MI355X, paired in one process (two runs): the ResNet-50 multi-ring -2.1..
+// -2.6% per pass, the 40-rank step -0.55% (all-reduce, SGD and LARS alike),
+// a 16-rank ring -0.1%; binary16 within +-1% either way (the torus +1.6,
+// +0.7, -0.4%, the multi-ring +1.0%).  In a plain probe kernel (one 4 KB
+// tile to 2 ranks per workgroup) the wait took the broadcast from 152 to
+// 120 us per 18.75 MB bucket.
+bool bcast_store_wait(int dtype) {
+    const int k = tuning(DDL_TUNE_BCAST_STORE_WAIT);
+    return k == 0 ? false : k == 1 ? true : dtype == DDL_F32;
+}
+
 }  // namespace
 
 int launch_bcast_update(int dtype, const RankPtrs &bufs, const RankPtrs &w, const BcastArgs &a,
@@ -967,23 +1012,12 @@ int launch_bcast_update(int dtype, const RankPtrs &bufs, const RankPtrs &w, cons
         return (int)hipErrorInvalidValue;
     if (blocks == 0)
         return (int)hipSuccess;
-    const dim3 grid((uint32_t)blocks), block(kBlock);
+    const dim3 grid((uint32_t)blocks);
     const int batch = tuning(DDL_TUNE_UPDATE_BATCH);
-    if (dtype == DDL_F32) {
-        if (batch <= 1)
-            hipLaunchKernelGGL((bcast_update_kernel<F32, 1>), grid, block, 0, s, bufs, w, a);
-        else if (batch == 2)
-            hipLaunchKernelGGL((bcast_update_kernel<F32, 2>), grid, block, 0, s, bufs, w, a);
-        else
-            hipLaunchKernelGGL((bcast_update_kernel<F32, 4>), grid, block, 0, s, bufs, w, a);
-    } else {
-        if (batch <= 1)
-            hipLaunchKernelGGL((bcast_update_kernel<F16, 1>), grid, block, 0, s, bufs, w, a);
-        else if (batch == 2)
-            hipLaunchKernelGGL((bcast_update_kernel<F16, 2>), grid, block, 0, s, bufs, w, a);
-        else
-            hipLaunchKernelGGL((bcast_update_kernel<F16, 4>), grid, block, 0, s, bufs, w, a);
-    }
+    if (bcast_store_wait(dtype))
+        launch_bcast_update_e<true>(dtype, batch, grid, s, bufs, w, a);
+    else
+        launch_bcast_update_e<false>(dtype, batch, grid, s, bufs, w, a);
     return (int)hipGetLastError();
 }
 
@@ -1004,10 +1038,18 @@ int launch_bcast(int dtype, const RankPtrs &bufs, const BcastArgs &a, void *stre
     if (blocks == 0)
         return (int)hipSuccess;
     const dim3 grid((uint32_t)blocks), block(kBlock);
-    if (dtype == DDL_F32)
-        hipLaunchKernelGGL((bcast_kernel<F32>), grid, block, 0, s, bufs, a);
-    else
-        hipLaunchKernelGGL((bcast_kernel<F16>), grid, block, 0, s, bufs, a);
+    const bool wait = bcast_store_wait(dtype);
+    if (dtype == DDL_F32) {
+        if (wait)
+            hipLaunchKernelGGL((bcast_kernel<F32, true>), grid, block, 0, s, bufs, a);
+        else
+            hipLaunchKernelGGL((bcast_kernel<F32, false>), grid, block, 0, s, bufs, a);
+    } else {
+        if (wait)
+            hipLaunchKernelGGL((bcast_kernel<F16, true>), grid, block, 0, s, bufs, a);
+        else
+            hipLaunchKernelGGL((bcast_kernel<F16, false>), grid, block, 0, s, bufs, a);
+    }
     return (int)hipGetLastError();
 }
 

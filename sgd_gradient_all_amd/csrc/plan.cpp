@@ -55,6 +55,7 @@ constexpr int kTuneDefault[] = {
     2,   // DDL_TUNE_UPDATE_REPS
     4,   // DDL_TUNE_UPDATE_BATCH
     16,  // DDL_TUNE_REDUCE_RANKS_MIN_P
+    2,   // DDL_TUNE_BCAST_STORE_WAIT: binary32
 };
 static_assert(sizeof(kTuneDefault) / sizeof(kTuneDefault[0]) == DDL_TUNE_COUNT,
               "one default per knob");

@@ -149,13 +149,14 @@ def test_lars_events_two_calls_and_zero_layers(mode, passes):
 @pytest.fixture
 def restore_knobs():
     yield
-    for k in ("update_reps", "update_batch", "reduce_ranks_min_p"):
+    for k in ("update_reps", "update_batch", "reduce_ranks_min_p", "bcast_store_wait"):
         ddl.set_tuning(k, -1)
 
 
 @pytest.mark.parametrize("knob,value", [("update_reps", g) for g in (0, 1, 3, 7, 100)] +
                          [("update_batch", b) for b in (1, 2, 8)] +
-                         [("reduce_ranks_min_p", 0), ("reduce_ranks_min_p", 1000)],
+                         [("reduce_ranks_min_p", 0), ("reduce_ranks_min_p", 1000)] +
+                         [("bcast_store_wait", 0), ("bcast_store_wait", 1)],
                          ids=lambda v: str(v))
 def test_lars_knobs(knob, value, restore_knobs):
     # the update's replica split and load batch change launch shapes only
