@@ -437,7 +437,12 @@ typedef enum {
      * steps weight replicas, for each batch of replicas): 0 never, 1
      * always, 2 (default) for binary32 */
     DDL_TUNE_BCAST_STORE_WAIT = 11,
-    DDL_TUNE_COUNT = 12
+    /* one-kernel form: each workgroup waits for each rank's stores to
+     * complete before storing to the next rank: 0 never, 1 always, 2
+     * (default) for binary32 groups of at least 2^27 elements per rank from
+     * 8 ranks on */
+    DDL_TUNE_FUSED_STORE_WAIT = 12,
+    DDL_TUNE_COUNT = 13
 } ddl_tune_knob;
 int ddl_set_tuning(int knob, int value);
 int ddl_get_tuning(int knob, int *value);

@@ -247,7 +247,7 @@ def ddl_cache_count():
 TUNE = {"bcast_ranks": 0, "reduce_nt_load": 1, "fused_nt_load_max_p": 2, "anchor": 3,
         "fused_batch": 4, "reduce_batch": 5, "bcast_tiles": 6, "bcast_xcd": 7,
         "update_reps": 8, "update_batch": 9, "reduce_ranks_min_p": 10,
-        "bcast_store_wait": 11}
+        "bcast_store_wait": 11, "fused_store_wait": 12}
 
 
 def set_tuning(knob, value):

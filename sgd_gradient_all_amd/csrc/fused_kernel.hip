@@ -71,6 +71,10 @@ __device__ __forceinline__ V ld_global(uint64_t addr) {
         return __builtin_nontemporal_load(p);
     return *p;
 }
+// Wait until this wave's memory operations in flight, its stores included,
+// have completed.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 template <class V>
 __device__ __forceinline__ void st_stream(void *p, V v) {
 #if DDL_NT_STORE
@@ -145,15 +149,18 @@ __device__ __forceinline__ void fused_vecs(const uint64_t *sp, int P, int group,
         out[u] = kGrouped ? c[u].acc : acc[u];
 }
 
-template <class E, int U>
+template <class E, int U, bool kWait = false>
 __device__ __forceinline__ void store_all(const RankPtrs &bufs, int P, uint64_t e,
                                           const typename E::V (&v)[U]) {
     using T = typename E::T;
     constexpr uint64_t kStride = (uint64_t)kBlock * E::N;
-    for (int r = 0; r < P; ++r)
+    for (int r = 0; r < P; ++r) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
             st_stream<typename E::V>(static_cast<T *>(bufs.p[r]) + e + u * kStride, v[u]);
+        if (kWait)
+            wait_stores();
+    }
 }
 
 // The SGD step of every weight replica on the reduced vectors v[0..U) of
@@ -194,7 +201,8 @@ __device__ __forceinline__ void store_home(void *home, uint64_t e,
 // result y and of replica 0's weights w0, each lane in element order, then
 // over the workgroup (block_sum), written to a.partial[2t] (w0) and
 // a.partial[2t + 1] (y).
-template <class E, bool kGrouped, bool kNt, bool kSgd, bool kHome, int kB, bool kLars = false>
+template <class E, bool kGrouped, bool kNt, bool kSgd, bool kHome, int kB, bool kLars = false,
+          bool kWait = false>
 __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs &a,
                                            const SgdArgs *g) {
     using T = typename E::T;
@@ -241,7 +249,7 @@ __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs
                 if (kHome)
                     store_home<E, U>(a.home, e, acc);
                 else if (!kSgd || g->keep_grads)
-                    store_all<E, U>(bufs, P, e, acc);
+                    store_all<E, U, kWait>(bufs, P, e, acc);
                 if (kSgd)
                     sgd_all<E, kNt, U>(g, e, acc);
                 if (kLars) {
@@ -265,7 +273,7 @@ __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs
                     if (kHome)
                         store_home<E, 1>(a.home, e, acc);
                     else if (!kSgd || g->keep_grads)
-                        store_all<E, 1>(bufs, P, e, acc);
+                        store_all<E, 1, kWait>(bufs, P, e, acc);
                     if (kSgd)
                         sgd_all<E, kNt, 1>(g, e, acc);
                     if (kLars) {
@@ -325,10 +333,10 @@ __device__ __forceinline__ void fused_body(const RankPtrs &bufs, const FusedArgs
                                            ? DDL_FUSED_WAVES_1                        \
                                            : DDL_FUSED_WAVES_2)))
 
-template <class E, bool kGrouped, bool kNt, int kB>
+template <class E, bool kGrouped, bool kNt, int kB, bool kWait>
 __global__ __launch_bounds__(kBlock) DDL_FUSED_OCCUPANCY
 void fused_kernel(RankPtrs bufs, FusedArgs a) {
-    fused_body<E, kGrouped, kNt, false, false, kB>(bufs, a, nullptr);
+    fused_body<E, kGrouped, kNt, false, false, kB, false, kWait>(bufs, a, nullptr);
 }
 
 template <class E, bool kGrouped, bool kNt, int kB>
@@ -613,10 +621,6 @@ void fused_reduce_ranks_lars_kernel(RankPtrs bufs, FusedArgs a) {
 // tile_base) to ranks r0 .. r1.  kUpd (table mode, the LARS step): with the
 // reduced values in hand, also step the weight replicas of rank group grp
 // (see BcastArgs) by the tile's bucket's rate.
-// Wait until this wave's memory operations in flight, its stores included,
-// have completed.
-__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 template <class E, bool kUpd, int kRB = 1, bool kWait = false>
 __device__ __forceinline__ void bcast_tile(const RankPtrs &bufs, const BcastArgs &a, uint64_t q,
                                            int r0, int r1, const RankPtrs *w, uint32_t grp) {
@@ -826,6 +830,21 @@ namespace {
 
 // One-kernel pass (home false; with the SGD step when sgd is set) or reduce
 // kernel (home true) with kB loads per batch.
+// Whether the one-kernel pass waits for each rank's stores to complete
+// before storing to the next (DDL_TUNE_FUSED_STORE_WAIT: 0 never, 1 always,
+// otherwise for binary32 groups of at least 2^27 elements per rank from 8
+// ranks on).  Measured on MI355X, paired in one process: 8 ranks 300M
+// elements -1.7..-3.3% (a 4-ring multi-ring -4.7%), 200M -1.7%, 128M
+// -0.3%; 16 ranks 150M -0.3%; 4 ranks +2.0..+2.7%; smaller groups -0.1..
+// +4.4% (8-40 ranks, 8M-64M elements); binary16 +0.7% at 8 ranks 300M.
+bool fused_store_wait(const FusedArgs &a, size_t esize) {
+    const int k = tuning(DDL_TUNE_FUSED_STORE_WAIT);
+    if (k == 0 || k == 1)
+        return k == 1;
+    const uint64_t elems = (uint64_t)(a.tile_end - a.tile_base) * fused_tile_elems(esize);
+    return esize == 4 && a.P >= 8 && elems >= (1ull << 27);
+}
+
 template <class E, bool kGrouped, bool kNt, int kB>
 void launch_b(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a,
               const SgdArgs *sgd, bool home) {
@@ -839,8 +858,12 @@ void launch_b(dim3 grid, hipStream_t s, const RankPtrs &bufs, const FusedArgs &a
     else if (sgd)
         hipLaunchKernelGGL((fused_sgd_kernel<E, kGrouped, kNt, kB>), grid, block, 0, s, bufs, a,
                            *sgd);
+    else if (fused_store_wait(a, sizeof(typename E::T)))
+        hipLaunchKernelGGL((fused_kernel<E, kGrouped, kNt, kB, true>), grid, block, 0, s, bufs,
+                           a);
     else
-        hipLaunchKernelGGL((fused_kernel<E, kGrouped, kNt, kB>), grid, block, 0, s, bufs, a);
+        hipLaunchKernelGGL((fused_kernel<E, kGrouped, kNt, kB, false>), grid, block, 0, s, bufs,
+                           a);
 }
 
 template <class E, bool kGrouped, bool kNt>

@@ -56,6 +56,7 @@ constexpr int kTuneDefault[] = {
     4,   // DDL_TUNE_UPDATE_BATCH
     16,  // DDL_TUNE_REDUCE_RANKS_MIN_P
     2,   // DDL_TUNE_BCAST_STORE_WAIT: binary32
+    2,   // DDL_TUNE_FUSED_STORE_WAIT: large binary32 groups, 8 ranks on
 };
 static_assert(sizeof(kTuneDefault) / sizeof(kTuneDefault[0]) == DDL_TUNE_COUNT,
               "one default per knob");

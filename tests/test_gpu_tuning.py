@@ -38,7 +38,8 @@ SETTINGS = ([("fused_batch", b) for b in (2, 4, 8)] +
             # by tile at every rank count
             [("reduce_ranks_min_p", 0), ("reduce_ranks_min_p", 1000)] +
             # the broadcast's store wait off and on for both element types
-            [("bcast_store_wait", 0), ("bcast_store_wait", 1)])
+            [("bcast_store_wait", 0), ("bcast_store_wait", 1)] +
+            [("fused_store_wait", 0), ("fused_store_wait", 1)])
 
 
 @pytest.fixture(autouse=True)

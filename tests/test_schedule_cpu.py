@@ -410,7 +410,8 @@ def test_fused_pass_form_setting():
 def test_tuning_knobs():
     defaults = {"bcast_ranks": 0, "reduce_nt_load": 1, "fused_nt_load_max_p": 24, "anchor": 0,
                 "fused_batch": 1, "reduce_batch": 4, "bcast_tiles": 1, "bcast_xcd": 0,
-                "update_reps": 2, "update_batch": 4, "reduce_ranks_min_p": 16, "bcast_store_wait": 2}
+                "update_reps": 2, "update_batch": 4, "reduce_ranks_min_p": 16, "bcast_store_wait": 2,
+                "fused_store_wait": 2}
     for k, v in defaults.items():
         assert ddl.get_tuning(k) == v, k
     for k in defaults:
