@@ -9,16 +9,23 @@
 // The pass runs in one of two forms:
 //  - one kernel (fused_kernel): each workgroup reads its tile from all P
 //    ranks and writes the result to all P ranks;
-//  - two kernels over the same tiles: fused_reduce_kernel reads all P ranks
+//  - two kernels over the same tiles: the reduce kernel reads all P ranks
 //    and writes the result to rank 0 only (or, for an SGD step that leaves
-//    the gradients as they were, to a scratch buffer), through the cache;
+//    the gradients as they were, to a scratch buffer), through the cache --
+//    rank by rank over 4 or 8 tiles per workgroup from 16 ranks on
+//    (fused_reduce_ranks_kernel), tile by tile below (fused_reduce_kernel);
 //    then bcast_kernel copies rank 0's result, still cache-resident, to
-//    ranks 1..P-1.  HBM then sees a read phase and a write phase instead of reads
-//    and writes interleaved.  Measured on MI355X in paired runs: 40 ranks
-//    binary32 +5..+18% (the spread is the physical placement of the
+//    ranks 1..P-1.  HBM then sees a read phase and a write phase instead of
+//    reads and writes interleaved.  Measured on MI355X in paired runs: 40
+//    ranks binary32 +5..+18% (the spread is the physical placement of the
 //    buffers, to which the two-kernel form is far less sensitive), 16 ranks
 //    binary16 +5%, 16 ranks binary32 -3..+7%, 8 ranks -3%.  Plans choose
 //    the form (plan.cpp, fused_passes).
+//
+// Writes: stores are non-temporal, and a wave that stores to several ranks
+// may wait for each rank's stores to complete before the next (the
+// broadcast in binary32, the one-kernel pass in large binary32 groups; see
+// bcast_store_wait, fused_store_wait).
 #include "device_common.h"
 
 namespace ddl {
@@ -36,13 +43,14 @@ using namespace dev;
 #ifndef DDL_NT_STORE
 #define DDL_NT_STORE 1
 #endif
-// Loads a lane issues ahead of their adds (kB, 1, 2, 4 or 8; knobs
-// DDL_TUNE_FUSED_BATCH and DDL_TUNE_REDUCE_BATCH).  The adds stay in chain
-// order; a batch only lets a wave keep kB requests in flight instead of
-// waiting for each load before issuing the next.  Measured on MI355X: the
-// read-only reduce kernel gains from 4 (+4.6% at 40 ranks, +2% at 16); the
-// one-kernel pass, whose writes share HBM with the reads, is best with 1
-// at 8 ranks (2: -1%, 4: -3.5%).
+// Loads a lane issues ahead of their adds in the tile-by-tile walks (kB,
+// 1, 2, 4 or 8; knobs DDL_TUNE_FUSED_BATCH and DDL_TUNE_REDUCE_BATCH).
+// The adds stay in chain order; a batch only lets a wave keep kB requests
+// in flight instead of waiting for each load before issuing the next.
+// Measured on MI355X: the read-only reduce kernel tile by tile gains from 4
+// (+4.6% at 40 ranks, +2% at 16); the one-kernel pass, whose writes share
+// HBM with the reads, is best with 1 at 8 ranks (2: -1%, 4: -3.5%).  The
+// rank-by-rank reduce issues its loads two at a time (kReduceIssue).
 // Waves per SIMD the register allocation must allow: 8 for one vector per
 // lane (no spills at 56 VGPRs), 4 for two.
 #ifndef DDL_FUSED_WAVES_1
