@@ -427,7 +427,7 @@ typedef enum {
      * as 4) */
     DDL_TUNE_UPDATE_BATCH = 9,
     /* two-kernel form: the reduce kernel walks the tiles of each workgroup
-     * rank by rank (eight tiles per workgroup from 32 ranks on, four below;
+     * rank by rank (six tiles per workgroup from 32 ranks on, four below;
      * the loads of one rank two at a time) from this many ranks on, and
      * tile by tile (one tile per workgroup, DDL_TUNE_REDUCE_BATCH loads at a
      * time) below; default 16 */

@@ -38,14 +38,16 @@ constexpr int fused_vecs_per_lane(int esz) {
 // P rank streams are reused from tile to tile).
 constexpr int kFusedTilesPerGroup = DDL_FUSED_TPW;
 // The two-kernel form's reduce kernel rank by rank (fused_kernel.hip,
-// reduce_tiles): consecutive tiles one workgroup takes -- 8 from 32 ranks
+// reduce_tiles): consecutive tiles one workgroup takes -- 6 from 32 ranks
 // on, 4 below -- and the loads it issues at a time ahead of their adds.
 // Measured on MI355X, paired against the reduce tile by tile: 40 ranks 8
-// tiles -3.3% per pass (4: -1.5%); 16 ranks 4 tiles, the binary16 torus
-// -1.6..-2.2% and the multi-ring ResNet-50 -0.7% (8 tiles: +1.5..+1.7% and
-// -0.4%); loads one or four at a time lose at both sizes.
+// tiles -3.3% per pass (4: -1.5%), and 6 tiles a further -1.0..-1.5% per
+// step against 8 (10 or 12: +7%, +15%); 16 ranks 4 tiles, the binary16
+// torus -1.6..-2.2% and the multi-ring ResNet-50 -0.7% (6 tiles: the
+// same within 1%; 8: +1.5..+3%); loads one or four at a time lose at both
+// sizes.  The tile count must be a multiple of the load group.
 #ifndef DDL_REDUCE_TILES_WIDE
-#define DDL_REDUCE_TILES_WIDE 8
+#define DDL_REDUCE_TILES_WIDE 6
 #endif
 #ifndef DDL_REDUCE_TILES_NARROW
 #define DDL_REDUCE_TILES_NARROW 4
