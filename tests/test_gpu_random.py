@@ -97,7 +97,7 @@ NRANKS_CASES = int(os.environ.get("DDL_RANDOM_RANKS_CASES", "16"))
 def test_random_rank_by_rank_reduce(seed):
     """The two-kernel pass with its reduce kernel rank by rank at every rank
     count (reduce_ranks_min_p = 0: four tiles per workgroup under 32 ranks,
-    eight from 32 on), on drawn configurations -- ragged, empty and
+    six from 32 on), on drawn configurations -- ragged, empty and
     misaligned buckets, rings, multi-rings and tori, both element types --
     every rank bit for bit against the oracle."""
     c = draw(300 + seed, wide=seed % 4 == 3)
