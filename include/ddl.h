@@ -247,7 +247,7 @@ int ddl_plan_execute_lars(ddl_plan plan, void *const *bufs, void *const *weights
  * DDL_E_SCRATCH, before anything else, for a plan whose tiles or buckets
  * exceed the scratch; DDL_E_NOMEM if the plan has already run on eight
  * other streams and this one is new (its completion tracking would need a
- * new event).  The scratch keeps the last call's contents and every call on
+ * new event; reported before anything is enqueued).  The scratch keeps the last call's contents and every call on
  * a device shares it: two such calls that may run at the same time on one
  * device (any plans, different streams, no ordering between them) race.
  * Other arguments, errors and the asynchrony are those of

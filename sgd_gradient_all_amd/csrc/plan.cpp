@@ -915,6 +915,12 @@ int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stre
     for (int b = 0; ready && b < nb; ++b)
         any_event = any_event || ready[b] != nullptr;
     hipStream_t ls = any_event ? p->side[0] : cs;
+    // the event that will mark the end of this call on ls (busy
+    // tracking), taken before anything is enqueued: a call that cannot
+    // track its work leaves none in flight
+    hipEvent_t *last = last_event(p, ls, !noalloc);
+    if (!last)
+        return noalloc ? DDL_E_NOMEM : DDL_E_HIP;
     if (any_event && hipEventRecord(p->call_ev, cs) != hipSuccess)
         return DDL_E_HIP;
 
@@ -1026,9 +1032,6 @@ int execute_locked(ddl_plan p, void *const *bufs, void *const *ready, void *stre
     }
     if (done_event && hipEventRecord(static_cast<hipEvent_t>(done_event), ls) != hipSuccess)
         return DDL_E_HIP;
-    hipEvent_t *last = last_event(p, ls, !noalloc);
-    if (!last)
-        return noalloc ? DDL_E_NOMEM : DDL_E_HIP;
     if (hipEventRecord(*last, ls) != hipSuccess)
         return DDL_E_HIP;
     p->in_flight = true;

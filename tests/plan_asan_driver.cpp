@@ -233,6 +233,46 @@ static void captured_plans_stay_cached() {
         std::free(b);
 }
 
+// The allocation-free call on more new streams than the plan has spare
+// tracking events for: once they are used up it reports DDL_E_NOMEM before
+// enqueuing anything, so that no work it cannot track is left in flight.
+static void noalloc_out_of_tracking_events() {
+    ddl_topo ring = {DDL_RING, 1, 0, 0, nullptr};
+    const int P = 4;
+    const size_t n = 8192;
+    std::vector<void *> bufs(P), w(P);
+    for (int r = 0; r < P; ++r) {
+        bufs[r] = std::aligned_alloc(16, n * 4);
+        w[r] = std::aligned_alloc(16, n * 4);
+    }
+    hipStream_t s0;
+    (void)hipStreamCreateWithFlags(&s0, 0);
+    ddl_plan plan = nullptr;
+    check(ddl_plan_create(&plan, P, n, DDL_F32, DDL_SUM, &ring, nullptr, 0, DDL_FUSED), "create");
+    check(ddl_plan_execute(plan, bufs.data(), nullptr, s0, nullptr), "binding call");
+    std::vector<hipStream_t> streams;
+    int rc = DDL_OK;
+    for (int i = 0; i < 64 && rc == DDL_OK; ++i) {
+        hipStream_t si;
+        (void)hipStreamCreateWithFlags(&si, 0);
+        streams.push_back(si);
+        const long k0 = g_launches;
+        rc = ddl_plan_execute_lars_noalloc(plan, bufs.data(), w.data(), P, 0.1f, 0.01, 1e-6,
+                                           nullptr, nullptr, si, nullptr);
+        if (rc != DDL_OK && g_launches != k0)
+            fail("an allocation-free call without a tracking event launched kernels");
+    }
+    expect(rc, DDL_E_NOMEM, "allocation-free call once the spare tracking events are used");
+    check(ddl_plan_destroy(plan), "destroy");
+    for (hipStream_t si : streams)
+        (void)hipStreamDestroy(si);
+    (void)hipStreamDestroy(s0);
+    for (int r = 0; r < P; ++r) {
+        std::free(bufs[r]);
+        std::free(w[r]);
+    }
+}
+
 int main(int argc, char **argv) {
     const int ncases = argc > 1 ? std::atoi(argv[1]) : 200;
     std::mt19937_64 rng(12345);
@@ -377,6 +417,7 @@ int main(int argc, char **argv) {
     }
     check(ddl_cache_clear(), "cache clear");
     stale_handles();
+    noalloc_out_of_tracking_events();
     event_groups_match();
     if (g_live_allocs || g_live_streams || g_live_events)
         std::printf("FAILED: leaked %ld allocations, %ld streams, %ld events\n", g_live_allocs,
